@@ -1,0 +1,404 @@
+/*
+ * svd_oracle.c -- plain double-precision CPU oracle (see svd_oracle.h).
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark, never by the library.
+ *
+ * Build: gcc -O2 -std=c99 -fPIC -shared -ffp-contract=off -fno-fast-math
+ *        svd_oracle.c -o liboracle.so -lm -lpthread
+ * (no contraction and no fast-math, so every operation rounds as written.)
+ */
+#include "svd_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Counter-based uniforms.  The SplitMix64 output function is taken from its
+ * published definition (Steele, Lea and Flood, "Fast splittable pseudorandom
+ * number generators", OOPSLA 2014; Vigna's splitmix64 reference code): add the
+ * golden-ratio increment, then two xor-shift-multiply rounds and a final
+ * xor-shift.  One uniform per (seed, prefix row, position, purpose) stands in
+ * for the per-test uniform draw of SpecDiff-2 appendix B.4. */
+
+uint64_t svdo_splitmix64(uint64_t x)
+{
+  uint64_t z = x + 0x9E3779B97F4A7C15ULL;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+uint64_t svdo_key(uint64_t seed, uint64_t row, uint64_t pos, uint64_t purpose)
+{
+  uint64_t h = svdo_splitmix64(seed);
+  h = svdo_splitmix64(h ^ row);
+  h = svdo_splitmix64(h ^ pos);
+  h = svdo_splitmix64(h ^ purpose);
+  return h;
+}
+
+double svdo_uniform(uint64_t seed, uint64_t row, uint64_t pos, uint64_t purpose)
+{
+  uint64_t k = svdo_key(seed, row, pos, purpose);
+  return (double)(k >> 11) * 0x1.0p-53;
+}
+
+enum { PURPOSE_ACCEPT = 1, PURPOSE_RESIDUAL = 2, PURPOSE_BONUS = 3 };
+
+/* ------------------------------------------------------------------------ */
+/* Logit widening: fp32 widens exactly to double; a bf16 value is the upper
+ * half of an fp32 bit pattern, so it also widens exactly. */
+
+static double logit_at(const void *row, int dtype, int64_t v)
+{
+  if (dtype == SVDO_F32) return (double)((const float *)row)[v];
+  uint32_t bits = (uint32_t)((const uint16_t *)row)[v] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static size_t elem_size(int dtype) { return dtype == SVDO_F32 ? 4 : 2; }
+
+/* Softmax of one row at temperature T (SpecDiff-2 section 2: next-token
+ * posteriors).  s_v = z_v / T (correctly rounded division of exact widenings),
+ * m = max s, w_v = exp(s_v - m), S = sum w_v in index order, p_v = w_v / S.
+ * Also returns m and S so that log p_v = (s_v - m) - log S is available. */
+static int softmax_full(const void *row, int dtype, int32_t V, float T, double *prob,
+                        double *m_out, double *S_out)
+{
+  const double Td = (double)T;
+  double m = -INFINITY;
+  int valid = 1;
+  for (int32_t v = 0; v < V; ++v) {
+    double z = logit_at(row, dtype, v);
+    if (isnan(z) || z == INFINITY) valid = 0;
+    double s = z / Td;
+    prob[v] = s;
+    if (s > m) m = s;
+  }
+  if (!valid || m == -INFINITY) return 0;
+  double S = 0.0;
+  for (int32_t v = 0; v < V; ++v) {
+    double w = exp(prob[v] - m);
+    prob[v] = w;
+    S += w;
+  }
+  for (int32_t v = 0; v < V; ++v) prob[v] = prob[v] / S;
+  if (m_out) *m_out = m;
+  if (S_out) *S_out = S;
+  return 1;
+}
+
+int svdo_softmax_row(const void *row, int dtype, int32_t V, float T, double *prob)
+{
+  return softmax_full(row, dtype, V, T, prob, NULL, NULL);
+}
+
+/* log p_x from the row's (m, S): (z_x / T - m) - log S. */
+static double log_prob_at(const void *row, int dtype, float T, int32_t x, double m, double S)
+{
+  double s = logit_at(row, dtype, x) / (double)T;
+  return (s - m) - log(S);
+}
+
+/* ------------------------------------------------------------------------ */
+/* The draw (SpecDiff-2 section 2; DiffuSpec section 3): on a rejection the
+ * replacement comes from the normalised residual max(0, p - q); after a fully
+ * accepted window the bonus token comes from p.  Inverse CDF: the first token
+ * whose running sum exceeds t = u * Z, so tokens of zero mass are never drawn. */
+
+double svdo_draw_weights(const double *p, const double *q, int32_t V, double *r)
+{
+  double Z = 0.0;
+  if (q) {
+    for (int32_t v = 0; v < V; ++v) {
+      double d = p[v] - q[v];
+      r[v] = d > 0.0 ? d : 0.0;
+      Z += r[v];
+    }
+    if (Z > 0.0) return Z;
+  }
+  /* bonus draw, or a residual without mass (p equals q numerically): draw from p */
+  Z = 0.0;
+  for (int32_t v = 0; v < V; ++v) {
+    r[v] = p[v];
+    Z += r[v];
+  }
+  return Z;
+}
+
+int32_t svdo_inverse_cdf(const double *r, int32_t V, double t, double *c_lo, double *c_hi)
+{
+  double C = 0.0;
+  for (int32_t v = 0; v < V; ++v) {
+    double before = C;
+    C += r[v];
+    if (C > t) {
+      if (c_lo) *c_lo = before;
+      if (c_hi) *c_hi = C;
+      return v;
+    }
+  }
+  /* t at or beyond the total through rounding: the last token with mass */
+  for (int32_t v = V - 1; v >= 0; --v) {
+    if (r[v] > 0.0) {
+      if (c_lo) *c_lo = t;
+      if (c_hi) *c_hi = t;
+      return v;
+    }
+  }
+  return -1;
+}
+
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const void *p, *q;
+  const int32_t *drafts;
+  int dtype;
+  int64_t B;
+  int32_t K, gamma, V;
+  float tp, tq;
+  uint64_t seed, row_base;
+  const int32_t *force_k, *force_L;
+  int32_t *selected, *accept_len, *next_token;
+  double *scores, *alpha, *beta, *px, *qx, *accept_margin;
+  svdo_diag_t *diag;
+  int nthreads, tid;
+  int status;
+} job_t;
+
+static const void *p_row(const job_t *J, int64_t b, int32_t k, int32_t j)
+{
+  size_t idx = (((size_t)b * J->K + k) * (size_t)(J->gamma + 1) + j) * (size_t)J->V;
+  return (const char *)J->p + idx * elem_size(J->dtype);
+}
+
+static const void *q_row(const job_t *J, int64_t b, int32_t k, int32_t j)
+{
+  size_t idx = (((size_t)b * J->K + k) * (size_t)J->gamma + j) * (size_t)J->V;
+  return (const char *)J->q + idx * elem_size(J->dtype);
+}
+
+static void mark_invalid(const job_t *J, int64_t b)
+{
+  J->selected[b] = -1;
+  J->accept_len[b] = -1;
+  J->next_token[b] = -1;
+}
+
+/* One prefix, steps in the order the pages give them. */
+static int do_prefix(const job_t *J, int64_t b, double *P, double *Q, double *R, double *a_buf,
+                     double *s_buf)
+{
+  const int32_t K = J->K, G = J->gamma, V = J->V;
+  const uint64_t row = J->row_base + (uint64_t)b;
+  int valid = 1;
+
+  /* drafted tokens must index the vocabulary */
+  for (int32_t k = 0; k < K; ++k)
+    for (int32_t j = 0; j < G; ++j) {
+      int32_t x = J->drafts[((size_t)b * K + k) * G + j];
+      if (x < 0 || x >= V) valid = 0;
+    }
+
+  /* 1-2. softmax of every scored row pair and the acceptance alpha_{k,j} */
+  for (int32_t k = 0; k < K && valid; ++k) {
+    for (int32_t j = 0; j < G && valid; ++j) {
+      const void *pr = p_row(J, b, k, j), *qr = q_row(J, b, k, j);
+      double mp, Sp, mq, Sq;
+      if (!softmax_full(pr, J->dtype, V, J->tp, P, &mp, &Sp) ||
+          !softmax_full(qr, J->dtype, V, J->tq, Q, &mq, &Sq)) {
+        valid = 0;
+        break;
+      }
+      int32_t x = J->drafts[((size_t)b * K + k) * G + j];
+      /* alpha = 1 when q(x) <= p(x), else p(x)/q(x); compared through log
+       * probabilities so that it stays defined when both underflow */
+      double lp = log_prob_at(pr, J->dtype, J->tp, x, mp, Sp);
+      double lq = log_prob_at(qr, J->dtype, J->tq, x, mq, Sq);
+      double a = (lq <= lp) ? 1.0 : exp(lp - lq);
+      size_t o = ((size_t)b * K + k) * G + j;
+      a_buf[(size_t)k * G + j] = a;
+      if (J->alpha) J->alpha[o] = a;
+      if (J->px) J->px[o] = P[x];
+      if (J->qx) J->qx[o] = Q[x];
+      if (J->beta) {
+        /* 3. overlap mass sum_v min(p_v, q_v) */
+        double s = 0.0;
+        for (int32_t v = 0; v < V; ++v) s += (P[v] < Q[v]) ? P[v] : Q[v];
+        J->beta[o] = s;
+      }
+    }
+  }
+  if (!valid) {
+    mark_invalid(J, b);
+    return 0;
+  }
+
+  /* 4. expected accepted streak of every draft: sum_j prod_{i<=j} alpha_i */
+  for (int32_t k = 0; k < K; ++k) {
+    double prod = 1.0, S = 0.0;
+    for (int32_t j = 0; j < G; ++j) {
+      prod *= a_buf[(size_t)k * G + j];
+      S += prod;
+    }
+    s_buf[k] = S;
+    if (J->scores) J->scores[(size_t)b * K + k] = S;
+  }
+
+  /* 5. self-selection: argmax, the lowest k on an exact tie */
+  int32_t ks = 0;
+  for (int32_t k = 1; k < K; ++k)
+    if (s_buf[k] > s_buf[ks]) ks = k;
+  double second = -INFINITY;
+  for (int32_t k = 0; k < K; ++k)
+    if (k != ks && s_buf[k] > second) second = s_buf[k];
+  if (J->force_k && J->force_k[b] >= 0) {
+    if (J->force_k[b] >= K) return -1;
+    ks = J->force_k[b];
+  }
+
+  /* 6. left-to-right acceptance: accept position j iff u_j < alpha_{k*,j} */
+  int32_t L = G;
+  for (int32_t j = 0; j < G; ++j) {
+    double u = svdo_uniform(J->seed, row, (uint64_t)j, PURPOSE_ACCEPT);
+    double a = a_buf[(size_t)ks * G + j];
+    if (J->accept_margin) J->accept_margin[(size_t)b * G + j] = fabs(u - a);
+    if (!(u < a) && L == G) L = j;
+  }
+  if (J->force_L && J->force_L[b] >= 0) {
+    if (J->force_L[b] > G) return -1;
+    L = J->force_L[b];
+  }
+
+  /* 7-8. residual draw at the first rejection, or bonus draw after gamma accepts */
+  double Z, u;
+  if (L < G) {
+    softmax_full(p_row(J, b, ks, L), J->dtype, V, J->tp, P, NULL, NULL);
+    softmax_full(q_row(J, b, ks, L), J->dtype, V, J->tq, Q, NULL, NULL);
+    Z = svdo_draw_weights(P, Q, V, R);
+    u = svdo_uniform(J->seed, row, (uint64_t)L, PURPOSE_RESIDUAL);
+  } else {
+    if (!softmax_full(p_row(J, b, ks, G), J->dtype, V, J->tp, P, NULL, NULL)) {
+      mark_invalid(J, b);
+      return 0;
+    }
+    Z = svdo_draw_weights(P, NULL, V, R);
+    u = svdo_uniform(J->seed, row, (uint64_t)G, PURPOSE_BONUS);
+  }
+  double t = u * Z, lo = 0.0, hi = 0.0;
+  int32_t tok = svdo_inverse_cdf(R, V, t, &lo, &hi);
+
+  /* 9. outputs */
+  J->selected[b] = ks;
+  J->accept_len[b] = L;
+  J->next_token[b] = tok;
+  if (J->diag) {
+    svdo_diag_t *d = &J->diag[b];
+    d->select_gap = (K > 1) ? s_buf[ks] - second : INFINITY;
+    double m1 = t - lo, m2 = hi - t;
+    d->emit_margin = (m1 < m2 ? m1 : m2) / Z;
+    d->draw_z = Z;
+    d->draw_t = t;
+  }
+  return 0;
+}
+
+static void *worker(void *arg)
+{
+  job_t *J = (job_t *)arg;
+  double *P = (double *)malloc(sizeof(double) * (size_t)J->V);
+  double *Q = (double *)malloc(sizeof(double) * (size_t)J->V);
+  double *R = (double *)malloc(sizeof(double) * (size_t)J->V);
+  double *A = (double *)malloc(sizeof(double) * (size_t)J->K * (size_t)J->gamma);
+  double *S = (double *)malloc(sizeof(double) * (size_t)J->K);
+  if (!P || !Q || !R || !A || !S) {
+    J->status = -1;
+  } else {
+    for (int64_t b = J->tid; b < J->B; b += J->nthreads)
+      if (do_prefix(J, b, P, Q, R, A, S) != 0) J->status = -1;
+  }
+  free(P);
+  free(Q);
+  free(R);
+  free(A);
+  free(S);
+  return NULL;
+}
+
+int svdo_select_and_verify(const void *p_logits, const void *q_logits, const int32_t *drafts,
+                           int dtype, int64_t B, int32_t K, int32_t gamma, int32_t V,
+                           float temp_p, float temp_q, uint64_t seed, uint64_t row_base,
+                           const int32_t *force_k, const int32_t *force_L,
+                           int32_t *selected, int32_t *accept_len, int32_t *next_token,
+                           double *scores, double *alpha, double *beta, double *px, double *qx,
+                           double *accept_margin, svdo_diag_t *diag, int nthreads)
+{
+  if (!p_logits || !q_logits || !drafts || !selected || !accept_len || !next_token) return -1;
+  if (dtype != SVDO_F32 && dtype != SVDO_BF16) return -1;
+  if (B < 1 || K < 1 || gamma < 1 || V < 1) return -1;
+  if (!(temp_p > 0.0f) || !(temp_q > 0.0f) || isinf(temp_p) || isinf(temp_q)) return -1;
+  if (nthreads < 1) nthreads = 1;
+  if ((int64_t)nthreads > B) nthreads = (int)B;
+
+  job_t base;
+  memset(&base, 0, sizeof base);
+  base.p = p_logits;
+  base.q = q_logits;
+  base.drafts = drafts;
+  base.dtype = dtype;
+  base.B = B;
+  base.K = K;
+  base.gamma = gamma;
+  base.V = V;
+  base.tp = temp_p;
+  base.tq = temp_q;
+  base.seed = seed;
+  base.row_base = row_base;
+  base.force_k = force_k;
+  base.force_L = force_L;
+  base.selected = selected;
+  base.accept_len = accept_len;
+  base.next_token = next_token;
+  base.scores = scores;
+  base.alpha = alpha;
+  base.beta = beta;
+  base.px = px;
+  base.qx = qx;
+  base.accept_margin = accept_margin;
+  base.diag = diag;
+  base.nthreads = nthreads;
+
+  job_t *jobs = (job_t *)malloc(sizeof(job_t) * (size_t)nthreads);
+  pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  if (!jobs || !th) {
+    free(jobs);
+    free(th);
+    return -1;
+  }
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = base;
+    jobs[i].tid = i;
+  }
+  int started = 0;
+  for (int i = 1; i < nthreads; ++i) {
+    if (pthread_create(&th[i], NULL, worker, &jobs[i]) != 0) break;
+    started = i;
+  }
+  worker(&jobs[0]);
+  for (int i = 1; i <= started; ++i) pthread_join(th[i], NULL);
+  /* prefixes of threads that failed to start run here */
+  for (int i = started + 1; i < nthreads; ++i) worker(&jobs[i]);
+
+  int status = 0;
+  for (int i = 0; i < nthreads; ++i)
+    if (jobs[i].status != 0) status = -1;
+  free(jobs);
+  free(th);
+  return status;
+}

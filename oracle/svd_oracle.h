@@ -1,0 +1,100 @@
+/*
+ * svd_oracle.h -- plain double-precision CPU oracle for lossless draft
+ * verification with self-selection.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This oracle exists to check the GPU library.
+ * Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load it.  It shares no source, header, table or helper with
+ * the HIP library, and the library never calls it.
+ *
+ * What it computes (sources are the SpecDiff-2 and DiffuSpec pages):
+ *   - softmax of every verifier row p(.|s,x_<j) and drafter row q(.|s,x_<j)
+ *     (SpecDiff-2, section 2 "Prelim: speculative decoding": both models expose
+ *     next-token posteriors; the verifier scores all positions in parallel);
+ *   - the position-wise acceptance alpha_j = min(1, p(x_j)/q(x_j)), written as
+ *     "accept at once when q <= p" (SpecDiff-2 section 2);
+ *   - the expected accepted streak sum_j prod_{i<=j} alpha_i of every draft
+ *     (SpecDiff-2 section 3 and Figure 2: alpha_j is the chance that token j is
+ *     accepted once the first j-1 were) and the argmax draft (SpecDiff-2
+ *     section 5.2, self-selection: keep the draft of greatest expected
+ *     throughput);
+ *   - left-to-right acceptance against counter-hash uniforms, stopping at the
+ *     first rejection (SpecDiff-2 section 2; DiffuSpec section 3 "Acceptance
+ *     and rejection");
+ *   - the replacement token from the normalised residual max(0, p - q)
+ *     (same passages), or a bonus token from verifier row gamma when every
+ *     drafted token is accepted.
+ *
+ * Every logit is widened exactly to double, every step runs in double, and
+ * every sum runs sequentially in vocabulary order.
+ */
+#ifndef SVD_ORACLE_H
+#define SVD_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of the logit arrays */
+enum { SVDO_F32 = 0, SVDO_BF16 = 1 };
+
+/* SplitMix64 output function (Steele, Lea and Flood, OOPSLA 2014). */
+uint64_t svdo_splitmix64(uint64_t x);
+/* KEY = SM64(SM64(SM64(SM64(seed) ^ row) ^ pos) ^ purpose) */
+uint64_t svdo_key(uint64_t seed, uint64_t row, uint64_t pos, uint64_t purpose);
+/* U = (KEY >> 11) * 2^-53, a double in [0, 1) */
+double svdo_uniform(uint64_t seed, uint64_t row, uint64_t pos, uint64_t purpose);
+
+/* Softmax of one row at temperature T.  prob[v] = exp(z_v/T - m) / S.
+ * Returns 1 for a valid row, 0 when the row holds a NaN or +inf, or is all
+ * -inf (prob is then left unspecified). */
+int svdo_softmax_row(const void *row, int dtype, int32_t V, float T, double *prob);
+
+/* Inverse CDF over non-negative weights r[0..V): the first v whose running sum
+ * (sequential, index order) exceeds t; if none does, the last v with r_v > 0;
+ * -1 if every weight is zero.  *c_lo and *c_hi (nullable) receive the running
+ * sum just before and just after the chosen index. */
+int32_t svdo_inverse_cdf(const double *r, int32_t V, double t, double *c_lo, double *c_hi);
+
+/* The distribution a draw is taken from, written into r[0..V): the residual
+ * max(0, p - q) for a rejection, or p itself when q is NULL (the bonus draw)
+ * or when the residual has no mass.  Returns Z = sum of r (sequential). */
+double svdo_draw_weights(const double *p, const double *q, int32_t V, double *r);
+
+/* Per-prefix diagnostics used by the parity harness to recognise near-ties. */
+typedef struct {
+  double select_gap;   /* S_best - S_second (+inf when K == 1)                    */
+  double emit_margin;  /* min(t - C_lo, C_hi - t) / Z at the emitted token         */
+  double draw_z;       /* Z of the draw                                             */
+  double draw_t;       /* t = u * Z                                                 */
+} svdo_diag_t;
+
+/*
+ * Full verification of B prefixes.
+ *   p_logits [B][K][gamma+1][V], q_logits [B][K][gamma][V], drafts [B][K][gamma].
+ *   force_k / force_L (nullable, per prefix, -1 = not forced) pin the selected
+ *   draft and / or the accepted length, so that a harness can re-run the later
+ *   steps conditioned on another implementation's earlier decision.
+ * Outputs (all nullable except selected, accept_len, next_token):
+ *   scores [B][K]; alpha, beta, px, qx [B][K][gamma];
+ *   accept_margin [B][gamma] = |u_j - alpha_{k*,j}| for every j;
+ *   diag [B].
+ * A prefix whose inputs are invalid gets -1 in selected, accept_len, next_token.
+ * nthreads >= 1 worker threads split the prefixes.  Returns 0, or -1 on bad
+ * arguments.
+ */
+int svdo_select_and_verify(const void *p_logits, const void *q_logits, const int32_t *drafts,
+                           int dtype, int64_t B, int32_t K, int32_t gamma, int32_t V,
+                           float temp_p, float temp_q, uint64_t seed, uint64_t row_base,
+                           const int32_t *force_k, const int32_t *force_L,
+                           int32_t *selected, int32_t *accept_len, int32_t *next_token,
+                           double *scores, double *alpha, double *beta, double *px, double *qx,
+                           double *accept_margin, svdo_diag_t *diag, int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVD_ORACLE_H */

@@ -1,0 +1,99 @@
+"""Seeded synthetic logits and drafts.
+
+Recipe (per prefix b, with its own generator seeded from (data_seed, b)):
+  * verifier logits z_p ~ N(0, 2^2), i.i.d. over the vocabulary, for all K
+    drafts and gamma+1 rows; every row gets a mode token m ~ U{0..V-1} whose
+    logit is raised by `boost` (on a `boost_prob` share of rows);
+  * row 0 of p is shared by the K drafts of a prefix: all drafts start from the
+    same prefix s, so the verifier's first posterior is the same;
+  * drafter logits z_q = z_p + sigma_j * N(0, 1) for rows j < gamma, independent
+    per draft and row;
+  * bf16 workloads round the fp32 values to nearest-even;
+  * drafted tokens x_j are sampled from softmax(z_q_j / T) of the rounded logits
+    with the Gumbel-max trick: argmax_v (z_q_jv / T + G_v), G_v i.i.d. Gumbel.
+
+Nothing here evaluates the verification rule; the draft sampler stands in for
+the diffusion drafter.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .configs import Config
+
+
+def _gen(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed & 0x7FFFFFFFFFFFFFFF)
+    return g
+
+
+def _gumbel_argmax(z: torch.Tensor, temp: float, g: torch.Generator) -> torch.Tensor:
+    u = torch.rand(z.shape, generator=g, device=z.device, dtype=torch.float32)
+    gumbel = -torch.log(-torch.log(u))
+    return torch.argmax(z.float() / temp + gumbel, dim=-1).to(torch.int32)
+
+
+def _one_prefix(cfg: Config, b: int, data_seed: int, device, K: int, G: int, V: int,
+                tdtype: torch.dtype):
+    g = _gen(device, data_seed * 1_000_003 + b)
+    zp = torch.randn((K, G + 1, V), generator=g, device=device, dtype=torch.float32) * 2.0
+    mode = torch.randint(0, V, (K, G + 1, 1), generator=g, device=device)
+    hit = torch.rand((K, G + 1, 1), generator=g, device=device) < cfg.boost_prob
+    zp.scatter_add_(-1, mode, hit.float() * cfg.boost)
+    zp[1:, 0, :] = zp[0, 0, :]
+    sig = cfg.sigma0 + cfg.sigma_step * torch.arange(G, device=device, dtype=torch.float32)
+    zq = zp[:, :G, :] + sig.view(1, G, 1) * torch.randn((K, G, V), generator=g, device=device)
+    zp = zp.to(tdtype)
+    zq = zq.to(tdtype)
+    drafts = _gumbel_argmax(zq, cfg.temp, g)
+    return zp, zq, drafts
+
+
+def generate(cfg: Config, device="cpu", B: int | None = None, data_seed: int | None = None,
+             V: int | None = None, K: int | None = None, gamma: int | None = None,
+             dtype: str | None = None):
+    """Logits and drafts for a workload: dict(p [B,K,G+1,V], q [B,K,G,V], drafts [B,K,G]).
+
+    Overrides (B, V, K, gamma, dtype) give smaller or ragged variants of a workload
+    for parity tests.
+    """
+    B = cfg.B if B is None else B
+    V = cfg.V if V is None else V
+    K = cfg.K if K is None else K
+    G = cfg.gamma if gamma is None else gamma
+    dt = cfg.dtype if dtype is None else dtype
+    ds = cfg.data_seed if data_seed is None else data_seed
+    tdtype = torch.float32 if dt == "f32" else torch.bfloat16
+    p = torch.empty((B, K, G + 1, V), dtype=tdtype, device=device)
+    q = torch.empty((B, K, G, V), dtype=tdtype, device=device)
+    d = torch.empty((B, K, G), dtype=torch.int32, device=device)
+    for b in range(B):
+        zp, zq, dr = _one_prefix(cfg, b, ds, device, K, G, V, tdtype)
+        p[b].copy_(zp)
+        q[b].copy_(zq)
+        d[b].copy_(dr)
+    return {"p": p, "q": q, "drafts": d, "temp": cfg.temp, "dtype": dt}
+
+
+def tiny_trial_drafts(q_logits: torch.Tensor, n: int, temp: float, seed: int) -> torch.Tensor:
+    """n independent draft sets for one logit instance: [n, K, gamma] int32.
+
+    q_logits is [1, K, gamma, V]; every trial samples fresh tokens from it.
+    """
+    g = _gen(q_logits.device, seed)
+    z = q_logits[0].float().unsqueeze(0).expand(n, *q_logits.shape[1:])
+    return _gumbel_argmax(z, temp, g)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    """Host copy for the oracle: float32 stays float32, bf16 becomes its uint16 bit pattern."""
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    if t.dtype == torch.int32:
+        return t.numpy()
+    raise TypeError(t.dtype)
