@@ -1,0 +1,160 @@
+/*
+ * svd.h -- C ABI of the MI355X (gfx950) library for lossless draft
+ * verification with self-selection.
+ *
+ * The operation.  For each prefix s, K drafts of gamma tokens arrive with the
+ * drafter's next-token logits q and the verifier's logits p over a vocabulary
+ * of V tokens.  The verifier has scored every drafted position in one
+ * parallel pass (SpecDiff-2, section 2 "Prelim: speculative decoding").  The
+ * library
+ *   1. takes the softmax of every verifier row and drafter row it needs, at
+ *      temperatures temp_p and temp_q;
+ *   2. computes the position-wise acceptance alpha_j = min(1, p(x_j)/q(x_j)),
+ *      i.e. accept at once whenever q(x_j) <= p(x_j) (SpecDiff-2 section 2;
+ *      the position-wise acceptance of SpecDiff-2 Figure 2);
+ *   3. scores every draft by its expected accepted streak
+ *      S_k = sum_{j<gamma} prod_{i<=j} alpha_{k,i} (SpecDiff-2 section 3) and
+ *      keeps the argmax draft, the lowest k on an exact tie (SpecDiff-2
+ *      section 5.2, self-selection by expected throughput);
+ *   4. accepts the kept draft left to right while u_j < alpha_j and stops at
+ *      the first rejection (SpecDiff-2 section 2; DiffuSpec section 3
+ *      "Acceptance and rejection");
+ *   5. draws the replacement token from the normalised residual max(0, p - q)
+ *      of the rejected position (same passages), or, when all gamma tokens
+ *      are accepted, a bonus token from the verifier's row gamma.
+ * The committed tokens are the accepted prefix of the kept draft followed by
+ * the drawn token (DiffuSpec section 3, "Accepted prefix length").
+ *
+ * Uniforms.  u = U(seed, row_base + b, position, purpose) with purpose 1 for
+ * acceptance tests, 2 for the residual draw (position = accepted length L) and
+ * 3 for the bonus draw (position = gamma).  U is the top 53 bits of
+ *   KEY = SM64(SM64(SM64(SM64(seed) ^ row) ^ pos) ^ purpose)
+ * times 2^-53, with SM64 the SplitMix64 output function (Steele, Lea and
+ * Flood, OOPSLA 2014).  Outputs are a pure function of the inputs, seed and
+ * row_base; a draw takes the first token whose cumulative weight exceeds u*Z.
+ *
+ * Precision.  Row statistics and alpha are computed in fp32 from exact
+ * widenings of the logits; streak scores accumulate in fp64; the row pair of
+ * the draw is recomputed from the logits in fp64.
+ *
+ * Conventions for every entry point:
+ *   - Pointers to logits, drafts, outputs and the workspace are DEVICE
+ *     pointers, owned by the caller; the library keeps none of them after the
+ *     call returns.  Arrays are row-major and contiguous with V innermost.
+ *   - Work is enqueued on hip_stream (a hipStream_t; NULL = the null stream)
+ *     after the work already on it.  Nothing synchronises the host, nothing
+ *     allocates device memory.  Results are valid once the stream reaches
+ *     them.  Calls on different streams with different workspaces may run
+ *     concurrently; calls that share a workspace must be ordered.
+ *   - The return code reports only what the host can check: SVD_EINVAL for a
+ *     NULL required pointer, a size below 1 or above the limits below, or a
+ *     temperature that is not finite and positive; SVD_EDTYPE for an unknown
+ *     dtype; SVD_EWORKSPACE for a workspace below svd_workspace_bytes();
+ *     SVD_EHIP when a kernel launch fails.  Nothing is enqueued when the
+ *     return code is not SVD_OK.
+ *   - Errors in the data go to the outputs: a drafted token outside [0, V),
+ *     or a NaN or +inf logit, or an all -inf row, among the rows a prefix
+ *     reads, sets that prefix's selected / accept_len / next_token to -1
+ *     (alpha, beta and scores of that prefix are then unspecified).  -inf
+ *     logits are legal and mean probability 0.
+ */
+#ifndef SVD_H
+#define SVD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of both logit arrays (p and q share one) */
+typedef enum { SVD_F32 = 0, SVD_BF16 = 1 } svd_dtype_t;
+
+enum {
+  SVD_OK = 0,
+  SVD_EINVAL = -1,
+  SVD_EDTYPE = -2,
+  SVD_EWORKSPACE = -3,
+  SVD_EHIP = -4
+};
+
+/* Documented limits. */
+#define SVD_MAX_K 64            /* drafts per prefix                      */
+#define SVD_MAX_GAMMA 4096      /* drafted positions per draft            */
+/* B * K * gamma must stay below 2^31; V below 2^31. */
+
+/*
+ * Bytes of device workspace one call with these sizes needs (256-byte
+ * aligned start is required).  Returns 0 for sizes the calls would reject.
+ */
+size_t svd_workspace_bytes(int64_t B, int32_t K, int32_t gamma, int32_t V);
+
+/*
+ * Single-draft verification: svd_select_and_verify with K = 1, bit for bit.
+ *   p_logits   [B][gamma+1][V]  verifier logits; row j is p(.|s, x_<j), row
+ *                               gamma is the bonus row p(.|s, x_<gamma)
+ *   q_logits   [B][gamma][V]    drafter logits; row j is q(.|s, x_<j)
+ *   draft      [B][gamma] int32 drafted tokens x_j
+ *   accept_len [B] out          L in [0, gamma], or -1
+ *   next_token [B] out          residual token (L < gamma) or bonus token
+ *                               (L == gamma), or -1
+ *   alpha      [B][gamma] out   nullable; fp32 alpha_j
+ *   beta       [B][gamma] out   nullable; fp32 sum_v min(p_v, q_v), the
+ *                               expected acceptance of position j (one
+ *                               extra pass over the scored rows)
+ */
+int svd_verify(const void *p_logits, const void *q_logits, const int32_t *draft,
+               svd_dtype_t dtype, int64_t B, int32_t gamma, int32_t V,
+               float temp_p, float temp_q, uint64_t seed, uint64_t row_base,
+               int32_t *accept_len, int32_t *next_token, float *alpha, float *beta,
+               void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Self-selection and verification of K drafts per prefix.
+ *   p_logits   [B][K][gamma+1][V]
+ *   q_logits   [B][K][gamma][V]
+ *   drafts     [B][K][gamma] int32
+ *   selected   [B] out          kept draft k*, or -1
+ *   accept_len [B] out          L of the kept draft, or -1
+ *   next_token [B] out          the drawn token, or -1
+ *   scores     [B][K] out       nullable; fp32 expected accepted streak S_k
+ *   alpha      [B][K][gamma]    nullable
+ *   beta       [B][K][gamma]    nullable
+ */
+int svd_select_and_verify(const void *p_logits, const void *q_logits, const int32_t *drafts,
+                          svd_dtype_t dtype, int64_t B, int32_t K, int32_t gamma, int32_t V,
+                          float temp_p, float temp_q, uint64_t seed, uint64_t row_base,
+                          int32_t *selected, int32_t *accept_len, int32_t *next_token,
+                          float *scores, float *alpha, float *beta,
+                          void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Static text for a status code. */
+const char *svd_strerror(int status);
+
+/*
+ * Kernel timing for benchmarks and profiling.  While enabled, every call
+ * records HIP events on its stream around each kernel it launches (creating
+ * the events on first use).  svd_profile_read() waits for the recorded
+ * events, adds up the elapsed milliseconds per kernel into ms[0..n) (index:
+ * SVD_KERNEL_*), writes the number of launches per kernel into launches[0..n)
+ * (nullable), clears the record and returns SVD_OK.  Not thread-safe; at most
+ * 4096 calls are recorded between reads (later ones are not timed).
+ */
+enum {
+  SVD_KERNEL_ROWSTATS = 0,   /* row statistics + alpha (streams every scored row pair) */
+  SVD_KERNEL_SELECT = 1,     /* streak scores, argmax, first rejection                 */
+  SVD_KERNEL_DRAW_SUMS = 2,  /* fp64 normalisers of the drawn row pair                 */
+  SVD_KERNEL_DRAW_MASS = 3,  /* fp64 residual mass per vocabulary segment              */
+  SVD_KERNEL_DRAW_PICK = 4,  /* fp64 inverse CDF                                        */
+  SVD_KERNEL_BETA = 5,       /* optional overlap mass                                   */
+  SVD_KERNEL_COUNT = 6
+};
+int svd_profile_enable(int on);
+int svd_profile_read(double *ms, int64_t *launches, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVD_H */

@@ -1,0 +1,223 @@
+"""Lossless draft verification with self-selection on MI355X (gfx950).
+
+Thin ctypes binding over ``libsvd.so`` (C ABI in ``include/svd.h``).  Every step
+of the verification runs in the library's HIP kernels; this module only
+marshals arguments.  PyTorch supplies device memory and the current stream.
+
+Raw entry points (same names and argument order as the C ABI; pointer
+arguments take an int address or a tensor):
+    svd_workspace_bytes, svd_verify, svd_select_and_verify, svd_strerror,
+    svd_profile_enable, svd_profile_read
+Tensor conveniences that allocate the outputs and the workspace with torch:
+    verify, select_and_verify, workspace_bytes
+
+Importing fails with ImportError when ``libsvd.so`` has not been built; there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsvd.so")
+
+SVD_F32, SVD_BF16 = 0, 1
+SVD_OK, SVD_EINVAL, SVD_EDTYPE, SVD_EWORKSPACE, SVD_EHIP = 0, -1, -2, -3, -4
+SVD_MAX_K, SVD_MAX_GAMMA = 64, 4096
+KERNELS = ("rowstats", "select", "draw_sums", "draw_mass", "draw_pick", "beta")
+
+C_EXPORTS = ("svd_workspace_bytes", "svd_verify", "svd_select_and_verify", "svd_strerror",
+             "svd_profile_enable", "svd_profile_read")
+
+
+class SvdError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, svd_strerror(status), status))
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libsvd.so is not built (expected at %s); build it with "
+            "__graft_entry__.build() or python -m lossless_draft_verification_verifier_amd._build"
+            % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t)
+    L.svd_workspace_bytes.restype = sz
+    L.svd_workspace_bytes.argtypes = [i64, i32, i32, i32]
+    L.svd_verify.restype = ctypes.c_int
+    L.svd_verify.argtypes = [vp, vp, vp, ctypes.c_int, i64, i32, i32, f32, f32, u64, u64,
+                             vp, vp, vp, vp, vp, sz, vp]
+    L.svd_select_and_verify.restype = ctypes.c_int
+    L.svd_select_and_verify.argtypes = [vp, vp, vp, ctypes.c_int, i64, i32, i32, i32, f32, f32,
+                                        u64, u64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.svd_strerror.restype = ctypes.c_char_p
+    L.svd_strerror.argtypes = [ctypes.c_int]
+    L.svd_profile_enable.restype = ctypes.c_int
+    L.svd_profile_enable.argtypes = [ctypes.c_int]
+    L.svd_profile_read.restype = ctypes.c_int
+    L.svd_profile_read.argtypes = [vp, vp, ctypes.c_int]
+    return L
+
+
+_lib = _load()
+_M64 = 0xFFFFFFFFFFFFFFFF
+
+
+def _addr(x):
+    """Device address of a tensor, an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+# --------------------------------------------------------------------------
+# Raw C ABI (argument marshalling only)
+
+def svd_workspace_bytes(B: int, K: int, gamma: int, V: int) -> int:
+    return int(_lib.svd_workspace_bytes(B, K, gamma, V))
+
+
+def svd_verify(p_logits, q_logits, draft, dtype, B, gamma, V, temp_p, temp_q, seed, row_base,
+               accept_len, next_token, alpha, beta, workspace, workspace_bytes, hip_stream) -> int:
+    return int(_lib.svd_verify(
+        _addr(p_logits), _addr(q_logits), _addr(draft), int(dtype), int(B), int(gamma), int(V),
+        float(temp_p), float(temp_q), int(seed) & _M64, int(row_base) & _M64, _addr(accept_len),
+        _addr(next_token), _addr(alpha), _addr(beta), _addr(workspace), int(workspace_bytes),
+        _addr(hip_stream)))
+
+
+def svd_select_and_verify(p_logits, q_logits, drafts, dtype, B, K, gamma, V, temp_p, temp_q,
+                          seed, row_base, selected, accept_len, next_token, scores, alpha, beta,
+                          workspace, workspace_bytes, hip_stream) -> int:
+    return int(_lib.svd_select_and_verify(
+        _addr(p_logits), _addr(q_logits), _addr(drafts), int(dtype), int(B), int(K), int(gamma),
+        int(V), float(temp_p), float(temp_q), int(seed) & _M64, int(row_base) & _M64,
+        _addr(selected), _addr(accept_len), _addr(next_token), _addr(scores), _addr(alpha),
+        _addr(beta), _addr(workspace), int(workspace_bytes), _addr(hip_stream)))
+
+
+def svd_strerror(status: int) -> str:
+    return _lib.svd_strerror(int(status)).decode()
+
+
+def svd_profile_enable(on: bool) -> int:
+    return int(_lib.svd_profile_enable(1 if on else 0))
+
+
+def svd_profile_read():
+    """(milliseconds per kernel, launches per kernel), indexed like KERNELS."""
+    n = len(KERNELS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    st = _lib.svd_profile_read(ctypes.cast(ms, ctypes.c_void_p), ctypes.cast(cnt, ctypes.c_void_p), n)
+    if st != SVD_OK:
+        raise SvdError(st, "svd_profile_read")
+    return list(ms), list(cnt)
+
+
+# --------------------------------------------------------------------------
+# Tensor conveniences
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SVD_BF16
+    if t.dtype == torch.float32:
+        return SVD_F32
+    raise TypeError("logits must be torch.bfloat16 or torch.float32, got %s" % t.dtype)
+
+
+def _check(t, name, device):
+    if not t.is_cuda or t.device != device:
+        raise ValueError("%s must be on %s" % (name, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def workspace_bytes(B, K, gamma, V) -> int:
+    n = svd_workspace_bytes(B, K, gamma, V)
+    if n == 0:
+        raise ValueError("sizes out of range: B=%d K=%d gamma=%d V=%d" % (B, K, gamma, V))
+    return n
+
+
+def alloc_workspace(B, K, gamma, V, device):
+    import torch
+    n = workspace_bytes(B, K, gamma, V)
+    return torch.empty(n, dtype=torch.uint8, device=device)  # torch allocations are 256-B aligned
+
+
+def select_and_verify(p, q, drafts, temp_p=1.0, temp_q=None, seed=0, row_base=0,
+                      want_alpha=False, want_beta=False, want_scores=False, workspace=None,
+                      stream=None):
+    """p [B,K,gamma+1,V], q [B,K,gamma,V] (bf16 or fp32), drafts [B,K,gamma] int32."""
+    import torch
+    dev = p.device
+    for t, n in ((p, "p"), (q, "q"), (drafts, "drafts")):
+        _check(t, n, dev)
+    if drafts.dtype != torch.int32:
+        raise TypeError("drafts must be int32")
+    if p.dtype != q.dtype:
+        raise TypeError("p and q must share one dtype")
+    if p.dim() != 4 or q.dim() != 4 or drafts.dim() != 3:
+        raise ValueError("expected p [B,K,G+1,V], q [B,K,G,V], drafts [B,K,G]")
+    B, K, G1, V = p.shape
+    G = G1 - 1
+    if tuple(q.shape) != (B, K, G, V) or tuple(drafts.shape) != (B, K, G):
+        raise ValueError("shape mismatch: p %s q %s drafts %s" % (tuple(p.shape), tuple(q.shape),
+                                                                 tuple(drafts.shape)))
+    temp_q = temp_p if temp_q is None else temp_q
+    out = {
+        "selected": torch.empty(B, dtype=torch.int32, device=dev),
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+        "scores": torch.empty((B, K), dtype=torch.float32, device=dev) if want_scores else None,
+        "alpha": torch.empty((B, K, G), dtype=torch.float32, device=dev) if want_alpha else None,
+        "beta": torch.empty((B, K, G), dtype=torch.float32, device=dev) if want_beta else None,
+    }
+    ws = alloc_workspace(B, K, G, V, dev) if workspace is None else workspace
+    st = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    rc = svd_select_and_verify(p, q, drafts, _dtype_code(p), B, K, G, V, temp_p, temp_q, seed,
+                               row_base, out["selected"], out["accept_len"], out["next_token"],
+                               out["scores"], out["alpha"], out["beta"], ws, ws.numel(), st)
+    if rc != SVD_OK:
+        raise SvdError(rc, "svd_select_and_verify")
+    return out
+
+
+def verify(p, q, draft, temp_p=1.0, temp_q=None, seed=0, row_base=0, want_alpha=False,
+           want_beta=False, workspace=None, stream=None):
+    """p [B,gamma+1,V], q [B,gamma,V] (bf16 or fp32), draft [B,gamma] int32."""
+    import torch
+    dev = p.device
+    for t, n in ((p, "p"), (q, "q"), (draft, "draft")):
+        _check(t, n, dev)
+    if draft.dtype != torch.int32:
+        raise TypeError("draft must be int32")
+    if p.dtype != q.dtype:
+        raise TypeError("p and q must share one dtype")
+    B, G1, V = p.shape
+    G = G1 - 1
+    if tuple(q.shape) != (B, G, V) or tuple(draft.shape) != (B, G):
+        raise ValueError("shape mismatch")
+    temp_q = temp_p if temp_q is None else temp_q
+    out = {
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+        "alpha": torch.empty((B, G), dtype=torch.float32, device=dev) if want_alpha else None,
+        "beta": torch.empty((B, G), dtype=torch.float32, device=dev) if want_beta else None,
+    }
+    ws = alloc_workspace(B, 1, G, V, dev) if workspace is None else workspace
+    st = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    rc = svd_verify(p, q, draft, _dtype_code(p), B, G, V, temp_p, temp_q, seed, row_base,
+                    out["accept_len"], out["next_token"], out["alpha"], out["beta"], ws,
+                    ws.numel(), st)
+    if rc != SVD_OK:
+        raise SvdError(rc, "svd_verify")
+    return out

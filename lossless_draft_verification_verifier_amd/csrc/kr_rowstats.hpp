@@ -1,0 +1,123 @@
+// kr_rowstats.hpp -- row statistics and acceptance of every scored row pair.
+//
+// One workgroup per (prefix b, draft k, position j < gamma).  It streams the
+// verifier row p(.|s, x_<j) and the drafter row q(.|s, x_<j) once, keeping an
+// online (max, sum) of exp2((z - max) * log2(e) / T) per thread, merges the
+// threads, and turns the two rows' statistics into
+//   alpha = min(1, p(x_j) / q(x_j))
+// (SpecDiff-2 section 2: accept at once whenever q <= p; Figure 2's
+// position-wise acceptance).  alpha is formed from log2-probabilities so it
+// stays defined when both probabilities are tiny.  Invalid rows or tokens give
+// alpha = NaN, which the selection epilogue turns into -1 outputs.
+//
+// Memory: 16-byte coalesced loads when every row starts 16-byte aligned (the
+// row length in bytes is a multiple of 16), otherwise one element per load.
+#pragma once
+
+#include "svd_device.hpp"
+
+namespace svd {
+
+// Fold one vector of n logits into a thread's (max, sum) state.
+template <int N>
+__device__ inline void ms_fold(float &m, float &s, const float *x, float c) {
+  float vm = x[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) vm = fmaxf(vm, x[i]);
+  const float mn = fmaxf(m, vm);  // fmaxf drops NaN: a NaN logit shows up in the sum
+  s *= (mn == m) ? 1.0f : fast_exp2((m - mn) * c);
+  m = mn;
+  const float mo = fmaxf(m, kLowest);  // keeps (-inf) - (-inf) out of the exponent
+#pragma unroll
+  for (int i = 0; i < N; ++i) s += fast_exp2((x[i] - mo) * c);
+}
+
+constexpr int kRowUnroll = 4;  // 16-byte loads in flight per thread and row
+
+// (max, sum) of one row; result valid in thread 0.
+template <typename E, bool kVec>
+__device__ inline void row_ms(const typename E::elem *row, int V, float c, float &m_out,
+                              float &s_out, float *lds) {
+  float m[kRowUnroll], s[kRowUnroll];
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    m[u] = kNegInf;
+    s[u] = 0.0f;
+  }
+  const int tid = threadIdx.x;
+  if constexpr (kVec) {
+    constexpr int P = E::kPerVec;
+    const vec16 *vrow = reinterpret_cast<const vec16 *>(row);
+    const int nvec = V / P;  // V * sizeof(elem) is a multiple of 16 on this path
+    int i = tid;
+    for (; i + (kRowUnroll - 1) * kBlock < nvec; i += kRowUnroll * kBlock) {
+      vec16 w[kRowUnroll];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) w[u] = __builtin_nontemporal_load(vrow + i + u * kBlock);
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        float x[P];
+        E::unpack(w[u], x);
+        ms_fold<P>(m[u], s[u], x, c);
+      }
+    }
+    for (; i < nvec; i += kBlock) {
+      vec16 w = __builtin_nontemporal_load(vrow + i);
+      float x[P];
+      E::unpack(w, x);
+      ms_fold<P>(m[0], s[0], x, c);
+    }
+  } else {
+    int i = tid;
+    for (; i + (kRowUnroll - 1) * kBlock < V; i += kRowUnroll * kBlock) {
+      float x[kRowUnroll];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) x[u] = E::at(row, i + u * kBlock);
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) ms_fold<1>(m[u], s[u], &x[u], c);
+    }
+    for (; i < V; i += kBlock) {
+      float x = E::at(row, i);
+      ms_fold<1>(m[0], s[0], &x, c);
+    }
+  }
+#pragma unroll
+  for (int u = 1; u < kRowUnroll; ++u) ms_merge(m[0], s[0], m[u], s[u], c);
+  block_ms(m[0], s[0], c, lds);
+  m_out = m[0];
+  s_out = s[0];
+}
+
+template <typename E, bool kVec>
+__global__ __launch_bounds__(kBlock) void kr_rowstats(
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
+    const int32_t *__restrict__ drafts, int gamma, int V, float cp, float cq,
+    RowStats *__restrict__ stats, float *__restrict__ alpha_ws, float *__restrict__ alpha_out) {
+  __shared__ float lds[2 * kWaves];
+  const int64_t rp = blockIdx.x;           // (b * K + k) * gamma + j
+  const int64_t bk = rp / gamma;
+  const int64_t j = rp - bk * gamma;
+  const typename E::elem *prow = p + (bk * (gamma + 1) + j) * (int64_t)V;
+  const typename E::elem *qrow = q + rp * (int64_t)V;
+
+  float mp, sp, mq, sq;
+  row_ms<E, kVec>(prow, V, cp, mp, sp, lds);
+  row_ms<E, kVec>(qrow, V, cq, mq, sq, lds);
+
+  if (threadIdx.x == 0) {
+    const int32_t x = drafts[rp];
+    float a = __builtin_nanf("");
+    const bool rows_ok = !(sp != sp) && !(sq != sq) && mp != kNegInf && mq != kNegInf;
+    if (rows_ok && x >= 0 && x < V) {
+      // log2 p(x) and log2 q(x); accept outright when q(x) <= p(x)
+      const float lp = (E::at(prow, x) - mp) * cp - log2f(sp);
+      const float lq = (E::at(qrow, x) - mq) * cq - log2f(sq);
+      a = (lq <= lp) ? 1.0f : exp2f(lp - lq);
+    }
+    stats[rp] = RowStats{mp, sp, mq, sq};
+    alpha_ws[rp] = a;
+    if (alpha_out) alpha_out[rp] = a;
+  }
+}
+
+}  // namespace svd

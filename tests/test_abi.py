@@ -1,0 +1,108 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/svd.h declares, sizes its workspace, and rejects bad arguments on the
+host before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svd.h")
+
+
+@pytest.fixture(scope="module")
+def svd():
+    lib = os.path.join(ROOT, "lossless_draft_verification_verifier_amd", "libsvd.so")
+    if not os.path.exists(lib):
+        from lossless_draft_verification_verifier_amd import _build
+        _build.build()
+    import lossless_draft_verification_verifier_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(svd_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("svd_verify", "svd_select_and_verify", "svd_workspace_bytes", "svd_strerror"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(svd):
+    lib = ctypes.CDLL(svd.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", svd.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (svd_\w+)", out))
+    assert set(declared_functions()) <= exported
+    assert set(svd.C_EXPORTS) == set(declared_functions())
+
+
+def test_workspace_bytes(svd):
+    a = svd.svd_workspace_bytes(256, 1, 8, 152064)
+    b = svd.svd_workspace_bytes(64, 16, 32, 152064)
+    assert a > 0 and b > a
+    assert a % 256 == 0
+    assert svd.svd_workspace_bytes(1, 1, 1, 1) > 0
+    for bad in [(0, 1, 1, 1), (1, 0, 1, 1), (1, 1, 0, 1), (1, 1, 1, 0), (1, 65, 1, 1),
+                (1, 1, 4097, 1), (1 << 40, 1, 1, 1)]:
+        assert svd.svd_workspace_bytes(*bad) == 0, bad
+
+
+def test_strerror(svd):
+    for st in (0, -1, -2, -3, -4):
+        assert isinstance(svd.svd_strerror(st), str) and svd.svd_strerror(st)
+    assert svd.svd_strerror(12345) == "unknown status"
+
+
+def _call(svd, **kw):
+    # fake, never dereferenced addresses: validation returns before any HIP call
+    a = dict(p=4096, q=8192, d=12288, dtype=svd.SVD_BF16, B=2, K=2, G=3, V=100, tp=1.0, tq=1.0,
+             sel=16384, L=20480, tok=24576, ws=1 << 20, n=0)
+    a.update(kw)
+    return svd.svd_select_and_verify(a["p"], a["q"], a["d"], a["dtype"], a["B"], a["K"], a["G"],
+                                     a["V"], a["tp"], a["tq"], 0, 0, a["sel"], a["L"], a["tok"],
+                                     None, None, None, a["ws"], a["n"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(p=None), -1), (dict(q=None), -1), (dict(d=None), -1), (dict(sel=None), -1),
+    (dict(L=None), -1), (dict(tok=None), -1), (dict(ws=None), -1),
+    (dict(dtype=2), -2), (dict(B=0), -1), (dict(K=0), -1), (dict(K=65), -1), (dict(G=0), -1),
+    (dict(G=4097), -1), (dict(V=0), -1), (dict(tp=0.0), -1), (dict(tq=-1.0), -1),
+    (dict(tp=float("nan")), -1), (dict(tq=float("inf")), -1), (dict(ws=(1 << 20) + 64), -1),
+    (dict(), -3),  # workspace of 0 bytes
+])
+def test_host_side_argument_errors(svd, kw, want):
+    assert _call(svd, **kw) == want
+
+
+def test_verify_argument_errors(svd):
+    ws = 1 << 20
+    rc = svd.svd_verify(4096, 8192, None, svd.SVD_BF16, 1, 2, 10, 1.0, 1.0, 0, 0, 16384, 20480,
+                        None, None, ws, 0, None)
+    assert rc == svd.SVD_EINVAL
+    rc = svd.svd_verify(4096, 8192, 12288, svd.SVD_F32, 1, 2, 10, 1.0, 1.0, 0, 0, 16384, 20480,
+                        None, None, ws, 0, None)
+    assert rc == svd.SVD_EWORKSPACE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    # a copy of the package without libsvd.so must refuse to import
+    import shutil
+    import sys
+    src = os.path.join(ROOT, "lossless_draft_verification_verifier_amd", "__init__.py")
+    pkg = tmp_path / "svdcopy"
+    pkg.mkdir()
+    shutil.copy(src, pkg / "__init__.py")
+    code = "import sys; sys.path.insert(0, %r); import svdcopy" % str(tmp_path)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
+    assert r.returncode != 0 and "libsvd.so is not built" in r.stderr

@@ -1,0 +1,44 @@
+"""Distribution check on GPU outputs: the tiny workload (V = 32, gamma = 4,
+fp32) with 10^6 seeded trials in one call; committed tokens must follow the
+verifier rows (chi-square, Bonferroni over gamma + 1 positions at 1e-3) and the
+accepted length must follow prod_{i<j} beta_i.  A sample of the trials is also
+compared with the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import require_gpu, say
+from parity_harness import compare
+from stats_util import accepted_length_pvalue, committed_token_pvalues
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_workload_chi_square_on_gpu(orc):
+    svd = require_gpu()
+    cfg = W.get_config(1)
+    n = cfg.trials
+    base = W.generate(cfg, device="cuda")
+    p = base["p"].expand(n, *base["p"].shape[1:]).contiguous()
+    q = base["q"].expand(n, *base["q"].shape[1:]).contiguous()
+    drafts = W.tiny_trial_drafts(base["q"], n, cfg.temp, seed=cfg.data_seed + 29).contiguous()
+    say("tiny trials on GPU:", n)
+    out = svd.select_and_verify(p, q, drafts, temp_p=cfg.temp, seed=cfg.seed)
+    torch.cuda.synchronize()
+    L = out["accept_len"].cpu().numpy()
+    tok = out["next_token"].cpu().numpy()
+    zp, zq, dr = W.to_host(base["p"]), W.to_host(base["q"]), drafts.cpu().numpy()
+    assert np.all(L >= 0) and np.all(tok >= 0)
+    pv = committed_token_pvalues(zp, zq, dr, L, tok, cfg.temp)
+    say("p-values", pv)
+    assert min(pv) > 1e-3 / (cfg.gamma + 1)
+    assert accepted_length_pvalue(zp, zq, L, cfg.temp) > 1e-3
+    # parity of the first 50000 trials
+    m = 50_000
+    hp = np.ascontiguousarray(np.broadcast_to(zp, (m,) + zp.shape[1:]))
+    hq = np.ascontiguousarray(np.broadcast_to(zq, (m,) + zq.shape[1:]))
+    g = {"selected": out["selected"][:m].cpu().numpy(), "accept_len": L[:m], "next_token": tok[:m]}
+    rep = compare(orc, hp, hq, dr[:m], g, cfg.temp, cfg.temp, cfg.seed)
+    say(rep.summary())
+    assert rep.ok(), rep.failures[:5]

@@ -1,0 +1,85 @@
+"""GPU parity on small and ragged shapes: every output of every prefix against
+the oracle, under the rules of parity_harness (several tiles of the row loop,
+ragged vocabulary tails, unaligned rows on the element-wise path, K up to 64,
+gamma beyond one wave of 64)."""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import gen, host_inputs, require_gpu, run_select, say, check_ranges
+from parity_harness import compare
+
+pytestmark = pytest.mark.gpu
+
+BASE = W.get_config(3)
+
+CASES = [
+    # (B, K, gamma, V, dtype, temp)
+    (1, 1, 4, 32, "f32", 1.0),
+    (3, 1, 5, 1000, "bf16", 1.0),        # 16-byte rows, vector path, ragged last tile
+    (3, 2, 3, 1001, "bf16", 0.7),        # odd V: element-wise path
+    (2, 3, 7, 4099, "f32", 1.3),         # odd V, fp32
+    (5, 4, 6, 8192, "bf16", 0.7),        # exactly one draw segment
+    (4, 3, 5, 8193, "bf16", 1.0),        # one token into a second segment
+    (2, 8, 16, 20000, "bf16", 1.0),
+    (3, 1, 70, 2048, "bf16", 1.0),       # gamma beyond one wave of 64
+    (1, 64, 2, 512, "bf16", 2.0),        # K at its limit
+    (17, 2, 4, 3000, "f32", 0.5),
+    (2, 1, 1, 1, "f32", 1.0),            # V = 1: every row is one token
+    (3, 2, 2, 2, "bf16", 1.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%d_K%d_G%d_V%d_%s" % c[:5])
+@pytest.mark.parametrize("seed", [1, 20261202])
+def test_small_shapes_match_oracle(orc, case, seed):
+    svd = require_gpu()
+    B, K, G, V, dt, T = case
+    say("case", case, "seed", seed)
+    cfg = W.Config(99, "custom", B=B, K=K, gamma=G, V=V, dtype=dt, sigma0=1.0, sigma_step=0.02,
+                   temp=T, boost=6.0, boost_prob=0.8)
+    d = gen(cfg, data_seed=seed * 7 + V)
+    g = run_select(svd, d, T, seed, row_base=seed % 5, want_beta=True)
+    check_ranges(g, K, G, V)
+    hp, hq, hd = host_inputs(d)
+    rep = compare(orc, hp, hq, hd, g, T, T, seed, row_base=seed % 5)
+    say(rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    assert rep.invalid == 0
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_tiny_workload_matches_oracle(orc, seed):
+    svd = require_gpu()
+    cfg = W.get_config(1)
+    d = gen(cfg)
+    g = run_select(svd, d, cfg.temp, seed)
+    rep = compare(orc, *host_inputs(d), g, cfg.temp, cfg.temp, seed)
+    assert rep.ok(), rep.failures
+
+
+def test_distinct_temperatures(orc):
+    svd = require_gpu()
+    cfg = W.Config(98, "custom", B=4, K=3, gamma=5, V=3000, dtype="bf16", sigma0=1.0,
+                   sigma_step=0.0, temp=1.0, boost=6.0, boost_prob=1.0)
+    d = gen(cfg, data_seed=5)
+    import torch
+    out = svd.select_and_verify(d["p"], d["q"], d["drafts"], temp_p=0.8, temp_q=1.7, seed=3,
+                                want_alpha=True, want_scores=True)
+    torch.cuda.synchronize()
+    g = {k: (None if v is None else v.cpu().numpy()) for k, v in out.items()}
+    rep = compare(orc, *host_inputs(d), g, 0.8, 1.7, 3)
+    assert rep.ok(), rep.failures
+
+
+def test_many_prefixes_flag_rates(orc):
+    # 400 prefixes of a mid-size vocabulary: no unflagged mismatch, few near-ties
+    svd = require_gpu()
+    cfg = W.Config(97, "custom", B=400, K=2, gamma=8, V=6000, dtype="bf16", sigma0=0.75,
+                   sigma_step=0.0, temp=0.7, boost=8.0, boost_prob=1.0)
+    d = gen(cfg, data_seed=11)
+    g = run_select(svd, d, 0.7, 9)
+    rep = compare(orc, *host_inputs(d), g, 0.7, 0.7, 9)
+    say(rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    assert rep.flag_rate() < 1e-3
