@@ -8,19 +8,92 @@
 // whose cumulative weight exceeds t = u * Z, so tokens of zero weight are
 // never drawn; if rounding leaves no such token, the last token with weight.
 //
-// The drawn rows are recomputed from the logits in fp64, in three launches
-// over vocabulary segments of kDrawSeg tokens:
-//   kr_draw_sums  (prefix, segment): segment max and sum of exp(z/T - m_seg)
-//   kr_draw_mass  (prefix, segment): exact row normalisers from all segments,
-//                 then the segment's residual mass and last weighted index
-//   kr_draw_pick  (prefix): find the segment holding t, then an LDS prefix
-//                 sum over thread-contiguous runs locates the token.
-// Every reduction has a fixed order, so the result is deterministic.
+// The drawn rows are recomputed from the logits in fp64, in three launches:
+//
+// kr_draw_pass (prefix, vocabulary segment of kDrawSeg tokens), one fp64 pass:
+//   residual draw: with the exact row maxima from the row-statistics kernel,
+//     w_p = exp(z_p/T_p - M_p) and w_q likewise; the segment sums of w_p and
+//     w_q give the exact normalisers S_p, S_q.  Whether p_v > q_v, i.e.
+//     w_p > (S_p/S_q) w_q, is decided against the fp32 ratio from the
+//     row-statistics kernel with a relative margin kClassMargin far above its
+//     error: sure-positive tokens add w_p and w_q to two more segment sums, so
+//     sum_v max(0, p_v - q_v) over them is (sum w_p)/S_p - (sum w_q)/S_q;
+//     tokens inside the margin (a few per row) are stored with their exact
+//     weights and settled once S_p and S_q are known.
+//   bonus draw: segment max, then the sum of exp(z/T - m_seg).
+// kr_draw_fix (prefix, segment): a segment whose list of uncertain tokens
+//   overflowed (a cluster of equal p/q ratios, which bf16 logits make
+//   possible) gets its residual mass recomputed exactly, in parallel.
+// kr_draw_pick (prefix): exact normalisers and per-segment masses, the
+//   segment that holds t, then each thread takes kRun consecutive tokens of
+//   that segment into registers, and a workgroup prefix sum over the threads'
+//   totals locates the token.
+// Every reduction has a fixed order and the uncertain tokens are summed in
+// token order, so the result is deterministic.
 #pragma once
 
 #include "svd_device.hpp"
 
 namespace svd {
+
+constexpr int kUncCap = 32;            // uncertain tokens kept per segment
+constexpr double kClassMargin = 2e-4;  // relative margin of the p > q test
+
+// ---------------------------------------------------------------------------
+// exp(x) in fp64 for x <= 0 (a few ulp above 0 is fine; x must not be NaN):
+// x = n ln2/64 + r with |r| <= ln2/128 (Cody-Waite split of ln2/64; n ln2_hi
+// is exact for |n| < 2^17), exp(r) by its degree-5 Taylor polynomial (the
+// next term is below 4e-17), 2^(j/64) from a 64-entry table, then ldexp.
+
+struct Exp64Table {
+  double t[64];
+};
+
+__device__ inline void exp64_table_init(Exp64Table &tab) {
+  if (threadIdx.x < 64) tab.t[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+}
+
+__device__ inline double exp_nonpos(double x, const Exp64Table &tab) {
+  x = fmax(x, -760.0);  // exp(-760) is 0 in double; also maps -inf
+  const double n = __builtin_rint(x * 92.33248261689366);  // 64 / ln 2
+  const int ni = (int)n;
+  double r = __builtin_fma(-n, 0x1.62e42fefa0000p-7, x);
+  r = __builtin_fma(-n, 0x1.cf79abc9e3b3ap-46, r);
+  double p = 1.0 / 120.0;
+  p = __builtin_fma(p, r, 1.0 / 24.0);
+  p = __builtin_fma(p, r, 1.0 / 6.0);
+  p = __builtin_fma(p, r, 0.5);
+  p = __builtin_fma(p, r, 1.0);
+  p = __builtin_fma(p, r, 1.0);
+  return ldexp(tab.t[ni & 63] * p, ni >> 6);
+}
+
+// ---------------------------------------------------------------------------
+// Workspace records of the draw.
+
+struct DrawSeg {       // one (prefix, segment)
+  double sp, sq;       // sum of w_p, w_q (residual: relative to the row max;
+                       // bonus: relative to the segment max)
+  double ap, aq;       // sums of w_p, w_q over sure-positive tokens (residual)
+  float mseg;          // bonus: raw max logit of the segment
+  int last_pos;        // last sure-positive token (residual), -1 if none
+  int last_p;          // last token with w_p > 0, -1 if none
+  int n_unc;           // stored uncertain tokens, -1 when the list overflowed
+  int bad;             // bonus: a NaN logit in the segment
+  int pad;
+};
+
+struct DrawUnc {       // one uncertain token
+  double wp, wq;
+  int v, pad;
+};
+
+struct DrawMass {      // one (prefix, segment) after the pick's first stage
+  double zr;           // residual mass (or p mass for a bonus draw)
+  double zp;           // p mass (fallback when the residual has no mass)
+  int last_r, last_p;
+  int pad[2];
+};
 
 template <typename E>
 struct DrawRows {
@@ -38,164 +111,292 @@ __device__ inline DrawRows<E> draw_rows(const typename E::elem *p, const typenam
   return r;
 }
 
-// max and fp64 sum of exp(z/T - m_seg) over row[lo, hi); valid in all threads
-template <typename E>
-__device__ inline void seg_sums(const typename E::elem *row, int lo, int hi, float T,
-                                float &m_raw, double &S, float *ldsf, double *ldsd) {
-  float m = kNegInf;
-  for (int v = lo + (int)threadIdx.x; v < hi; v += kBlock) m = fmaxf(m, E::at(row, v));
-  m = block_max(m, ldsf);
-  const double Td = (double)T;
-  const double M = (double)fmaxf(m, kLowest) / Td;
-  const double invT = 1.0 / Td;
-  double s = 0.0;
-  for (int v = lo + (int)threadIdx.x; v < hi; v += kBlock)
-    s += exp((double)E::at(row, v) * invT - M);  // NaN logits poison the sum
-  S = block_sum_d(s, ldsd);
-  m_raw = m;
-}
-
-// Row normaliser from the per-segment sums, in segment order.  The same code
-// runs in kr_draw_mass and kr_draw_pick, so both see the same bits.
-__device__ inline bool row_norm(const DrawSums *s, int nseg, bool use_q, float T, double &M,
-                                double &S) {
-  float mr = kNegInf;
-  for (int i = 0; i < nseg; ++i) mr = fmaxf(mr, use_q ? s[i].mq : s[i].mp);
-  const double Td = (double)T;
-  M = (double)mr / Td;
-  double acc = 0.0;
-  for (int i = 0; i < nseg; ++i) {
-    const float mi = use_q ? s[i].mq : s[i].mp;
-    const double si = use_q ? s[i].sq : s[i].sp;
-    acc += (mi == mr) ? si : si * exp((double)mi / Td - M);
+// Visit the logits of [lo, hi) of one or two rows: f(v, zp, zq).
+template <typename E, bool kVec, bool kTwo, typename F>
+__device__ inline void visit_segment(const typename E::elem *rp, const typename E::elem *rq,
+                                     int lo, int hi, F &&f) {
+  if constexpr (kVec) {
+    constexpr int P = E::kPerVec;
+    const vec16 *vp = reinterpret_cast<const vec16 *>(rp);
+    const vec16 *vq = reinterpret_cast<const vec16 *>(rq);
+    for (int i = lo / P + (int)threadIdx.x; i < hi / P; i += kBlock) {
+      float xp[P], xq[P];
+      E::unpack(vp[i], xp);
+      if constexpr (kTwo) E::unpack(vq[i], xq);
+#pragma unroll
+      for (int e = 0; e < P; ++e) f(i * P + e, xp[e], kTwo ? xq[e] : 0.0f);
+    }
+  } else {
+    for (int v = lo + (int)threadIdx.x; v < hi; v += kBlock)
+      f(v, E::at(rp, v), kTwo ? E::at(rq, v) : 0.0f);
   }
-  S = acc;
-  return mr != kNegInf && mr != -kNegInf && acc == acc && acc > 0.0;
 }
 
-template <typename E>
-__global__ __launch_bounds__(kBlock) void kr_draw_sums(
+template <typename E, bool kVec>
+__global__ __launch_bounds__(kBlock) void kr_draw_pass(
     const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int K,
-    int gamma, int V, int nseg, float tp, float tq, const DrawDesc *__restrict__ desc,
-    DrawSums *__restrict__ sums) {
+    int gamma, int V, int nseg, float tp, float tq, const RowStats *__restrict__ stats,
+    const DrawDesc *__restrict__ desc, DrawSeg *__restrict__ segs, DrawUnc *__restrict__ uncs) {
+  __shared__ Exp64Table tab;
   __shared__ float ldsf[kWaves];
   __shared__ double ldsd[kWaves];
+  __shared__ int ldsi[kWaves];
+  __shared__ int n_unc;
+  __shared__ DrawUnc unc[kUncCap];
   const int64_t b = blockIdx.x / nseg;
   const int seg = (int)(blockIdx.x - b * nseg);
   const DrawDesc d = desc[b];
   if (!d.valid) return;
+  exp64_table_init(tab);
+  if (threadIdx.x == 0) n_unc = 0;
+  __syncthreads();
   const DrawRows<E> r = draw_rows<E>(p, q, K, gamma, V, b, d);
   const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
-  DrawSums out{};
-  seg_sums<E>(r.p, lo, hi, tp, out.mp, out.sp, ldsf, ldsd);
-  if (r.q) {
-    seg_sums<E>(r.q, lo, hi, tq, out.mq, out.sq, ldsf, ldsd);
+  const double invTp = 1.0 / (double)tp, invTq = 1.0 / (double)tq;
+  double sp = 0.0, sq = 0.0, ap = 0.0, aq = 0.0;
+  int last_pos = -1, last_p = -1, bad = 0;
+  float mseg = kNegInf;
+
+  if (d.purpose == kResidual) {
+    const RowStats st = stats[(b * K + d.k) * gamma + d.pos];
+    const double Mp = (double)st.mp / (double)tp, Mq = (double)st.mq / (double)tq;
+    const double rho = (double)st.sp / (double)st.sq;  // fp32 estimate of S_p / S_q
+    const double up = rho * (1.0 + kClassMargin), dn = rho * (1.0 - kClassMargin);
+    visit_segment<E, kVec, true>(r.p, r.q, lo, hi, [&](int v, float zp, float zq) {
+      const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -Mp), tab);
+      const double wq = exp_nonpos(__builtin_fma((double)zq, invTq, -Mq), tab);
+      sp += wp;
+      sq += wq;
+      if (wp > 0.0) last_p = v;
+      if (wp > up * wq) {
+        ap += wp;
+        aq += wq;
+        last_pos = v;
+      } else if (wp > 0.0 && wp >= dn * wq) {
+        const int i = atomicAdd(&n_unc, 1);
+        if (i < kUncCap) unc[i] = DrawUnc{wp, wq, v, 0};
+      }
+    });
   } else {
-    out.mq = kNegInf;
-    out.sq = 0.0;
+    float m = kNegInf;
+    visit_segment<E, kVec, false>(r.p, r.p, lo, hi, [&](int, float zp, float) {
+      m = fmaxf(m, zp);
+      bad |= (zp != zp);
+    });
+    mseg = block_max(m, ldsf);
+    bad = block_max_i(bad, ldsi);
+    const double M = (double)fmaxf(mseg, kLowest) / (double)tp;
+    visit_segment<E, kVec, false>(r.p, r.p, lo, hi, [&](int v, float zp, float) {
+      const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -M), tab);
+      sp += wp;
+      if (wp > 0.0) last_p = v;
+    });
   }
-  if (threadIdx.x == 0) sums[b * nseg + seg] = out;
+  DrawSeg out{};
+  out.sp = block_sum_d(sp, ldsd);
+  out.sq = block_sum_d(sq, ldsd);
+  out.ap = block_sum_d(ap, ldsd);
+  out.aq = block_sum_d(aq, ldsd);
+  out.last_pos = block_max_i(last_pos, ldsi);
+  out.last_p = block_max_i(last_p, ldsi);
+  out.mseg = mseg;
+  out.bad = bad;
+  // uncertain tokens in token order (distinct tokens: the ranks are a permutation)
+  const int64_t so = b * nseg + seg;
+  const int n = n_unc;
+  if (n <= kUncCap && (int)threadIdx.x < n) {
+    const DrawUnc e = unc[threadIdx.x];
+    int rank = 0;
+    for (int i = 0; i < n; ++i) rank += (unc[i].v < e.v);
+    uncs[so * kUncCap + rank] = e;
+  }
+  if (threadIdx.x == 0) {
+    out.n_unc = (n > kUncCap) ? -1 : n;
+    segs[so] = out;
+  }
 }
 
-// weight of token v in the draw
+// Exact weights of the draw.
 template <typename E>
 struct DrawWeight {
   const typename E::elem *p, *q;
   double invTp, invTq, Mp, Mq, invSp, invSq;
   bool resid;
-  __device__ inline void at(int v, double &w, double &pv) const {
-    pv = exp((double)E::at(p, v) * invTp - Mp) * invSp;
-    if (resid) {
-      const double qv = exp((double)E::at(q, v) * invTq - Mq) * invSq;
-      const double d = pv - qv;
-      w = d > 0.0 ? d : 0.0;
-    } else {
-      w = pv;
-    }
+  // weight from the two logits of token v
+  __device__ inline double from(float zp, float zq, const Exp64Table &tab) const {
+    const double pv = exp_nonpos(__builtin_fma((double)zp, invTp, -Mp), tab) * invSp;
+    if (!resid) return pv;
+    const double qv = exp_nonpos(__builtin_fma((double)zq, invTq, -Mq), tab) * invSq;
+    const double dd = pv - qv;
+    return dd > 0.0 ? dd : 0.0;
   }
 };
 
+// Exact row normalisers of the draw from the pass's segment sums, in segment
+// order (kr_draw_fix and kr_draw_pick run this same code, so they agree to the
+// bit).  Returns false for an invalid bonus row.
 template <typename E>
-__device__ inline bool make_weight(const DrawRows<E> &r, const DrawSums *s, int nseg, float tp,
-                                   float tq, DrawWeight<E> &w) {
-  double Sp, Sq = 1.0;
-  bool ok = row_norm(s, nseg, false, tp, w.Mp, Sp);
-  w.Mq = 0.0;
-  if (r.q) ok = row_norm(s, nseg, true, tq, w.Mq, Sq) && ok;
-  w.p = r.p;
-  w.q = r.q;
-  w.invTp = 1.0 / (double)tp;
-  w.invTq = 1.0 / (double)tq;
-  w.invSp = 1.0 / Sp;
-  w.invSq = 1.0 / Sq;
-  w.resid = r.q != nullptr;
-  return ok;
+__device__ inline bool draw_setup(const DrawRows<E> &rows, const DrawDesc &d, const RowStats *stats,
+                                  const DrawSeg *S, int K, int gamma, int nseg, int64_t b,
+                                  float tp, float tq, DrawWeight<E> &W) {
+  W.p = rows.p;
+  W.q = rows.q;
+  W.invTp = 1.0 / (double)tp;
+  W.invTq = 1.0 / (double)tq;
+  W.resid = d.purpose == kResidual;
+  double Sp = 0.0, Sq = 1.0;
+  if (W.resid) {
+    const RowStats st = stats[(b * K + d.k) * gamma + d.pos];
+    W.Mp = (double)st.mp / (double)tp;
+    W.Mq = (double)st.mq / (double)tq;
+    Sq = 0.0;
+    for (int s = 0; s < nseg; ++s) {
+      Sp += S[s].sp;
+      Sq += S[s].sq;
+    }
+  } else {
+    float mr = kNegInf;
+    int bad = 0;
+    for (int s = 0; s < nseg; ++s) {
+      mr = fmaxf(mr, S[s].mseg);
+      bad |= S[s].bad;
+    }
+    if (bad || mr == kNegInf || mr == -kNegInf) return false;
+    W.Mp = (double)mr / (double)tp;
+    W.Mq = 0.0;
+    for (int s = 0; s < nseg; ++s) {
+      const double Ms = (double)fmaxf(S[s].mseg, kLowest) / (double)tp;
+      Sp += (S[s].mseg == mr) ? S[s].sp : S[s].sp * exp(Ms - W.Mp);
+    }
+  }
+  W.invSp = 1.0 / Sp;
+  W.invSq = 1.0 / Sq;
+  return true;
 }
 
-template <typename E>
-__global__ __launch_bounds__(kBlock) void kr_draw_mass(
+// (prefix, segment): exact residual mass of a segment whose uncertain list
+// overflowed; every other workgroup returns at once.
+template <typename E, bool kVec>
+__global__ __launch_bounds__(kBlock) void kr_draw_fix(
     const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int K,
-    int gamma, int V, int nseg, float tp, float tq, const DrawDesc *__restrict__ desc,
-    const DrawSums *__restrict__ sums, DrawMass *__restrict__ mass) {
+    int gamma, int V, int nseg, float tp, float tq, const RowStats *__restrict__ stats,
+    const DrawDesc *__restrict__ desc, const DrawSeg *__restrict__ segs,
+    DrawMass *__restrict__ mass) {
+  __shared__ Exp64Table tab;
   __shared__ double ldsd[kWaves];
   __shared__ int ldsi[kWaves];
   const int64_t b = blockIdx.x / nseg;
   const int seg = (int)(blockIdx.x - b * nseg);
   const DrawDesc d = desc[b];
-  if (!d.valid) return;
-  const DrawRows<E> r = draw_rows<E>(p, q, K, gamma, V, b, d);
+  const DrawSeg *S = segs + b * nseg;
+  if (!d.valid || d.purpose != kResidual || S[seg].n_unc >= 0) return;
+  exp64_table_init(tab);
+  __syncthreads();
+  const DrawRows<E> rows = draw_rows<E>(p, q, K, gamma, V, b, d);
   DrawWeight<E> W;
-  if (!make_weight<E>(r, sums + b * nseg, nseg, tp, tq, W)) return;  // the pick reports it
+  draw_setup<E>(rows, d, stats, S, K, gamma, nseg, b, tp, tq, W);
   const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
-  double zr = 0.0, zp = 0.0;
-  int lr = -1, lp = -1;
-  for (int v = lo + (int)threadIdx.x; v < hi; v += kBlock) {
-    double w, pv;
-    W.at(v, w, pv);
-    zr += w;
-    zp += pv;
-    if (w > 0.0) lr = v;
-    if (pv > 0.0) lp = v;
-  }
-  DrawMass out{};
-  out.zr = block_sum_d(zr, ldsd);
-  out.zp = block_sum_d(zp, ldsd);
-  out.last_r = block_max_i(lr, ldsi);
-  out.last_p = block_max_i(lp, ldsi);
-  if (threadIdx.x == 0) mass[b * nseg + seg] = out;
+  double z = 0.0;
+  int last = -1;
+  visit_segment<E, kVec, true>(rows.p, rows.q, lo, hi, [&](int v, float zp, float zq) {
+    const double w = W.from(zp, zq, tab);
+    z += w;
+    if (w > 0.0) last = v;
+  });
+  DrawMass m{};
+  m.zr = block_sum_d(z, ldsd);
+  m.last_r = block_max_i(last, ldsi);
+  m.zp = S[seg].sp * W.invSp;
+  m.last_p = S[seg].last_p;
+  if (threadIdx.x == 0) mass[b * nseg + seg] = m;
 }
 
-template <typename E>
+constexpr int kRun = kDrawSeg / kBlock;  // tokens per thread in the pick's scan
+
+// Exclusive prefix sum over the workgroup in thread order (fixed pattern).
+__device__ inline double block_exclusive_scan(double x, double *lds /* kWaves */) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  double inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) lds[w] = inc;
+  __syncthreads();
+  double base = 0.0;
+  for (int i = 0; i < w; ++i) base += lds[i];
+  const double prev = __shfl_up(inc, 1, 64);
+  __syncthreads();
+  return base + (lane == 0 ? 0.0 : prev);
+}
+
+template <typename E, bool kVec>
 __global__ __launch_bounds__(kBlock) void kr_draw_pick(
     const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int K,
     int gamma, int V, int nseg, float tp, float tq, uint64_t seed, uint64_t row_base,
-    const DrawDesc *__restrict__ desc, const DrawSums *__restrict__ sums,
-    const DrawMass *__restrict__ mass, int32_t *__restrict__ selected,
+    const RowStats *__restrict__ stats, const DrawDesc *__restrict__ desc,
+    const DrawSeg *__restrict__ segs, const DrawUnc *__restrict__ uncs,
+    DrawMass *__restrict__ mass, int32_t *__restrict__ selected,
     int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token) {
-  __shared__ double scan[kBlock];
+  __shared__ Exp64Table tab;
+  __shared__ double ldsd[kWaves];
   __shared__ int ldsi[kWaves];
   const int64_t b = blockIdx.x;
   const int tid = threadIdx.x;
   const DrawDesc d = desc[b];
   if (!d.valid) return;
-  const DrawRows<E> r = draw_rows<E>(p, q, K, gamma, V, b, d);
+  exp64_table_init(tab);
+  __syncthreads();
+  const DrawRows<E> rows = draw_rows<E>(p, q, K, gamma, V, b, d);
+  const DrawSeg *S = segs + b * nseg;
+  DrawMass *ms = mass + b * nseg;
+  const bool residual = d.purpose == kResidual;
   DrawWeight<E> W;
-  if (!make_weight<E>(r, sums + b * nseg, nseg, tp, tq, W)) {
-    // only a bonus row can be invalid here: the scored rows were checked
-    if (tid == 0) {
+  if (!draw_setup<E>(rows, d, stats, S, K, gamma, nseg, b, tp, tq, W)) {
+    if (tid == 0) {  // invalid bonus row (the scored rows were checked earlier)
       if (selected) selected[b] = -1;
       accept_len[b] = -1;
       next_token[b] = -1;
     }
     return;
   }
-  const DrawMass *ms = mass + b * nseg;
+
+  // per-segment masses (overflowed segments came from kr_draw_fix)
+  for (int s = tid; s < nseg; s += kBlock) {
+    if (residual && S[s].n_unc < 0) continue;
+    DrawMass m{};
+    m.last_p = S[s].last_p;
+    if (residual) {
+      m.zp = S[s].sp * W.invSp;
+      double z = S[s].ap * W.invSp - S[s].aq * W.invSq;
+      int last = S[s].last_pos;
+      const DrawUnc *u = uncs + (b * nseg + s) * kUncCap;
+      for (int i = 0; i < S[s].n_unc; ++i) {
+        const double dd = u[i].wp * W.invSp - u[i].wq * W.invSq;
+        if (dd > 0.0) {
+          z += dd;
+          last = max(last, u[i].v);
+        }
+      }
+      m.zr = z;
+      m.last_r = last;
+    } else {
+      const double Ms = (double)fmaxf(S[s].mseg, kLowest) / (double)tp;
+      m.zp = ((S[s].mseg == kNegInf) ? 0.0 : S[s].sp * exp(Ms - W.Mp)) * W.invSp;
+      m.zr = m.zp;
+      m.last_r = m.last_p;
+    }
+    ms[s] = m;
+  }
+  __syncthreads();
+
   double zr = 0.0;
   for (int s = 0; s < nseg; ++s) zr += ms[s].zr;
-  const bool resid = W.resid && zr > 0.0;
-  W.resid = resid;  // no residual mass: draw from p
+  const bool use_r = !residual || zr > 0.0;  // a residual without mass draws from p
+  W.resid = residual && use_r;
   double Z = zr;
-  if (!resid) {
+  if (!use_r) {
     Z = 0.0;
     for (int s = 0; s < nseg; ++s) Z += ms[s].zp;
   }
@@ -205,7 +406,7 @@ __global__ __launch_bounds__(kBlock) void kr_draw_pick(
   double cum = 0.0;
   int s0 = -1;
   for (int s = 0; s < nseg; ++s) {
-    const double w = resid ? ms[s].zr : ms[s].zp;
+    const double w = use_r ? ms[s].zr : ms[s].zp;
     if (cum + w > t) {
       s0 = s;
       break;
@@ -215,47 +416,52 @@ __global__ __launch_bounds__(kBlock) void kr_draw_pick(
   int tok = -1;
   if (s0 >= 0) {
     for (int s = s0; s < nseg; ++s) {
+      // thread tid owns tokens [a, a + kRun) of the segment, kept in registers
       const int lo = s * kDrawSeg, hi = min(V, lo + kDrawSeg);
-      const int chunk = (hi - lo + kBlock - 1) / kBlock;
-      const int a = min(hi, lo + tid * chunk), e = min(hi, a + chunk);
+      const int a = lo + tid * kRun;
+      double w[kRun];
+      if constexpr (kVec) {
+        constexpr int P = E::kPerVec;
+        const vec16 *vp = reinterpret_cast<const vec16 *>(W.p + a);
+        const vec16 *vq = reinterpret_cast<const vec16 *>(W.q + (W.resid ? a : 0));
+#pragma unroll
+        for (int c = 0; c < kRun / P; ++c) {
+          float xp[P], xq[P];
+          if (a + c * P < hi) {  // hi - lo is a multiple of P on this path
+            E::unpack(vp[c], xp);
+            if (W.resid) E::unpack(vq[c], xq);
+          }
+#pragma unroll
+          for (int e = 0; e < P; ++e)
+            w[c * P + e] = (a + c * P < hi) ? W.from(xp[e], W.resid ? xq[e] : 0.0f, tab) : 0.0;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) {
+          const int v = a + i;
+          w[i] = (v < hi) ? W.from(E::at(W.p, v), W.resid ? E::at(W.q, v) : 0.0f, tab) : 0.0;
+        }
+      }
       double loc = 0.0;
-      for (int v = a; v < e; ++v) {
-        double w, pv;
-        W.at(v, w, pv);
-        loc += w;
-      }
-      scan[tid] = loc;
-      __syncthreads();
-      if (tid == 0) {  // exclusive prefix sum in thread order
-        double run = 0.0;
-        for (int i = 0; i < kBlock; ++i) {
-          const double x = scan[i];
-          scan[i] = run;
-          run += x;
-        }
-      }
-      __syncthreads();
-      double C = cum + scan[tid];
+#pragma unroll
+      for (int i = 0; i < kRun; ++i) loc += w[i];
+      double C = cum + block_exclusive_scan(loc, ldsd);
       int found = 0x7fffffff;
-      for (int v = a; v < e; ++v) {
-        double w, pv;
-        W.at(v, w, pv);
-        C += w;
-        if (w > 0.0 && C > t) {
-          found = v;
-          break;
-        }
+#pragma unroll
+      for (int i = 0; i < kRun; ++i) {
+        C += w[i];
+        if (found == 0x7fffffff && w[i] > 0.0 && C > t) found = a + i;
       }
       found = block_min_i(found, ldsi);
       if (found != 0x7fffffff) {
         tok = found;
         break;
       }
-      cum += resid ? ms[s].zr : ms[s].zp;
+      cum += use_r ? ms[s].zr : ms[s].zp;
     }
   }
   if (tok < 0) {  // t at or past the total through rounding
-    for (int s = 0; s < nseg; ++s) tok = max(tok, resid ? ms[s].last_r : ms[s].last_p);
+    for (int s = 0; s < nseg; ++s) tok = max(tok, use_r ? ms[s].last_r : ms[s].last_p);
   }
   if (tid == 0) next_token[b] = tok;
 }

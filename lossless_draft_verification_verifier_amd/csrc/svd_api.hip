@@ -21,7 +21,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-  size_t stats, alpha, desc, sums, mass, total;
+  size_t stats, alpha, desc, segs, uncs, mass, total;
   int nseg;
 };
 
@@ -46,8 +46,10 @@ Layout layout(int64_t B, int32_t K, int32_t G, int32_t V) {
   off = align_up(off + rp * sizeof(float));
   L.desc = off;
   off = align_up(off + (size_t)B * sizeof(DrawDesc));
-  L.sums = off;
-  off = align_up(off + (size_t)B * L.nseg * sizeof(DrawSums));
+  L.segs = off;
+  off = align_up(off + (size_t)B * L.nseg * sizeof(DrawSeg));
+  L.uncs = off;
+  off = align_up(off + (size_t)B * L.nseg * kUncCap * sizeof(DrawUnc));
   L.mass = off;
   off = align_up(off + (size_t)B * L.nseg * sizeof(DrawMass));
   L.total = off;
@@ -130,7 +132,8 @@ int run(const void *p_logits, const void *q_logits, const int32_t *drafts, int64
   RowStats *stats = reinterpret_cast<RowStats *>(ws + Lo.stats);
   float *alpha_ws = reinterpret_cast<float *>(ws + Lo.alpha);
   DrawDesc *desc = reinterpret_cast<DrawDesc *>(ws + Lo.desc);
-  DrawSums *sums = reinterpret_cast<DrawSums *>(ws + Lo.sums);
+  DrawSeg *segs = reinterpret_cast<DrawSeg *>(ws + Lo.segs);
+  DrawUnc *uncs = reinterpret_cast<DrawUnc *>(ws + Lo.uncs);
   DrawMass *mass = reinterpret_cast<DrawMass *>(ws + Lo.mass);
   const unsigned rp = (unsigned)((int64_t)B * K * G);
   const unsigned nb = (unsigned)B;
@@ -151,16 +154,17 @@ int run(const void *p_logits, const void *q_logits, const int32_t *drafts, int64
   tm.mark(SVD_KERNEL_SELECT);
   SVD_LAUNCH(kr_select, dim3(nb), dim3(64), stream, (const float *)alpha_ws, K, G, seed,
              row_base, selected, accept_len, next_token, scores, desc);
-  tm.mark(SVD_KERNEL_DRAW_SUMS);
-  SVD_LAUNCH(kr_draw_sums<E>, dim3(nbs), dim3(kBlock), stream, p, q, K, G, V, Lo.nseg, tp, tq,
-             (const DrawDesc *)desc, sums);
-  tm.mark(SVD_KERNEL_DRAW_MASS);
-  SVD_LAUNCH(kr_draw_mass<E>, dim3(nbs), dim3(kBlock), stream, p, q, K, G, V, Lo.nseg, tp, tq,
-             (const DrawDesc *)desc, (const DrawSums *)sums, mass);
+  tm.mark(SVD_KERNEL_DRAW_PASS);
+  SVD_LAUNCH(kr_draw_pass<E, kVec>, dim3(nbs), dim3(kBlock), stream, p, q, K, G, V, Lo.nseg, tp,
+             tq, (const RowStats *)stats, (const DrawDesc *)desc, segs, uncs);
+  tm.mark(SVD_KERNEL_DRAW_FIX);
+  SVD_LAUNCH(kr_draw_fix<E, kVec>, dim3(nbs), dim3(kBlock), stream, p, q, K, G, V, Lo.nseg, tp,
+             tq, (const RowStats *)stats, (const DrawDesc *)desc, (const DrawSeg *)segs, mass);
   tm.mark(SVD_KERNEL_DRAW_PICK);
-  SVD_LAUNCH(kr_draw_pick<E>, dim3(nb), dim3(kBlock), stream, p, q, K, G, V, Lo.nseg, tp, tq,
-             seed, row_base, (const DrawDesc *)desc, (const DrawSums *)sums,
-             (const DrawMass *)mass, selected, accept_len, next_token);
+  SVD_LAUNCH(kr_draw_pick<E, kVec>, dim3(nb), dim3(kBlock), stream, p, q, K, G, V, Lo.nseg, tp,
+             tq, seed, row_base, (const RowStats *)stats, (const DrawDesc *)desc,
+             (const DrawSeg *)segs, (const DrawUnc *)uncs, mass, selected, accept_len,
+             next_token);
   tm.mark(-1);
   return SVD_OK;
 }

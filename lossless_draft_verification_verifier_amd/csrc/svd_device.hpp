@@ -178,17 +178,4 @@ struct DrawDesc {      // one prefix: which row pair the draw reads
   int valid;           // 0: prefix invalid, nothing to draw
 };
 
-struct DrawSums {      // one (prefix, vocabulary segment): fp64 normalisers
-  double sp, sq;       // sum over the segment of exp(z/T - m_seg)
-  float mp, mq;        // raw max logit over the segment (m_seg = max / T)
-  int pad[2];
-};
-
-struct DrawMass {      // one (prefix, vocabulary segment): fp64 draw mass
-  double zr;           // sum of max(0, p - q) (residual) or of p (bonus)
-  double zp;           // sum of p (fallback when the residual has no mass)
-  int last_r, last_p;  // last index with positive weight, -1 if none
-  int pad[2];
-};
-
 }  // namespace svd

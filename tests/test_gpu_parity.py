@@ -83,3 +83,38 @@ def test_many_prefixes_flag_rates(orc):
     say(rep.summary())
     assert rep.ok(), rep.failures[:5]
     assert rep.flag_rate() < 1e-3
+
+
+def test_residual_inside_the_margin_everywhere(orc):
+    # q equals p except at the drafted token, raised by 2: every other token has
+    # p_v / q_v = S_q / S_p, within the classification margin of 1, so every
+    # segment's list of uncertain tokens overflows and is recomputed exactly
+    svd = require_gpu()
+    import torch
+    B, G, V = 8, 3, 20000
+    gen_ = torch.Generator(device="cuda").manual_seed(77)
+    zp = torch.randn((B, 1, G + 1, V), generator=gen_, device="cuda") * 2.0
+    zq = zp[:, :, :G].clone()
+    x = torch.argsort(zp[:, :, :G], dim=-1)[..., V // 2].to(torch.int32)  # a median token
+    zq.scatter_add_(-1, x.long().unsqueeze(-1), torch.full((B, 1, G, 1), 2.0, device="cuda"))
+    d = {"p": zp.contiguous(), "q": zq.contiguous(), "drafts": x.contiguous()}
+    g = run_select(svd, d, 1.0, 5)
+    say("accept lengths", g["accept_len"])
+    assert (g["accept_len"] < G).sum() >= 4
+    rep = compare(orc, *host_inputs(d), g, 1.0, 1.0, 5)
+    say(rep.summary())
+    assert rep.ok(), rep.failures
+
+
+@pytest.mark.parametrize("V", [5000, 20000, 40001])
+def test_bonus_draws_across_segments(orc, V):
+    svd = require_gpu()
+    cfg = W.Config(92, "custom", B=6, K=2, gamma=3, V=V, dtype="bf16", sigma0=1.0,
+                   sigma_step=0.0, temp=0.9, boost=6.0, boost_prob=0.5)
+    d = gen(cfg, data_seed=V)
+    d["q"].copy_(d["p"][:, :, :3])  # alpha == 1: every prefix draws its bonus token
+    for seed in (1, 2):
+        g = run_select(svd, d, 0.9, seed)
+        assert np.all(g["accept_len"] == 3)
+        rep = compare(orc, *host_inputs(d), g, 0.9, 0.9, seed)
+        assert rep.ok(), rep.failures
