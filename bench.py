@@ -72,6 +72,19 @@ def cpu_baseline(d, cfg, seed):
             "seconds": dt}
 
 
+def calibrate_copy(torch, steps):
+    """A plain copy of a known number of bytes, to scale the HBM counters."""
+    n = 1 << 29  # 1 GiB of bf16 each way
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n,
+                      "launches": steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -79,6 +92,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batched_serving")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of known size (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the verification path shards by prefix with no "
@@ -87,6 +102,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(torch, max(args.steps, 1))
+        return
 
     import lossless_draft_verification_verifier_amd as svd
     import workloads as W

@@ -37,13 +37,13 @@ class SvdError(RuntimeError):
         super().__init__("%s failed: %s (status %d)" % (where, svd_strerror(status), status))
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise ImportError(
             "libsvd.so is not built (expected at %s); build it with "
             "__graft_entry__.build() or python -m lossless_draft_verification_verifier_amd._build"
-            % LIB_PATH)
-    L = ctypes.CDLL(LIB_PATH)
+            % path)
+    L = ctypes.CDLL(path)
     vp, i32, i64, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                   ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t)
     L.svd_workspace_bytes.restype = sz

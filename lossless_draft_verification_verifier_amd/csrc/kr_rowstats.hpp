@@ -32,7 +32,27 @@ __device__ inline void ms_fold(float &m, float &s, const float *x, float c) {
   for (int i = 0; i < N; ++i) s += fast_exp2((x[i] - mo) * c);
 }
 
-constexpr int kRowUnroll = 4;  // 16-byte loads in flight per thread and row
+// Launch shape of the streaming kernel: threads per workgroup, 16-byte loads
+// in flight per thread and row, and nontemporal (streaming) loads.
+#ifndef SVD_ROW_BLOCK
+#define SVD_ROW_BLOCK 1024
+#endif
+#ifndef SVD_ROW_UNROLL
+#define SVD_ROW_UNROLL 2
+#endif
+#ifndef SVD_ROW_NT
+#define SVD_ROW_NT 1
+#endif
+constexpr int kRowBlock = SVD_ROW_BLOCK;
+constexpr int kRowUnroll = SVD_ROW_UNROLL;
+
+__device__ inline vec16 stream_load(const vec16 *p) {
+#if SVD_ROW_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
 
 // (max, sum) of one row; result valid in thread 0.
 template <typename E, bool kVec>
@@ -50,10 +70,10 @@ __device__ inline void row_ms(const typename E::elem *row, int V, float c, float
     const vec16 *vrow = reinterpret_cast<const vec16 *>(row);
     const int nvec = V / P;  // V * sizeof(elem) is a multiple of 16 on this path
     int i = tid;
-    for (; i + (kRowUnroll - 1) * kBlock < nvec; i += kRowUnroll * kBlock) {
+    for (; i + (kRowUnroll - 1) * kRowBlock < nvec; i += kRowUnroll * kRowBlock) {
       vec16 w[kRowUnroll];
 #pragma unroll
-      for (int u = 0; u < kRowUnroll; ++u) w[u] = __builtin_nontemporal_load(vrow + i + u * kBlock);
+      for (int u = 0; u < kRowUnroll; ++u) w[u] = stream_load(vrow + i + u * kRowBlock);
 #pragma unroll
       for (int u = 0; u < kRowUnroll; ++u) {
         float x[P];
@@ -61,39 +81,39 @@ __device__ inline void row_ms(const typename E::elem *row, int V, float c, float
         ms_fold<P>(m[u], s[u], x, c);
       }
     }
-    for (; i < nvec; i += kBlock) {
-      vec16 w = __builtin_nontemporal_load(vrow + i);
+    for (; i < nvec; i += kRowBlock) {
+      vec16 w = stream_load(vrow + i);
       float x[P];
       E::unpack(w, x);
       ms_fold<P>(m[0], s[0], x, c);
     }
   } else {
     int i = tid;
-    for (; i + (kRowUnroll - 1) * kBlock < V; i += kRowUnroll * kBlock) {
+    for (; i + (kRowUnroll - 1) * kRowBlock < V; i += kRowUnroll * kRowBlock) {
       float x[kRowUnroll];
 #pragma unroll
-      for (int u = 0; u < kRowUnroll; ++u) x[u] = E::at(row, i + u * kBlock);
+      for (int u = 0; u < kRowUnroll; ++u) x[u] = E::at(row, i + u * kRowBlock);
 #pragma unroll
       for (int u = 0; u < kRowUnroll; ++u) ms_fold<1>(m[u], s[u], &x[u], c);
     }
-    for (; i < V; i += kBlock) {
+    for (; i < V; i += kRowBlock) {
       float x = E::at(row, i);
       ms_fold<1>(m[0], s[0], &x, c);
     }
   }
 #pragma unroll
   for (int u = 1; u < kRowUnroll; ++u) ms_merge(m[0], s[0], m[u], s[u], c);
-  block_ms(m[0], s[0], c, lds);
+  block_ms<kRowBlock / 64>(m[0], s[0], c, lds);
   m_out = m[0];
   s_out = s[0];
 }
 
 template <typename E, bool kVec>
-__global__ __launch_bounds__(kBlock) void kr_rowstats(
+__global__ __launch_bounds__(kRowBlock) void kr_rowstats(
     const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
     const int32_t *__restrict__ drafts, int gamma, int V, float cp, float cq,
     RowStats *__restrict__ stats, float *__restrict__ alpha_ws, float *__restrict__ alpha_out) {
-  __shared__ float lds[2 * kWaves];
+  __shared__ float lds[2 * (kRowBlock / 64)];
   const int64_t rp = blockIdx.x;           // (b * K + k) * gamma + j
   const int64_t bk = rp / gamma;
   const int64_t j = rp - bk * gamma;

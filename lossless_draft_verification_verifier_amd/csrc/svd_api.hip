@@ -144,7 +144,7 @@ int run(const void *p_logits, const void *q_logits, const int32_t *drafts, int64
 
   CallTimer tm(stream);
   tm.mark(SVD_KERNEL_ROWSTATS);
-  SVD_LAUNCH(kr_rowstats<E, kVec>, dim3(rp), dim3(kBlock), stream, p, q, drafts, G, V, cp, cq,
+  SVD_LAUNCH(kr_rowstats<E, kVec>, dim3(rp), dim3(kRowBlock), stream, p, q, drafts, G, V, cp, cq,
              stats, alpha_ws, alpha);
   if (beta) {
     tm.mark(SVD_KERNEL_BETA);

@@ -81,8 +81,9 @@ __device__ inline void ms_merge(float &m, float &s, float mo, float so, float c)
   s = a + b;
 }
 
-// Workgroup-wide merge of (max, sum); the result is valid in thread 0.
-__device__ inline void block_ms(float &m, float &s, float c, float *lds /* 2*kWaves */) {
+// Workgroup-wide merge of (max, sum) over NW waves; the result is valid in thread 0.
+template <int NW>
+__device__ inline void block_ms(float &m, float &s, float c, float *lds /* 2*NW */) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     float mo = __shfl_xor(m, off, 64);
@@ -98,7 +99,7 @@ __device__ inline void block_ms(float &m, float &s, float c, float *lds /* 2*kWa
   if (threadIdx.x == 0) {
     m = lds[0];
     s = lds[1];
-    for (int i = 1; i < kWaves; ++i) ms_merge(m, s, lds[2 * i], lds[2 * i + 1], c);
+    for (int i = 1; i < NW; ++i) ms_merge(m, s, lds[2 * i], lds[2 * i + 1], c);
   }
   __syncthreads();
 }
