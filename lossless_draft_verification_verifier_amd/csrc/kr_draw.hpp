@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kBlock) void kr_draw_pass(
         ap += wp;
         aq += wq;
         last_pos = v;
-      } else if (wp > 0.0 && wp >= dn * wq) {
+      } else if (wp > 0.0 && wp >= dn * wq) {  // rare: inside the margin
         const int i = atomicAdd(&n_unc, 1);
         if (i < kUncCap) unc[i] = DrawUnc{wp, wq, v, 0};
       }
