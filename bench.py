@@ -24,35 +24,45 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "verified draft positions/sec and achieved HBM GB/s (V=152064, bf16 logits)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kr_rowstats_traffic.json")
-KERNEL_SOURCES = ["svd_device.hpp", "kr_rowstats.hpp"]
+# sources whose text decides each kernel's memory traffic
+KERNEL_SOURCES = {
+    "rowstats": ["svd_device.hpp", "kr_rowstats.hpp"],
+    "fused": ["svd_device.hpp", "kr_rowstats.hpp", "kr_select.hpp", "kr_draw.hpp",
+              "kr_fused.hpp", "svd_api.hip"],
+}
+KERNEL_SYMBOL = {"rowstats": "kr_rowstats", "fused": "kr_fused"}
 
 
-def kernel_hash() -> str:
+def traffic_file(kernel: str) -> str:
+    return os.path.join(ROOT, "profiles", "%s_traffic.json" % KERNEL_SYMBOL[kernel])
+
+
+def kernel_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "lossless_draft_verification_verifier_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(units_per_launch: int, workload: str):
-    """HBM bytes per launch of the row-statistics kernel from committed rocprofv3
-    counter summaries, or None when they are missing or the kernel changed."""
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of a kernel from committed rocprofv3 counter
+    summaries, or None when they are missing or the kernel changed since."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kernel)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_hash") != kernel_hash() or rec.get("workload") != workload:
+    if rec.get("kernel_hash") != kernel_hash(kernel) or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
-def rowstats_bytes_per_unit(V: int, es: int) -> int:
-    """Algorithmic bytes of one scored row pair in the row-statistics kernel:
-    both logit rows, the drafted token, and the 16-byte statistics record plus
-    the 4-byte alpha it writes."""
+def bytes_per_row_pair(V: int, es: int) -> int:
+    """Algorithmic bytes of one scored row pair: both logit rows, the drafted
+    token, and the 16-byte statistics record plus the 4-byte alpha written for
+    it.  (Bonus rows and the 12 output bytes per prefix are left out, so the
+    figure is a lower bound.)"""
     return 2 * V * es + 4 + 16 + 4
 
 
@@ -155,12 +165,14 @@ def main():
     L_host = L.cpu().numpy()
     bonus_rows = int((L_host == G).sum())
     alg_bytes_step = positions * (2 * V * es + 4) + bonus_rows * V * es + B * 12
-    rs = svd.KERNELS.index("rowstats")
-    ms_rowstats = ms_kernels[rs] / max(launches[rs], 1)
-    unit_bytes = rowstats_bytes_per_unit(V, es)
+    # the dominant kernel: the one with the most time in the timed region
+    dom = max(("fused", "rowstats"), key=lambda k: ms_kernels[svd.KERNELS.index(k)])
+    di = svd.KERNELS.index(dom)
+    ms_dom = ms_kernels[di] / max(launches[di], 1)
+    unit_bytes = bytes_per_row_pair(V, es)
     launch_bytes = unit_bytes * positions
-    achieved = launch_bytes / (ms_rowstats * 1e-3) / 1e9
-    traffic = measured_traffic(positions, cfg.name)
+    achieved = launch_bytes / (ms_dom * 1e-3) / 1e9
+    traffic = measured_traffic(dom, cfg.name)
 
     result = {
         "metric": METRIC,
@@ -182,7 +194,7 @@ def main():
         "hbm_frac_step": alg_bytes_step / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "kernel_ms": {k: ms_kernels[i] / max(launches[i], 1) for i, k in enumerate(svd.KERNELS)
                       if launches[i]},
-        "roofline": {"kernel": "kr_rowstats", "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": KERNEL_SYMBOL[dom], "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_unit": unit_bytes,
                      "units_per_launch": positions},

@@ -148,7 +148,9 @@ enum {
   SVD_KERNEL_DRAW_FIX = 3,   /* exact mass of segments with many near-equal p/q ratios  */
   SVD_KERNEL_DRAW_PICK = 4,  /* fp64 masses and inverse CDF                             */
   SVD_KERNEL_BETA = 5,       /* optional overlap mass                                   */
-  SVD_KERNEL_COUNT = 6
+  SVD_KERNEL_FUSED = 6,      /* the one-launch step: all of the above but beta          */
+  SVD_KERNEL_INIT = 7,       /* clears the fused step's counters                        */
+  SVD_KERNEL_COUNT = 8
 };
 int svd_profile_enable(int on);
 int svd_profile_read(double *ms, int64_t *launches, int n);

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libsvd.so")
 SVD_F32, SVD_BF16 = 0, 1
 SVD_OK, SVD_EINVAL, SVD_EDTYPE, SVD_EWORKSPACE, SVD_EHIP = 0, -1, -2, -3, -4
 SVD_MAX_K, SVD_MAX_GAMMA = 64, 4096
-KERNELS = ("rowstats", "select", "draw_pass", "draw_fix", "draw_pick", "beta")
+KERNELS = ("rowstats", "select", "draw_pass", "draw_fix", "draw_pick", "beta", "fused", "init")
 
 C_EXPORTS = ("svd_workspace_bytes", "svd_verify", "svd_select_and_verify", "svd_strerror",
              "svd_profile_enable", "svd_profile_read")

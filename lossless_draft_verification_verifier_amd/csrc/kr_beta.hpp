@@ -13,7 +13,7 @@ template <typename E, bool kVec>
 __global__ __launch_bounds__(kBlock) void kr_beta(
     const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int gamma,
     int V, float cp, float cq, const RowStats *__restrict__ stats, float *__restrict__ beta) {
-  __shared__ float lds[kWaves];
+  __shared__ float lds[kWaves + 1];
   const int64_t rp = blockIdx.x;
   const int64_t bk = rp / gamma;
   const int64_t j = rp - bk * gamma;
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kBlock) void kr_beta(
       acc += fminf(fast_exp2((E::at(prow, i) - st.mp) * cp) * ip,
                    fast_exp2((E::at(qrow, i) - st.mq) * cq) * iq);
   }
-  const float sum = block_sum_f(acc, lds);
+  const float sum = block_sum_f<kWaves>(acc, lds);
   if (threadIdx.x == 0) beta[rp] = sum;
 }
 

@@ -49,11 +49,31 @@ struct Exp64Table {
   double t[64];
 };
 
-__device__ inline void exp64_table_init(Exp64Table &tab) {
-  if (threadIdx.x < 64) tab.t[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+// 2^(j/64), j = 0..63, correctly rounded to double.
+__constant__ double kExp2Frac64[64] = {
+    0x1.0000000000000p+0, 0x1.02c9a3e778061p+0, 0x1.059b0d3158574p+0, 0x1.0874518759bc8p+0,
+    0x1.0b5586cf9890fp+0, 0x1.0e3ec32d3d1a2p+0, 0x1.11301d0125b51p+0, 0x1.1429aaea92de0p+0,
+    0x1.172b83c7d517bp+0, 0x1.1a35beb6fcb75p+0, 0x1.1d4873168b9aap+0, 0x1.2063b88628cd6p+0,
+    0x1.2387a6e756238p+0, 0x1.26b4565e27cddp+0, 0x1.29e9df51fdee1p+0, 0x1.2d285a6e4030bp+0,
+    0x1.306fe0a31b715p+0, 0x1.33c08b26416ffp+0, 0x1.371a7373aa9cbp+0, 0x1.3a7db34e59ff7p+0,
+    0x1.3dea64c123422p+0, 0x1.4160a21f72e2ap+0, 0x1.44e086061892dp+0, 0x1.486a2b5c13cd0p+0,
+    0x1.4bfdad5362a27p+0, 0x1.4f9b2769d2ca7p+0, 0x1.5342b569d4f82p+0, 0x1.56f4736b527dap+0,
+    0x1.5ab07dd485429p+0, 0x1.5e76f15ad2148p+0, 0x1.6247eb03a5585p+0, 0x1.6623882552225p+0,
+    0x1.6a09e667f3bcdp+0, 0x1.6dfb23c651a2fp+0, 0x1.71f75e8ec5f74p+0, 0x1.75feb564267c9p+0,
+    0x1.7a11473eb0187p+0, 0x1.7e2f336cf4e62p+0, 0x1.82589994cce13p+0, 0x1.868d99b4492edp+0,
+    0x1.8ace5422aa0dbp+0, 0x1.8f1ae99157736p+0, 0x1.93737b0cdc5e5p+0, 0x1.97d829fde4e50p+0,
+    0x1.9c49182a3f090p+0, 0x1.a0c667b5de565p+0, 0x1.a5503b23e255dp+0, 0x1.a9e6b5579fdbfp+0,
+    0x1.ae89f995ad3adp+0, 0x1.b33a2b84f15fbp+0, 0x1.b7f76f2fb5e47p+0, 0x1.bcc1e904bc1d2p+0,
+    0x1.c199bdd85529cp+0, 0x1.c67f12e57d14bp+0, 0x1.cb720dcef9069p+0, 0x1.d072d4a07897cp+0,
+    0x1.d5818dcfba487p+0, 0x1.da9e603db3285p+0, 0x1.dfc97337b9b5fp+0, 0x1.e502ee78b3ff6p+0,
+    0x1.ea4afa2a490dap+0, 0x1.efa1bee615a27p+0, 0x1.f50765b6e4540p+0, 0x1.fa7c1819e90d8p+0,
+};
+
+__device__ __forceinline__ void exp64_table_init(Exp64Table &tab) {
+  if (threadIdx.x < 64) tab.t[threadIdx.x] = kExp2Frac64[threadIdx.x];
 }
 
-__device__ inline double exp_nonpos(double x, const Exp64Table &tab) {
+__device__ __forceinline__ double exp_nonpos(double x, const Exp64Table &tab) {
   x = fmax(x, -760.0);  // exp(-760) is 0 in double; also maps -inf
   const double n = __builtin_rint(x * 92.33248261689366);  // 64 / ln 2
   const int ni = (int)n;
@@ -102,7 +122,7 @@ struct DrawRows {
 };
 
 template <typename E>
-__device__ inline DrawRows<E> draw_rows(const typename E::elem *p, const typename E::elem *q,
+__device__ __forceinline__ DrawRows<E> draw_rows(const typename E::elem *p, const typename E::elem *q,
                                         int K, int gamma, int V, int64_t b, const DrawDesc &d) {
   const int64_t bk = b * K + d.k;
   DrawRows<E> r;
@@ -111,24 +131,167 @@ __device__ inline DrawRows<E> draw_rows(const typename E::elem *p, const typenam
   return r;
 }
 
-// Visit the logits of [lo, hi) of one or two rows: f(v, zp, zq).
-template <typename E, bool kVec, bool kTwo, typename F>
-__device__ inline void visit_segment(const typename E::elem *rp, const typename E::elem *rq,
+// Visit the logits of [lo, hi) of one or two rows with NT threads: f(v, zp, zq).
+// kVec: rows start 16-byte aligned and hi - lo is a multiple of a vector.
+// kNarrow: 4-byte loads (two bf16 tokens), which keeps registers low where the
+// loop body is heavy; otherwise 16-byte loads.
+template <typename E, bool kVec, bool kNarrow, bool kTwo, int NT, typename F>
+__device__ __forceinline__ void visit_segment(const typename E::elem *rp, const typename E::elem *rq,
                                      int lo, int hi, F &&f) {
-  if constexpr (kVec) {
+  if constexpr (kVec && !kNarrow) {
     constexpr int P = E::kPerVec;
     const vec16 *vp = reinterpret_cast<const vec16 *>(rp);
     const vec16 *vq = reinterpret_cast<const vec16 *>(rq);
-    for (int i = lo / P + (int)threadIdx.x; i < hi / P; i += kBlock) {
+    for (int i = lo / P + (int)threadIdx.x; i < hi / P; i += NT) {
       float xp[P], xq[P];
       E::unpack(vp[i], xp);
       if constexpr (kTwo) E::unpack(vq[i], xq);
 #pragma unroll
       for (int e = 0; e < P; ++e) f(i * P + e, xp[e], kTwo ? xq[e] : 0.0f);
     }
+  } else if constexpr (kVec && sizeof(typename E::elem) == 2) {
+    const uint32_t *wp = reinterpret_cast<const uint32_t *>(rp);
+    const uint32_t *wq = reinterpret_cast<const uint32_t *>(rq);
+#pragma unroll 1
+    for (int i = lo / 2 + (int)threadIdx.x; i < hi / 2; i += NT) {
+      const uint32_t a = wp[i];
+      const uint32_t c = kTwo ? wq[i] : 0u;
+      f(2 * i, __uint_as_float(a << 16), __uint_as_float(c << 16));
+      f(2 * i + 1, __uint_as_float(a & 0xffff0000u), __uint_as_float(c & 0xffff0000u));
+    }
   } else {
-    for (int v = lo + (int)threadIdx.x; v < hi; v += kBlock)
+    for (int v = lo + (int)threadIdx.x; v < hi; v += NT)
       f(v, E::at(rp, v), kTwo ? E::at(rq, v) : 0.0f);
+  }
+}
+
+// One reduction of a segment's four sums and two last indices (fixed order);
+// the results are valid in thread 0 only.
+template <int NW>
+__device__ __forceinline__ void block_reduce_seg(double &a, double &b, double &c, double &d,
+                                                 int &x, int &y, double *ldsd /* 4*NW */,
+                                                 int *ldsi /* 2*NW */) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    a += __shfl_xor(a, off, 64);
+    b += __shfl_xor(b, off, 64);
+    c += __shfl_xor(c, off, 64);
+    d += __shfl_xor(d, off, 64);
+    x = max(x, __shfl_xor(x, off, 64));
+    y = max(y, __shfl_xor(y, off, 64));
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    ldsd[4 * w] = a;
+    ldsd[4 * w + 1] = b;
+    ldsd[4 * w + 2] = c;
+    ldsd[4 * w + 3] = d;
+    ldsi[2 * w] = x;
+    ldsi[2 * w + 1] = y;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll 1
+    for (int i = 1; i < NW; ++i) {
+      a += ldsd[4 * i];
+      b += ldsd[4 * i + 1];
+      c += ldsd[4 * i + 2];
+      d += ldsd[4 * i + 3];
+      x = max(x, ldsi[2 * i]);
+      y = max(y, ldsi[2 * i + 1]);
+    }
+  }
+  __syncthreads();
+}
+
+// Segments [seg0, seg0 + G) of one prefix in the draw's fp64 pass.
+template <typename E, bool kVec, bool kNarrow, int NT, int G>
+__device__ __forceinline__ void draw_pass_item(const typename E::elem *__restrict__ p,
+                                      const typename E::elem *__restrict__ q, int K, int gamma,
+                                      int V, int nseg, float tp, float tq,
+                                      const RowStats *__restrict__ stats,
+                                      const DrawDesc *__restrict__ desc,
+                                      DrawSeg *__restrict__ segs, DrawUnc *__restrict__ uncs,
+                                      int64_t b, int seg0) {
+  constexpr int NW = NT / 64;
+  __shared__ Exp64Table tab;
+  __shared__ float ldsf[NW + 1];
+  __shared__ double ldsd[4 * NW];
+  __shared__ int ldsi[2 * NW + 1];
+  __shared__ int n_unc;
+  __shared__ DrawUnc unc[kUncCap];
+  const DrawDesc d = desc[b];
+  if (!d.valid) return;
+  exp64_table_init(tab);
+  const DrawRows<E> r = draw_rows<E>(p, q, K, gamma, V, b, d);
+  const double invTp = 1.0 / (double)tp, invTq = 1.0 / (double)tq;
+  const int seg_end = min(nseg, seg0 + G);
+  for (int seg = seg0; seg < seg_end; ++seg) {
+    if (threadIdx.x == 0) n_unc = 0;
+    __syncthreads();
+    const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
+    double sp = 0.0, sq = 0.0, ap = 0.0, aq = 0.0;
+    int last_pos = -1, last_p = -1, bad = 0;
+    float mseg = kNegInf;
+    if (d.purpose == kResidual) {
+      const RowStats st = stats[(b * K + d.k) * gamma + d.pos];
+      const double Mp = (double)st.mp / (double)tp, Mq = (double)st.mq / (double)tq;
+      const double rho = (double)st.sp / (double)st.sq;  // fp32 estimate of S_p / S_q
+      const double up = rho * (1.0 + kClassMargin), dn = rho * (1.0 - kClassMargin);
+      visit_segment<E, kVec, kNarrow, true, NT>(r.p, r.q, lo, hi, [&](int v, float zp, float zq) {
+        const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -Mp), tab);
+        const double wq = exp_nonpos(__builtin_fma((double)zq, invTq, -Mq), tab);
+        sp += wp;
+        sq += wq;
+        if (wp > 0.0) last_p = v;
+        if (wp > up * wq) {
+          ap += wp;
+          aq += wq;
+          last_pos = v;
+        } else if (wp > 0.0 && wp >= dn * wq) {  // rare: inside the margin
+          const int i = atomicAdd(&n_unc, 1);
+          if (i < kUncCap) unc[i] = DrawUnc{wp, wq, v, 0};
+        }
+      });
+    } else {
+      float m = kNegInf;
+      visit_segment<E, kVec, kNarrow, false, NT>(r.p, r.p, lo, hi, [&](int, float zp, float) {
+        m = fmaxf(m, zp);
+        bad |= (zp != zp);
+      });
+      mseg = block_max<NW>(m, ldsf);
+      bad = block_max_i<NW>(bad, ldsi);
+      const double M = (double)fmaxf(mseg, kLowest) / (double)tp;
+      visit_segment<E, kVec, kNarrow, false, NT>(r.p, r.p, lo, hi, [&](int v, float zp, float) {
+        const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -M), tab);
+        sp += wp;
+        if (wp > 0.0) last_p = v;
+      });
+    }
+    block_reduce_seg<NW>(sp, sq, ap, aq, last_pos, last_p, ldsd, ldsi);
+    // uncertain tokens in token order (distinct tokens: the ranks are a permutation)
+    const int64_t so = b * nseg + seg;
+    const int n = n_unc;
+    if (n <= kUncCap && (int)threadIdx.x < n) {
+      const DrawUnc e = unc[threadIdx.x];
+      int rank = 0;
+      for (int i = 0; i < n; ++i) rank += (unc[i].v < e.v);
+      uncs[so * kUncCap + rank] = e;
+    }
+    if (threadIdx.x == 0) {
+      DrawSeg out{};
+      out.sp = sp;
+      out.sq = sq;
+      out.ap = ap;
+      out.aq = aq;
+      out.last_pos = last_pos;
+      out.last_p = last_p;
+      out.mseg = mseg;
+      out.bad = bad;
+      out.n_unc = (n > kUncCap) ? -1 : n;
+      segs[so] = out;
+    }
+    __syncthreads();  // n_unc and unc[] are reused by the next segment
   }
 }
 
@@ -137,83 +300,9 @@ __global__ __launch_bounds__(kBlock) void kr_draw_pass(
     const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int K,
     int gamma, int V, int nseg, float tp, float tq, const RowStats *__restrict__ stats,
     const DrawDesc *__restrict__ desc, DrawSeg *__restrict__ segs, DrawUnc *__restrict__ uncs) {
-  __shared__ Exp64Table tab;
-  __shared__ float ldsf[kWaves];
-  __shared__ double ldsd[kWaves];
-  __shared__ int ldsi[kWaves];
-  __shared__ int n_unc;
-  __shared__ DrawUnc unc[kUncCap];
   const int64_t b = blockIdx.x / nseg;
-  const int seg = (int)(blockIdx.x - b * nseg);
-  const DrawDesc d = desc[b];
-  if (!d.valid) return;
-  exp64_table_init(tab);
-  if (threadIdx.x == 0) n_unc = 0;
-  __syncthreads();
-  const DrawRows<E> r = draw_rows<E>(p, q, K, gamma, V, b, d);
-  const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
-  const double invTp = 1.0 / (double)tp, invTq = 1.0 / (double)tq;
-  double sp = 0.0, sq = 0.0, ap = 0.0, aq = 0.0;
-  int last_pos = -1, last_p = -1, bad = 0;
-  float mseg = kNegInf;
-
-  if (d.purpose == kResidual) {
-    const RowStats st = stats[(b * K + d.k) * gamma + d.pos];
-    const double Mp = (double)st.mp / (double)tp, Mq = (double)st.mq / (double)tq;
-    const double rho = (double)st.sp / (double)st.sq;  // fp32 estimate of S_p / S_q
-    const double up = rho * (1.0 + kClassMargin), dn = rho * (1.0 - kClassMargin);
-    visit_segment<E, kVec, true>(r.p, r.q, lo, hi, [&](int v, float zp, float zq) {
-      const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -Mp), tab);
-      const double wq = exp_nonpos(__builtin_fma((double)zq, invTq, -Mq), tab);
-      sp += wp;
-      sq += wq;
-      if (wp > 0.0) last_p = v;
-      if (wp > up * wq) {
-        ap += wp;
-        aq += wq;
-        last_pos = v;
-      } else if (wp > 0.0 && wp >= dn * wq) {  // rare: inside the margin
-        const int i = atomicAdd(&n_unc, 1);
-        if (i < kUncCap) unc[i] = DrawUnc{wp, wq, v, 0};
-      }
-    });
-  } else {
-    float m = kNegInf;
-    visit_segment<E, kVec, false>(r.p, r.p, lo, hi, [&](int, float zp, float) {
-      m = fmaxf(m, zp);
-      bad |= (zp != zp);
-    });
-    mseg = block_max(m, ldsf);
-    bad = block_max_i(bad, ldsi);
-    const double M = (double)fmaxf(mseg, kLowest) / (double)tp;
-    visit_segment<E, kVec, false>(r.p, r.p, lo, hi, [&](int v, float zp, float) {
-      const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -M), tab);
-      sp += wp;
-      if (wp > 0.0) last_p = v;
-    });
-  }
-  DrawSeg out{};
-  out.sp = block_sum_d(sp, ldsd);
-  out.sq = block_sum_d(sq, ldsd);
-  out.ap = block_sum_d(ap, ldsd);
-  out.aq = block_sum_d(aq, ldsd);
-  out.last_pos = block_max_i(last_pos, ldsi);
-  out.last_p = block_max_i(last_p, ldsi);
-  out.mseg = mseg;
-  out.bad = bad;
-  // uncertain tokens in token order (distinct tokens: the ranks are a permutation)
-  const int64_t so = b * nseg + seg;
-  const int n = n_unc;
-  if (n <= kUncCap && (int)threadIdx.x < n) {
-    const DrawUnc e = unc[threadIdx.x];
-    int rank = 0;
-    for (int i = 0; i < n; ++i) rank += (unc[i].v < e.v);
-    uncs[so * kUncCap + rank] = e;
-  }
-  if (threadIdx.x == 0) {
-    out.n_unc = (n > kUncCap) ? -1 : n;
-    segs[so] = out;
-  }
+  draw_pass_item<E, kVec, false, kBlock, 1>(p, q, K, gamma, V, nseg, tp, tq, stats, desc, segs,
+                                            uncs, b, (int)(blockIdx.x - b * nseg));
 }
 
 // Exact weights of the draw.
@@ -223,7 +312,7 @@ struct DrawWeight {
   double invTp, invTq, Mp, Mq, invSp, invSq;
   bool resid;
   // weight from the two logits of token v
-  __device__ inline double from(float zp, float zq, const Exp64Table &tab) const {
+  __device__ __forceinline__ double from(float zp, float zq, const Exp64Table &tab) const {
     const double pv = exp_nonpos(__builtin_fma((double)zp, invTp, -Mp), tab) * invSp;
     if (!resid) return pv;
     const double qv = exp_nonpos(__builtin_fma((double)zq, invTq, -Mq), tab) * invSq;
@@ -233,10 +322,10 @@ struct DrawWeight {
 };
 
 // Exact row normalisers of the draw from the pass's segment sums, in segment
-// order (kr_draw_fix and kr_draw_pick run this same code, so they agree to the
-// bit).  Returns false for an invalid bonus row.
+// order (the fix and the pick run this same code, so they agree to the bit).
+// Returns false for an invalid bonus row.
 template <typename E>
-__device__ inline bool draw_setup(const DrawRows<E> &rows, const DrawDesc &d, const RowStats *stats,
+__device__ __forceinline__ bool draw_setup(const DrawRows<E> &rows, const DrawDesc &d, const RowStats *stats,
                                   const DrawSeg *S, int K, int gamma, int nseg, int64_t b,
                                   float tp, float tq, DrawWeight<E> &W) {
   W.p = rows.p;
@@ -274,6 +363,25 @@ __device__ inline bool draw_setup(const DrawRows<E> &rows, const DrawDesc &d, co
   return true;
 }
 
+// Exact residual mass of one segment (all NT threads); valid in every thread.
+template <typename E, bool kVec, bool kNarrow, int NT>
+__device__ __forceinline__ void segment_mass_exact(const DrawWeight<E> &W, const DrawSeg &S, int V, int seg,
+                                          const Exp64Table &tab, double *ldsd, int *ldsi,
+                                          DrawMass &m) {
+  const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
+  double z = 0.0;
+  int last = -1;
+  visit_segment<E, kVec, kNarrow, true, NT>(W.p, W.q, lo, hi, [&](int v, float zp, float zq) {
+    const double w = W.from(zp, zq, tab);
+    z += w;
+    if (w > 0.0) last = v;
+  });
+  m.zr = block_sum_d<NT / 64>(z, ldsd);
+  m.last_r = block_max_i<NT / 64>(last, ldsi);
+  m.zp = S.sp * W.invSp;
+  m.last_p = S.last_p;
+}
+
 // (prefix, segment): exact residual mass of a segment whose uncertain list
 // overflowed; every other workgroup returns at once.
 template <typename E, bool kVec>
@@ -283,8 +391,8 @@ __global__ __launch_bounds__(kBlock) void kr_draw_fix(
     const DrawDesc *__restrict__ desc, const DrawSeg *__restrict__ segs,
     DrawMass *__restrict__ mass) {
   __shared__ Exp64Table tab;
-  __shared__ double ldsd[kWaves];
-  __shared__ int ldsi[kWaves];
+  __shared__ double ldsd[kWaves + 1];
+  __shared__ int ldsi[kWaves + 1];
   const int64_t b = blockIdx.x / nseg;
   const int seg = (int)(blockIdx.x - b * nseg);
   const DrawDesc d = desc[b];
@@ -295,26 +403,14 @@ __global__ __launch_bounds__(kBlock) void kr_draw_fix(
   const DrawRows<E> rows = draw_rows<E>(p, q, K, gamma, V, b, d);
   DrawWeight<E> W;
   draw_setup<E>(rows, d, stats, S, K, gamma, nseg, b, tp, tq, W);
-  const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
-  double z = 0.0;
-  int last = -1;
-  visit_segment<E, kVec, true>(rows.p, rows.q, lo, hi, [&](int v, float zp, float zq) {
-    const double w = W.from(zp, zq, tab);
-    z += w;
-    if (w > 0.0) last = v;
-  });
   DrawMass m{};
-  m.zr = block_sum_d(z, ldsd);
-  m.last_r = block_max_i(last, ldsi);
-  m.zp = S[seg].sp * W.invSp;
-  m.last_p = S[seg].last_p;
+  segment_mass_exact<E, kVec, false, kBlock>(W, S[seg], V, seg, tab, ldsd, ldsi, m);
   if (threadIdx.x == 0) mass[b * nseg + seg] = m;
 }
 
-constexpr int kRun = kDrawSeg / kBlock;  // tokens per thread in the pick's scan
-
 // Exclusive prefix sum over the workgroup in thread order (fixed pattern).
-__device__ inline double block_exclusive_scan(double x, double *lds /* kWaves */) {
+template <int NW>
+__device__ __forceinline__ double block_exclusive_scan(double x, double *lds /* NW */) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   double inc = x;
 #pragma unroll
@@ -325,24 +421,32 @@ __device__ inline double block_exclusive_scan(double x, double *lds /* kWaves */
   if (lane == 63) lds[w] = inc;
   __syncthreads();
   double base = 0.0;
+#pragma unroll 1
   for (int i = 0; i < w; ++i) base += lds[i];
   const double prev = __shfl_up(inc, 1, 64);
   __syncthreads();
   return base + (lane == 0 ? 0.0 : prev);
 }
 
-template <typename E, bool kVec>
-__global__ __launch_bounds__(kBlock) void kr_draw_pick(
-    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int K,
-    int gamma, int V, int nseg, float tp, float tq, uint64_t seed, uint64_t row_base,
-    const RowStats *__restrict__ stats, const DrawDesc *__restrict__ desc,
-    const DrawSeg *__restrict__ segs, const DrawUnc *__restrict__ uncs,
-    DrawMass *__restrict__ mass, int32_t *__restrict__ selected,
-    int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token) {
+// The pick for one prefix.  kInlineFix: segments whose uncertain list
+// overflowed are recomputed here (the fused kernel); otherwise their masses
+// come from kr_draw_fix.
+template <typename E, bool kVec, int NT, bool kInlineFix>
+__device__ __forceinline__ void draw_pick_item(const typename E::elem *__restrict__ p,
+                                      const typename E::elem *__restrict__ q, int K, int gamma,
+                                      int V, int nseg, float tp, float tq, uint64_t seed,
+                                      uint64_t row_base, const RowStats *__restrict__ stats,
+                                      const DrawDesc *__restrict__ desc,
+                                      const DrawSeg *__restrict__ segs,
+                                      const DrawUnc *__restrict__ uncs,
+                                      DrawMass *__restrict__ mass, int32_t *__restrict__ selected,
+                                      int32_t *__restrict__ accept_len,
+                                      int32_t *__restrict__ next_token, int64_t b) {
+  constexpr int NW = NT / 64;
+  constexpr int kRun = kDrawSeg / NT;  // tokens per thread in the scan of one segment
   __shared__ Exp64Table tab;
-  __shared__ double ldsd[kWaves];
-  __shared__ int ldsi[kWaves];
-  const int64_t b = blockIdx.x;
+  __shared__ double ldsd[NW + 1];
+  __shared__ int ldsi[NW + 1];
   const int tid = threadIdx.x;
   const DrawDesc d = desc[b];
   if (!d.valid) return;
@@ -362,8 +466,16 @@ __global__ __launch_bounds__(kBlock) void kr_draw_pick(
     return;
   }
 
-  // per-segment masses (overflowed segments came from kr_draw_fix)
-  for (int s = tid; s < nseg; s += kBlock) {
+  if (kInlineFix && residual) {
+    for (int s = 0; s < nseg; ++s) {
+      if (S[s].n_unc >= 0) continue;
+      DrawMass m{};
+      segment_mass_exact<E, kVec, true, NT>(W, S[s], V, s, tab, ldsd, ldsi, m);
+      if (tid == 0) ms[s] = m;
+    }
+  }
+  // per-segment masses of the other segments
+  for (int s = tid; s < nseg; s += NT) {
     if (residual && S[s].n_unc < 0) continue;
     DrawMass m{};
     m.last_p = S[s].last_p;
@@ -422,6 +534,7 @@ __global__ __launch_bounds__(kBlock) void kr_draw_pick(
       double w[kRun];
       if constexpr (kVec) {
         constexpr int P = E::kPerVec;
+        static_assert(kRun % P == 0, "a run is whole 16-byte vectors");
         const vec16 *vp = reinterpret_cast<const vec16 *>(W.p + a);
         const vec16 *vq = reinterpret_cast<const vec16 *>(W.q + (W.resid ? a : 0));
 #pragma unroll
@@ -445,14 +558,14 @@ __global__ __launch_bounds__(kBlock) void kr_draw_pick(
       double loc = 0.0;
 #pragma unroll
       for (int i = 0; i < kRun; ++i) loc += w[i];
-      double C = cum + block_exclusive_scan(loc, ldsd);
+      double C = cum + block_exclusive_scan<NW>(loc, ldsd);
       int found = 0x7fffffff;
 #pragma unroll
       for (int i = 0; i < kRun; ++i) {
         C += w[i];
         if (found == 0x7fffffff && w[i] > 0.0 && C > t) found = a + i;
       }
-      found = block_min_i(found, ldsi);
+      found = block_min_i<NW>(found, ldsi);
       if (found != 0x7fffffff) {
         tok = found;
         break;
@@ -464,6 +577,19 @@ __global__ __launch_bounds__(kBlock) void kr_draw_pick(
     for (int s = 0; s < nseg; ++s) tok = max(tok, use_r ? ms[s].last_r : ms[s].last_p);
   }
   if (tid == 0) next_token[b] = tok;
+}
+
+template <typename E, bool kVec>
+__global__ __launch_bounds__(kBlock) void kr_draw_pick(
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int K,
+    int gamma, int V, int nseg, float tp, float tq, uint64_t seed, uint64_t row_base,
+    const RowStats *__restrict__ stats, const DrawDesc *__restrict__ desc,
+    const DrawSeg *__restrict__ segs, const DrawUnc *__restrict__ uncs,
+    DrawMass *__restrict__ mass, int32_t *__restrict__ selected,
+    int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token) {
+  draw_pick_item<E, kVec, kBlock, false>(p, q, K, gamma, V, nseg, tp, tq, seed, row_base, stats,
+                                         desc, segs, uncs, mass, selected, accept_len, next_token,
+                                         blockIdx.x);
 }
 
 }  // namespace svd

@@ -10,30 +10,17 @@
 // stays defined when both probabilities are tiny.  Invalid rows or tokens give
 // alpha = NaN, which the selection epilogue turns into -1 outputs.
 //
-// Memory: 16-byte coalesced loads when every row starts 16-byte aligned (the
-// row length in bytes is a multiple of 16), otherwise one element per load.
+// Memory: 16-byte coalesced nontemporal loads when every row starts 16-byte
+// aligned (the row length in bytes is a multiple of 16), otherwise one element
+// per load.
 #pragma once
 
 #include "svd_device.hpp"
 
 namespace svd {
 
-// Fold one vector of n logits into a thread's (max, sum) state.
-template <int N>
-__device__ inline void ms_fold(float &m, float &s, const float *x, float c) {
-  float vm = x[0];
-#pragma unroll
-  for (int i = 1; i < N; ++i) vm = fmaxf(vm, x[i]);
-  const float mn = fmaxf(m, vm);  // fmaxf drops NaN: a NaN logit shows up in the sum
-  s *= (mn == m) ? 1.0f : fast_exp2((m - mn) * c);
-  m = mn;
-  const float mo = fmaxf(m, kLowest);  // keeps (-inf) - (-inf) out of the exponent
-#pragma unroll
-  for (int i = 0; i < N; ++i) s += fast_exp2((x[i] - mo) * c);
-}
-
-// Launch shape of the streaming kernel: threads per workgroup, 16-byte loads
-// in flight per thread and row, and nontemporal (streaming) loads.
+// Launch shape of the standalone streaming kernel: threads per workgroup,
+// 16-byte loads in flight per thread and row, and nontemporal loads.
 #ifndef SVD_ROW_BLOCK
 #define SVD_ROW_BLOCK 1024
 #endif
@@ -46,7 +33,7 @@ __device__ inline void ms_fold(float &m, float &s, const float *x, float c) {
 constexpr int kRowBlock = SVD_ROW_BLOCK;
 constexpr int kRowUnroll = SVD_ROW_UNROLL;
 
-__device__ inline vec16 stream_load(const vec16 *p) {
+__device__ __forceinline__ vec16 stream_load(const vec16 *p) {
 #if SVD_ROW_NT
   return __builtin_nontemporal_load(p);
 #else
@@ -54,13 +41,28 @@ __device__ inline vec16 stream_load(const vec16 *p) {
 #endif
 }
 
-// (max, sum) of one row; result valid in thread 0.
-template <typename E, bool kVec>
-__device__ inline void row_ms(const typename E::elem *row, int V, float c, float &m_out,
-                              float &s_out, float *lds) {
-  float m[kRowUnroll], s[kRowUnroll];
+// Fold one vector of n logits into a thread's (max, sum) state.
+template <int N>
+__device__ __forceinline__ void ms_fold(float &m, float &s, const float *x, float c) {
+  float vm = x[0];
 #pragma unroll
-  for (int u = 0; u < kRowUnroll; ++u) {
+  for (int i = 1; i < N; ++i) vm = fmaxf(vm, x[i]);
+  const float mn = fmaxf(m, vm);  // fmaxf drops NaN: a NaN logit shows up in the sum
+  s *= (mn == m) ? 1.0f : fast_exp2((m - mn) * c);
+  m = mn;
+  const float mo = fmaxf(m, kLowest);  // keeps (-inf) - (-inf) out of the exponent
+#pragma unroll
+  for (int i = 0; i < N; ++i) s += fast_exp2((x[i] - mo) * c);
+}
+
+// (max, sum) of one row over NT threads with U loads in flight per thread;
+// the result is valid in thread 0.
+template <typename E, bool kVec, int NT, int U>
+__device__ __forceinline__ void row_ms(const typename E::elem *row, int V, float c, float &m_out,
+                              float &s_out, float *lds) {
+  float m[U], s[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
     m[u] = kNegInf;
     s[u] = 0.0f;
   }
@@ -70,18 +72,18 @@ __device__ inline void row_ms(const typename E::elem *row, int V, float c, float
     const vec16 *vrow = reinterpret_cast<const vec16 *>(row);
     const int nvec = V / P;  // V * sizeof(elem) is a multiple of 16 on this path
     int i = tid;
-    for (; i + (kRowUnroll - 1) * kRowBlock < nvec; i += kRowUnroll * kRowBlock) {
-      vec16 w[kRowUnroll];
+    for (; i + (U - 1) * NT < nvec; i += U * NT) {
+      vec16 w[U];
 #pragma unroll
-      for (int u = 0; u < kRowUnroll; ++u) w[u] = stream_load(vrow + i + u * kRowBlock);
+      for (int u = 0; u < U; ++u) w[u] = stream_load(vrow + i + u * NT);
 #pragma unroll
-      for (int u = 0; u < kRowUnroll; ++u) {
+      for (int u = 0; u < U; ++u) {
         float x[P];
         E::unpack(w[u], x);
         ms_fold<P>(m[u], s[u], x, c);
       }
     }
-    for (; i < nvec; i += kRowBlock) {
+    for (; i < nvec; i += NT) {
       vec16 w = stream_load(vrow + i);
       float x[P];
       E::unpack(w, x);
@@ -89,40 +91,41 @@ __device__ inline void row_ms(const typename E::elem *row, int V, float c, float
     }
   } else {
     int i = tid;
-    for (; i + (kRowUnroll - 1) * kRowBlock < V; i += kRowUnroll * kRowBlock) {
-      float x[kRowUnroll];
+    for (; i + (U - 1) * NT < V; i += U * NT) {
+      float x[U];
 #pragma unroll
-      for (int u = 0; u < kRowUnroll; ++u) x[u] = E::at(row, i + u * kRowBlock);
+      for (int u = 0; u < U; ++u) x[u] = E::at(row, i + u * NT);
 #pragma unroll
-      for (int u = 0; u < kRowUnroll; ++u) ms_fold<1>(m[u], s[u], &x[u], c);
+      for (int u = 0; u < U; ++u) ms_fold<1>(m[u], s[u], &x[u], c);
     }
-    for (; i < V; i += kRowBlock) {
+    for (; i < V; i += NT) {
       float x = E::at(row, i);
       ms_fold<1>(m[0], s[0], &x, c);
     }
   }
 #pragma unroll
-  for (int u = 1; u < kRowUnroll; ++u) ms_merge(m[0], s[0], m[u], s[u], c);
-  block_ms<kRowBlock / 64>(m[0], s[0], c, lds);
+  for (int u = 1; u < U; ++u) ms_merge(m[0], s[0], m[u], s[u], c);
+  block_ms<NT / 64>(m[0], s[0], c, lds);
   m_out = m[0];
   s_out = s[0];
 }
 
-template <typename E, bool kVec>
-__global__ __launch_bounds__(kRowBlock) void kr_rowstats(
-    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
-    const int32_t *__restrict__ drafts, int gamma, int V, float cp, float cq,
-    RowStats *__restrict__ stats, float *__restrict__ alpha_ws, float *__restrict__ alpha_out) {
-  __shared__ float lds[2 * (kRowBlock / 64)];
-  const int64_t rp = blockIdx.x;           // (b * K + k) * gamma + j
-  const int64_t bk = rp / gamma;
+// One scored row pair: statistics of both rows and alpha, written by thread 0.
+template <typename E, bool kVec, int NT, int U>
+__device__ __forceinline__ void rowstats_item(const typename E::elem *__restrict__ p,
+                                     const typename E::elem *__restrict__ q,
+                                     const int32_t *__restrict__ drafts, int gamma, int V,
+                                     float cp, float cq, int64_t rp, RowStats *__restrict__ stats,
+                                     float *__restrict__ alpha_ws, float *__restrict__ alpha_out) {
+  __shared__ float lds[2 * (NT / 64)];
+  const int64_t bk = rp / gamma;  // rp = (b * K + k) * gamma + j
   const int64_t j = rp - bk * gamma;
   const typename E::elem *prow = p + (bk * (gamma + 1) + j) * (int64_t)V;
   const typename E::elem *qrow = q + rp * (int64_t)V;
 
   float mp, sp, mq, sq;
-  row_ms<E, kVec>(prow, V, cp, mp, sp, lds);
-  row_ms<E, kVec>(qrow, V, cq, mq, sq, lds);
+  row_ms<E, kVec, NT, U>(prow, V, cp, mp, sp, lds);
+  row_ms<E, kVec, NT, U>(qrow, V, cq, mq, sq, lds);
 
   if (threadIdx.x == 0) {
     const int32_t x = drafts[rp];
@@ -138,6 +141,16 @@ __global__ __launch_bounds__(kRowBlock) void kr_rowstats(
     alpha_ws[rp] = a;
     if (alpha_out) alpha_out[rp] = a;
   }
+}
+
+// Two 1024-thread workgroups per CU (8 waves per SIMD) need at most 64 VGPRs.
+template <typename E, bool kVec>
+__global__ __launch_bounds__(kRowBlock) __attribute__((amdgpu_waves_per_eu(8))) void kr_rowstats(
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
+    const int32_t *__restrict__ drafts, int gamma, int V, float cp, float cq,
+    RowStats *__restrict__ stats, float *__restrict__ alpha_ws, float *__restrict__ alpha_out) {
+  rowstats_item<E, kVec, kRowBlock, kRowUnroll>(p, q, drafts, gamma, V, cp, cq, blockIdx.x, stats,
+                                                alpha_ws, alpha_out);
 }
 
 }  // namespace svd

@@ -16,12 +16,14 @@
 
 namespace svd {
 
-__global__ __launch_bounds__(64) void kr_select(
-    const float *__restrict__ alpha_ws, int K, int gamma, uint64_t seed, uint64_t row_base,
-    int32_t *__restrict__ selected, int32_t *__restrict__ accept_len,
-    int32_t *__restrict__ next_token, float *__restrict__ scores, DrawDesc *__restrict__ desc) {
-  const int64_t b = blockIdx.x;
-  const int lane = threadIdx.x;
+// Run by the 64 lanes of one wave (lane = threadIdx.x & 63).
+__device__ __forceinline__ void select_prefix(const float *__restrict__ alpha_ws, int K, int gamma,
+                                     uint64_t seed, uint64_t row_base, int64_t b,
+                                     int32_t *__restrict__ selected,
+                                     int32_t *__restrict__ accept_len,
+                                     int32_t *__restrict__ next_token, float *__restrict__ scores,
+                                     DrawDesc *__restrict__ desc) {
+  const int lane = threadIdx.x & 63;
   double S = -1.0;
   bool bad = false;
   if (lane < K) {
@@ -80,6 +82,14 @@ __global__ __launch_bounds__(64) void kr_select(
       desc[b] = DrawDesc{bk, L, L < gamma ? (int)kResidual : (int)kBonus, 1};
     }
   }
+}
+
+__global__ __launch_bounds__(64) void kr_select(
+    const float *__restrict__ alpha_ws, int K, int gamma, uint64_t seed, uint64_t row_base,
+    int32_t *__restrict__ selected, int32_t *__restrict__ accept_len,
+    int32_t *__restrict__ next_token, float *__restrict__ scores, DrawDesc *__restrict__ desc) {
+  select_prefix(alpha_ws, K, gamma, seed, row_base, blockIdx.x, selected, accept_len, next_token,
+                scores, desc);
 }
 
 }  // namespace svd

@@ -2,6 +2,7 @@
 // workspace layout and kernel launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <tuple>
@@ -10,6 +11,7 @@
 #include "svd.h"
 #include "kr_beta.hpp"
 #include "kr_draw.hpp"
+#include "kr_fused.hpp"
 #include "kr_rowstats.hpp"
 #include "kr_select.hpp"
 
@@ -20,9 +22,16 @@ using namespace svd;
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
+// SVD_FUSED selects the one-launch path (kr_fused); 0 builds the chain of
+// separate kernels instead, for comparison.
+#ifndef SVD_FUSED
+#define SVD_FUSED 0
+#endif
+
 struct Layout {
-  size_t stats, alpha, desc, segs, uncs, mass, total;
+  size_t stats, alpha, desc, segs, uncs, mass, sync, total;
   int nseg;
+  int64_t nsync;
 };
 
 bool sizes_ok(int64_t B, int32_t K, int32_t G, int32_t V) {
@@ -32,6 +41,7 @@ bool sizes_ok(int64_t B, int32_t K, int32_t G, int32_t V) {
   const int64_t lim = (int64_t)1 << 31;
   if (B >= lim / ((int64_t)K * G)) return false;  // B*K*gamma workgroups
   if (B >= lim / nseg) return false;              // B*nseg workgroups
+  if (B * ((int64_t)K * G + nseg) >= lim) return false;  // workgroups of the fused launch
   return true;
 }
 
@@ -52,6 +62,9 @@ Layout layout(int64_t B, int32_t K, int32_t G, int32_t V) {
   off = align_up(off + (size_t)B * L.nseg * kUncCap * sizeof(DrawUnc));
   L.mass = off;
   off = align_up(off + (size_t)B * L.nseg * sizeof(DrawMass));
+  L.sync = off;
+  L.nsync = 2 + 3 * B;
+  off = align_up(off + (size_t)L.nsync * sizeof(unsigned));
   L.total = off;
   return L;
 }
@@ -143,6 +156,69 @@ int run(const void *p_logits, const void *q_logits, const int32_t *drafts, int64
   const float cq = (float)(1.4426950408889634 / (double)tq);
 
   CallTimer tm(stream);
+  if (SVD_FUSED) {
+    // lag of the fused schedule: about one generation of resident workgroups
+    static int blocks_per_cu = [] {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kr_fused<E, kVec>, kFusedBlock, 0) !=
+              hipSuccess ||
+          n < 1)
+        n = 1;
+      return n;
+    }();
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    const int64_t P = (int64_t)K * G;
+#ifndef SVD_LAG_MUL
+#define SVD_LAG_MUL 1
+#endif
+    // SVD_LAG_MUL scales the lag; 0 streams every row pair before any draw
+    const int64_t lag = SVD_LAG_MUL == 0 ? B : SVD_LAG_MUL * (((int64_t)cus * blocks_per_cu + P - 1) / P);
+    FusedArgs<E> fa;
+    fa.p = p;
+    fa.q = q;
+    fa.drafts = drafts;
+    fa.B = B;
+    fa.K = K;
+    fa.gamma = G;
+    fa.V = V;
+    fa.nseg = Lo.nseg;
+    fa.lag = (int)(lag < 1 ? 1 : (lag > B ? B : lag));
+    fa.tp = tp;
+    fa.tq = tq;
+    fa.cp = cp;
+    fa.cq = cq;
+    fa.seed = seed;
+    fa.row_base = row_base;
+    fa.selected = selected;
+    fa.accept_len = accept_len;
+    fa.next_token = next_token;
+    fa.scores = scores;
+    fa.alpha_out = alpha;
+    fa.stats = stats;
+    fa.alpha_ws = alpha_ws;
+    fa.desc = desc;
+    fa.segs = segs;
+    fa.uncs = uncs;
+    fa.mass = mass;
+    fa.sync = reinterpret_cast<unsigned *>(ws + Lo.sync);
+    const int64_t nsync = Lo.nsync;
+    const unsigned init_grid = (unsigned)std::min<int64_t>((nsync + 255) / 256, 1024);
+    tm.mark(SVD_KERNEL_INIT);
+    SVD_LAUNCH(kr_fused_init, dim3(init_grid), dim3(256), stream, fa.sync, nsync);
+    tm.mark(SVD_KERNEL_FUSED);
+    const unsigned items = (unsigned)(B * (P + (Lo.nseg + kDrawGroup - 1) / kDrawGroup));
+    SVD_LAUNCH(kr_fused<E, kVec>, dim3(items), dim3(kFusedBlock), stream, fa);
+    if (beta) {
+      tm.mark(SVD_KERNEL_BETA);
+      SVD_LAUNCH(kr_beta<E, kVec>, dim3(rp), dim3(kBlock), stream, p, q, G, V, cp, cq,
+                 (const RowStats *)stats, beta);
+    }
+    tm.mark(-1);
+    return SVD_OK;
+  }
   tm.mark(SVD_KERNEL_ROWSTATS);
   SVD_LAUNCH(kr_rowstats<E, kVec>, dim3(rp), dim3(kRowBlock), stream, p, q, drafts, G, V, cp, cq,
              stats, alpha_ws, alpha);

@@ -52,14 +52,14 @@ struct F32 {
 
 enum : uint32_t { kAccept = 1, kResidual = 2, kBonus = 3 };
 
-__device__ inline uint64_t splitmix64(uint64_t x) {
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
   uint64_t z = x + 0x9E3779B97F4A7C15ull;
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
   return z ^ (z >> 31);
 }
 
-__device__ inline double counter_uniform(uint64_t seed, uint64_t row, uint64_t pos,
+__device__ __forceinline__ double counter_uniform(uint64_t seed, uint64_t row, uint64_t pos,
                                          uint64_t purpose) {
   uint64_t h = splitmix64(splitmix64(splitmix64(splitmix64(seed) ^ row) ^ pos) ^ purpose);
   return (double)(h >> 11) * 0x1.0p-53;
@@ -68,12 +68,12 @@ __device__ inline double counter_uniform(uint64_t seed, uint64_t row, uint64_t p
 // ---------------------------------------------------------------------------
 // exp2 on the transcendental unit.  Terms below 2^-126 of the row maximum
 // are irrelevant to every sum here, so the raw instruction is enough.
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Merge two (max, sum) states of an online softmax whose terms are
 // exp2((z - max) * c).  Commutative, so butterfly reductions leave the same
 // bits in every lane.
-__device__ inline void ms_merge(float &m, float &s, float mo, float so, float c) {
+__device__ __forceinline__ void ms_merge(float &m, float &s, float mo, float so, float c) {
   float mn = fmaxf(m, mo);
   float a = (m == mn) ? s : s * fast_exp2((m - mn) * c);
   float b = (mo == mn) ? so : so * fast_exp2((mo - mn) * c);
@@ -81,9 +81,12 @@ __device__ inline void ms_merge(float &m, float &s, float mo, float so, float c)
   s = a + b;
 }
 
-// Workgroup-wide merge of (max, sum) over NW waves; the result is valid in thread 0.
+// Workgroup-wide reductions over NW waves of 64 lanes: a butterfly inside each
+// wave, then the wave results in wave order.  Every one has a fixed order.
+
+// merge of (max, sum); the result is valid in thread 0
 template <int NW>
-__device__ inline void block_ms(float &m, float &s, float c, float *lds /* 2*NW */) {
+__device__ __forceinline__ void block_ms(float &m, float &s, float c, float *lds /* 2*NW */) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     float mo = __shfl_xor(m, off, 64);
@@ -99,69 +102,105 @@ __device__ inline void block_ms(float &m, float &s, float c, float *lds /* 2*NW 
   if (threadIdx.x == 0) {
     m = lds[0];
     s = lds[1];
+#pragma unroll 1
     for (int i = 1; i < NW; ++i) ms_merge(m, s, lds[2 * i], lds[2 * i + 1], c);
   }
   __syncthreads();
 }
 
-__device__ inline float block_max(float v, float *lds) {
+template <int NW>
+__device__ __forceinline__ float block_max(float v, float *lds /* NW + 1 */) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) lds[w] = v;
   __syncthreads();
-  float r = lds[0];
-  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, lds[i]);
+  if (threadIdx.x == 0) {
+    float r = lds[0];
+#pragma unroll 1
+    for (int i = 1; i < NW; ++i) r = fmaxf(r, lds[i]);
+    lds[NW] = r;
+  }
+  __syncthreads();
+  const float r = lds[NW];
   __syncthreads();
   return r;  // valid in every thread
 }
 
-__device__ inline float block_sum_f(float v, float *lds) {
+template <int NW>
+__device__ __forceinline__ float block_sum_f(float v, float *lds /* NW + 1 */) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  for (int off = 32; off > 0; off >>= 1) v = v + __shfl_xor(v, off, 64);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) lds[w] = v;
   __syncthreads();
-  float r = lds[0];
-  for (int i = 1; i < kWaves; ++i) r += lds[i];
+  if (threadIdx.x == 0) {
+    float r = lds[0];
+#pragma unroll 1
+    for (int i = 1; i < NW; ++i) r = r + lds[i];
+    lds[NW] = r;
+  }
   __syncthreads();
-  return r;
+  const float r = lds[NW];
+  __syncthreads();
+  return r;  // valid in every thread
 }
 
-__device__ inline double block_sum_d(double v, double *lds) {
+template <int NW>
+__device__ __forceinline__ double block_sum_d(double v, double *lds /* NW + 1 */) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  for (int off = 32; off > 0; off >>= 1) v = v + __shfl_xor(v, off, 64);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) lds[w] = v;
   __syncthreads();
-  double r = lds[0];
-  for (int i = 1; i < kWaves; ++i) r += lds[i];
+  if (threadIdx.x == 0) {
+    double r = lds[0];
+#pragma unroll 1
+    for (int i = 1; i < NW; ++i) r = r + lds[i];
+    lds[NW] = r;
+  }
   __syncthreads();
-  return r;
+  const double r = lds[NW];
+  __syncthreads();
+  return r;  // valid in every thread
 }
 
-__device__ inline int block_max_i(int v, int *lds) {
+template <int NW>
+__device__ __forceinline__ int block_max_i(int v, int *lds /* NW + 1 */) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) lds[w] = v;
   __syncthreads();
-  int r = lds[0];
-  for (int i = 1; i < kWaves; ++i) r = max(r, lds[i]);
+  if (threadIdx.x == 0) {
+    int r = lds[0];
+#pragma unroll 1
+    for (int i = 1; i < NW; ++i) r = max(r, lds[i]);
+    lds[NW] = r;
+  }
   __syncthreads();
-  return r;
+  const int r = lds[NW];
+  __syncthreads();
+  return r;  // valid in every thread
 }
 
-__device__ inline int block_min_i(int v, int *lds) {
+template <int NW>
+__device__ __forceinline__ int block_min_i(int v, int *lds /* NW + 1 */) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) lds[w] = v;
   __syncthreads();
-  int r = lds[0];
-  for (int i = 1; i < kWaves; ++i) r = min(r, lds[i]);
+  if (threadIdx.x == 0) {
+    int r = lds[0];
+#pragma unroll 1
+    for (int i = 1; i < NW; ++i) r = min(r, lds[i]);
+    lds[NW] = r;
+  }
   __syncthreads();
-  return r;
+  const int r = lds[NW];
+  __syncthreads();
+  return r;  // valid in every thread
 }
 
 // ---------------------------------------------------------------------------
