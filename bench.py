@@ -25,12 +25,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "verified draft positions/sec and achieved HBM GB/s (V=152064, bf16 logits)"
 # sources whose text decides each kernel's memory traffic
-KERNEL_SOURCES = {
-    "rowstats": ["svd_device.hpp", "kr_rowstats.hpp"],
-    "fused": ["svd_device.hpp", "kr_rowstats.hpp", "kr_select.hpp", "kr_draw.hpp",
-              "kr_fused.hpp", "svd_api.hip"],
-}
-KERNEL_SYMBOL = {"rowstats": "kr_rowstats", "fused": "kr_fused"}
+KERNEL_SOURCES = {"rowstats": ["svd_device.hpp", "kr_rowstats.hpp"]}
+KERNEL_SYMBOL = {"rowstats": "kr_rowstats"}
 
 
 def traffic_file(kernel: str) -> str:
@@ -58,6 +54,50 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _counter_per_dispatch(run_dir: str, counter: str, name_part: str):
+    """Mean over dispatches of one rocprofv3 counter (summed over its
+    instances) for the kernels whose name contains name_part."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter or name_part not in row["Kernel_Name"]:
+                    continue
+                key = (f, row["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit("no %s samples for %s under %s" % (counter, name_part, run_dir))
+    return sum(per.values()) / len(per), len(per)
+
+
+def record_traffic(kernel, workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """Write profiles/<kernel>_traffic.json from four rocprofv3 --pmc runs: FETCH_SIZE
+    and WRITE_SIZE of the kernel, and of a plain 1 GiB copy that scales them."""
+    sym = KERNEL_SYMBOL[kernel]
+    fetch, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", sym + "<")
+    write, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", sym + "<")
+    cfetch, _ = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cwrite, _ = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    copy_kib = COPY_BYTES / 1024.0
+    fscale, wscale = cfetch / copy_kib, cwrite / copy_kib
+    hbm = (fetch / fscale + write / wscale) * 1024.0
+    import workloads as W
+    cfg = W.get_config(workload)
+    es = 2 if cfg.dtype == "bf16" else 4
+    alg = bytes_per_row_pair(cfg.V, es) * cfg.B * cfg.K * cfg.gamma
+    rec = {"kernel": sym, "workload": workload, "kernel_hash": kernel_hash(kernel),
+           "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+           "dispatches": [nf, nw], "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
+           "copy_bytes_each_way": COPY_BYTES, "fetch_scale": fscale, "write_scale": wscale,
+           "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": alg,
+           "traffic_over_algorithmic": hbm / alg}
+    with open(traffic_file(kernel), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def bytes_per_row_pair(V: int, es: int) -> int:
     """Algorithmic bytes of one scored row pair: both logit rows, the drafted
     token, and the 16-byte statistics record plus the 4-byte alpha written for
@@ -66,25 +106,33 @@ def bytes_per_row_pair(V: int, es: int) -> int:
     return 2 * V * es + 4 + 16 + 4
 
 
-def cpu_baseline(d, cfg, seed):
-    import numpy as np  # noqa: F401
+def cpu_baseline(d, cfg, seed, seconds=10.0):
+    """The oracle, untuned, on the same batch, repeated until about `seconds`
+    of wall time have passed (at least once)."""
     import oracle
     import workloads as W
     threads = max(1, min(16, os.cpu_count() or 1))
     hp, hq, hd = W.to_host(d["p"]), W.to_host(d["q"]), W.to_host(d["drafts"])
-    t0 = time.perf_counter()
-    oracle.select_and_verify(hp, hq, hd, temp_p=cfg.temp, seed=seed, nthreads=threads)
-    dt = time.perf_counter() - t0
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < seconds:
+        t0 = time.perf_counter()
+        oracle.select_and_verify(hp, hq, hd, temp_p=cfg.temp, seed=seed, nthreads=threads)
+        dt += time.perf_counter() - t0
+        reps += 1
     positions = cfg.B * cfg.K * cfg.gamma
-    return {"value": positions / dt, "unit": "positions/s", "cores": threads, "kind": "oracle",
-            "sample": "the full %s batch (%d prefixes, %d positions), %.2f s wall on %d threads"
-                      % (cfg.name, cfg.B, positions, dt, threads),
+    return {"value": positions * reps / dt, "unit": "positions/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "the full %s batch (%d prefixes, %d positions) %d times, %.1f s wall on %d "
+                      "threads" % (cfg.name, cfg.B, positions, reps, dt, threads),
             "seconds": dt}
+
+
+COPY_BYTES = 1 << 30
 
 
 def calibrate_copy(torch, steps):
     """A plain copy of a known number of bytes, to scale the HBM counters."""
-    n = 1 << 29  # 1 GiB of bf16 each way
+    n = COPY_BYTES // 2  # bf16 elements: 1 GiB each way
     x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
     y = torch.empty_like(x)
     torch.cuda.synchronize()
@@ -104,7 +152,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (for counter calibration)")
+    ap.add_argument("--record-traffic", nargs=4, metavar="DIR",
+                    help="write the dominant kernel's traffic record from four rocprofv3 --pmc "
+                         "output folders: FETCH_SIZE and WRITE_SIZE of this workload, then of "
+                         "--calibrate-copy")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic("rowstats", args.workload, *args.record_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the verification path shards by prefix with no "
               "exchange, and multi-GPU runs are not part of this build (got --gpus %d)"
@@ -145,8 +200,10 @@ def main():
     torch.cuda.synchronize()
     svd.svd_profile_read()  # clear
 
-    # timed region: K steps, kernel events recorded on the call's stream
-    svd.svd_profile_enable(True)
+    # timed region: K steps; events around the dominant kernel's launches only,
+    # recorded on the stream the kernel is launched on
+    dom = "rowstats"
+    svd.svd_profile_enable([dom])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -157,16 +214,22 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    svd.svd_profile_enable(False)
+    svd.svd_profile_enable(())
     ms_kernels, launches = svd.svd_profile_read()
     ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # after the timed region: a few steps with every kernel timed, for the breakdown
+    svd.svd_profile_enable("all")
+    for _ in range(min(args.steps, 10)):
+        step()
+    torch.cuda.synchronize()
+    svd.svd_profile_enable(())
+    ms_all, launches_all = svd.svd_profile_read()
 
     positions = B * K * G
     L_host = L.cpu().numpy()
     bonus_rows = int((L_host == G).sum())
     alg_bytes_step = positions * (2 * V * es + 4) + bonus_rows * V * es + B * 12
-    # the dominant kernel: the one with the most time in the timed region
-    dom = max(("fused", "rowstats"), key=lambda k: ms_kernels[svd.KERNELS.index(k)])
     di = svd.KERNELS.index(dom)
     ms_dom = ms_kernels[di] / max(launches[di], 1)
     unit_bytes = bytes_per_row_pair(V, es)
@@ -192,8 +255,8 @@ def main():
                    "parallelism": "single GPU"},
         "achieved_hbm_gbps": alg_bytes_step / (ms_step * 1e-3) / 1e9,
         "hbm_frac_step": alg_bytes_step / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "kernel_ms": {k: ms_kernels[i] / max(launches[i], 1) for i, k in enumerate(svd.KERNELS)
-                      if launches[i]},
+        "kernel_ms": {k: ms_all[i] / max(launches_all[i], 1) for i, k in enumerate(svd.KERNELS)
+                      if launches_all[i]},
         "roofline": {"kernel": KERNEL_SYMBOL[dom], "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_unit": unit_bytes,

@@ -133,13 +133,16 @@ int svd_select_and_verify(const void *p_logits, const void *q_logits, const int3
 const char *svd_strerror(int status);
 
 /*
- * Kernel timing for benchmarks and profiling.  While enabled, every call
- * records HIP events on its stream around each kernel it launches (creating
- * the events on first use).  svd_profile_read() waits for the recorded
- * events, adds up the elapsed milliseconds per kernel into ms[0..n) (index:
- * SVD_KERNEL_*), writes the number of launches per kernel into launches[0..n)
- * (nullable), clears the record and returns SVD_OK.  Not thread-safe; at most
- * 4096 calls are recorded between reads (later ones are not timed).
+ * Kernel timing for benchmarks and profiling.  svd_profile_enable(mask) turns
+ * timing on for the kernels whose bit (1 << SVD_KERNEL_*) is set in mask, and
+ * off for all with mask 0.  While on, every call records a HIP event before
+ * and after each timed launch, on the stream that launch goes to (creating the
+ * events on first use).  svd_profile_read() waits for the recorded events,
+ * adds up the elapsed milliseconds per kernel into ms[0..n) (index:
+ * SVD_KERNEL_*), writes the number of timed launches per kernel into
+ * launches[0..n) (nullable), clears the record and returns SVD_OK.  Not
+ * thread-safe; at most 4096 calls are recorded between reads (later ones are
+ * not timed).
  */
 enum {
   SVD_KERNEL_ROWSTATS = 0,   /* row statistics + alpha (streams every scored row pair) */
@@ -148,11 +151,9 @@ enum {
   SVD_KERNEL_DRAW_FIX = 3,   /* exact mass of segments with many near-equal p/q ratios  */
   SVD_KERNEL_DRAW_PICK = 4,  /* fp64 masses and inverse CDF                             */
   SVD_KERNEL_BETA = 5,       /* optional overlap mass                                   */
-  SVD_KERNEL_FUSED = 6,      /* the one-launch step: all of the above but beta          */
-  SVD_KERNEL_INIT = 7,       /* clears the fused step's counters                        */
-  SVD_KERNEL_COUNT = 8
+  SVD_KERNEL_COUNT = 6
 };
-int svd_profile_enable(int on);
+int svd_profile_enable(unsigned kernel_mask);
 int svd_profile_read(double *ms, int64_t *launches, int n);
 
 #ifdef __cplusplus

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libsvd.so")
 SVD_F32, SVD_BF16 = 0, 1
 SVD_OK, SVD_EINVAL, SVD_EDTYPE, SVD_EWORKSPACE, SVD_EHIP = 0, -1, -2, -3, -4
 SVD_MAX_K, SVD_MAX_GAMMA = 64, 4096
-KERNELS = ("rowstats", "select", "draw_pass", "draw_fix", "draw_pick", "beta", "fused", "init")
+KERNELS = ("rowstats", "select", "draw_pass", "draw_fix", "draw_pick", "beta")
 
 C_EXPORTS = ("svd_workspace_bytes", "svd_verify", "svd_select_and_verify", "svd_strerror",
              "svd_profile_enable", "svd_profile_read")
@@ -57,7 +57,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.svd_strerror.restype = ctypes.c_char_p
     L.svd_strerror.argtypes = [ctypes.c_int]
     L.svd_profile_enable.restype = ctypes.c_int
-    L.svd_profile_enable.argtypes = [ctypes.c_int]
+    L.svd_profile_enable.argtypes = [ctypes.c_uint]
     L.svd_profile_read.restype = ctypes.c_int
     L.svd_profile_read.argtypes = [vp, vp, ctypes.c_int]
     return L
@@ -106,8 +106,15 @@ def svd_strerror(status: int) -> str:
     return _lib.svd_strerror(int(status)).decode()
 
 
-def svd_profile_enable(on: bool) -> int:
-    return int(_lib.svd_profile_enable(1 if on else 0))
+def svd_profile_enable(kernels=()) -> int:
+    """Time the named kernels (names from KERNELS; "all" for every one) in
+    later calls; an empty selection stops timing."""
+    if kernels == "all":
+        kernels = KERNELS
+    mask = 0
+    for k in kernels:
+        mask |= 1 << KERNELS.index(k)
+    return int(_lib.svd_profile_enable(mask))
 
 
 def svd_profile_read():

@@ -133,12 +133,10 @@ __device__ __forceinline__ DrawRows<E> draw_rows(const typename E::elem *p, cons
 
 // Visit the logits of [lo, hi) of one or two rows with NT threads: f(v, zp, zq).
 // kVec: rows start 16-byte aligned and hi - lo is a multiple of a vector.
-// kNarrow: 4-byte loads (two bf16 tokens), which keeps registers low where the
-// loop body is heavy; otherwise 16-byte loads.
-template <typename E, bool kVec, bool kNarrow, bool kTwo, int NT, typename F>
+template <typename E, bool kVec, bool kTwo, int NT, typename F>
 __device__ __forceinline__ void visit_segment(const typename E::elem *rp, const typename E::elem *rq,
                                      int lo, int hi, F &&f) {
-  if constexpr (kVec && !kNarrow) {
+  if constexpr (kVec) {
     constexpr int P = E::kPerVec;
     const vec16 *vp = reinterpret_cast<const vec16 *>(rp);
     const vec16 *vq = reinterpret_cast<const vec16 *>(rq);
@@ -148,16 +146,6 @@ __device__ __forceinline__ void visit_segment(const typename E::elem *rp, const 
       if constexpr (kTwo) E::unpack(vq[i], xq);
 #pragma unroll
       for (int e = 0; e < P; ++e) f(i * P + e, xp[e], kTwo ? xq[e] : 0.0f);
-    }
-  } else if constexpr (kVec && sizeof(typename E::elem) == 2) {
-    const uint32_t *wp = reinterpret_cast<const uint32_t *>(rp);
-    const uint32_t *wq = reinterpret_cast<const uint32_t *>(rq);
-#pragma unroll 1
-    for (int i = lo / 2 + (int)threadIdx.x; i < hi / 2; i += NT) {
-      const uint32_t a = wp[i];
-      const uint32_t c = kTwo ? wq[i] : 0u;
-      f(2 * i, __uint_as_float(a << 16), __uint_as_float(c << 16));
-      f(2 * i + 1, __uint_as_float(a & 0xffff0000u), __uint_as_float(c & 0xffff0000u));
     }
   } else {
     for (int v = lo + (int)threadIdx.x; v < hi; v += NT)
@@ -204,15 +192,15 @@ __device__ __forceinline__ void block_reduce_seg(double &a, double &b, double &c
   __syncthreads();
 }
 
-// Segments [seg0, seg0 + G) of one prefix in the draw's fp64 pass.
-template <typename E, bool kVec, bool kNarrow, int NT, int G>
+// Segment seg of one prefix in the draw's fp64 pass, for the decision d and
+// (residual draws) the drawn row pair's statistics st.
+template <typename E, bool kVec, int NT>
 __device__ __forceinline__ void draw_pass_item(const typename E::elem *__restrict__ p,
-                                      const typename E::elem *__restrict__ q, int K, int gamma,
-                                      int V, int nseg, float tp, float tq,
-                                      const RowStats *__restrict__ stats,
-                                      const DrawDesc *__restrict__ desc,
-                                      DrawSeg *__restrict__ segs, DrawUnc *__restrict__ uncs,
-                                      int64_t b, int seg0) {
+                                               const typename E::elem *__restrict__ q, int K,
+                                               int gamma, int V, int nseg, float tp, float tq,
+                                               const DrawDesc d, const RowStats st,
+                                               DrawSeg *__restrict__ segs,
+                                               DrawUnc *__restrict__ uncs, int64_t b, int seg) {
   constexpr int NW = NT / 64;
   __shared__ Exp64Table tab;
   __shared__ float ldsf[NW + 1];
@@ -220,79 +208,80 @@ __device__ __forceinline__ void draw_pass_item(const typename E::elem *__restric
   __shared__ int ldsi[2 * NW + 1];
   __shared__ int n_unc;
   __shared__ DrawUnc unc[kUncCap];
-  const DrawDesc d = desc[b];
   if (!d.valid) return;
   exp64_table_init(tab);
   const DrawRows<E> r = draw_rows<E>(p, q, K, gamma, V, b, d);
   const double invTp = 1.0 / (double)tp, invTq = 1.0 / (double)tq;
-  const int seg_end = min(nseg, seg0 + G);
-  for (int seg = seg0; seg < seg_end; ++seg) {
-    if (threadIdx.x == 0) n_unc = 0;
-    __syncthreads();
-    const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
-    double sp = 0.0, sq = 0.0, ap = 0.0, aq = 0.0;
-    int last_pos = -1, last_p = -1, bad = 0;
-    float mseg = kNegInf;
-    if (d.purpose == kResidual) {
-      const RowStats st = stats[(b * K + d.k) * gamma + d.pos];
-      const double Mp = (double)st.mp / (double)tp, Mq = (double)st.mq / (double)tq;
-      const double rho = (double)st.sp / (double)st.sq;  // fp32 estimate of S_p / S_q
-      const double up = rho * (1.0 + kClassMargin), dn = rho * (1.0 - kClassMargin);
-      visit_segment<E, kVec, kNarrow, true, NT>(r.p, r.q, lo, hi, [&](int v, float zp, float zq) {
-        const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -Mp), tab);
-        const double wq = exp_nonpos(__builtin_fma((double)zq, invTq, -Mq), tab);
-        sp += wp;
-        sq += wq;
-        if (wp > 0.0) last_p = v;
-        if (wp > up * wq) {
-          ap += wp;
-          aq += wq;
-          last_pos = v;
-        } else if (wp > 0.0 && wp >= dn * wq) {  // rare: inside the margin
-          const int i = atomicAdd(&n_unc, 1);
-          if (i < kUncCap) unc[i] = DrawUnc{wp, wq, v, 0};
-        }
-      });
-    } else {
-      float m = kNegInf;
-      visit_segment<E, kVec, kNarrow, false, NT>(r.p, r.p, lo, hi, [&](int, float zp, float) {
-        m = fmaxf(m, zp);
-        bad |= (zp != zp);
-      });
-      mseg = block_max<NW>(m, ldsf);
-      bad = block_max_i<NW>(bad, ldsi);
-      const double M = (double)fmaxf(mseg, kLowest) / (double)tp;
-      visit_segment<E, kVec, kNarrow, false, NT>(r.p, r.p, lo, hi, [&](int v, float zp, float) {
-        const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -M), tab);
-        sp += wp;
-        if (wp > 0.0) last_p = v;
-      });
-    }
-    block_reduce_seg<NW>(sp, sq, ap, aq, last_pos, last_p, ldsd, ldsi);
-    // uncertain tokens in token order (distinct tokens: the ranks are a permutation)
-    const int64_t so = b * nseg + seg;
-    const int n = n_unc;
-    if (n <= kUncCap && (int)threadIdx.x < n) {
-      const DrawUnc e = unc[threadIdx.x];
-      int rank = 0;
-      for (int i = 0; i < n; ++i) rank += (unc[i].v < e.v);
-      uncs[so * kUncCap + rank] = e;
-    }
-    if (threadIdx.x == 0) {
-      DrawSeg out{};
-      out.sp = sp;
-      out.sq = sq;
-      out.ap = ap;
-      out.aq = aq;
-      out.last_pos = last_pos;
-      out.last_p = last_p;
-      out.mseg = mseg;
-      out.bad = bad;
-      out.n_unc = (n > kUncCap) ? -1 : n;
-      segs[so] = out;
-    }
-    __syncthreads();  // n_unc and unc[] are reused by the next segment
+  if (threadIdx.x == 0) n_unc = 0;
+  __syncthreads();
+  const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
+  double sp = 0.0, sq = 0.0, ap = 0.0, aq = 0.0;
+  int last_pos = -1, last_p = -1, bad = 0;
+  float mseg = kNegInf;
+  if (d.purpose == kResidual) {
+    const double Mp = (double)st.mp / (double)tp, Mq = (double)st.mq / (double)tq;
+    const double rho = (double)st.sp / (double)st.sq;  // fp32 estimate of S_p / S_q
+    const double up = rho * (1.0 + kClassMargin), dn = rho * (1.0 - kClassMargin);
+    visit_segment<E, kVec, true, NT>(r.p, r.q, lo, hi, [&](int v, float zp, float zq) {
+      const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -Mp), tab);
+      const double wq = exp_nonpos(__builtin_fma((double)zq, invTq, -Mq), tab);
+      sp += wp;
+      sq += wq;
+      if (wp > 0.0) last_p = v;
+      if (wp > up * wq) {
+        ap += wp;
+        aq += wq;
+        last_pos = v;
+      } else if (wp > 0.0 && wp >= dn * wq) {  // rare: inside the margin
+        const int i = atomicAdd(&n_unc, 1);
+        if (i < kUncCap) unc[i] = DrawUnc{wp, wq, v, 0};
+      }
+    });
+  } else {
+    float m = kNegInf;
+    visit_segment<E, kVec, false, NT>(r.p, r.p, lo, hi, [&](int, float zp, float) {
+      m = fmaxf(m, zp);
+      bad |= (zp != zp);
+    });
+    mseg = block_max<NW>(m, ldsf);
+    bad = block_max_i<NW>(bad, ldsi);
+    const double M = (double)fmaxf(mseg, kLowest) / (double)tp;
+    visit_segment<E, kVec, false, NT>(r.p, r.p, lo, hi, [&](int v, float zp, float) {
+      const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -M), tab);
+      sp += wp;
+      if (wp > 0.0) last_p = v;
+    });
   }
+  block_reduce_seg<NW>(sp, sq, ap, aq, last_pos, last_p, ldsd, ldsi);
+  // uncertain tokens in token order (distinct tokens: the ranks are a permutation)
+  const int64_t so = b * nseg + seg;
+  const int n = n_unc;
+  if (n <= kUncCap && (int)threadIdx.x < n) {
+    const DrawUnc e = unc[threadIdx.x];
+    int rank = 0;
+    for (int i = 0; i < n; ++i) rank += (unc[i].v < e.v);
+    uncs[so * kUncCap + rank] = e;
+  }
+  if (threadIdx.x == 0) {
+    DrawSeg out{};
+    out.sp = sp;
+    out.sq = sq;
+    out.ap = ap;
+    out.aq = aq;
+    out.last_pos = last_pos;
+    out.last_p = last_p;
+    out.mseg = mseg;
+    out.bad = bad;
+    out.n_unc = (n > kUncCap) ? -1 : n;
+    segs[so] = out;
+  }
+}
+
+// decision and drawn-row statistics from the workspace (separate launches)
+__device__ __forceinline__ RowStats drawn_stats(const RowStats *stats, const DrawDesc &d, int K,
+                                                int gamma, int64_t b) {
+  if (d.valid && d.purpose == kResidual) return stats[(b * K + d.k) * gamma + d.pos];
+  return RowStats{0.0f, 1.0f, 0.0f, 1.0f};
 }
 
 template <typename E, bool kVec>
@@ -301,8 +290,10 @@ __global__ __launch_bounds__(kBlock) void kr_draw_pass(
     int gamma, int V, int nseg, float tp, float tq, const RowStats *__restrict__ stats,
     const DrawDesc *__restrict__ desc, DrawSeg *__restrict__ segs, DrawUnc *__restrict__ uncs) {
   const int64_t b = blockIdx.x / nseg;
-  draw_pass_item<E, kVec, false, kBlock, 1>(p, q, K, gamma, V, nseg, tp, tq, stats, desc, segs,
-                                            uncs, b, (int)(blockIdx.x - b * nseg));
+  const DrawDesc d = desc[b];
+  draw_pass_item<E, kVec, kBlock>(p, q, K, gamma, V, nseg, tp, tq, d,
+                                  drawn_stats(stats, d, K, gamma, b), segs, uncs, b,
+                                  (int)(blockIdx.x - b * nseg));
 }
 
 // Exact weights of the draw.
@@ -325,9 +316,9 @@ struct DrawWeight {
 // order (the fix and the pick run this same code, so they agree to the bit).
 // Returns false for an invalid bonus row.
 template <typename E>
-__device__ __forceinline__ bool draw_setup(const DrawRows<E> &rows, const DrawDesc &d, const RowStats *stats,
-                                  const DrawSeg *S, int K, int gamma, int nseg, int64_t b,
-                                  float tp, float tq, DrawWeight<E> &W) {
+__device__ __forceinline__ bool draw_setup(const DrawRows<E> &rows, const DrawDesc &d,
+                                           const RowStats &st, const DrawSeg *S, int nseg,
+                                           float tp, float tq, DrawWeight<E> &W) {
   W.p = rows.p;
   W.q = rows.q;
   W.invTp = 1.0 / (double)tp;
@@ -335,27 +326,29 @@ __device__ __forceinline__ bool draw_setup(const DrawRows<E> &rows, const DrawDe
   W.resid = d.purpose == kResidual;
   double Sp = 0.0, Sq = 1.0;
   if (W.resid) {
-    const RowStats st = stats[(b * K + d.k) * gamma + d.pos];
     W.Mp = (double)st.mp / (double)tp;
     W.Mq = (double)st.mq / (double)tq;
     Sq = 0.0;
     for (int s = 0; s < nseg; ++s) {
-      Sp += S[s].sp;
-      Sq += S[s].sq;
+      const DrawSeg g = S[s];
+      Sp += g.sp;
+      Sq += g.sq;
     }
   } else {
     float mr = kNegInf;
     int bad = 0;
     for (int s = 0; s < nseg; ++s) {
-      mr = fmaxf(mr, S[s].mseg);
-      bad |= S[s].bad;
+      const DrawSeg g = S[s];
+      mr = fmaxf(mr, g.mseg);
+      bad |= g.bad;
     }
     if (bad || mr == kNegInf || mr == -kNegInf) return false;
     W.Mp = (double)mr / (double)tp;
     W.Mq = 0.0;
     for (int s = 0; s < nseg; ++s) {
-      const double Ms = (double)fmaxf(S[s].mseg, kLowest) / (double)tp;
-      Sp += (S[s].mseg == mr) ? S[s].sp : S[s].sp * exp(Ms - W.Mp);
+      const DrawSeg g = S[s];
+      const double Ms = (double)fmaxf(g.mseg, kLowest) / (double)tp;
+      Sp += (g.mseg == mr) ? g.sp : g.sp * exp(Ms - W.Mp);
     }
   }
   W.invSp = 1.0 / Sp;
@@ -363,15 +356,15 @@ __device__ __forceinline__ bool draw_setup(const DrawRows<E> &rows, const DrawDe
   return true;
 }
 
-// Exact residual mass of one segment (all NT threads); valid in every thread.
-template <typename E, bool kVec, bool kNarrow, int NT>
-__device__ __forceinline__ void segment_mass_exact(const DrawWeight<E> &W, const DrawSeg &S, int V, int seg,
-                                          const Exp64Table &tab, double *ldsd, int *ldsi,
-                                          DrawMass &m) {
+// Exact residual mass of one segment (all NT threads); valid in thread 0.
+template <typename E, bool kVec, int NT>
+__device__ __forceinline__ void segment_mass_exact(const DrawWeight<E> &W, const DrawSeg &S, int V,
+                                                   int seg, const Exp64Table &tab, double *ldsd,
+                                                   int *ldsi, DrawMass &m) {
   const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
   double z = 0.0;
   int last = -1;
-  visit_segment<E, kVec, kNarrow, true, NT>(W.p, W.q, lo, hi, [&](int v, float zp, float zq) {
+  visit_segment<E, kVec, true, NT>(W.p, W.q, lo, hi, [&](int v, float zp, float zq) {
     const double w = W.from(zp, zq, tab);
     z += w;
     if (w > 0.0) last = v;
@@ -402,9 +395,9 @@ __global__ __launch_bounds__(kBlock) void kr_draw_fix(
   __syncthreads();
   const DrawRows<E> rows = draw_rows<E>(p, q, K, gamma, V, b, d);
   DrawWeight<E> W;
-  draw_setup<E>(rows, d, stats, S, K, gamma, nseg, b, tp, tq, W);
+  draw_setup<E>(rows, d, drawn_stats(stats, d, K, gamma, b), S, nseg, tp, tq, W);
   DrawMass m{};
-  segment_mass_exact<E, kVec, false, kBlock>(W, S[seg], V, seg, tab, ldsd, ldsi, m);
+  segment_mass_exact<E, kVec, kBlock>(W, S[seg], V, seg, tab, ldsd, ldsi, m);
   if (threadIdx.x == 0) mass[b * nseg + seg] = m;
 }
 
@@ -428,27 +421,23 @@ __device__ __forceinline__ double block_exclusive_scan(double x, double *lds /* 
   return base + (lane == 0 ? 0.0 : prev);
 }
 
-// The pick for one prefix.  kInlineFix: segments whose uncertain list
-// overflowed are recomputed here (the fused kernel); otherwise their masses
-// come from kr_draw_fix.
-template <typename E, bool kVec, int NT, bool kInlineFix>
-__device__ __forceinline__ void draw_pick_item(const typename E::elem *__restrict__ p,
-                                      const typename E::elem *__restrict__ q, int K, int gamma,
-                                      int V, int nseg, float tp, float tq, uint64_t seed,
-                                      uint64_t row_base, const RowStats *__restrict__ stats,
-                                      const DrawDesc *__restrict__ desc,
-                                      const DrawSeg *__restrict__ segs,
-                                      const DrawUnc *__restrict__ uncs,
-                                      DrawMass *__restrict__ mass, int32_t *__restrict__ selected,
-                                      int32_t *__restrict__ accept_len,
-                                      int32_t *__restrict__ next_token, int64_t b) {
+// The pick for one prefix, for the decision d and the drawn row pair's
+// statistics st.  The masses of segments whose uncertain list overflowed come
+// from kr_draw_fix.
+template <typename E, bool kVec, int NT>
+__device__ __forceinline__ void draw_pick_item(
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int K,
+    int gamma, int V, int nseg, float tp, float tq, uint64_t seed, uint64_t row_base,
+    const DrawDesc d, const RowStats st, const DrawSeg *__restrict__ segs,
+    const DrawUnc *__restrict__ uncs, DrawMass *__restrict__ mass,
+    int32_t *__restrict__ selected, int32_t *__restrict__ accept_len,
+    int32_t *__restrict__ next_token, int64_t b) {
   constexpr int NW = NT / 64;
   constexpr int kRun = kDrawSeg / NT;  // tokens per thread in the scan of one segment
   __shared__ Exp64Table tab;
   __shared__ double ldsd[NW + 1];
   __shared__ int ldsi[NW + 1];
   const int tid = threadIdx.x;
-  const DrawDesc d = desc[b];
   if (!d.valid) return;
   exp64_table_init(tab);
   __syncthreads();
@@ -457,7 +446,7 @@ __device__ __forceinline__ void draw_pick_item(const typename E::elem *__restric
   DrawMass *ms = mass + b * nseg;
   const bool residual = d.purpose == kResidual;
   DrawWeight<E> W;
-  if (!draw_setup<E>(rows, d, stats, S, K, gamma, nseg, b, tp, tq, W)) {
+  if (!draw_setup<E>(rows, d, st, S, nseg, tp, tq, W)) {
     if (tid == 0) {  // invalid bonus row (the scored rows were checked earlier)
       if (selected) selected[b] = -1;
       accept_len[b] = -1;
@@ -466,36 +455,30 @@ __device__ __forceinline__ void draw_pick_item(const typename E::elem *__restric
     return;
   }
 
-  if (kInlineFix && residual) {
-    for (int s = 0; s < nseg; ++s) {
-      if (S[s].n_unc >= 0) continue;
-      DrawMass m{};
-      segment_mass_exact<E, kVec, true, NT>(W, S[s], V, s, tab, ldsd, ldsi, m);
-      if (tid == 0) ms[s] = m;
-    }
-  }
   // per-segment masses of the other segments
   for (int s = tid; s < nseg; s += NT) {
-    if (residual && S[s].n_unc < 0) continue;
+    const DrawSeg g = S[s];
+    if (residual && g.n_unc < 0) continue;
     DrawMass m{};
-    m.last_p = S[s].last_p;
+    m.last_p = g.last_p;
     if (residual) {
-      m.zp = S[s].sp * W.invSp;
-      double z = S[s].ap * W.invSp - S[s].aq * W.invSq;
-      int last = S[s].last_pos;
+      m.zp = g.sp * W.invSp;
+      double z = g.ap * W.invSp - g.aq * W.invSq;
+      int last = g.last_pos;
       const DrawUnc *u = uncs + (b * nseg + s) * kUncCap;
-      for (int i = 0; i < S[s].n_unc; ++i) {
-        const double dd = u[i].wp * W.invSp - u[i].wq * W.invSq;
+      for (int i = 0; i < g.n_unc; ++i) {
+        const DrawUnc e = u[i];
+        const double dd = e.wp * W.invSp - e.wq * W.invSq;
         if (dd > 0.0) {
           z += dd;
-          last = max(last, u[i].v);
+          last = max(last, e.v);
         }
       }
       m.zr = z;
       m.last_r = last;
     } else {
-      const double Ms = (double)fmaxf(S[s].mseg, kLowest) / (double)tp;
-      m.zp = ((S[s].mseg == kNegInf) ? 0.0 : S[s].sp * exp(Ms - W.Mp)) * W.invSp;
+      const double Ms = (double)fmaxf(g.mseg, kLowest) / (double)tp;
+      m.zp = ((g.mseg == kNegInf) ? 0.0 : g.sp * exp(Ms - W.Mp)) * W.invSp;
       m.zr = m.zp;
       m.last_r = m.last_p;
     }
@@ -587,9 +570,11 @@ __global__ __launch_bounds__(kBlock) void kr_draw_pick(
     const DrawSeg *__restrict__ segs, const DrawUnc *__restrict__ uncs,
     DrawMass *__restrict__ mass, int32_t *__restrict__ selected,
     int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token) {
-  draw_pick_item<E, kVec, kBlock, false>(p, q, K, gamma, V, nseg, tp, tq, seed, row_base, stats,
-                                         desc, segs, uncs, mass, selected, accept_len, next_token,
-                                         blockIdx.x);
+  const int64_t b = blockIdx.x;
+  const DrawDesc d = desc[b];
+  draw_pick_item<E, kVec, kBlock>(p, q, K, gamma, V, nseg, tp, tq, seed, row_base, d,
+                                  drawn_stats(stats, d, K, gamma, b), segs, uncs, mass, selected,
+                                  accept_len, next_token, b);
 }
 
 }  // namespace svd

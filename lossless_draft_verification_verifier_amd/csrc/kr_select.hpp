@@ -16,22 +16,24 @@
 
 namespace svd {
 
-// Run by the 64 lanes of one wave (lane = threadIdx.x & 63).
-__device__ __forceinline__ void select_prefix(const float *__restrict__ alpha_ws, int K, int gamma,
-                                     uint64_t seed, uint64_t row_base, int64_t b,
-                                     int32_t *__restrict__ selected,
-                                     int32_t *__restrict__ accept_len,
-                                     int32_t *__restrict__ next_token, float *__restrict__ scores,
-                                     DrawDesc *__restrict__ desc) {
+// Run by the 64 lanes of one wave (lane = threadIdx.x & 63); every lane gets
+// the decision.  Lane 0 writes selected / accept_len (and -1 next_token for an
+// invalid prefix), lane k writes scores[k].
+__device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alpha_ws, int K,
+                                                  int gamma, uint64_t seed, uint64_t row_base,
+                                                  int64_t b, int32_t *__restrict__ selected,
+                                                  int32_t *__restrict__ accept_len,
+                                                  int32_t *__restrict__ next_token,
+                                                  float *__restrict__ scores) {
   const int lane = threadIdx.x & 63;
   double S = -1.0;
   bool bad = false;
   if (lane < K) {
-    const float *a = alpha_ws + ((int64_t)b * K + lane) * gamma;
+    const int64_t base = ((int64_t)b * K + lane) * gamma;
     double prod = 1.0;
     S = 0.0;
     for (int j = 0; j < gamma; ++j) {
-      const float aj = a[j];
+      const float aj = alpha_ws[base + j];
       bad |= (aj != aj);
       prod *= (double)aj;
       S += prod;
@@ -56,12 +58,13 @@ __device__ __forceinline__ void select_prefix(const float *__restrict__ alpha_ws
 
   int L = gamma;
   if (!invalid) {
-    const float *ak = alpha_ws + ((int64_t)b * K + bk) * gamma;
+    const int64_t base = ((int64_t)b * K + bk) * gamma;
     const uint64_t row = row_base + (uint64_t)b;
     for (int j0 = 0; j0 < gamma; j0 += 64) {
       const int j = j0 + lane;
       bool rej = false;
-      if (j < gamma) rej = !(counter_uniform(seed, row, (uint64_t)j, kAccept) < (double)ak[j]);
+      if (j < gamma)
+        rej = !(counter_uniform(seed, row, (uint64_t)j, kAccept) < (double)alpha_ws[base + j]);
       const uint64_t m = __ballot(rej);
       if (m) {
         L = j0 + __ffsll((unsigned long long)m) - 1;
@@ -75,21 +78,22 @@ __device__ __forceinline__ void select_prefix(const float *__restrict__ alpha_ws
       if (selected) selected[b] = -1;
       accept_len[b] = -1;
       next_token[b] = -1;
-      desc[b] = DrawDesc{0, 0, 0, 0};
     } else {
       if (selected) selected[b] = bk;
       accept_len[b] = L;
-      desc[b] = DrawDesc{bk, L, L < gamma ? (int)kResidual : (int)kBonus, 1};
     }
   }
+  if (invalid) return DrawDesc{0, 0, 0, 0};
+  return DrawDesc{bk, L, L < gamma ? (int)kResidual : (int)kBonus, 1};
 }
 
 __global__ __launch_bounds__(64) void kr_select(
     const float *__restrict__ alpha_ws, int K, int gamma, uint64_t seed, uint64_t row_base,
     int32_t *__restrict__ selected, int32_t *__restrict__ accept_len,
     int32_t *__restrict__ next_token, float *__restrict__ scores, DrawDesc *__restrict__ desc) {
-  select_prefix(alpha_ws, K, gamma, seed, row_base, blockIdx.x, selected, accept_len, next_token,
-                scores, desc);
+  const DrawDesc d = select_prefix(alpha_ws, K, gamma, seed, row_base, blockIdx.x, selected,
+                                   accept_len, next_token, scores);
+  if (threadIdx.x == 0) desc[blockIdx.x] = d;
 }
 
 }  // namespace svd

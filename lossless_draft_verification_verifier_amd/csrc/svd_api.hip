@@ -11,7 +11,6 @@
 #include "svd.h"
 #include "kr_beta.hpp"
 #include "kr_draw.hpp"
-#include "kr_fused.hpp"
 #include "kr_rowstats.hpp"
 #include "kr_select.hpp"
 
@@ -22,16 +21,9 @@ using namespace svd;
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
-// SVD_FUSED selects the one-launch path (kr_fused); 0 builds the chain of
-// separate kernels instead, for comparison.
-#ifndef SVD_FUSED
-#define SVD_FUSED 0
-#endif
-
 struct Layout {
-  size_t stats, alpha, desc, segs, uncs, mass, sync, total;
+  size_t stats, alpha, desc, segs, uncs, mass, total;
   int nseg;
-  int64_t nsync;
 };
 
 bool sizes_ok(int64_t B, int32_t K, int32_t G, int32_t V) {
@@ -41,7 +33,6 @@ bool sizes_ok(int64_t B, int32_t K, int32_t G, int32_t V) {
   const int64_t lim = (int64_t)1 << 31;
   if (B >= lim / ((int64_t)K * G)) return false;  // B*K*gamma workgroups
   if (B >= lim / nseg) return false;              // B*nseg workgroups
-  if (B * ((int64_t)K * G + nseg) >= lim) return false;  // workgroups of the fused launch
   return true;
 }
 
@@ -62,9 +53,6 @@ Layout layout(int64_t B, int32_t K, int32_t G, int32_t V) {
   off = align_up(off + (size_t)B * L.nseg * kUncCap * sizeof(DrawUnc));
   L.mass = off;
   off = align_up(off + (size_t)B * L.nseg * sizeof(DrawMass));
-  L.sync = off;
-  L.nsync = 2 + 3 * B;
-  off = align_up(off + (size_t)L.nsync * sizeof(unsigned));
   L.total = off;
   return L;
 }
@@ -84,53 +72,108 @@ hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s
 }
 
 // ---------------------------------------------------------------------------
-// Kernel timing (svd_profile_*): events around every launch of a call.
+// Kernel timing (svd_profile_*): a start and an end event around every launch
+// of a call, recorded on the stream the kernel goes to.
 
 constexpr int kProfCalls = 4096;
-constexpr int kProfMarks = SVD_KERNEL_COUNT + 1;
+constexpr int kProfLaunches = 48;
 
 struct Profiler {
-  bool on = false;
+  unsigned mask = 0;  // bit k: time kernel k
   int ncalls = 0;
-  bool created[kProfCalls] = {};
-  hipEvent_t ev[kProfCalls][kProfMarks];
-  int kid[kProfCalls][kProfMarks];
-  int nmarks[kProfCalls] = {};
+  hipEvent_t ev[kProfCalls][kProfLaunches][2] = {};
+  int kid[kProfCalls][kProfLaunches];
+  int nl[kProfCalls] = {};
 };
 Profiler g_prof;
 
 struct CallTimer {
   int slot = -1;
-  hipStream_t stream;
-  explicit CallTimer(hipStream_t s) : stream(s) {
-    if (!g_prof.on || g_prof.ncalls >= kProfCalls) return;
+  CallTimer() {
+    if (!g_prof.mask || g_prof.ncalls >= kProfCalls) return;
     slot = g_prof.ncalls++;
-    if (!g_prof.created[slot]) {
-      for (int i = 0; i < kProfMarks; ++i)
-        if (hipEventCreate(&g_prof.ev[slot][i]) != hipSuccess) {
-          slot = -1;
-          g_prof.ncalls--;
-          return;
-        }
-      g_prof.created[slot] = true;
-    }
-    g_prof.nmarks[slot] = 0;
+    g_prof.nl[slot] = 0;
   }
-  // mark the start of kernel `kernel_id` (or the end of the call with -1)
-  void mark(int kernel_id) {
-    if (slot < 0) return;
-    int &n = g_prof.nmarks[slot];
-    if (n >= kProfMarks) return;
-    if (hipEventRecord(g_prof.ev[slot][n], stream) != hipSuccess) return;
-    g_prof.kid[slot][n] = kernel_id;
-    ++n;
+  // start of a launch of kernel `kernel_id` on `s`; returns its record or -1
+  int begin(int kernel_id, hipStream_t s) {
+    if (slot < 0 || !((g_prof.mask >> kernel_id) & 1u)) return -1;
+    const int i = g_prof.nl[slot];
+    if (i >= kProfLaunches) return -1;
+    hipEvent_t *e = g_prof.ev[slot][i];
+    for (int j = 0; j < 2; ++j)
+      if (!e[j] && hipEventCreate(&e[j]) != hipSuccess) {
+        e[j] = nullptr;
+        return -1;
+      }
+    if (hipEventRecord(e[0], s) != hipSuccess) return -1;
+    g_prof.kid[slot][i] = -1;  // until the end event is recorded
+    g_prof.nl[slot] = i + 1;
+    return i;
+  }
+  void end(int rec, int kernel_id, hipStream_t s) {
+    if (rec < 0) return;
+    if (hipEventRecord(g_prof.ev[slot][rec][1], s) == hipSuccess) g_prof.kid[slot][rec] = kernel_id;
   }
 };
 
-#define SVD_LAUNCH(...)                               \
-  do {                                                \
-    if (launch(__VA_ARGS__) != hipSuccess) return SVD_EHIP; \
+// Everything the launch chain reads and writes.
+template <typename E>
+struct Batch {
+  const typename E::elem *p, *q;
+  const int32_t *drafts;
+  int64_t B;
+  int K, G, V, nseg;
+  float tp, tq, cp, cq;
+  uint64_t seed, row_base;
+  int32_t *selected, *accept_len, *next_token;
+  float *scores, *alpha, *beta;
+  RowStats *stats;
+  float *alpha_ws;
+  DrawDesc *desc;
+  DrawSeg *segs;
+  DrawUnc *uncs;
+  DrawMass *mass;
+};
+
+#define SVD_LAUNCH(tm, kid, stream, ...)                            \
+  do {                                                              \
+    const int rec_ = (tm).begin((kid), (stream));                   \
+    if (launch(__VA_ARGS__) != hipSuccess) return SVD_EHIP;         \
+    (tm).end(rec_, (kid), (stream));                                \
   } while (0)
+
+// row statistics and alpha (and the optional overlap mass) of a batch
+template <typename E, bool kVec>
+int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
+  const unsigned rp = (unsigned)(a.B * a.K * a.G);
+  SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec>, dim3(rp), dim3(kRowBlock), s, a.p,
+             a.q, a.drafts, a.G, a.V, a.cp, a.cq, a.stats, a.alpha_ws, a.alpha);
+  if (a.beta)
+    SVD_LAUNCH(tm, SVD_KERNEL_BETA, s, kr_beta<E, kVec>, dim3(rp), dim3(kBlock), s, a.p, a.q, a.G,
+               a.V, a.cp, a.cq, (const RowStats *)a.stats, a.beta);
+  return SVD_OK;
+}
+
+// selection, first rejection and the draw of a batch whose statistics are done
+template <typename E, bool kVec>
+int enqueue_draw(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
+  const unsigned nb = (unsigned)a.B;
+  const unsigned nbs = (unsigned)(a.B * a.nseg);
+  SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_select, dim3(nb), dim3(64), s,
+             (const float *)a.alpha_ws, a.K, a.G, a.seed, a.row_base, a.selected, a.accept_len,
+             a.next_token, a.scores, a.desc);
+  SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PASS, s, kr_draw_pass<E, kVec>, dim3(nbs), dim3(kBlock), s,
+             a.p, a.q, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
+             (const DrawDesc *)a.desc, a.segs, a.uncs);
+  SVD_LAUNCH(tm, SVD_KERNEL_DRAW_FIX, s, kr_draw_fix<E, kVec>, dim3(nbs), dim3(kBlock), s, a.p,
+             a.q, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
+             (const DrawDesc *)a.desc, (const DrawSeg *)a.segs, a.mass);
+  SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PICK, s, kr_draw_pick<E, kVec>, dim3(nb), dim3(kBlock), s, a.p,
+             a.q, a.K, a.G, a.V, a.nseg, a.tp, a.tq, a.seed, a.row_base,
+             (const RowStats *)a.stats, (const DrawDesc *)a.desc, (const DrawSeg *)a.segs,
+             (const DrawUnc *)a.uncs, a.mass, a.selected, a.accept_len, a.next_token);
+  return SVD_OK;
+}
 
 template <typename E, bool kVec>
 int run(const void *p_logits, const void *q_logits, const int32_t *drafts, int64_t B, int32_t K,
@@ -138,111 +181,40 @@ int run(const void *p_logits, const void *q_logits, const int32_t *drafts, int64
         int32_t *selected, int32_t *accept_len, int32_t *next_token, float *scores, float *alpha,
         float *beta, void *workspace, hipStream_t stream) {
   using T = typename E::elem;
-  const T *p = static_cast<const T *>(p_logits);
-  const T *q = static_cast<const T *>(q_logits);
   const Layout Lo = layout(B, K, G, V);
   char *ws = static_cast<char *>(workspace);
-  RowStats *stats = reinterpret_cast<RowStats *>(ws + Lo.stats);
-  float *alpha_ws = reinterpret_cast<float *>(ws + Lo.alpha);
-  DrawDesc *desc = reinterpret_cast<DrawDesc *>(ws + Lo.desc);
-  DrawSeg *segs = reinterpret_cast<DrawSeg *>(ws + Lo.segs);
-  DrawUnc *uncs = reinterpret_cast<DrawUnc *>(ws + Lo.uncs);
-  DrawMass *mass = reinterpret_cast<DrawMass *>(ws + Lo.mass);
-  const unsigned rp = (unsigned)((int64_t)B * K * G);
-  const unsigned nb = (unsigned)B;
-  const unsigned nbs = (unsigned)(B * Lo.nseg);
+  Batch<E> a;
+  a.p = static_cast<const T *>(p_logits);
+  a.q = static_cast<const T *>(q_logits);
+  a.drafts = drafts;
+  a.B = B;
+  a.K = K;
+  a.G = G;
+  a.V = V;
+  a.nseg = Lo.nseg;
+  a.tp = tp;
+  a.tq = tq;
   // log2(e) / T folded into one factor per row: exp(z/T) = exp2(z * c)
-  const float cp = (float)(1.4426950408889634 / (double)tp);
-  const float cq = (float)(1.4426950408889634 / (double)tq);
+  a.cp = (float)(1.4426950408889634 / (double)tp);
+  a.cq = (float)(1.4426950408889634 / (double)tq);
+  a.seed = seed;
+  a.row_base = row_base;
+  a.selected = selected;
+  a.accept_len = accept_len;
+  a.next_token = next_token;
+  a.scores = scores;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.stats = reinterpret_cast<RowStats *>(ws + Lo.stats);
+  a.alpha_ws = reinterpret_cast<float *>(ws + Lo.alpha);
+  a.desc = reinterpret_cast<DrawDesc *>(ws + Lo.desc);
+  a.segs = reinterpret_cast<DrawSeg *>(ws + Lo.segs);
+  a.uncs = reinterpret_cast<DrawUnc *>(ws + Lo.uncs);
+  a.mass = reinterpret_cast<DrawMass *>(ws + Lo.mass);
 
-  CallTimer tm(stream);
-  if (SVD_FUSED) {
-    // lag of the fused schedule: about one generation of resident workgroups
-    static int blocks_per_cu = [] {
-      int n = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kr_fused<E, kVec>, kFusedBlock, 0) !=
-              hipSuccess ||
-          n < 1)
-        n = 1;
-      return n;
-    }();
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus = 256;
-    const int64_t P = (int64_t)K * G;
-#ifndef SVD_LAG_MUL
-#define SVD_LAG_MUL 1
-#endif
-    // SVD_LAG_MUL scales the lag; 0 streams every row pair before any draw
-    const int64_t lag = SVD_LAG_MUL == 0 ? B : SVD_LAG_MUL * (((int64_t)cus * blocks_per_cu + P - 1) / P);
-    FusedArgs<E> fa;
-    fa.p = p;
-    fa.q = q;
-    fa.drafts = drafts;
-    fa.B = B;
-    fa.K = K;
-    fa.gamma = G;
-    fa.V = V;
-    fa.nseg = Lo.nseg;
-    fa.lag = (int)(lag < 1 ? 1 : (lag > B ? B : lag));
-    fa.tp = tp;
-    fa.tq = tq;
-    fa.cp = cp;
-    fa.cq = cq;
-    fa.seed = seed;
-    fa.row_base = row_base;
-    fa.selected = selected;
-    fa.accept_len = accept_len;
-    fa.next_token = next_token;
-    fa.scores = scores;
-    fa.alpha_out = alpha;
-    fa.stats = stats;
-    fa.alpha_ws = alpha_ws;
-    fa.desc = desc;
-    fa.segs = segs;
-    fa.uncs = uncs;
-    fa.mass = mass;
-    fa.sync = reinterpret_cast<unsigned *>(ws + Lo.sync);
-    const int64_t nsync = Lo.nsync;
-    const unsigned init_grid = (unsigned)std::min<int64_t>((nsync + 255) / 256, 1024);
-    tm.mark(SVD_KERNEL_INIT);
-    SVD_LAUNCH(kr_fused_init, dim3(init_grid), dim3(256), stream, fa.sync, nsync);
-    tm.mark(SVD_KERNEL_FUSED);
-    const unsigned items = (unsigned)(B * (P + (Lo.nseg + kDrawGroup - 1) / kDrawGroup));
-    SVD_LAUNCH(kr_fused<E, kVec>, dim3(items), dim3(kFusedBlock), stream, fa);
-    if (beta) {
-      tm.mark(SVD_KERNEL_BETA);
-      SVD_LAUNCH(kr_beta<E, kVec>, dim3(rp), dim3(kBlock), stream, p, q, G, V, cp, cq,
-                 (const RowStats *)stats, beta);
-    }
-    tm.mark(-1);
-    return SVD_OK;
-  }
-  tm.mark(SVD_KERNEL_ROWSTATS);
-  SVD_LAUNCH(kr_rowstats<E, kVec>, dim3(rp), dim3(kRowBlock), stream, p, q, drafts, G, V, cp, cq,
-             stats, alpha_ws, alpha);
-  if (beta) {
-    tm.mark(SVD_KERNEL_BETA);
-    SVD_LAUNCH(kr_beta<E, kVec>, dim3(rp), dim3(kBlock), stream, p, q, G, V, cp, cq,
-               (const RowStats *)stats, beta);
-  }
-  tm.mark(SVD_KERNEL_SELECT);
-  SVD_LAUNCH(kr_select, dim3(nb), dim3(64), stream, (const float *)alpha_ws, K, G, seed,
-             row_base, selected, accept_len, next_token, scores, desc);
-  tm.mark(SVD_KERNEL_DRAW_PASS);
-  SVD_LAUNCH(kr_draw_pass<E, kVec>, dim3(nbs), dim3(kBlock), stream, p, q, K, G, V, Lo.nseg, tp,
-             tq, (const RowStats *)stats, (const DrawDesc *)desc, segs, uncs);
-  tm.mark(SVD_KERNEL_DRAW_FIX);
-  SVD_LAUNCH(kr_draw_fix<E, kVec>, dim3(nbs), dim3(kBlock), stream, p, q, K, G, V, Lo.nseg, tp,
-             tq, (const RowStats *)stats, (const DrawDesc *)desc, (const DrawSeg *)segs, mass);
-  tm.mark(SVD_KERNEL_DRAW_PICK);
-  SVD_LAUNCH(kr_draw_pick<E, kVec>, dim3(nb), dim3(kBlock), stream, p, q, K, G, V, Lo.nseg, tp,
-             tq, seed, row_base, (const RowStats *)stats, (const DrawDesc *)desc,
-             (const DrawSeg *)segs, (const DrawUnc *)uncs, mass, selected, accept_len,
-             next_token);
-  tm.mark(-1);
-  return SVD_OK;
+  CallTimer tm;
+  const int rc = enqueue_rows<E, kVec>(a, stream, tm);
+  return rc != SVD_OK ? rc : enqueue_draw<E, kVec>(a, stream, tm);
 }
 
 bool temp_ok(float t) { return std::isfinite(t) && t > 0.0f; }
@@ -316,8 +288,8 @@ const char *svd_strerror(int status) {
   }
 }
 
-int svd_profile_enable(int on) {
-  g_prof.on = on != 0;
+int svd_profile_enable(unsigned kernel_mask) {
+  g_prof.mask = kernel_mask & ((1u << SVD_KERNEL_COUNT) - 1u);
   return SVD_OK;
 }
 
@@ -328,14 +300,12 @@ int svd_profile_read(double *ms, int64_t *launches, int n) {
     if (launches) launches[i] = 0;
   }
   for (int c = 0; c < g_prof.ncalls; ++c) {
-    const int nm = g_prof.nmarks[c];
-    if (nm == 0) continue;
-    if (hipEventSynchronize(g_prof.ev[c][nm - 1]) != hipSuccess) return SVD_EHIP;
-    for (int i = 0; i + 1 < nm; ++i) {
+    for (int i = 0; i < g_prof.nl[c]; ++i) {
       const int k = g_prof.kid[c][i];
       if (k < 0 || k >= n) continue;
+      if (hipEventSynchronize(g_prof.ev[c][i][1]) != hipSuccess) return SVD_EHIP;
       float t = 0.0f;
-      if (hipEventElapsedTime(&t, g_prof.ev[c][i], g_prof.ev[c][i + 1]) != hipSuccess)
+      if (hipEventElapsedTime(&t, g_prof.ev[c][i][0], g_prof.ev[c][i][1]) != hipSuccess)
         return SVD_EHIP;
       ms[k] += t;
       if (launches) launches[k] += 1;
