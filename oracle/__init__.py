@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.svdo_select_and_verify.argtypes = [
             vp, vp, vp, ctypes.c_int, i64, i32, i32, i32, ctypes.c_float, ctypes.c_float,
             u64, u64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+        L.svdo_greedy_select_and_verify.restype = ctypes.c_int
+        L.svdo_greedy_select_and_verify.argtypes = [
+            vp, vp, ctypes.c_int, i64, i32, i32, i32, ctypes.c_float, u64, u64, vp, vp, vp, vp,
+            vp, vp, vp, vp, vp, ctypes.c_int]
         _lib = L
     return _lib
 
@@ -189,3 +193,37 @@ def select_and_verify(p_logits, q_logits, drafts, temp_p=1.0, temp_q=None, seed=
     dg = np.frombuffer(diag, dtype=np.float64).reshape(B, 4) if B else np.zeros((0, 4))
     return OracleResult(sel, L, tok, scores, alpha, beta, px, qx, am,
                         dg[:, 0].copy(), dg[:, 1].copy(), dg[:, 2].copy(), dg[:, 3].copy())
+
+
+def greedy_select_and_verify(p_logits, drafts, temp_p=1.0, seed=0, row_base=0, force_k=None,
+                             force_L=None, nthreads=None) -> OracleResult:
+    """Greedy acceptance (alpha = p(x); a rejected token is resampled from p with
+    that token zeroed).  p_logits [B, K, gamma+1, V], drafts [B, K, gamma]."""
+    p, dt = _logits(p_logits)
+    if p.ndim != 4:
+        raise ValueError("expected p [B,K,gamma+1,V]")
+    B, K, G1, V = p.shape
+    G = G1 - 1
+    d = np.ascontiguousarray(drafts, dtype=np.int32)
+    if d.shape != (B, K, G):
+        raise ValueError("drafts shape %s, expected %s" % (d.shape, (B, K, G)))
+    if nthreads is None:
+        nthreads = min(os.cpu_count() or 1, 16)
+    fk = None if force_k is None else np.ascontiguousarray(force_k, dtype=np.int32)
+    fl = None if force_L is None else np.ascontiguousarray(force_L, dtype=np.int32)
+    sel = np.empty(B, np.int32)
+    L = np.empty(B, np.int32)
+    tok = np.empty(B, np.int32)
+    scores = np.full((B, K), np.nan)
+    alpha = np.full((B, K, G), np.nan)
+    am = np.full((B, G), np.nan)
+    diag = (_Diag * B)()
+    rc = lib().svdo_greedy_select_and_verify(
+        _ptr(p), _ptr(d), dt, B, K, G, V, float(temp_p), seed & 0xFFFFFFFFFFFFFFFF,
+        row_base & 0xFFFFFFFFFFFFFFFF, _ptr(fk), _ptr(fl), _ptr(sel), _ptr(L), _ptr(tok),
+        _ptr(scores), _ptr(alpha), _ptr(am), ctypes.cast(diag, ctypes.c_void_p), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+    dg = np.frombuffer(diag, dtype=np.float64).reshape(B, 4) if B else np.zeros((0, 4))
+    return OracleResult(sel, L, tok, scores, alpha, None, alpha.copy(), np.full((B, K, G), np.nan),
+                        am, dg[:, 0].copy(), dg[:, 1].copy(), dg[:, 2].copy(), dg[:, 3].copy())

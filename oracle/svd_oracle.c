@@ -168,6 +168,7 @@ typedef struct {
   int32_t *selected, *accept_len, *next_token;
   double *scores, *alpha, *beta, *px, *qx, *accept_margin;
   svdo_diag_t *diag;
+  int greedy;  /* greedy acceptance: alpha = p(x), no drafter rows */
   int nthreads, tid;
   int status;
 } job_t;
@@ -207,7 +208,23 @@ static int do_prefix(const job_t *J, int64_t b, double *P, double *Q, double *R,
     }
 
   /* 1-2. softmax of every scored row pair and the acceptance alpha_{k,j} */
-  for (int32_t k = 0; k < K && valid; ++k) {
+  for (int32_t k = 0; k < K && valid && J->greedy; ++k) {
+    /* greedy acceptance (SpecDiff-2 section 5.2 and appendix B.4): the test
+     * compares the uniform with the verifier probability of the drafted
+     * token, alpha = p(x); the drafter's probabilities are not used */
+    for (int32_t j = 0; j < G && valid; ++j) {
+      if (!softmax_full(p_row(J, b, k, j), J->dtype, V, J->tp, P, NULL, NULL)) {
+        valid = 0;
+        break;
+      }
+      int32_t x = J->drafts[((size_t)b * K + k) * G + j];
+      size_t o = ((size_t)b * K + k) * G + j;
+      a_buf[(size_t)k * G + j] = P[x];
+      if (J->alpha) J->alpha[o] = P[x];
+      if (J->px) J->px[o] = P[x];
+    }
+  }
+  for (int32_t k = 0; k < K && valid && !J->greedy; ++k) {
     for (int32_t j = 0; j < G && valid; ++j) {
       const void *pr = p_row(J, b, k, j), *qr = q_row(J, b, k, j);
       double mp, Sp, mq, Sq;
@@ -278,7 +295,15 @@ static int do_prefix(const job_t *J, int64_t b, double *P, double *Q, double *R,
 
   /* 7-8. residual draw at the first rejection, or bonus draw after gamma accepts */
   double Z, u;
-  if (L < G) {
+  if (L < G && J->greedy) {
+    /* the rejected token zeroed out (SpecDiff-2 appendix B.4): the residual
+     * max(0, p - q) with q the point mass at the drafted token */
+    softmax_full(p_row(J, b, ks, L), J->dtype, V, J->tp, P, NULL, NULL);
+    for (int32_t v = 0; v < V; ++v) Q[v] = 0.0;
+    Q[J->drafts[((size_t)b * K + ks) * G + L]] = 1.0;
+    Z = svdo_draw_weights(P, Q, V, R);
+    u = svdo_uniform(J->seed, row, (uint64_t)L, PURPOSE_RESIDUAL);
+  } else if (L < G) {
     softmax_full(p_row(J, b, ks, L), J->dtype, V, J->tp, P, NULL, NULL);
     softmax_full(q_row(J, b, ks, L), J->dtype, V, J->tq, Q, NULL, NULL);
     Z = svdo_draw_weights(P, Q, V, R);
@@ -331,6 +356,41 @@ static void *worker(void *arg)
   return NULL;
 }
 
+static int run_jobs(const job_t *base_in)
+{
+  job_t base = *base_in;
+  int nthreads = base.nthreads < 1 ? 1 : base.nthreads;
+  if ((int64_t)nthreads > base.B) nthreads = (int)base.B;
+  base.nthreads = nthreads;
+  job_t *jobs = (job_t *)malloc(sizeof(job_t) * (size_t)nthreads);
+  pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  if (!jobs || !th) {
+    free(jobs);
+    free(th);
+    return -1;
+  }
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = base;
+    jobs[i].tid = i;
+  }
+  int started = 0;
+  for (int i = 1; i < nthreads; ++i) {
+    if (pthread_create(&th[i], NULL, worker, &jobs[i]) != 0) break;
+    started = i;
+  }
+  worker(&jobs[0]);
+  for (int i = 1; i <= started; ++i) pthread_join(th[i], NULL);
+  /* prefixes of threads that failed to start run here */
+  for (int i = started + 1; i < nthreads; ++i) worker(&jobs[i]);
+
+  int status = 0;
+  for (int i = 0; i < nthreads; ++i)
+    if (jobs[i].status != 0) status = -1;
+  free(jobs);
+  free(th);
+  return status;
+}
+
 int svdo_select_and_verify(const void *p_logits, const void *q_logits, const int32_t *drafts,
                            int dtype, int64_t B, int32_t K, int32_t gamma, int32_t V,
                            float temp_p, float temp_q, uint64_t seed, uint64_t row_base,
@@ -343,8 +403,6 @@ int svdo_select_and_verify(const void *p_logits, const void *q_logits, const int
   if (dtype != SVDO_F32 && dtype != SVDO_BF16) return -1;
   if (B < 1 || K < 1 || gamma < 1 || V < 1) return -1;
   if (!(temp_p > 0.0f) || !(temp_q > 0.0f) || isinf(temp_p) || isinf(temp_q)) return -1;
-  if (nthreads < 1) nthreads = 1;
-  if ((int64_t)nthreads > B) nthreads = (int)B;
 
   job_t base;
   memset(&base, 0, sizeof base);
@@ -373,32 +431,44 @@ int svdo_select_and_verify(const void *p_logits, const void *q_logits, const int
   base.accept_margin = accept_margin;
   base.diag = diag;
   base.nthreads = nthreads;
+  return run_jobs(&base);
+}
 
-  job_t *jobs = (job_t *)malloc(sizeof(job_t) * (size_t)nthreads);
-  pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
-  if (!jobs || !th) {
-    free(jobs);
-    free(th);
-    return -1;
-  }
-  for (int i = 0; i < nthreads; ++i) {
-    jobs[i] = base;
-    jobs[i].tid = i;
-  }
-  int started = 0;
-  for (int i = 1; i < nthreads; ++i) {
-    if (pthread_create(&th[i], NULL, worker, &jobs[i]) != 0) break;
-    started = i;
-  }
-  worker(&jobs[0]);
-  for (int i = 1; i <= started; ++i) pthread_join(th[i], NULL);
-  /* prefixes of threads that failed to start run here */
-  for (int i = started + 1; i < nthreads; ++i) worker(&jobs[i]);
+int svdo_greedy_select_and_verify(const void *p_logits, const int32_t *drafts, int dtype,
+                                  int64_t B, int32_t K, int32_t gamma, int32_t V, float temp_p,
+                                  uint64_t seed, uint64_t row_base, const int32_t *force_k,
+                                  const int32_t *force_L, int32_t *selected, int32_t *accept_len,
+                                  int32_t *next_token, double *scores, double *alpha,
+                                  double *accept_margin, svdo_diag_t *diag, int nthreads)
+{
+  if (!p_logits || !drafts || !selected || !accept_len || !next_token) return -1;
+  if (dtype != SVDO_F32 && dtype != SVDO_BF16) return -1;
+  if (B < 1 || K < 1 || gamma < 1 || V < 1) return -1;
+  if (!(temp_p > 0.0f) || isinf(temp_p)) return -1;
 
-  int status = 0;
-  for (int i = 0; i < nthreads; ++i)
-    if (jobs[i].status != 0) status = -1;
-  free(jobs);
-  free(th);
-  return status;
+  job_t base;
+  memset(&base, 0, sizeof base);
+  base.p = p_logits;
+  base.drafts = drafts;
+  base.dtype = dtype;
+  base.B = B;
+  base.K = K;
+  base.gamma = gamma;
+  base.V = V;
+  base.tp = temp_p;
+  base.tq = temp_p;
+  base.seed = seed;
+  base.row_base = row_base;
+  base.force_k = force_k;
+  base.force_L = force_L;
+  base.selected = selected;
+  base.accept_len = accept_len;
+  base.next_token = next_token;
+  base.scores = scores;
+  base.alpha = alpha;
+  base.accept_margin = accept_margin;
+  base.diag = diag;
+  base.greedy = 1;
+  base.nthreads = nthreads;
+  return run_jobs(&base);
 }

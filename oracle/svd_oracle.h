@@ -93,6 +93,23 @@ int svdo_select_and_verify(const void *p_logits, const void *q_logits, const int
                            double *scores, double *alpha, double *beta, double *px, double *qx,
                            double *accept_margin, svdo_diag_t *diag, int nthreads);
 
+/*
+ * Greedy acceptance (SpecDiff-2 section 5.2: the kept draft is verified
+ * without its drafting probabilities; appendix B.4: the uniform is compared
+ * with the verifier probability, and a rejected token is resampled from the
+ * verifier distribution with that token zeroed).  alpha_{k,j} = p_j(x_{k,j});
+ * scores, selection, acceptance and the bonus draw as above; the rejection
+ * draw is the residual max(0, p - q) with q the point mass at the rejected
+ * token.  p_logits and drafts as above; no drafter rows.  alpha and px
+ * receive the same values.
+ */
+int svdo_greedy_select_and_verify(const void *p_logits, const int32_t *drafts, int dtype,
+                                  int64_t B, int32_t K, int32_t gamma, int32_t V, float temp_p,
+                                  uint64_t seed, uint64_t row_base, const int32_t *force_k,
+                                  const int32_t *force_L, int32_t *selected, int32_t *accept_len,
+                                  int32_t *next_token, double *scores, double *alpha,
+                                  double *accept_margin, svdo_diag_t *diag, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
