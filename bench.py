@@ -29,8 +29,9 @@ KERNEL_SOURCES = {"rowstats": ["svd_device.hpp", "kr_rowstats.hpp"]}
 KERNEL_SYMBOL = {"rowstats": "kr_rowstats"}
 
 
-def traffic_file(kernel: str) -> str:
-    return os.path.join(ROOT, "profiles", "%s_traffic.json" % KERNEL_SYMBOL[kernel])
+def traffic_file(kernel: str, mode: str = "standard") -> str:
+    tag = "" if mode == "standard" else "_" + mode
+    return os.path.join(ROOT, "profiles", "%s%s_traffic.json" % (KERNEL_SYMBOL[kernel], tag))
 
 
 def kernel_hash(kernel: str) -> str:
@@ -41,11 +42,11 @@ def kernel_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, mode: str = "standard"):
     """HBM bytes per launch of a kernel from committed rocprofv3 counter
     summaries, or None when they are missing or the kernel changed since."""
     try:
-        with open(traffic_file(kernel)) as f:
+        with open(traffic_file(kernel, mode)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -72,7 +73,7 @@ def _counter_per_dispatch(run_dir: str, counter: str, name_part: str):
     return sum(per.values()) / len(per), len(per)
 
 
-def record_traffic(kernel, workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+def record_traffic(kernel, workload, mode, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     """Write profiles/<kernel>_traffic.json from four rocprofv3 --pmc runs: FETCH_SIZE
     and WRITE_SIZE of the kernel, and of a plain 1 GiB copy that scales them."""
     sym = KERNEL_SYMBOL[kernel]
@@ -86,27 +87,29 @@ def record_traffic(kernel, workload, fetch_dir, write_dir, copy_fetch_dir, copy_
     import workloads as W
     cfg = W.get_config(workload)
     es = 2 if cfg.dtype == "bf16" else 4
-    alg = bytes_per_row_pair(cfg.V, es) * cfg.B * cfg.K * cfg.gamma
-    rec = {"kernel": sym, "workload": workload, "kernel_hash": kernel_hash(kernel),
+    alg = bytes_per_row_pair(cfg.V, es, mode) * cfg.B * cfg.K * cfg.gamma
+    rec = {"kernel": sym, "workload": workload, "mode": mode, "kernel_hash": kernel_hash(kernel),
            "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
            "dispatches": [nf, nw], "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
            "copy_bytes_each_way": COPY_BYTES, "fetch_scale": fscale, "write_scale": wscale,
            "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": alg,
            "traffic_over_algorithmic": hbm / alg}
-    with open(traffic_file(kernel), "w") as f:
+    with open(traffic_file(kernel, mode), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
 
 
-def bytes_per_row_pair(V: int, es: int) -> int:
-    """Algorithmic bytes of one scored row pair: both logit rows, the drafted
-    token, and the 16-byte statistics record plus the 4-byte alpha written for
-    it.  (Bonus rows and the 12 output bytes per prefix are left out, so the
-    figure is a lower bound.)"""
-    return 2 * V * es + 4 + 16 + 4
+def bytes_per_row_pair(V: int, es: int, mode: str = "standard") -> int:
+    """Algorithmic bytes of one scored position: its logit rows (p and q; p
+    alone under greedy acceptance), the drafted token, and the 16-byte
+    statistics record plus the 4-byte alpha written for it.  (Bonus rows and
+    the 12 output bytes per prefix are left out, so the figure is a lower
+    bound.)"""
+    rows = 1 if mode == "greedy" else 2
+    return rows * V * es + 4 + 16 + 4
 
 
-def cpu_baseline(d, cfg, seed, seconds=10.0):
+def cpu_baseline(d, cfg, seed, mode="standard", seconds=10.0):
     """The oracle, untuned, on the same batch, repeated until about `seconds`
     of wall time have passed (at least once)."""
     import oracle
@@ -116,7 +119,10 @@ def cpu_baseline(d, cfg, seed, seconds=10.0):
     reps, dt = 0, 0.0
     while reps == 0 or dt < seconds:
         t0 = time.perf_counter()
-        oracle.select_and_verify(hp, hq, hd, temp_p=cfg.temp, seed=seed, nthreads=threads)
+        if mode == "greedy":
+            oracle.greedy_select_and_verify(hp, hd, temp_p=cfg.temp, seed=seed, nthreads=threads)
+        else:
+            oracle.select_and_verify(hp, hq, hd, temp_p=cfg.temp, seed=seed, nthreads=threads)
         dt += time.perf_counter() - t0
         reps += 1
     positions = cfg.B * cfg.K * cfg.gamma
@@ -149,6 +155,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batched_serving")
+    ap.add_argument("--mode", choices=("standard", "greedy"), default="standard",
+                    help="acceptance rule: standard (alpha = min(1, p/q)) or greedy (alpha = p(x), "
+                         "no drafter rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (for counter calibration)")
@@ -158,7 +167,7 @@ def main():
                          "--calibrate-copy")
     args = ap.parse_args()
     if args.record_traffic:
-        record_traffic("rowstats", args.workload, *args.record_traffic)
+        record_traffic("rowstats", args.workload, args.mode, *args.record_traffic)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the verification path shards by prefix with no "
@@ -188,12 +197,19 @@ def main():
     stream = torch.cuda.current_stream(dev)
     code = svd.SVD_BF16 if cfg.dtype == "bf16" else svd.SVD_F32
 
+    greedy = args.mode == "greedy"
+
     def step():
-        rc = svd.svd_select_and_verify(d["p"], d["q"], d["drafts"], code, B, K, G, V, cfg.temp,
-                                       cfg.temp, cfg.seed, 0, sel, L, tok, None, None, None, ws,
-                                       ws.numel(), stream.cuda_stream)
+        if greedy:
+            rc = svd.svd_greedy_select_and_verify(d["p"], d["drafts"], code, B, K, G, V, cfg.temp,
+                                                  cfg.seed, 0, sel, L, tok, None, None, ws,
+                                                  ws.numel(), stream.cuda_stream)
+        else:
+            rc = svd.svd_select_and_verify(d["p"], d["q"], d["drafts"], code, B, K, G, V,
+                                           cfg.temp, cfg.temp, cfg.seed, 0, sel, L, tok, None,
+                                           None, None, ws, ws.numel(), stream.cuda_stream)
         if rc != svd.SVD_OK:
-            raise svd.SvdError(rc, "svd_select_and_verify")
+            raise svd.SvdError(rc, "select_and_verify (%s)" % args.mode)
 
     for _ in range(args.warmup):
         step()
@@ -229,13 +245,14 @@ def main():
     positions = B * K * G
     L_host = L.cpu().numpy()
     bonus_rows = int((L_host == G).sum())
-    alg_bytes_step = positions * (2 * V * es + 4) + bonus_rows * V * es + B * 12
+    rows = 1 if greedy else 2
+    alg_bytes_step = positions * (rows * V * es + 4) + bonus_rows * V * es + B * 12
     di = svd.KERNELS.index(dom)
     ms_dom = ms_kernels[di] / max(launches[di], 1)
-    unit_bytes = bytes_per_row_pair(V, es)
+    unit_bytes = bytes_per_row_pair(V, es, args.mode)
     launch_bytes = unit_bytes * positions
     achieved = launch_bytes / (ms_dom * 1e-3) / 1e9
-    traffic = measured_traffic(dom, cfg.name)
+    traffic = measured_traffic(dom, cfg.name, args.mode)
 
     result = {
         "metric": METRIC,
@@ -250,7 +267,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": B, "K": K, "gamma": G, "V": V,
+        "config": {"workload": cfg.name, "mode": args.mode, "B": B, "K": K, "gamma": G, "V": V,
                    "logits": cfg.dtype, "temperature": cfg.temp, "global_batch": B,
                    "parallelism": "single GPU"},
         "achieved_hbm_gbps": alg_bytes_step / (ms_step * 1e-3) / 1e9,
@@ -266,7 +283,7 @@ def main():
         "wall_s": wall,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(d, cfg, cfg.seed)
+        result["cpu_baseline"] = cpu_baseline(d, cfg, cfg.seed, args.mode)
     print(json.dumps(result), flush=True)
 
 

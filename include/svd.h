@@ -129,6 +129,40 @@ int svd_select_and_verify(const void *p_logits, const void *q_logits, const int3
                           float *scores, float *alpha, float *beta,
                           void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * Greedy acceptance (SpecDiff-2 section 5.2: the kept draft is verified
+ * without its drafting probabilities, which lets drafter and verifier use
+ * different tokenizers; appendix B.4: the uniform is compared with the
+ * verifier probability, and a rejected token is resampled from the verifier
+ * distribution with that token zeroed out).
+ *
+ * Same as svd_verify / svd_select_and_verify with
+ *   alpha_j = p_j(x_j)                        (step 2; also the score's alpha)
+ *   rejection at L: the draw is from p_L with token x_L zeroed and the rest
+ *                   renormalised, i.e. the residual max(0, p - q) with q the
+ *                   point mass at x_L (step 5); if nothing else has mass, p_L.
+ * Selection, the acceptance test, the uniforms and the bonus draw are
+ * unchanged.  No drafter logits are read, so a scored position moves one
+ * logit row instead of two; temp_q does not exist.  Unlike the standard rule,
+ * this one keeps the verifier's output law under any selection among the K
+ * drafts.  The workspace of svd_workspace_bytes(B, K, gamma, V) suffices;
+ * argument checks, data errors and outputs follow the conventions above.
+ *
+ *   p_logits [B][K][gamma+1][V] (svd_greedy_verify: [B][gamma+1][V])
+ *   drafts   [B][K][gamma]      (svd_greedy_verify: [B][gamma])
+ *   alpha    [B][K][gamma] out, nullable: p(x) in fp32
+ */
+int svd_greedy_verify(const void *p_logits, const int32_t *draft, svd_dtype_t dtype, int64_t B,
+                      int32_t gamma, int32_t V, float temp_p, uint64_t seed, uint64_t row_base,
+                      int32_t *accept_len, int32_t *next_token, float *alpha, void *workspace,
+                      size_t workspace_bytes, void *hip_stream);
+int svd_greedy_select_and_verify(const void *p_logits, const int32_t *drafts, svd_dtype_t dtype,
+                                 int64_t B, int32_t K, int32_t gamma, int32_t V, float temp_p,
+                                 uint64_t seed, uint64_t row_base, int32_t *selected,
+                                 int32_t *accept_len, int32_t *next_token, float *scores,
+                                 float *alpha, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream);
+
 /* Static text for a status code. */
 const char *svd_strerror(int status);
 

@@ -6,10 +6,11 @@ marshals arguments.  PyTorch supplies device memory and the current stream.
 
 Raw entry points (same names and argument order as the C ABI; pointer
 arguments take an int address or a tensor):
-    svd_workspace_bytes, svd_verify, svd_select_and_verify, svd_strerror,
-    svd_profile_enable, svd_profile_read
+    svd_workspace_bytes, svd_verify, svd_select_and_verify, svd_greedy_verify,
+    svd_greedy_select_and_verify, svd_strerror, svd_profile_enable, svd_profile_read
 Tensor conveniences that allocate the outputs and the workspace with torch:
-    verify, select_and_verify, workspace_bytes
+    verify, select_and_verify, greedy_verify, greedy_select_and_verify,
+    workspace_bytes
 
 Importing fails with ImportError when ``libsvd.so`` has not been built; there
 is no fallback path.
@@ -27,8 +28,9 @@ SVD_OK, SVD_EINVAL, SVD_EDTYPE, SVD_EWORKSPACE, SVD_EHIP = 0, -1, -2, -3, -4
 SVD_MAX_K, SVD_MAX_GAMMA = 64, 4096
 KERNELS = ("rowstats", "select", "draw_pass", "draw_fix", "draw_pick", "beta")
 
-C_EXPORTS = ("svd_workspace_bytes", "svd_verify", "svd_select_and_verify", "svd_strerror",
-             "svd_profile_enable", "svd_profile_read")
+C_EXPORTS = ("svd_workspace_bytes", "svd_verify", "svd_select_and_verify", "svd_greedy_verify",
+             "svd_greedy_select_and_verify", "svd_strerror", "svd_profile_enable",
+             "svd_profile_read")
 
 
 class SvdError(RuntimeError):
@@ -54,6 +56,12 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.svd_select_and_verify.restype = ctypes.c_int
     L.svd_select_and_verify.argtypes = [vp, vp, vp, ctypes.c_int, i64, i32, i32, i32, f32, f32,
                                         u64, u64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.svd_greedy_verify.restype = ctypes.c_int
+    L.svd_greedy_verify.argtypes = [vp, vp, ctypes.c_int, i64, i32, i32, f32, u64, u64, vp, vp,
+                                    vp, vp, sz, vp]
+    L.svd_greedy_select_and_verify.restype = ctypes.c_int
+    L.svd_greedy_select_and_verify.argtypes = [vp, vp, ctypes.c_int, i64, i32, i32, i32, f32, u64,
+                                               u64, vp, vp, vp, vp, vp, vp, sz, vp]
     L.svd_strerror.restype = ctypes.c_char_p
     L.svd_strerror.argtypes = [ctypes.c_int]
     L.svd_profile_enable.restype = ctypes.c_int
@@ -100,6 +108,24 @@ def svd_select_and_verify(p_logits, q_logits, drafts, dtype, B, K, gamma, V, tem
         int(V), float(temp_p), float(temp_q), int(seed) & _M64, int(row_base) & _M64,
         _addr(selected), _addr(accept_len), _addr(next_token), _addr(scores), _addr(alpha),
         _addr(beta), _addr(workspace), int(workspace_bytes), _addr(hip_stream)))
+
+
+def svd_greedy_verify(p_logits, draft, dtype, B, gamma, V, temp_p, seed, row_base, accept_len,
+                      next_token, alpha, workspace, workspace_bytes, hip_stream) -> int:
+    return int(_lib.svd_greedy_verify(
+        _addr(p_logits), _addr(draft), int(dtype), int(B), int(gamma), int(V), float(temp_p),
+        int(seed) & _M64, int(row_base) & _M64, _addr(accept_len), _addr(next_token),
+        _addr(alpha), _addr(workspace), int(workspace_bytes), _addr(hip_stream)))
+
+
+def svd_greedy_select_and_verify(p_logits, drafts, dtype, B, K, gamma, V, temp_p, seed, row_base,
+                                 selected, accept_len, next_token, scores, alpha, workspace,
+                                 workspace_bytes, hip_stream) -> int:
+    return int(_lib.svd_greedy_select_and_verify(
+        _addr(p_logits), _addr(drafts), int(dtype), int(B), int(K), int(gamma), int(V),
+        float(temp_p), int(seed) & _M64, int(row_base) & _M64, _addr(selected),
+        _addr(accept_len), _addr(next_token), _addr(scores), _addr(alpha), _addr(workspace),
+        int(workspace_bytes), _addr(hip_stream)))
 
 
 def svd_strerror(status: int) -> str:
@@ -227,4 +253,64 @@ def verify(p, q, draft, temp_p=1.0, temp_q=None, seed=0, row_base=0, want_alpha=
                     ws.numel(), st)
     if rc != SVD_OK:
         raise SvdError(rc, "svd_verify")
+    return out
+
+
+def greedy_select_and_verify(p, drafts, temp_p=1.0, seed=0, row_base=0, want_alpha=False,
+                             want_scores=False, workspace=None, stream=None):
+    """Greedy acceptance: p [B,K,gamma+1,V] (bf16 or fp32), drafts [B,K,gamma] int32."""
+    import torch
+    dev = p.device
+    for t, n in ((p, "p"), (drafts, "drafts")):
+        _check(t, n, dev)
+    if drafts.dtype != torch.int32:
+        raise TypeError("drafts must be int32")
+    if p.dim() != 4 or drafts.dim() != 3:
+        raise ValueError("expected p [B,K,G+1,V], drafts [B,K,G]")
+    B, K, G1, V = p.shape
+    G = G1 - 1
+    if tuple(drafts.shape) != (B, K, G):
+        raise ValueError("shape mismatch: p %s drafts %s" % (tuple(p.shape), tuple(drafts.shape)))
+    out = {
+        "selected": torch.empty(B, dtype=torch.int32, device=dev),
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+        "scores": torch.empty((B, K), dtype=torch.float32, device=dev) if want_scores else None,
+        "alpha": torch.empty((B, K, G), dtype=torch.float32, device=dev) if want_alpha else None,
+    }
+    ws = alloc_workspace(B, K, G, V, dev) if workspace is None else workspace
+    st = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    rc = svd_greedy_select_and_verify(p, drafts, _dtype_code(p), B, K, G, V, temp_p, seed,
+                                      row_base, out["selected"], out["accept_len"],
+                                      out["next_token"], out["scores"], out["alpha"], ws,
+                                      ws.numel(), st)
+    if rc != SVD_OK:
+        raise SvdError(rc, "svd_greedy_select_and_verify")
+    return out
+
+
+def greedy_verify(p, draft, temp_p=1.0, seed=0, row_base=0, want_alpha=False, workspace=None,
+                  stream=None):
+    """Greedy acceptance, one draft: p [B,gamma+1,V] (bf16 or fp32), draft [B,gamma] int32."""
+    import torch
+    dev = p.device
+    for t, n in ((p, "p"), (draft, "draft")):
+        _check(t, n, dev)
+    if draft.dtype != torch.int32:
+        raise TypeError("draft must be int32")
+    B, G1, V = p.shape
+    G = G1 - 1
+    if tuple(draft.shape) != (B, G):
+        raise ValueError("shape mismatch")
+    out = {
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+        "alpha": torch.empty((B, G), dtype=torch.float32, device=dev) if want_alpha else None,
+    }
+    ws = alloc_workspace(B, 1, G, V, dev) if workspace is None else workspace
+    st = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    rc = svd_greedy_verify(p, draft, _dtype_code(p), B, G, V, temp_p, seed, row_base,
+                           out["accept_len"], out["next_token"], out["alpha"], ws, ws.numel(), st)
+    if rc != SVD_OK:
+        raise SvdError(rc, "svd_greedy_verify")
     return out

@@ -127,7 +127,7 @@ __device__ __forceinline__ DrawRows<E> draw_rows(const typename E::elem *p, cons
   const int64_t bk = b * K + d.k;
   DrawRows<E> r;
   r.p = p + (bk * (gamma + 1) + d.pos) * (int64_t)V;
-  r.q = (d.purpose == kResidual) ? q + (bk * gamma + d.pos) * (int64_t)V : nullptr;
+  r.q = d.two ? q + (bk * gamma + d.pos) * (int64_t)V : nullptr;
   return r;
 }
 
@@ -218,7 +218,7 @@ __device__ __forceinline__ void draw_pass_item(const typename E::elem *__restric
   double sp = 0.0, sq = 0.0, ap = 0.0, aq = 0.0;
   int last_pos = -1, last_p = -1, bad = 0;
   float mseg = kNegInf;
-  if (d.purpose == kResidual) {
+  if (d.two) {
     const double Mp = (double)st.mp / (double)tp, Mq = (double)st.mq / (double)tq;
     const double rho = (double)st.sp / (double)st.sq;  // fp32 estimate of S_p / S_q
     const double up = rho * (1.0 + kClassMargin), dn = rho * (1.0 - kClassMargin);
@@ -246,10 +246,15 @@ __device__ __forceinline__ void draw_pass_item(const typename E::elem *__restric
     mseg = block_max<NW>(m, ldsf);
     bad = block_max_i<NW>(bad, ldsi);
     const double M = (double)fmaxf(mseg, kLowest) / (double)tp;
+    const int excl = d.excl;  // sp: every token; ap: all but the excluded one
     visit_segment<E, kVec, false, NT>(r.p, r.p, lo, hi, [&](int v, float zp, float) {
       const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -M), tab);
       sp += wp;
       if (wp > 0.0) last_p = v;
+      if (v != excl) {
+        ap += wp;
+        if (wp > 0.0) last_pos = v;
+      }
     });
   }
   block_reduce_seg<NW>(sp, sq, ap, aq, last_pos, last_p, ldsd, ldsi);
@@ -280,7 +285,7 @@ __device__ __forceinline__ void draw_pass_item(const typename E::elem *__restric
 // decision and drawn-row statistics from the workspace (separate launches)
 __device__ __forceinline__ RowStats drawn_stats(const RowStats *stats, const DrawDesc &d, int K,
                                                 int gamma, int64_t b) {
-  if (d.valid && d.purpose == kResidual) return stats[(b * K + d.k) * gamma + d.pos];
+  if (d.valid && d.two) return stats[(b * K + d.k) * gamma + d.pos];
   return RowStats{0.0f, 1.0f, 0.0f, 1.0f};
 }
 
@@ -301,11 +306,12 @@ template <typename E>
 struct DrawWeight {
   const typename E::elem *p, *q;
   double invTp, invTq, Mp, Mq, invSp, invSq;
-  bool resid;
-  // weight from the two logits of token v
-  __device__ __forceinline__ double from(float zp, float zq, const Exp64Table &tab) const {
+  bool resid;  // max(0, p - q); otherwise p with token excl zeroed
+  int excl;
+  // weight of token v from its two logits
+  __device__ __forceinline__ double from(int v, float zp, float zq, const Exp64Table &tab) const {
     const double pv = exp_nonpos(__builtin_fma((double)zp, invTp, -Mp), tab) * invSp;
-    if (!resid) return pv;
+    if (!resid) return v == excl ? 0.0 : pv;
     const double qv = exp_nonpos(__builtin_fma((double)zq, invTq, -Mq), tab) * invSq;
     const double dd = pv - qv;
     return dd > 0.0 ? dd : 0.0;
@@ -323,7 +329,8 @@ __device__ __forceinline__ bool draw_setup(const DrawRows<E> &rows, const DrawDe
   W.q = rows.q;
   W.invTp = 1.0 / (double)tp;
   W.invTq = 1.0 / (double)tq;
-  W.resid = d.purpose == kResidual;
+  W.resid = d.two != 0;
+  W.excl = d.excl;
   double Sp = 0.0, Sq = 1.0;
   if (W.resid) {
     W.Mp = (double)st.mp / (double)tp;
@@ -365,7 +372,7 @@ __device__ __forceinline__ void segment_mass_exact(const DrawWeight<E> &W, const
   double z = 0.0;
   int last = -1;
   visit_segment<E, kVec, true, NT>(W.p, W.q, lo, hi, [&](int v, float zp, float zq) {
-    const double w = W.from(zp, zq, tab);
+    const double w = W.from(v, zp, zq, tab);
     z += w;
     if (w > 0.0) last = v;
   });
@@ -390,7 +397,7 @@ __global__ __launch_bounds__(kBlock) void kr_draw_fix(
   const int seg = (int)(blockIdx.x - b * nseg);
   const DrawDesc d = desc[b];
   const DrawSeg *S = segs + b * nseg;
-  if (!d.valid || d.purpose != kResidual || S[seg].n_unc >= 0) return;
+  if (!d.valid || !d.two || S[seg].n_unc >= 0) return;
   exp64_table_init(tab);
   __syncthreads();
   const DrawRows<E> rows = draw_rows<E>(p, q, K, gamma, V, b, d);
@@ -444,7 +451,7 @@ __device__ __forceinline__ void draw_pick_item(
   const DrawRows<E> rows = draw_rows<E>(p, q, K, gamma, V, b, d);
   const DrawSeg *S = segs + b * nseg;
   DrawMass *ms = mass + b * nseg;
-  const bool residual = d.purpose == kResidual;
+  const bool residual = d.two != 0;
   DrawWeight<E> W;
   if (!draw_setup<E>(rows, d, st, S, nseg, tp, tq, W)) {
     if (tid == 0) {  // invalid bonus row (the scored rows were checked earlier)
@@ -476,11 +483,12 @@ __device__ __forceinline__ void draw_pick_item(
       }
       m.zr = z;
       m.last_r = last;
-    } else {
+    } else {  // p row: zp with every token, zr without the excluded one
       const double Ms = (double)fmaxf(g.mseg, kLowest) / (double)tp;
-      m.zp = ((g.mseg == kNegInf) ? 0.0 : g.sp * exp(Ms - W.Mp)) * W.invSp;
-      m.zr = m.zp;
-      m.last_r = m.last_p;
+      const double scale = (g.mseg == kNegInf) ? 0.0 : exp(Ms - W.Mp);
+      m.zp = g.sp * scale * W.invSp;
+      m.zr = g.ap * scale * W.invSp;
+      m.last_r = g.last_pos;
     }
     ms[s] = m;
   }
@@ -488,8 +496,9 @@ __device__ __forceinline__ void draw_pick_item(
 
   double zr = 0.0;
   for (int s = 0; s < nseg; ++s) zr += ms[s].zr;
-  const bool use_r = !residual || zr > 0.0;  // a residual without mass draws from p
+  const bool use_r = zr > 0.0;  // a residual without mass draws from p
   W.resid = residual && use_r;
+  if (!use_r) W.excl = -1;
   double Z = zr;
   if (!use_r) {
     Z = 0.0;
@@ -529,13 +538,14 @@ __device__ __forceinline__ void draw_pick_item(
           }
 #pragma unroll
           for (int e = 0; e < P; ++e)
-            w[c * P + e] = (a + c * P < hi) ? W.from(xp[e], W.resid ? xq[e] : 0.0f, tab) : 0.0;
+            w[c * P + e] =
+                (a + c * P < hi) ? W.from(a + c * P + e, xp[e], W.resid ? xq[e] : 0.0f, tab) : 0.0;
         }
       } else {
 #pragma unroll
         for (int i = 0; i < kRun; ++i) {
           const int v = a + i;
-          w[i] = (v < hi) ? W.from(E::at(W.p, v), W.resid ? E::at(W.q, v) : 0.0f, tab) : 0.0;
+          w[i] = (v < hi) ? W.from(v, E::at(W.p, v), W.resid ? E::at(W.q, v) : 0.0f, tab) : 0.0;
         }
       }
       double loc = 0.0;

@@ -111,7 +111,11 @@ __device__ __forceinline__ void row_ms(const typename E::elem *row, int V, float
 }
 
 // One scored row pair: statistics of both rows and alpha, written by thread 0.
-template <typename E, bool kVec, int NT, int U>
+// kGreedy: greedy acceptance (SpecDiff-2 section 5.2 and appendix B.4), which
+// compares the uniform with the verifier probability of the drafted token, so
+// alpha = p(x) and the drafter row is not read (its statistics are left as
+// {0, 1}).
+template <typename E, bool kVec, int NT, int U, bool kGreedy = false>
 __device__ __forceinline__ void rowstats_item(const typename E::elem *__restrict__ p,
                                      const typename E::elem *__restrict__ q,
                                      const int32_t *__restrict__ drafts, int gamma, int V,
@@ -121,21 +125,25 @@ __device__ __forceinline__ void rowstats_item(const typename E::elem *__restrict
   const int64_t bk = rp / gamma;  // rp = (b * K + k) * gamma + j
   const int64_t j = rp - bk * gamma;
   const typename E::elem *prow = p + (bk * (gamma + 1) + j) * (int64_t)V;
-  const typename E::elem *qrow = q + rp * (int64_t)V;
+  const typename E::elem *qrow = kGreedy ? nullptr : q + rp * (int64_t)V;
 
-  float mp, sp, mq, sq;
+  float mp, sp, mq = 0.0f, sq = 1.0f;
   row_ms<E, kVec, NT, U>(prow, V, cp, mp, sp, lds);
-  row_ms<E, kVec, NT, U>(qrow, V, cq, mq, sq, lds);
+  if constexpr (!kGreedy) row_ms<E, kVec, NT, U>(qrow, V, cq, mq, sq, lds);
 
   if (threadIdx.x == 0) {
     const int32_t x = drafts[rp];
     float a = __builtin_nanf("");
     const bool rows_ok = !(sp != sp) && !(sq != sq) && mp != kNegInf && mq != kNegInf;
     if (rows_ok && x >= 0 && x < V) {
-      // log2 p(x) and log2 q(x); accept outright when q(x) <= p(x)
+      // log2 p(x) (and log2 q(x)); accept outright when q(x) <= p(x)
       const float lp = (E::at(prow, x) - mp) * cp - log2f(sp);
-      const float lq = (E::at(qrow, x) - mq) * cq - log2f(sq);
-      a = (lq <= lp) ? 1.0f : exp2f(lp - lq);
+      if constexpr (kGreedy) {
+        a = fminf(exp2f(lp), 1.0f);
+      } else {
+        const float lq = (E::at(qrow, x) - mq) * cq - log2f(sq);
+        a = (lq <= lp) ? 1.0f : exp2f(lp - lq);
+      }
     }
     stats[rp] = RowStats{mp, sp, mq, sq};
     alpha_ws[rp] = a;
@@ -144,13 +152,13 @@ __device__ __forceinline__ void rowstats_item(const typename E::elem *__restrict
 }
 
 // Two 1024-thread workgroups per CU (8 waves per SIMD) need at most 64 VGPRs.
-template <typename E, bool kVec>
+template <typename E, bool kVec, bool kGreedy>
 __global__ __launch_bounds__(kRowBlock) __attribute__((amdgpu_waves_per_eu(8))) void kr_rowstats(
     const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
     const int32_t *__restrict__ drafts, int gamma, int V, float cp, float cq,
     RowStats *__restrict__ stats, float *__restrict__ alpha_ws, float *__restrict__ alpha_out) {
-  rowstats_item<E, kVec, kRowBlock, kRowUnroll>(p, q, drafts, gamma, V, cp, cq, blockIdx.x, stats,
-                                                alpha_ws, alpha_out);
+  rowstats_item<E, kVec, kRowBlock, kRowUnroll, kGreedy>(p, q, drafts, gamma, V, cp, cq,
+                                                         blockIdx.x, stats, alpha_ws, alpha_out);
 }
 
 }  // namespace svd

@@ -9,7 +9,9 @@
 // accept), and the accepted length L is the first failing j, or gamma
 // (SpecDiff-2 section 2; DiffuSpec section 3).  The row pair of the draw is
 // recorded for the sampler: position L of the kept draft for a residual
-// draw, or its bonus row gamma.
+// draw, or its bonus row gamma.  Under greedy acceptance the rejection draw
+// reads only the verifier row, with the rejected token zeroed (SpecDiff-2
+// appendix B.4).
 #pragma once
 
 #include "svd_device.hpp"
@@ -19,9 +21,11 @@ namespace svd {
 // Run by the 64 lanes of one wave (lane = threadIdx.x & 63); every lane gets
 // the decision.  Lane 0 writes selected / accept_len (and -1 next_token for an
 // invalid prefix), lane k writes scores[k].
-__device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alpha_ws, int K,
-                                                  int gamma, uint64_t seed, uint64_t row_base,
-                                                  int64_t b, int32_t *__restrict__ selected,
+__device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alpha_ws,
+                                                  const int32_t *__restrict__ drafts, bool greedy,
+                                                  int K, int gamma, uint64_t seed,
+                                                  uint64_t row_base, int64_t b,
+                                                  int32_t *__restrict__ selected,
                                                   int32_t *__restrict__ accept_len,
                                                   int32_t *__restrict__ next_token,
                                                   float *__restrict__ scores) {
@@ -83,16 +87,20 @@ __device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alph
       accept_len[b] = L;
     }
   }
-  if (invalid) return DrawDesc{0, 0, 0, 0};
-  return DrawDesc{bk, L, L < gamma ? (int)kResidual : (int)kBonus, 1};
+  if (invalid) return DrawDesc{0, 0, 0, 0, 0, -1};
+  if (L == gamma) return DrawDesc{bk, L, (int)kBonus, 1, 0, -1};
+  if (greedy)
+    return DrawDesc{bk, L, (int)kResidual, 1, 0, drafts[((int64_t)b * K + bk) * gamma + L]};
+  return DrawDesc{bk, L, (int)kResidual, 1, 1, -1};
 }
 
 __global__ __launch_bounds__(64) void kr_select(
-    const float *__restrict__ alpha_ws, int K, int gamma, uint64_t seed, uint64_t row_base,
-    int32_t *__restrict__ selected, int32_t *__restrict__ accept_len,
-    int32_t *__restrict__ next_token, float *__restrict__ scores, DrawDesc *__restrict__ desc) {
-  const DrawDesc d = select_prefix(alpha_ws, K, gamma, seed, row_base, blockIdx.x, selected,
-                                   accept_len, next_token, scores);
+    const float *__restrict__ alpha_ws, const int32_t *__restrict__ drafts, int greedy, int K,
+    int gamma, uint64_t seed, uint64_t row_base, int32_t *__restrict__ selected,
+    int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token,
+    float *__restrict__ scores, DrawDesc *__restrict__ desc) {
+  const DrawDesc d = select_prefix(alpha_ws, drafts, greedy != 0, K, gamma, seed, row_base,
+                                   blockIdx.x, selected, accept_len, next_token, scores);
   if (threadIdx.x == 0) desc[blockIdx.x] = d;
 }
 

@@ -125,6 +125,7 @@ struct Batch {
   int K, G, V, nseg;
   float tp, tq, cp, cq;
   uint64_t seed, row_base;
+  bool greedy;  // greedy acceptance: alpha = p(x), q unused
   int32_t *selected, *accept_len, *next_token;
   float *scores, *alpha, *beta;
   RowStats *stats;
@@ -146,8 +147,12 @@ struct Batch {
 template <typename E, bool kVec>
 int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   const unsigned rp = (unsigned)(a.B * a.K * a.G);
-  SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec>, dim3(rp), dim3(kRowBlock), s, a.p,
-             a.q, a.drafts, a.G, a.V, a.cp, a.cq, a.stats, a.alpha_ws, a.alpha);
+  if (a.greedy)
+    SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, true>, dim3(rp), dim3(kRowBlock), s,
+               a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, a.stats, a.alpha_ws, a.alpha);
+  else
+    SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, false>, dim3(rp), dim3(kRowBlock),
+               s, a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, a.stats, a.alpha_ws, a.alpha);
   if (a.beta)
     SVD_LAUNCH(tm, SVD_KERNEL_BETA, s, kr_beta<E, kVec>, dim3(rp), dim3(kBlock), s, a.p, a.q, a.G,
                a.V, a.cp, a.cq, (const RowStats *)a.stats, a.beta);
@@ -160,14 +165,15 @@ int enqueue_draw(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   const unsigned nb = (unsigned)a.B;
   const unsigned nbs = (unsigned)(a.B * a.nseg);
   SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_select, dim3(nb), dim3(64), s,
-             (const float *)a.alpha_ws, a.K, a.G, a.seed, a.row_base, a.selected, a.accept_len,
-             a.next_token, a.scores, a.desc);
+             (const float *)a.alpha_ws, a.drafts, (int)a.greedy, a.K, a.G, a.seed, a.row_base,
+             a.selected, a.accept_len, a.next_token, a.scores, a.desc);
   SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PASS, s, kr_draw_pass<E, kVec>, dim3(nbs), dim3(kBlock), s,
              a.p, a.q, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
              (const DrawDesc *)a.desc, a.segs, a.uncs);
-  SVD_LAUNCH(tm, SVD_KERNEL_DRAW_FIX, s, kr_draw_fix<E, kVec>, dim3(nbs), dim3(kBlock), s, a.p,
-             a.q, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
-             (const DrawDesc *)a.desc, (const DrawSeg *)a.segs, a.mass);
+  if (!a.greedy)  // only residuals max(0, p - q) can leave uncertain tokens
+    SVD_LAUNCH(tm, SVD_KERNEL_DRAW_FIX, s, kr_draw_fix<E, kVec>, dim3(nbs), dim3(kBlock), s, a.p,
+               a.q, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
+               (const DrawDesc *)a.desc, (const DrawSeg *)a.segs, a.mass);
   SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PICK, s, kr_draw_pick<E, kVec>, dim3(nb), dim3(kBlock), s, a.p,
              a.q, a.K, a.G, a.V, a.nseg, a.tp, a.tq, a.seed, a.row_base,
              (const RowStats *)a.stats, (const DrawDesc *)a.desc, (const DrawSeg *)a.segs,
@@ -177,7 +183,7 @@ int enqueue_draw(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
 
 template <typename E, bool kVec>
 int run(const void *p_logits, const void *q_logits, const int32_t *drafts, int64_t B, int32_t K,
-        int32_t G, int32_t V, float tp, float tq, uint64_t seed, uint64_t row_base,
+        int32_t G, int32_t V, float tp, float tq, uint64_t seed, uint64_t row_base, bool greedy,
         int32_t *selected, int32_t *accept_len, int32_t *next_token, float *scores, float *alpha,
         float *beta, void *workspace, hipStream_t stream) {
   using T = typename E::elem;
@@ -199,6 +205,7 @@ int run(const void *p_logits, const void *q_logits, const int32_t *drafts, int64
   a.cq = (float)(1.4426950408889634 / (double)tq);
   a.seed = seed;
   a.row_base = row_base;
+  a.greedy = greedy;
   a.selected = selected;
   a.accept_len = accept_len;
   a.next_token = next_token;
@@ -221,10 +228,11 @@ bool temp_ok(float t) { return std::isfinite(t) && t > 0.0f; }
 
 int dispatch(const void *p, const void *q, const int32_t *drafts, svd_dtype_t dtype, int64_t B,
              int32_t K, int32_t G, int32_t V, float tp, float tq, uint64_t seed,
-             uint64_t row_base, int32_t *selected, int32_t *accept_len, int32_t *next_token,
-             float *scores, float *alpha, float *beta, void *workspace, size_t workspace_bytes,
-             void *hip_stream) {
-  if (!p || !q || !drafts || !accept_len || !next_token || !workspace) return SVD_EINVAL;
+             uint64_t row_base, bool greedy, int32_t *selected, int32_t *accept_len,
+             int32_t *next_token, float *scores, float *alpha, float *beta, void *workspace,
+             size_t workspace_bytes, void *hip_stream) {
+  if (!p || (!q && !greedy) || !drafts || !accept_len || !next_token || !workspace)
+    return SVD_EINVAL;
   if (dtype != SVD_F32 && dtype != SVD_BF16) return SVD_EDTYPE;
   if (!sizes_ok(B, K, G, V) || !temp_ok(tp) || !temp_ok(tq)) return SVD_EINVAL;
   if (((uintptr_t)workspace) % kAlign != 0) return SVD_EINVAL;
@@ -235,15 +243,18 @@ int dispatch(const void *p, const void *q, const int32_t *drafts, svd_dtype_t dt
   const bool vec = ((size_t)V * es) % 16 == 0 && ((uintptr_t)p) % 16 == 0 &&
                    ((uintptr_t)q) % 16 == 0;
   if (dtype == SVD_BF16) {
-    return vec ? run<BF16, true>(p, q, drafts, B, K, G, V, tp, tq, seed, row_base, selected,
-                                 accept_len, next_token, scores, alpha, beta, workspace, s)
-               : run<BF16, false>(p, q, drafts, B, K, G, V, tp, tq, seed, row_base, selected,
-                                  accept_len, next_token, scores, alpha, beta, workspace, s);
+    return vec ? run<BF16, true>(p, q, drafts, B, K, G, V, tp, tq, seed, row_base, greedy,
+                                 selected, accept_len, next_token, scores, alpha, beta,
+                                 workspace, s)
+               : run<BF16, false>(p, q, drafts, B, K, G, V, tp, tq, seed, row_base, greedy,
+                                  selected, accept_len, next_token, scores, alpha, beta,
+                                  workspace, s);
   }
-  return vec ? run<F32, true>(p, q, drafts, B, K, G, V, tp, tq, seed, row_base, selected,
+  return vec ? run<F32, true>(p, q, drafts, B, K, G, V, tp, tq, seed, row_base, greedy, selected,
                               accept_len, next_token, scores, alpha, beta, workspace, s)
-             : run<F32, false>(p, q, drafts, B, K, G, V, tp, tq, seed, row_base, selected,
-                               accept_len, next_token, scores, alpha, beta, workspace, s);
+             : run<F32, false>(p, q, drafts, B, K, G, V, tp, tq, seed, row_base, greedy,
+                               selected, accept_len, next_token, scores, alpha, beta, workspace,
+                               s);
 }
 
 }  // namespace
@@ -261,8 +272,8 @@ int svd_verify(const void *p_logits, const void *q_logits, const int32_t *draft,
                int32_t *next_token, float *alpha, float *beta, void *workspace,
                size_t workspace_bytes, void *hip_stream) {
   return dispatch(p_logits, q_logits, draft, dtype, B, 1, gamma, V, temp_p, temp_q, seed,
-                  row_base, nullptr, accept_len, next_token, nullptr, alpha, beta, workspace,
-                  workspace_bytes, hip_stream);
+                  row_base, false, nullptr, accept_len, next_token, nullptr, alpha, beta,
+                  workspace, workspace_bytes, hip_stream);
 }
 
 int svd_select_and_verify(const void *p_logits, const void *q_logits, const int32_t *drafts,
@@ -273,8 +284,29 @@ int svd_select_and_verify(const void *p_logits, const void *q_logits, const int3
                           size_t workspace_bytes, void *hip_stream) {
   if (!selected) return SVD_EINVAL;
   return dispatch(p_logits, q_logits, drafts, dtype, B, K, gamma, V, temp_p, temp_q, seed,
-                  row_base, selected, accept_len, next_token, scores, alpha, beta, workspace,
-                  workspace_bytes, hip_stream);
+                  row_base, false, selected, accept_len, next_token, scores, alpha, beta,
+                  workspace, workspace_bytes, hip_stream);
+}
+
+int svd_greedy_verify(const void *p_logits, const int32_t *draft, svd_dtype_t dtype, int64_t B,
+                      int32_t gamma, int32_t V, float temp_p, uint64_t seed, uint64_t row_base,
+                      int32_t *accept_len, int32_t *next_token, float *alpha, void *workspace,
+                      size_t workspace_bytes, void *hip_stream) {
+  return dispatch(p_logits, nullptr, draft, dtype, B, 1, gamma, V, temp_p, temp_p, seed,
+                  row_base, true, nullptr, accept_len, next_token, nullptr, alpha, nullptr,
+                  workspace, workspace_bytes, hip_stream);
+}
+
+int svd_greedy_select_and_verify(const void *p_logits, const int32_t *drafts, svd_dtype_t dtype,
+                                 int64_t B, int32_t K, int32_t gamma, int32_t V, float temp_p,
+                                 uint64_t seed, uint64_t row_base, int32_t *selected,
+                                 int32_t *accept_len, int32_t *next_token, float *scores,
+                                 float *alpha, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream) {
+  if (!selected) return SVD_EINVAL;
+  return dispatch(p_logits, nullptr, drafts, dtype, B, K, gamma, V, temp_p, temp_p, seed,
+                  row_base, true, selected, accept_len, next_token, scores, alpha, nullptr,
+                  workspace, workspace_bytes, hip_stream);
 }
 
 const char *svd_strerror(int status) {

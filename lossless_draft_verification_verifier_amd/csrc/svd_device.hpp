@@ -211,11 +211,13 @@ struct RowStats {      // one scored row pair
   float mq, sq;        // the same for the q row
 };
 
-struct DrawDesc {      // one prefix: which row pair the draw reads
+struct DrawDesc {      // one prefix: which rows the draw reads
   int k;               // kept draft
-  int pos;             // accepted length L (residual) or gamma (bonus)
-  int purpose;         // kResidual or kBonus
+  int pos;             // accepted length L (rejection) or gamma (bonus)
+  int purpose;         // kResidual or kBonus: the uniform's purpose
   int valid;           // 0: prefix invalid, nothing to draw
+  int two;             // 1: residual max(0, p - q) of row pair (k, pos); 0: p row (k, pos)
+  int excl;            // p-row draw: a token of weight zero (the rejected one), or -1
 };
 
 }  // namespace svd

@@ -59,10 +59,20 @@ def _slice(a, b):
     return np.ascontiguousarray(a[b:b + 1])
 
 
+def _run(orc, greedy, p, q, d, temp_p, temp_q, seed, row_base, want_beta=False, **force):
+    """One oracle call in the standard or the greedy-acceptance mode."""
+    if greedy:
+        return orc.greedy_select_and_verify(p, d, temp_p=temp_p, seed=seed, row_base=row_base,
+                                            **force)
+    return orc.select_and_verify(p, q, d, temp_p=temp_p, temp_q=temp_q, seed=seed,
+                                 row_base=row_base, want_beta=want_beta, **force)
+
+
 def compare(orc, host_p, host_q, host_d, gpu, temp_p, temp_q, seed, row_base=0,
-            prefixes=None, rep: ParityReport | None = None) -> ParityReport:
+            prefixes=None, rep: ParityReport | None = None, greedy=False) -> ParityReport:
     """host_p/host_q/host_d: host arrays of the prefixes in `prefixes` (in that order);
     gpu: dict of host numpy outputs of the full batch (selected may be None for svd_verify).
+    greedy: compare with the oracle's greedy-acceptance mode (host_q is then unused).
     """
     rep = rep or ParityReport()
     B, K, G1, V = host_p.shape
@@ -73,7 +83,7 @@ def compare(orc, host_p, host_q, host_d, gpu, temp_p, temp_q, seed, row_base=0,
     # uniform rows follow the batch index of each prefix
     rows = np.array(idx, dtype=np.int64)
     res = _oracle_rows(orc, host_p, host_q, host_d, temp_p, temp_q, seed, row_base, rows,
-                       want_beta)
+                       want_beta, greedy)
     sel_tol = ALPHA_TOL * G
     for i, b in enumerate(idx):
         rep.prefixes += 1
@@ -103,7 +113,7 @@ def compare(orc, host_p, host_q, host_d, gpu, temp_p, temp_q, seed, row_base=0,
                 rep.failures.append((b, "scores", e))
 
         pb = _slice(host_p, i)
-        qb = _slice(host_q, i)
+        qb = None if greedy else _slice(host_q, i)
         db = _slice(host_d, i)
         row = row_base + b
         cur = res
@@ -116,9 +126,8 @@ def compare(orc, host_p, host_q, host_d, gpu, temp_p, temp_q, seed, row_base=0,
             if g_sel != o_sel:
                 if res.select_gap[i] < sel_tol:
                     rep.flagged["select"] += 1
-                    cur = orc.select_and_verify(pb, qb, db, temp_p=temp_p, temp_q=temp_q,
-                                                seed=seed, row_base=row,
-                                                force_k=np.array([g_sel], np.int32))
+                    cur = _run(orc, greedy, pb, qb, db, temp_p, temp_q, seed, row,
+                               force_k=np.array([g_sel], np.int32))
                     ci = 0
                 else:
                     rep.failures.append((b, "selected", (g_sel, o_sel, res.select_gap[i])))
@@ -132,9 +141,8 @@ def compare(orc, host_p, host_q, host_d, gpu, temp_p, temp_q, seed, row_base=0,
             j = min(g_L, o_L)
             if 0 <= j < G and m[j] < ACCEPT_EPS:
                 rep.flagged["accept"] += 1
-                cur = orc.select_and_verify(pb, qb, db, temp_p=temp_p, temp_q=temp_q, seed=seed,
-                                            row_base=row, force_k=np.array([g_sel], np.int32),
-                                            force_L=np.array([g_L], np.int32))
+                cur = _run(orc, greedy, pb, qb, db, temp_p, temp_q, seed, row,
+                           force_k=np.array([g_sel], np.int32), force_L=np.array([g_L], np.int32))
                 ci = 0
             else:
                 rep.failures.append((b, "accept_len", (g_L, o_L, float(m[j]) if 0 <= j < G else None)))
@@ -155,16 +163,15 @@ def compare(orc, host_p, host_q, host_d, gpu, temp_p, temp_q, seed, row_base=0,
     return rep
 
 
-def _oracle_rows(orc, host_p, host_q, host_d, temp_p, temp_q, seed, row_base, rows, want_beta):
+def _oracle_rows(orc, host_p, host_q, host_d, temp_p, temp_q, seed, row_base, rows, want_beta,
+                 greedy=False):
     """Oracle over a host batch whose prefix i sits at batch row rows[i]."""
     rows = np.asarray(rows)
     if len(rows) and np.all(np.diff(rows) == 1):
-        return orc.select_and_verify(host_p, host_q, host_d, temp_p=temp_p, temp_q=temp_q,
-                                     seed=seed, row_base=row_base + int(rows[0]),
-                                     want_beta=want_beta)
-    parts = [orc.select_and_verify(_slice(host_p, i), _slice(host_q, i), _slice(host_d, i),
-                                   temp_p=temp_p, temp_q=temp_q, seed=seed,
-                                   row_base=row_base + int(r), want_beta=want_beta)
+        return _run(orc, greedy, host_p, host_q, host_d, temp_p, temp_q, seed,
+                    row_base + int(rows[0]), want_beta)
+    parts = [_run(orc, greedy, _slice(host_p, i), None if greedy else _slice(host_q, i),
+                  _slice(host_d, i), temp_p, temp_q, seed, row_base + int(r), want_beta)
              for i, r in enumerate(rows)]
     out = parts[0]
     for f in out.__dataclass_fields__:

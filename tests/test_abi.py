@@ -31,7 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("svd_verify", "svd_select_and_verify", "svd_workspace_bytes", "svd_strerror"):
+    for n in ("svd_verify", "svd_select_and_verify", "svd_workspace_bytes", "svd_strerror",
+              "svd_greedy_verify", "svd_greedy_select_and_verify"):
         assert n in names
 
 
@@ -95,6 +96,35 @@ def test_verify_argument_errors(svd):
     assert rc == svd.SVD_EINVAL
     rc = svd.svd_verify(4096, 8192, 12288, svd.SVD_F32, 1, 2, 10, 1.0, 1.0, 0, 0, 16384, 20480,
                         None, None, ws, 0, None)
+    assert rc == svd.SVD_EWORKSPACE
+
+
+def _greedy(svd, **kw):
+    a = dict(p=4096, d=12288, dtype=svd.SVD_BF16, B=2, K=2, G=3, V=100, tp=1.0, sel=16384,
+             L=20480, tok=24576, ws=1 << 20, n=0)
+    a.update(kw)
+    return svd.svd_greedy_select_and_verify(a["p"], a["d"], a["dtype"], a["B"], a["K"], a["G"],
+                                            a["V"], a["tp"], 0, 0, a["sel"], a["L"], a["tok"],
+                                            None, None, a["ws"], a["n"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(p=None), -1), (dict(d=None), -1), (dict(sel=None), -1), (dict(L=None), -1),
+    (dict(tok=None), -1), (dict(ws=None), -1), (dict(dtype=7), -2), (dict(B=0), -1),
+    (dict(K=65), -1), (dict(G=0), -1), (dict(V=0), -1), (dict(tp=0.0), -1),
+    (dict(tp=float("inf")), -1), (dict(ws=(1 << 20) + 32), -1),
+    (dict(), -3),  # workspace of 0 bytes
+])
+def test_greedy_host_side_argument_errors(svd, kw, want):
+    assert _greedy(svd, **kw) == want
+
+
+def test_greedy_verify_argument_errors(svd):
+    rc = svd.svd_greedy_verify(4096, None, svd.SVD_BF16, 1, 2, 10, 1.0, 0, 0, 16384, 20480, None,
+                               1 << 20, 0, None)
+    assert rc == svd.SVD_EINVAL
+    rc = svd.svd_greedy_verify(4096, 12288, svd.SVD_F32, 1, 2, 10, 1.0, 0, 0, 16384, 20480, None,
+                               1 << 20, 0, None)
     assert rc == svd.SVD_EWORKSPACE
 
 
