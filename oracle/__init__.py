@@ -227,3 +227,34 @@ def greedy_select_and_verify(p_logits, drafts, temp_p=1.0, seed=0, row_base=0, f
     dg = np.frombuffer(diag, dtype=np.float64).reshape(B, 4) if B else np.zeros((0, 4))
     return OracleResult(sel, L, tok, scores, alpha, None, alpha.copy(), np.full((B, K, G), np.nan),
                         am, dg[:, 0].copy(), dg[:, 1].copy(), dg[:, 2].copy(), dg[:, 3].copy())
+
+
+def _gather_rows(pool: np.ndarray, index: np.ndarray) -> np.ndarray:
+    """Rows of a pool at index[...] -> array of shape index.shape + (V,); an index
+    outside the pool gives a row of NaN logits (so the prefix reading it is invalid)."""
+    idx = np.asarray(index, dtype=np.int64)
+    ok = (idx >= 0) & (idx < pool.shape[0])
+    out = pool[np.where(ok, idx, 0)]
+    nan = np.uint16(0x7FC0) if pool.dtype == np.uint16 else np.float32(np.nan)
+    out[~ok] = nan
+    return out
+
+
+def select_and_verify_rows(p_pool, p_index, q_pool, q_index, drafts, temp_p=1.0, temp_q=None,
+                           seed=0, row_base=0, greedy=False, force_k=None, force_L=None,
+                           nthreads=None) -> OracleResult:
+    """Verification over shared rows: p row (b, k, j) is p_pool[p_index[b, k, j]] and q row
+    (b, k, j) is q_pool[q_index[b, k, j]].  By definition this is the dense rule on the
+    gathered rows; an index outside its pool reads as a row of NaN logits.
+    greedy: the greedy-acceptance rule (q_pool and q_index unused)."""
+    p_pool, _ = _logits(p_pool)
+    p = _gather_rows(p_pool, p_index)
+    d = np.ascontiguousarray(drafts, dtype=np.int32)
+    if greedy:
+        return greedy_select_and_verify(p, d, temp_p=temp_p, seed=seed, row_base=row_base,
+                                        force_k=force_k, force_L=force_L, nthreads=nthreads)
+    q_pool, _ = _logits(q_pool)
+    q = _gather_rows(q_pool, q_index)
+    return select_and_verify(p, q, d, temp_p=temp_p, temp_q=temp_q, seed=seed,
+                             row_base=row_base, force_k=force_k, force_L=force_L,
+                             nthreads=nthreads)

@@ -1,4 +1,4 @@
-"""The five verification workloads.
+"""The verification workloads: five dense ones and one with shared rows.
 
 Shapes follow the pages' settings: Qwen2.5-scale vocabularies and bf16 verifier
 logits (SpecDiff-2 appendix B.1), windows of gamma = 16 and 32 tokens (appendix
@@ -26,6 +26,8 @@ class Config:
     boost: float      # logit added to the row's mode token
     boost_prob: float  # share of rows that receive the boost
     trials: int = 0   # distribution-check trials (tiny workload only)
+    layout: str = "dense"  # "dense" rows per (prefix, draft), or "pooled" shared rows
+    tau: float = 0.0  # pooled: verifier-row spread between draft prefixes at one position
     notes: str = field(default="", compare=False)
 
     @property
@@ -58,6 +60,10 @@ CONFIGS = {
               sigma_step=0.0, temp=0.7, boost=8.0, boost_prob=1.0),
     5: Config(5, "long_window", B=64, K=16, gamma=32, V=152064, dtype="bf16", sigma0=0.5,
               sigma_step=0.05, temp=0.7, boost=8.0, boost_prob=0.7),
+    6: Config(6, "shared_marginal", B=16, K=8, gamma=16, V=152064, dtype="bf16", sigma0=1.5,
+              sigma_step=0.0, temp=1.0, boost=8.0, boost_prob=1.0, layout="pooled", tau=0.5,
+              notes="the K drafts sampled from one set of drafter marginals (shared q rows); "
+                    "one verifier row per distinct draft prefix"),
 }
 
 

@@ -77,6 +77,64 @@ def generate(cfg: Config, device="cpu", B: int | None = None, data_seed: int | N
     return {"p": p, "q": q, "drafts": d, "temp": cfg.temp, "dtype": dt}
 
 
+def generate_pooled(cfg: Config, device="cpu", B: int | None = None,
+                    data_seed: int | None = None, V: int | None = None, K: int | None = None,
+                    gamma: int | None = None, dtype: str | None = None, tau: float | None = None):
+    """Inputs with shared rows: dict(p_pool [NP,V], p_index [B,K,G+1], q_pool [B*G,V],
+    q_index [B,K,G], drafts [B,K,G]).
+
+    Recipe (per prefix b, own generator): position-j base logits 2 N(0,1) with
+    a boosted mode token; one set of drafter rows z_q_j = base_j + sigma_j N(0,1)
+    shared by the K drafts (one denoising pass exposes the marginals, and the K
+    drafts are sampled from them); K drafts sampled independently from those
+    rows; one verifier row per distinct draft prefix x_<j (a node of the draft
+    tree, so row 0 is shared by all drafts), z_p = base_j + tau N(0,1).
+    """
+    B = cfg.B if B is None else B
+    V = cfg.V if V is None else V
+    K = cfg.K if K is None else K
+    G = cfg.gamma if gamma is None else gamma
+    dt = cfg.dtype if dtype is None else dtype
+    ds = cfg.data_seed if data_seed is None else data_seed
+    tau = cfg.tau if tau is None else tau
+    tdtype = torch.float32 if dt == "f32" else torch.bfloat16
+    p_rows, q_rows = [], []
+    p_index = torch.empty((B, K, G + 1), dtype=torch.int32)
+    q_index = torch.empty((B, K, G), dtype=torch.int32)
+    drafts = torch.empty((B, K, G), dtype=torch.int32, device=device)
+    n_p = 0
+    for b in range(B):
+        g = _gen(device, ds * 1_000_003 + b)
+        base = torch.randn((G + 1, V), generator=g, device=device, dtype=torch.float32) * 2.0
+        mode = torch.randint(0, V, (G + 1, 1), generator=g, device=device)
+        hit = torch.rand((G + 1, 1), generator=g, device=device) < cfg.boost_prob
+        base.scatter_add_(-1, mode, hit.float() * cfg.boost)
+        sig = cfg.sigma0 + cfg.sigma_step * torch.arange(G, device=device, dtype=torch.float32)
+        zq = (base[:G] + sig.view(G, 1) * torch.randn((G, V), generator=g, device=device))
+        zq = zq.to(tdtype)
+        dr = _gumbel_argmax(zq.unsqueeze(0).expand(K, G, V), cfg.temp, g)
+        drafts[b].copy_(dr)
+        q_rows.append(zq)
+        q_index[b] = (b * G + torch.arange(G, dtype=torch.int32)).view(1, G).expand(K, G)
+        # one verifier row per node of the draft tree, in (position, first draft) order
+        dh = dr.cpu().tolist()
+        nodes, node_pos = {}, []
+        for j in range(G + 1):
+            for k in range(K):
+                key = (j, tuple(dh[k][:j]))
+                if key not in nodes:
+                    nodes[key] = len(node_pos)
+                    node_pos.append(j)
+                p_index[b, k, j] = n_p + nodes[key]
+        pos = torch.tensor(node_pos, device=device)
+        zp = base[pos] + tau * torch.randn((len(node_pos), V), generator=g, device=device)
+        p_rows.append(zp.to(tdtype))
+        n_p += len(node_pos)
+    return {"p_pool": torch.cat(p_rows, 0), "p_index": p_index.to(device),
+            "q_pool": torch.cat(q_rows, 0), "q_index": q_index.to(device), "drafts": drafts,
+            "temp": cfg.temp, "dtype": dt}
+
+
 def tiny_trial_drafts(q_logits: torch.Tensor, n: int, temp: float, seed: int) -> torch.Tensor:
     """n independent draft sets for one logit instance: [n, K, gamma] int32.
 
