@@ -25,8 +25,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "verified draft positions/sec and achieved HBM GB/s (V=152064, bf16 logits)"
 # sources whose text decides each kernel's memory traffic
-KERNEL_SOURCES = {"rowstats": ["svd_device.hpp", "kr_rowstats.hpp"]}
-KERNEL_SYMBOL = {"rowstats": "kr_rowstats"}
+KERNEL_SOURCES = {"rowstats": ["svd_device.hpp", "kr_rowstats.hpp"],
+                  "pool_stats": ["svd_device.hpp", "kr_rowstats.hpp", "kr_rows.hpp"]}
+KERNEL_SYMBOL = {"rowstats": "kr_rowstats", "pool_stats": "kr_pool_stats"}
 
 
 def traffic_file(kernel: str, mode: str = "standard") -> str:
@@ -87,7 +88,11 @@ def record_traffic(kernel, workload, mode, fetch_dir, write_dir, copy_fetch_dir,
     import workloads as W
     cfg = W.get_config(workload)
     es = 2 if cfg.dtype == "bf16" else 4
-    alg = bytes_per_row_pair(cfg.V, es, mode) * cfg.B * cfg.K * cfg.gamma
+    if cfg.layout == "pooled":
+        rows = pool_rows_read(W.generate_pooled(cfg), mode)
+        alg = rows * (cfg.V * es + POOL_STAT_BYTES)
+    else:
+        alg = bytes_per_row_pair(cfg.V, es, mode) * cfg.B * cfg.K * cfg.gamma
     rec = {"kernel": sym, "workload": workload, "mode": mode, "kernel_hash": kernel_hash(kernel),
            "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
            "dispatches": [nf, nw], "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
@@ -97,6 +102,19 @@ def record_traffic(kernel, workload, mode, fetch_dir, write_dir, copy_fetch_dir,
     with open(traffic_file(kernel, mode), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+POOL_STAT_BYTES = 8  # (max, sum) written per pool row
+
+
+def pool_rows_read(d, mode: str) -> int:
+    """Distinct pool rows that scored positions read (the rows kr_pool_stats streams)."""
+    import numpy as np
+    G = d["drafts"].shape[-1]
+    n = len(np.unique(d["p_index"][:, :, :G].cpu().numpy()))
+    if mode != "greedy":
+        n += len(np.unique(d["q_index"].cpu().numpy()))
+    return n
 
 
 def bytes_per_row_pair(V: int, es: int, mode: str = "standard") -> int:
@@ -109,17 +127,24 @@ def bytes_per_row_pair(V: int, es: int, mode: str = "standard") -> int:
     return rows * V * es + 4 + 16 + 4
 
 
-def cpu_baseline(d, cfg, seed, mode="standard", seconds=10.0):
+def cpu_baseline(d, cfg, seed, mode="standard", pooled=False, seconds=10.0):
     """The oracle, untuned, on the same batch, repeated until about `seconds`
     of wall time have passed (at least once)."""
     import oracle
     import workloads as W
     threads = max(1, min(16, os.cpu_count() or 1))
-    hp, hq, hd = W.to_host(d["p"]), W.to_host(d["q"]), W.to_host(d["drafts"])
+    if pooled:
+        hp, hq = W.to_host(d["p_pool"]), W.to_host(d["q_pool"])
+        pi, qi, hd = W.to_host(d["p_index"]), W.to_host(d["q_index"]), W.to_host(d["drafts"])
+    else:
+        hp, hq, hd = W.to_host(d["p"]), W.to_host(d["q"]), W.to_host(d["drafts"])
     reps, dt = 0, 0.0
     while reps == 0 or dt < seconds:
         t0 = time.perf_counter()
-        if mode == "greedy":
+        if pooled:
+            oracle.select_and_verify_rows(hp, pi, hq, qi, hd, temp_p=cfg.temp, seed=seed,
+                                          greedy=mode == "greedy", nthreads=threads)
+        elif mode == "greedy":
             oracle.greedy_select_and_verify(hp, hd, temp_p=cfg.temp, seed=seed, nthreads=threads)
         else:
             oracle.select_and_verify(hp, hq, hd, temp_p=cfg.temp, seed=seed, nthreads=threads)
@@ -167,7 +192,9 @@ def main():
                          "--calibrate-copy")
     args = ap.parse_args()
     if args.record_traffic:
-        record_traffic("rowstats", args.workload, args.mode, *args.record_traffic)
+        import workloads as W
+        kern = "pool_stats" if W.get_config(args.workload).layout == "pooled" else "rowstats"
+        record_traffic(kern, args.workload, args.mode, *args.record_traffic)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the verification path shards by prefix with no "
@@ -187,10 +214,16 @@ def main():
     cfg = W.get_config(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    d = W.generate(cfg, device=dev)
+    pooled = cfg.layout == "pooled"
+    d = W.generate_pooled(cfg, device=dev) if pooled else W.generate(cfg, device=dev)
     B, K, G, V = cfg.B, cfg.K, cfg.gamma, cfg.V
     es = 2 if cfg.dtype == "bf16" else 4
-    ws = svd.alloc_workspace(B, K, G, V, dev)
+    if pooled:
+        NP, NQ = d["p_pool"].shape[0], d["q_pool"].shape[0]
+        ws = torch.empty(svd.svd_rows_workspace_bytes(B, K, G, V, NP, NQ), dtype=torch.uint8,
+                         device=dev)
+    else:
+        ws = svd.alloc_workspace(B, K, G, V, dev)
     sel = torch.empty(B, dtype=torch.int32, device=dev)
     L = torch.empty(B, dtype=torch.int32, device=dev)
     tok = torch.empty(B, dtype=torch.int32, device=dev)
@@ -200,7 +233,13 @@ def main():
     greedy = args.mode == "greedy"
 
     def step():
-        if greedy:
+        if pooled:
+            rc = svd.svd_select_and_verify_rows(
+                svd.SVD_RULE_GREEDY if greedy else svd.SVD_RULE_STANDARD, d["p_pool"], NP,
+                d["p_index"], d["q_pool"], NQ, d["q_index"], d["drafts"], code, B, K, G, V,
+                cfg.temp, cfg.temp, cfg.seed, 0, sel, L, tok, None, None, ws, ws.numel(),
+                stream.cuda_stream)
+        elif greedy:
             rc = svd.svd_greedy_select_and_verify(d["p"], d["drafts"], code, B, K, G, V, cfg.temp,
                                                   cfg.seed, 0, sel, L, tok, None, None, ws,
                                                   ws.numel(), stream.cuda_stream)
@@ -218,7 +257,7 @@ def main():
 
     # timed region: K steps; events around the dominant kernel's launches only,
     # recorded on the stream the kernel is launched on
-    dom = "rowstats"
+    dom = "pool_stats" if pooled else "rowstats"
     svd.svd_profile_enable([dom])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -245,12 +284,20 @@ def main():
     positions = B * K * G
     L_host = L.cpu().numpy()
     bonus_rows = int((L_host == G).sum())
-    rows = 1 if greedy else 2
-    alg_bytes_step = positions * (rows * V * es + 4) + bonus_rows * V * es + B * 12
+    if pooled:
+        units = pool_rows_read(d, args.mode)
+        unit_bytes = V * es + POOL_STAT_BYTES
+        # the pool rows read once, drafts and index tables, bonus rows drawn, outputs
+        alg_bytes_step = (units * V * es + positions * (4 + 4 + (0 if greedy else 4)) +
+                          bonus_rows * V * es + B * 12)
+    else:
+        units = positions
+        unit_bytes = bytes_per_row_pair(V, es, args.mode)
+        rows = 1 if greedy else 2
+        alg_bytes_step = positions * (rows * V * es + 4) + bonus_rows * V * es + B * 12
     di = svd.KERNELS.index(dom)
     ms_dom = ms_kernels[di] / max(launches[di], 1)
-    unit_bytes = bytes_per_row_pair(V, es, args.mode)
-    launch_bytes = unit_bytes * positions
+    launch_bytes = unit_bytes * units
     achieved = launch_bytes / (ms_dom * 1e-3) / 1e9
     traffic = measured_traffic(dom, cfg.name, args.mode)
 
@@ -277,13 +324,13 @@ def main():
         "roofline": {"kernel": KERNEL_SYMBOL[dom], "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_unit": unit_bytes,
-                     "units_per_launch": positions},
+                     "units_per_launch": units},
         "mean_accept_len": float(L_host.mean()),
         "mat": float(L_host.mean() + 1.0),
         "wall_s": wall,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(d, cfg, cfg.seed, args.mode)
+        result["cpu_baseline"] = cpu_baseline(d, cfg, cfg.seed, args.mode, pooled)
     print(json.dumps(result), flush=True)
 
 

@@ -163,6 +163,41 @@ int svd_greedy_select_and_verify(const void *p_logits, const int32_t *drafts, sv
                                  float *alpha, void *workspace, size_t workspace_bytes,
                                  void *hip_stream);
 
+/*
+ * Shared rows.  The K drafts of one diffusion pass are sampled from one set of
+ * drafter marginals (SpecDiff-2 section 5.2), so their q rows can be one; and
+ * drafts with a common prefix read the same verifier rows, as in the flattened
+ * draft tree of SpecDiff-2 appendix B.8 (all drafts of a prefix share p row 0).
+ * Here p and q are pools of rows with index tables saying which pool row each
+ * scored position reads:
+ *   p_rows   [n_p_rows][V]         verifier rows
+ *   p_index  [B][K][gamma+1] int32 p row (b, k, j) = p_rows[p_index[b][k][j]];
+ *                                  j = gamma is the bonus row
+ *   q_rows   [n_q_rows][V]         drafter rows (unused, may be NULL, for
+ *                                  SVD_RULE_GREEDY)
+ *   q_index  [B][K][gamma] int32   q row (b, k, j) = q_rows[q_index[b][k][j]]
+ *   drafts   [B][K][gamma] int32
+ * The result is that of svd_select_and_verify (rule SVD_RULE_STANDARD) or
+ * svd_greedy_select_and_verify (SVD_RULE_GREEDY) on the gathered dense arrays,
+ * but each pool row that a scored position reads is streamed once, however
+ * many positions read it.  An index outside its pool is a data error: the
+ * prefix that reads it (for the bonus row: when the bonus is drawn) gets -1
+ * outputs.  Limits: 1 <= n_p_rows < 2^30, 0 <= n_q_rows < 2^30 (>= 1 for the
+ * standard rule); the workspace is svd_rows_workspace_bytes(B, K, gamma, V,
+ * n_p_rows, n_q_rows) bytes (0 for sizes out of range).  No beta output.
+ */
+typedef enum { SVD_RULE_STANDARD = 0, SVD_RULE_GREEDY = 1 } svd_rule_t;
+size_t svd_rows_workspace_bytes(int64_t B, int32_t K, int32_t gamma, int32_t V,
+                                int64_t n_p_rows, int64_t n_q_rows);
+int svd_select_and_verify_rows(svd_rule_t rule, const void *p_rows, int64_t n_p_rows,
+                               const int32_t *p_index, const void *q_rows, int64_t n_q_rows,
+                               const int32_t *q_index, const int32_t *drafts, svd_dtype_t dtype,
+                               int64_t B, int32_t K, int32_t gamma, int32_t V, float temp_p,
+                               float temp_q, uint64_t seed, uint64_t row_base, int32_t *selected,
+                               int32_t *accept_len, int32_t *next_token, float *scores,
+                               float *alpha, void *workspace, size_t workspace_bytes,
+                               void *hip_stream);
+
 /* Static text for a status code. */
 const char *svd_strerror(int status);
 
@@ -185,7 +220,10 @@ enum {
   SVD_KERNEL_DRAW_FIX = 3,   /* exact mass of segments with many near-equal p/q ratios  */
   SVD_KERNEL_DRAW_PICK = 4,  /* fp64 masses and inverse CDF                             */
   SVD_KERNEL_BETA = 5,       /* optional overlap mass                                   */
-  SVD_KERNEL_COUNT = 6
+  SVD_KERNEL_MARK = 6,       /* shared rows: flags of the pool rows read               */
+  SVD_KERNEL_POOL_STATS = 7, /* shared rows: statistics once per pool row read          */
+  SVD_KERNEL_ALPHA_ROWS = 8, /* shared rows: alpha per scored position                  */
+  SVD_KERNEL_COUNT = 9
 };
 int svd_profile_enable(unsigned kernel_mask);
 int svd_profile_read(double *ms, int64_t *launches, int n);

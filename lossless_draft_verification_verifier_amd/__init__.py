@@ -7,10 +7,11 @@ marshals arguments.  PyTorch supplies device memory and the current stream.
 Raw entry points (same names and argument order as the C ABI; pointer
 arguments take an int address or a tensor):
     svd_workspace_bytes, svd_verify, svd_select_and_verify, svd_greedy_verify,
-    svd_greedy_select_and_verify, svd_strerror, svd_profile_enable, svd_profile_read
+    svd_greedy_select_and_verify, svd_rows_workspace_bytes, svd_select_and_verify_rows,
+    svd_strerror, svd_profile_enable, svd_profile_read
 Tensor conveniences that allocate the outputs and the workspace with torch:
     verify, select_and_verify, greedy_verify, greedy_select_and_verify,
-    workspace_bytes
+    select_and_verify_rows, workspace_bytes
 
 Importing fails with ImportError when ``libsvd.so`` has not been built; there
 is no fallback path.
@@ -26,10 +27,13 @@ LIB_PATH = os.path.join(_PKG, "libsvd.so")
 SVD_F32, SVD_BF16 = 0, 1
 SVD_OK, SVD_EINVAL, SVD_EDTYPE, SVD_EWORKSPACE, SVD_EHIP = 0, -1, -2, -3, -4
 SVD_MAX_K, SVD_MAX_GAMMA = 64, 4096
-KERNELS = ("rowstats", "select", "draw_pass", "draw_fix", "draw_pick", "beta")
+KERNELS = ("rowstats", "select", "draw_pass", "draw_fix", "draw_pick", "beta", "mark",
+           "pool_stats", "alpha_rows")
+SVD_RULE_STANDARD, SVD_RULE_GREEDY = 0, 1
 
 C_EXPORTS = ("svd_workspace_bytes", "svd_verify", "svd_select_and_verify", "svd_greedy_verify",
-             "svd_greedy_select_and_verify", "svd_strerror", "svd_profile_enable",
+             "svd_greedy_select_and_verify", "svd_rows_workspace_bytes",
+             "svd_select_and_verify_rows", "svd_strerror", "svd_profile_enable",
              "svd_profile_read")
 
 
@@ -62,6 +66,12 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.svd_greedy_select_and_verify.restype = ctypes.c_int
     L.svd_greedy_select_and_verify.argtypes = [vp, vp, ctypes.c_int, i64, i32, i32, i32, f32, u64,
                                                u64, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.svd_rows_workspace_bytes.restype = sz
+    L.svd_rows_workspace_bytes.argtypes = [i64, i32, i32, i32, i64, i64]
+    L.svd_select_and_verify_rows.restype = ctypes.c_int
+    L.svd_select_and_verify_rows.argtypes = [ctypes.c_int, vp, i64, vp, vp, i64, vp, vp,
+                                             ctypes.c_int, i64, i32, i32, i32, f32, f32, u64, u64,
+                                             vp, vp, vp, vp, vp, vp, sz, vp]
     L.svd_strerror.restype = ctypes.c_char_p
     L.svd_strerror.argtypes = [ctypes.c_int]
     L.svd_profile_enable.restype = ctypes.c_int
@@ -124,6 +134,23 @@ def svd_greedy_select_and_verify(p_logits, drafts, dtype, B, K, gamma, V, temp_p
     return int(_lib.svd_greedy_select_and_verify(
         _addr(p_logits), _addr(drafts), int(dtype), int(B), int(K), int(gamma), int(V),
         float(temp_p), int(seed) & _M64, int(row_base) & _M64, _addr(selected),
+        _addr(accept_len), _addr(next_token), _addr(scores), _addr(alpha), _addr(workspace),
+        int(workspace_bytes), _addr(hip_stream)))
+
+
+def svd_rows_workspace_bytes(B: int, K: int, gamma: int, V: int, n_p_rows: int,
+                             n_q_rows: int) -> int:
+    return int(_lib.svd_rows_workspace_bytes(B, K, gamma, V, n_p_rows, n_q_rows))
+
+
+def svd_select_and_verify_rows(rule, p_rows, n_p_rows, p_index, q_rows, n_q_rows, q_index, drafts,
+                               dtype, B, K, gamma, V, temp_p, temp_q, seed, row_base, selected,
+                               accept_len, next_token, scores, alpha, workspace, workspace_bytes,
+                               hip_stream) -> int:
+    return int(_lib.svd_select_and_verify_rows(
+        int(rule), _addr(p_rows), int(n_p_rows), _addr(p_index), _addr(q_rows), int(n_q_rows),
+        _addr(q_index), _addr(drafts), int(dtype), int(B), int(K), int(gamma), int(V),
+        float(temp_p), float(temp_q), int(seed) & _M64, int(row_base) & _M64, _addr(selected),
         _addr(accept_len), _addr(next_token), _addr(scores), _addr(alpha), _addr(workspace),
         int(workspace_bytes), _addr(hip_stream)))
 
@@ -313,4 +340,56 @@ def greedy_verify(p, draft, temp_p=1.0, seed=0, row_base=0, want_alpha=False, wo
                            out["accept_len"], out["next_token"], out["alpha"], ws, ws.numel(), st)
     if rc != SVD_OK:
         raise SvdError(rc, "svd_greedy_verify")
+    return out
+
+
+def select_and_verify_rows(p_pool, p_index, q_pool, q_index, drafts, rule="standard", temp_p=1.0,
+                           temp_q=None, seed=0, row_base=0, want_alpha=False, want_scores=False,
+                           workspace=None, stream=None):
+    """Shared rows: p_pool [NP,V], p_index [B,K,gamma+1] int32, q_pool [NQ,V] and
+    q_index [B,K,gamma] int32 (None for rule="greedy"), drafts [B,K,gamma] int32."""
+    import torch
+    greedy = rule == "greedy"
+    if rule not in ("standard", "greedy"):
+        raise ValueError("rule must be 'standard' or 'greedy'")
+    dev = p_pool.device
+    tens = [(p_pool, "p_pool"), (p_index, "p_index"), (drafts, "drafts")]
+    if not greedy:
+        tens += [(q_pool, "q_pool"), (q_index, "q_index")]
+        if q_pool.dtype != p_pool.dtype:
+            raise TypeError("p_pool and q_pool must share one dtype")
+    for t, n in tens:
+        _check(t, n, dev)
+    for t, n in ((p_index, "p_index"), (drafts, "drafts")) + (() if greedy else ((q_index, "q_index"),)):
+        if t.dtype != torch.int32:
+            raise TypeError("%s must be int32" % n)
+    B, K, G = drafts.shape
+    V = p_pool.shape[1]
+    if tuple(p_index.shape) != (B, K, G + 1) or (not greedy and tuple(q_index.shape) != (B, K, G)):
+        raise ValueError("index tables must be [B,K,gamma+1] and [B,K,gamma]")
+    if not greedy and q_pool.shape[1] != V:
+        raise ValueError("pools must share V")
+    NP = p_pool.shape[0]
+    NQ = 0 if greedy else q_pool.shape[0]
+    out = {
+        "selected": torch.empty(B, dtype=torch.int32, device=dev),
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+        "scores": torch.empty((B, K), dtype=torch.float32, device=dev) if want_scores else None,
+        "alpha": torch.empty((B, K, G), dtype=torch.float32, device=dev) if want_alpha else None,
+    }
+    if workspace is None:
+        n = svd_rows_workspace_bytes(B, K, G, V, NP, NQ)
+        if n == 0:
+            raise ValueError("sizes out of range")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    temp_q = temp_p if temp_q is None else temp_q
+    rc = svd_select_and_verify_rows(
+        SVD_RULE_GREEDY if greedy else SVD_RULE_STANDARD, p_pool, NP, p_index,
+        None if greedy else q_pool, NQ, None if greedy else q_index, drafts, _dtype_code(p_pool),
+        B, K, G, V, temp_p, temp_q, seed, row_base, out["selected"], out["accept_len"],
+        out["next_token"], out["scores"], out["alpha"], workspace, workspace.numel(), st)
+    if rc != SVD_OK:
+        raise SvdError(rc, "svd_select_and_verify_rows")
     return out

@@ -121,13 +121,26 @@ struct DrawRows {
   const typename E::elem *q;  // nullptr for a bonus draw
 };
 
+// Rows taken from pools through index tables ([B][K][gamma+1] and
+// [B][K][gamma]); null tables mean the dense layout.
+struct RowIndex {
+  const int32_t *p;
+  const int32_t *q;
+};
+
 template <typename E>
 __device__ __forceinline__ DrawRows<E> draw_rows(const typename E::elem *p, const typename E::elem *q,
-                                        int K, int gamma, int V, int64_t b, const DrawDesc &d) {
+                                                 const RowIndex ix, int K, int gamma, int V,
+                                                 int64_t b, const DrawDesc &d) {
   const int64_t bk = b * K + d.k;
+  const int64_t pr = ix.p ? (int64_t)ix.p[bk * (gamma + 1) + d.pos] : bk * (gamma + 1) + d.pos;
   DrawRows<E> r;
-  r.p = p + (bk * (gamma + 1) + d.pos) * (int64_t)V;
-  r.q = d.two ? q + (bk * gamma + d.pos) * (int64_t)V : nullptr;
+  r.p = p + pr * (int64_t)V;
+  r.q = nullptr;
+  if (d.two) {
+    const int64_t qr = ix.q ? (int64_t)ix.q[bk * gamma + d.pos] : bk * gamma + d.pos;
+    r.q = q + qr * (int64_t)V;
+  }
   return r;
 }
 
@@ -196,9 +209,10 @@ __device__ __forceinline__ void block_reduce_seg(double &a, double &b, double &c
 // (residual draws) the drawn row pair's statistics st.
 template <typename E, bool kVec, int NT>
 __device__ __forceinline__ void draw_pass_item(const typename E::elem *__restrict__ p,
-                                               const typename E::elem *__restrict__ q, int K,
-                                               int gamma, int V, int nseg, float tp, float tq,
-                                               const DrawDesc d, const RowStats st,
+                                               const typename E::elem *__restrict__ q,
+                                               const RowIndex ix, int K, int gamma, int V,
+                                               int nseg, float tp, float tq, const DrawDesc d,
+                                               const RowStats st,
                                                DrawSeg *__restrict__ segs,
                                                DrawUnc *__restrict__ uncs, int64_t b, int seg) {
   constexpr int NW = NT / 64;
@@ -210,7 +224,7 @@ __device__ __forceinline__ void draw_pass_item(const typename E::elem *__restric
   __shared__ DrawUnc unc[kUncCap];
   if (!d.valid) return;
   exp64_table_init(tab);
-  const DrawRows<E> r = draw_rows<E>(p, q, K, gamma, V, b, d);
+  const DrawRows<E> r = draw_rows<E>(p, q, ix, K, gamma, V, b, d);
   const double invTp = 1.0 / (double)tp, invTq = 1.0 / (double)tq;
   if (threadIdx.x == 0) n_unc = 0;
   __syncthreads();
@@ -291,12 +305,13 @@ __device__ __forceinline__ RowStats drawn_stats(const RowStats *stats, const Dra
 
 template <typename E, bool kVec>
 __global__ __launch_bounds__(kBlock) void kr_draw_pass(
-    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int K,
-    int gamma, int V, int nseg, float tp, float tq, const RowStats *__restrict__ stats,
-    const DrawDesc *__restrict__ desc, DrawSeg *__restrict__ segs, DrawUnc *__restrict__ uncs) {
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
+    const RowIndex ix, int K, int gamma, int V, int nseg, float tp, float tq,
+    const RowStats *__restrict__ stats, const DrawDesc *__restrict__ desc,
+    DrawSeg *__restrict__ segs, DrawUnc *__restrict__ uncs) {
   const int64_t b = blockIdx.x / nseg;
   const DrawDesc d = desc[b];
-  draw_pass_item<E, kVec, kBlock>(p, q, K, gamma, V, nseg, tp, tq, d,
+  draw_pass_item<E, kVec, kBlock>(p, q, ix, K, gamma, V, nseg, tp, tq, d,
                                   drawn_stats(stats, d, K, gamma, b), segs, uncs, b,
                                   (int)(blockIdx.x - b * nseg));
 }
@@ -386,8 +401,9 @@ __device__ __forceinline__ void segment_mass_exact(const DrawWeight<E> &W, const
 // overflowed; every other workgroup returns at once.
 template <typename E, bool kVec>
 __global__ __launch_bounds__(kBlock) void kr_draw_fix(
-    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int K,
-    int gamma, int V, int nseg, float tp, float tq, const RowStats *__restrict__ stats,
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
+    const RowIndex ix, int K, int gamma, int V, int nseg, float tp, float tq,
+    const RowStats *__restrict__ stats,
     const DrawDesc *__restrict__ desc, const DrawSeg *__restrict__ segs,
     DrawMass *__restrict__ mass) {
   __shared__ Exp64Table tab;
@@ -400,7 +416,7 @@ __global__ __launch_bounds__(kBlock) void kr_draw_fix(
   if (!d.valid || !d.two || S[seg].n_unc >= 0) return;
   exp64_table_init(tab);
   __syncthreads();
-  const DrawRows<E> rows = draw_rows<E>(p, q, K, gamma, V, b, d);
+  const DrawRows<E> rows = draw_rows<E>(p, q, ix, K, gamma, V, b, d);
   DrawWeight<E> W;
   draw_setup<E>(rows, d, drawn_stats(stats, d, K, gamma, b), S, nseg, tp, tq, W);
   DrawMass m{};
@@ -433,8 +449,9 @@ __device__ __forceinline__ double block_exclusive_scan(double x, double *lds /* 
 // from kr_draw_fix.
 template <typename E, bool kVec, int NT>
 __device__ __forceinline__ void draw_pick_item(
-    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int K,
-    int gamma, int V, int nseg, float tp, float tq, uint64_t seed, uint64_t row_base,
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
+    const RowIndex ix, int K, int gamma, int V, int nseg, float tp, float tq, uint64_t seed,
+    uint64_t row_base,
     const DrawDesc d, const RowStats st, const DrawSeg *__restrict__ segs,
     const DrawUnc *__restrict__ uncs, DrawMass *__restrict__ mass,
     int32_t *__restrict__ selected, int32_t *__restrict__ accept_len,
@@ -448,7 +465,7 @@ __device__ __forceinline__ void draw_pick_item(
   if (!d.valid) return;
   exp64_table_init(tab);
   __syncthreads();
-  const DrawRows<E> rows = draw_rows<E>(p, q, K, gamma, V, b, d);
+  const DrawRows<E> rows = draw_rows<E>(p, q, ix, K, gamma, V, b, d);
   const DrawSeg *S = segs + b * nseg;
   DrawMass *ms = mass + b * nseg;
   const bool residual = d.two != 0;
@@ -574,15 +591,16 @@ __device__ __forceinline__ void draw_pick_item(
 
 template <typename E, bool kVec>
 __global__ __launch_bounds__(kBlock) void kr_draw_pick(
-    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int K,
-    int gamma, int V, int nseg, float tp, float tq, uint64_t seed, uint64_t row_base,
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
+    const RowIndex ix, int K, int gamma, int V, int nseg, float tp, float tq, uint64_t seed,
+    uint64_t row_base,
     const RowStats *__restrict__ stats, const DrawDesc *__restrict__ desc,
     const DrawSeg *__restrict__ segs, const DrawUnc *__restrict__ uncs,
     DrawMass *__restrict__ mass, int32_t *__restrict__ selected,
     int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token) {
   const int64_t b = blockIdx.x;
   const DrawDesc d = desc[b];
-  draw_pick_item<E, kVec, kBlock>(p, q, K, gamma, V, nseg, tp, tq, seed, row_base, d,
+  draw_pick_item<E, kVec, kBlock>(p, q, ix, K, gamma, V, nseg, tp, tq, seed, row_base, d,
                                   drawn_stats(stats, d, K, gamma, b), segs, uncs, mass, selected,
                                   accept_len, next_token, b);
 }

@@ -110,6 +110,24 @@ __device__ __forceinline__ void row_ms(const typename E::elem *row, int V, float
   s_out = s[0];
 }
 
+// alpha of one scored position from its two rows' statistics (raw max m and
+// sum s of exp2((z - m) * c)) and the drafted token's logits; NaN when a row
+// is invalid.  kGreedy: alpha = p(x), the q row is ignored.
+template <bool kGreedy>
+__device__ __forceinline__ float acceptance(float zpx, float mp, float sp, float cp, float zqx,
+                                            float mq, float sq, float cq) {
+  const bool rows_ok = !(sp != sp) && !(sq != sq) && mp != kNegInf && mq != kNegInf;
+  if (!rows_ok) return __builtin_nanf("");
+  // log2 p(x) (and log2 q(x)); accept outright when q(x) <= p(x)
+  const float lp = (zpx - mp) * cp - log2f(sp);
+  if constexpr (kGreedy) {
+    return fminf(exp2f(lp), 1.0f);
+  } else {
+    const float lq = (zqx - mq) * cq - log2f(sq);
+    return (lq <= lp) ? 1.0f : exp2f(lp - lq);
+  }
+}
+
 // One scored row pair: statistics of both rows and alpha, written by thread 0.
 // kGreedy: greedy acceptance (SpecDiff-2 section 5.2 and appendix B.4), which
 // compares the uniform with the verifier probability of the drafted token, so
@@ -134,17 +152,9 @@ __device__ __forceinline__ void rowstats_item(const typename E::elem *__restrict
   if (threadIdx.x == 0) {
     const int32_t x = drafts[rp];
     float a = __builtin_nanf("");
-    const bool rows_ok = !(sp != sp) && !(sq != sq) && mp != kNegInf && mq != kNegInf;
-    if (rows_ok && x >= 0 && x < V) {
-      // log2 p(x) (and log2 q(x)); accept outright when q(x) <= p(x)
-      const float lp = (E::at(prow, x) - mp) * cp - log2f(sp);
-      if constexpr (kGreedy) {
-        a = fminf(exp2f(lp), 1.0f);
-      } else {
-        const float lq = (E::at(qrow, x) - mq) * cq - log2f(sq);
-        a = (lq <= lp) ? 1.0f : exp2f(lp - lq);
-      }
-    }
+    if (x >= 0 && x < V)
+      a = acceptance<kGreedy>(E::at(prow, x), mp, sp, cp, kGreedy ? 0.0f : E::at(qrow, x), mq,
+                              sq, cq);
     stats[rp] = RowStats{mp, sp, mq, sq};
     alpha_ws[rp] = a;
     if (alpha_out) alpha_out[rp] = a;

@@ -20,9 +20,12 @@ namespace svd {
 
 // Run by the 64 lanes of one wave (lane = threadIdx.x & 63); every lane gets
 // the decision.  Lane 0 writes selected / accept_len (and -1 next_token for an
-// invalid prefix), lane k writes scores[k].
+// invalid prefix), lane k writes scores[k].  p_index (nullable): the verifier
+// rows come from a pool of np rows, and a bonus row outside it makes the
+// prefix invalid.
 __device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alpha_ws,
                                                   const int32_t *__restrict__ drafts, bool greedy,
+                                                  const int32_t *__restrict__ p_index, int64_t np,
                                                   int K, int gamma, uint64_t seed,
                                                   uint64_t row_base, int64_t b,
                                                   int32_t *__restrict__ selected,
@@ -44,7 +47,7 @@ __device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alph
     }
     if (scores) scores[b * K + lane] = (float)S;
   }
-  const bool invalid = __any(bad);
+  bool invalid = __any(bad);
 
   // argmax over lanes, the lower index on an exact tie (a total order, so
   // every lane of the butterfly ends with the same winner)
@@ -77,6 +80,11 @@ __device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alph
     }
   }
 
+  if (!invalid && L == gamma && p_index) {
+    const int32_t pi = p_index[((int64_t)b * K + bk) * (gamma + 1) + gamma];
+    invalid = pi < 0 || pi >= np;
+  }
+
   if (lane == 0) {
     if (invalid) {
       if (selected) selected[b] = -1;
@@ -95,12 +103,13 @@ __device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alph
 }
 
 __global__ __launch_bounds__(64) void kr_select(
-    const float *__restrict__ alpha_ws, const int32_t *__restrict__ drafts, int greedy, int K,
-    int gamma, uint64_t seed, uint64_t row_base, int32_t *__restrict__ selected,
-    int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token,
-    float *__restrict__ scores, DrawDesc *__restrict__ desc) {
-  const DrawDesc d = select_prefix(alpha_ws, drafts, greedy != 0, K, gamma, seed, row_base,
-                                   blockIdx.x, selected, accept_len, next_token, scores);
+    const float *__restrict__ alpha_ws, const int32_t *__restrict__ drafts, int greedy,
+    const int32_t *__restrict__ p_index, int64_t np, int K, int gamma, uint64_t seed,
+    uint64_t row_base, int32_t *__restrict__ selected, int32_t *__restrict__ accept_len,
+    int32_t *__restrict__ next_token, float *__restrict__ scores, DrawDesc *__restrict__ desc) {
+  const DrawDesc d = select_prefix(alpha_ws, drafts, greedy != 0, p_index, np, K, gamma, seed,
+                                   row_base, blockIdx.x, selected, accept_len, next_token,
+                                   scores);
   if (threadIdx.x == 0) desc[blockIdx.x] = d;
 }
 

@@ -11,6 +11,7 @@
 #include "svd.h"
 #include "kr_beta.hpp"
 #include "kr_draw.hpp"
+#include "kr_rows.hpp"
 #include "kr_rowstats.hpp"
 #include "kr_select.hpp"
 
@@ -22,7 +23,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-  size_t stats, alpha, desc, segs, uncs, mass, total;
+  size_t stats, alpha, desc, segs, uncs, mass, pstat, flags, total;
   int nseg;
 };
 
@@ -36,7 +37,8 @@ bool sizes_ok(int64_t B, int32_t K, int32_t G, int32_t V) {
   return true;
 }
 
-Layout layout(int64_t B, int32_t K, int32_t G, int32_t V) {
+// np, nq: pool rows of the shared-row entry point (0 for the dense layout)
+Layout layout(int64_t B, int32_t K, int32_t G, int32_t V, int64_t np = 0, int64_t nq = 0) {
   Layout L{};
   const size_t rp = (size_t)B * K * G;
   L.nseg = (int)(((int64_t)V + kDrawSeg - 1) / kDrawSeg);
@@ -53,6 +55,10 @@ Layout layout(int64_t B, int32_t K, int32_t G, int32_t V) {
   off = align_up(off + (size_t)B * L.nseg * kUncCap * sizeof(DrawUnc));
   L.mass = off;
   off = align_up(off + (size_t)B * L.nseg * sizeof(DrawMass));
+  L.pstat = off;
+  off = align_up(off + (size_t)(np + nq) * sizeof(PoolStat));
+  L.flags = off;
+  off = align_up(off + (size_t)(np + nq) * sizeof(uint32_t));
   L.total = off;
   return L;
 }
@@ -126,6 +132,10 @@ struct Batch {
   float tp, tq, cp, cq;
   uint64_t seed, row_base;
   bool greedy;  // greedy acceptance: alpha = p(x), q unused
+  RowIndex ix;  // shared rows: p and q are pools of np and nq rows (ix.p null: dense)
+  int64_t np, nq;
+  PoolStat *pstat;
+  uint32_t *flags;
   int32_t *selected, *accept_len, *next_token;
   float *scores, *alpha, *beta;
   RowStats *stats;
@@ -147,6 +157,27 @@ struct Batch {
 template <typename E, bool kVec>
 int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   const unsigned rp = (unsigned)(a.B * a.K * a.G);
+  if (a.ix.p) {  // shared rows: statistics once per pool row read, then alpha per position
+    const int64_t nrows = a.np + (a.greedy ? 0 : a.nq);
+    const unsigned gp = (unsigned)((rp + kBlock - 1) / kBlock);
+    const unsigned gf = (unsigned)std::min<int64_t>((nrows + kBlock - 1) / kBlock, 4096);
+    SVD_LAUNCH(tm, SVD_KERNEL_MARK, s, kr_fill_u32, dim3(gf), dim3(kBlock), s, a.flags, nrows,
+               0u);
+    SVD_LAUNCH(tm, SVD_KERNEL_MARK, s, kr_mark_rows, dim3(gp), dim3(kBlock), s, a.ix.p,
+               a.greedy ? nullptr : a.ix.q, (int64_t)rp, a.G, a.np, a.nq, a.flags);
+    SVD_LAUNCH(tm, SVD_KERNEL_POOL_STATS, s, kr_pool_stats<E, kVec>, dim3((unsigned)nrows),
+               dim3(kRowBlock), s, a.p, a.q, a.np, a.V, a.cp, a.cq, (const uint32_t *)a.flags,
+               a.pstat);
+    if (a.greedy)
+      SVD_LAUNCH(tm, SVD_KERNEL_ALPHA_ROWS, s, kr_alpha_rows<E, true>, dim3(gp), dim3(kBlock), s,
+                 a.p, a.q, a.ix.p, a.ix.q, a.drafts, (int64_t)rp, a.G, a.V, a.np, a.nq, a.cp,
+                 a.cq, (const PoolStat *)a.pstat, a.stats, a.alpha_ws, a.alpha);
+    else
+      SVD_LAUNCH(tm, SVD_KERNEL_ALPHA_ROWS, s, kr_alpha_rows<E, false>, dim3(gp), dim3(kBlock), s,
+                 a.p, a.q, a.ix.p, a.ix.q, a.drafts, (int64_t)rp, a.G, a.V, a.np, a.nq, a.cp,
+                 a.cq, (const PoolStat *)a.pstat, a.stats, a.alpha_ws, a.alpha);
+    return SVD_OK;
+  }
   if (a.greedy)
     SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, true>, dim3(rp), dim3(kRowBlock), s,
                a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, a.stats, a.alpha_ws, a.alpha);
@@ -165,53 +196,74 @@ int enqueue_draw(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   const unsigned nb = (unsigned)a.B;
   const unsigned nbs = (unsigned)(a.B * a.nseg);
   SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_select, dim3(nb), dim3(64), s,
-             (const float *)a.alpha_ws, a.drafts, (int)a.greedy, a.K, a.G, a.seed, a.row_base,
-             a.selected, a.accept_len, a.next_token, a.scores, a.desc);
+             (const float *)a.alpha_ws, a.drafts, (int)a.greedy, a.ix.p, a.np, a.K, a.G, a.seed,
+             a.row_base, a.selected, a.accept_len, a.next_token, a.scores, a.desc);
   SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PASS, s, kr_draw_pass<E, kVec>, dim3(nbs), dim3(kBlock), s,
-             a.p, a.q, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
+             a.p, a.q, a.ix, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
              (const DrawDesc *)a.desc, a.segs, a.uncs);
   if (!a.greedy)  // only residuals max(0, p - q) can leave uncertain tokens
     SVD_LAUNCH(tm, SVD_KERNEL_DRAW_FIX, s, kr_draw_fix<E, kVec>, dim3(nbs), dim3(kBlock), s, a.p,
-               a.q, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
+               a.q, a.ix, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
                (const DrawDesc *)a.desc, (const DrawSeg *)a.segs, a.mass);
   SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PICK, s, kr_draw_pick<E, kVec>, dim3(nb), dim3(kBlock), s, a.p,
-             a.q, a.K, a.G, a.V, a.nseg, a.tp, a.tq, a.seed, a.row_base,
+             a.q, a.ix, a.K, a.G, a.V, a.nseg, a.tp, a.tq, a.seed, a.row_base,
              (const RowStats *)a.stats, (const DrawDesc *)a.desc, (const DrawSeg *)a.segs,
              (const DrawUnc *)a.uncs, a.mass, a.selected, a.accept_len, a.next_token);
   return SVD_OK;
 }
 
+// The arguments of one entry-point call.
+struct Call {
+  const void *p, *q;  // logits (dense), or row pools when p_index is set
+  const int32_t *drafts;
+  svd_dtype_t dtype;
+  int64_t B;
+  int32_t K, G, V;
+  float tp, tq;
+  uint64_t seed, row_base;
+  bool greedy;
+  const int32_t *p_index, *q_index;  // shared rows (null: dense layout)
+  int64_t np, nq;
+  int32_t *selected, *accept_len, *next_token;
+  float *scores, *alpha, *beta;
+  void *workspace;
+  size_t workspace_bytes;
+  void *stream;
+};
+
 template <typename E, bool kVec>
-int run(const void *p_logits, const void *q_logits, const int32_t *drafts, int64_t B, int32_t K,
-        int32_t G, int32_t V, float tp, float tq, uint64_t seed, uint64_t row_base, bool greedy,
-        int32_t *selected, int32_t *accept_len, int32_t *next_token, float *scores, float *alpha,
-        float *beta, void *workspace, hipStream_t stream) {
+int run(const Call &c) {
   using T = typename E::elem;
-  const Layout Lo = layout(B, K, G, V);
-  char *ws = static_cast<char *>(workspace);
+  const Layout Lo = layout(c.B, c.K, c.G, c.V, c.np, c.nq);
+  char *ws = static_cast<char *>(c.workspace);
   Batch<E> a;
-  a.p = static_cast<const T *>(p_logits);
-  a.q = static_cast<const T *>(q_logits);
-  a.drafts = drafts;
-  a.B = B;
-  a.K = K;
-  a.G = G;
-  a.V = V;
+  a.p = static_cast<const T *>(c.p);
+  a.q = static_cast<const T *>(c.q);
+  a.drafts = c.drafts;
+  a.B = c.B;
+  a.K = c.K;
+  a.G = c.G;
+  a.V = c.V;
   a.nseg = Lo.nseg;
-  a.tp = tp;
-  a.tq = tq;
+  a.tp = c.tp;
+  a.tq = c.tq;
   // log2(e) / T folded into one factor per row: exp(z/T) = exp2(z * c)
-  a.cp = (float)(1.4426950408889634 / (double)tp);
-  a.cq = (float)(1.4426950408889634 / (double)tq);
-  a.seed = seed;
-  a.row_base = row_base;
-  a.greedy = greedy;
-  a.selected = selected;
-  a.accept_len = accept_len;
-  a.next_token = next_token;
-  a.scores = scores;
-  a.alpha = alpha;
-  a.beta = beta;
+  a.cp = (float)(1.4426950408889634 / (double)c.tp);
+  a.cq = (float)(1.4426950408889634 / (double)c.tq);
+  a.seed = c.seed;
+  a.row_base = c.row_base;
+  a.greedy = c.greedy;
+  a.ix = RowIndex{c.p_index, c.q_index};
+  a.np = c.np;
+  a.nq = c.nq;
+  a.pstat = reinterpret_cast<PoolStat *>(ws + Lo.pstat);
+  a.flags = reinterpret_cast<uint32_t *>(ws + Lo.flags);
+  a.selected = c.selected;
+  a.accept_len = c.accept_len;
+  a.next_token = c.next_token;
+  a.scores = c.scores;
+  a.alpha = c.alpha;
+  a.beta = c.beta;
   a.stats = reinterpret_cast<RowStats *>(ws + Lo.stats);
   a.alpha_ws = reinterpret_cast<float *>(ws + Lo.alpha);
   a.desc = reinterpret_cast<DrawDesc *>(ws + Lo.desc);
@@ -219,6 +271,7 @@ int run(const void *p_logits, const void *q_logits, const int32_t *drafts, int64
   a.uncs = reinterpret_cast<DrawUnc *>(ws + Lo.uncs);
   a.mass = reinterpret_cast<DrawMass *>(ws + Lo.mass);
 
+  hipStream_t stream = static_cast<hipStream_t>(c.stream);
   CallTimer tm;
   const int rc = enqueue_rows<E, kVec>(a, stream, tm);
   return rc != SVD_OK ? rc : enqueue_draw<E, kVec>(a, stream, tm);
@@ -226,35 +279,58 @@ int run(const void *p_logits, const void *q_logits, const int32_t *drafts, int64
 
 bool temp_ok(float t) { return std::isfinite(t) && t > 0.0f; }
 
-int dispatch(const void *p, const void *q, const int32_t *drafts, svd_dtype_t dtype, int64_t B,
-             int32_t K, int32_t G, int32_t V, float tp, float tq, uint64_t seed,
-             uint64_t row_base, bool greedy, int32_t *selected, int32_t *accept_len,
-             int32_t *next_token, float *scores, float *alpha, float *beta, void *workspace,
-             size_t workspace_bytes, void *hip_stream) {
-  if (!p || (!q && !greedy) || !drafts || !accept_len || !next_token || !workspace)
+bool pools_ok(int64_t np, int64_t nq, bool greedy) {
+  const int64_t lim = (int64_t)1 << 30;
+  return np >= 1 && np < lim && nq >= (greedy ? 0 : 1) && nq < lim;
+}
+
+int dispatch(const Call &c) {
+  const bool rows = c.p_index != nullptr;
+  if (!c.p || (!c.q && !c.greedy) || !c.drafts || !c.accept_len || !c.next_token ||
+      !c.workspace || (rows && !c.greedy && !c.q_index))
     return SVD_EINVAL;
-  if (dtype != SVD_F32 && dtype != SVD_BF16) return SVD_EDTYPE;
-  if (!sizes_ok(B, K, G, V) || !temp_ok(tp) || !temp_ok(tq)) return SVD_EINVAL;
-  if (((uintptr_t)workspace) % kAlign != 0) return SVD_EINVAL;
-  if (workspace_bytes < layout(B, K, G, V).total) return SVD_EWORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  const size_t es = dtype == SVD_F32 ? 4 : 2;
+  if (c.dtype != SVD_F32 && c.dtype != SVD_BF16) return SVD_EDTYPE;
+  if (!sizes_ok(c.B, c.K, c.G, c.V) || !temp_ok(c.tp) || !temp_ok(c.tq)) return SVD_EINVAL;
+  if (rows && !pools_ok(c.np, c.nq, c.greedy)) return SVD_EINVAL;
+  if (((uintptr_t)c.workspace) % kAlign != 0) return SVD_EINVAL;
+  if (c.workspace_bytes < layout(c.B, c.K, c.G, c.V, c.np, c.nq).total) return SVD_EWORKSPACE;
+  const size_t es = c.dtype == SVD_F32 ? 4 : 2;
   // 16-byte loads need every row to start 16-byte aligned
-  const bool vec = ((size_t)V * es) % 16 == 0 && ((uintptr_t)p) % 16 == 0 &&
-                   ((uintptr_t)q) % 16 == 0;
-  if (dtype == SVD_BF16) {
-    return vec ? run<BF16, true>(p, q, drafts, B, K, G, V, tp, tq, seed, row_base, greedy,
-                                 selected, accept_len, next_token, scores, alpha, beta,
-                                 workspace, s)
-               : run<BF16, false>(p, q, drafts, B, K, G, V, tp, tq, seed, row_base, greedy,
-                                  selected, accept_len, next_token, scores, alpha, beta,
-                                  workspace, s);
-  }
-  return vec ? run<F32, true>(p, q, drafts, B, K, G, V, tp, tq, seed, row_base, greedy, selected,
-                              accept_len, next_token, scores, alpha, beta, workspace, s)
-             : run<F32, false>(p, q, drafts, B, K, G, V, tp, tq, seed, row_base, greedy,
-                               selected, accept_len, next_token, scores, alpha, beta, workspace,
-                               s);
+  const bool vec = ((size_t)c.V * es) % 16 == 0 && ((uintptr_t)c.p) % 16 == 0 &&
+                   ((uintptr_t)c.q) % 16 == 0;
+  if (c.dtype == SVD_BF16) return vec ? run<BF16, true>(c) : run<BF16, false>(c);
+  return vec ? run<F32, true>(c) : run<F32, false>(c);
+}
+
+Call make_call(const void *p, const void *q, const int32_t *drafts, svd_dtype_t dtype, int64_t B,
+               int32_t K, int32_t G, int32_t V, float tp, float tq, uint64_t seed,
+               uint64_t row_base, bool greedy, int32_t *selected, int32_t *accept_len,
+               int32_t *next_token, float *scores, float *alpha, float *beta, void *workspace,
+               size_t workspace_bytes, void *stream) {
+  Call c{};
+  c.p = p;
+  c.q = q;
+  c.drafts = drafts;
+  c.dtype = dtype;
+  c.B = B;
+  c.K = K;
+  c.G = G;
+  c.V = V;
+  c.tp = tp;
+  c.tq = tq;
+  c.seed = seed;
+  c.row_base = row_base;
+  c.greedy = greedy;
+  c.selected = selected;
+  c.accept_len = accept_len;
+  c.next_token = next_token;
+  c.scores = scores;
+  c.alpha = alpha;
+  c.beta = beta;
+  c.workspace = workspace;
+  c.workspace_bytes = workspace_bytes;
+  c.stream = stream;
+  return c;
 }
 
 }  // namespace
@@ -271,9 +347,9 @@ int svd_verify(const void *p_logits, const void *q_logits, const int32_t *draft,
                float temp_q, uint64_t seed, uint64_t row_base, int32_t *accept_len,
                int32_t *next_token, float *alpha, float *beta, void *workspace,
                size_t workspace_bytes, void *hip_stream) {
-  return dispatch(p_logits, q_logits, draft, dtype, B, 1, gamma, V, temp_p, temp_q, seed,
-                  row_base, false, nullptr, accept_len, next_token, nullptr, alpha, beta,
-                  workspace, workspace_bytes, hip_stream);
+  return dispatch(make_call(p_logits, q_logits, draft, dtype, B, 1, gamma, V, temp_p, temp_q,
+                            seed, row_base, false, nullptr, accept_len, next_token, nullptr,
+                            alpha, beta, workspace, workspace_bytes, hip_stream));
 }
 
 int svd_select_and_verify(const void *p_logits, const void *q_logits, const int32_t *drafts,
@@ -283,18 +359,18 @@ int svd_select_and_verify(const void *p_logits, const void *q_logits, const int3
                           float *scores, float *alpha, float *beta, void *workspace,
                           size_t workspace_bytes, void *hip_stream) {
   if (!selected) return SVD_EINVAL;
-  return dispatch(p_logits, q_logits, drafts, dtype, B, K, gamma, V, temp_p, temp_q, seed,
-                  row_base, false, selected, accept_len, next_token, scores, alpha, beta,
-                  workspace, workspace_bytes, hip_stream);
+  return dispatch(make_call(p_logits, q_logits, drafts, dtype, B, K, gamma, V, temp_p, temp_q,
+                            seed, row_base, false, selected, accept_len, next_token, scores,
+                            alpha, beta, workspace, workspace_bytes, hip_stream));
 }
 
 int svd_greedy_verify(const void *p_logits, const int32_t *draft, svd_dtype_t dtype, int64_t B,
                       int32_t gamma, int32_t V, float temp_p, uint64_t seed, uint64_t row_base,
                       int32_t *accept_len, int32_t *next_token, float *alpha, void *workspace,
                       size_t workspace_bytes, void *hip_stream) {
-  return dispatch(p_logits, nullptr, draft, dtype, B, 1, gamma, V, temp_p, temp_p, seed,
-                  row_base, true, nullptr, accept_len, next_token, nullptr, alpha, nullptr,
-                  workspace, workspace_bytes, hip_stream);
+  return dispatch(make_call(p_logits, nullptr, draft, dtype, B, 1, gamma, V, temp_p, temp_p,
+                            seed, row_base, true, nullptr, accept_len, next_token, nullptr, alpha,
+                            nullptr, workspace, workspace_bytes, hip_stream));
 }
 
 int svd_greedy_select_and_verify(const void *p_logits, const int32_t *drafts, svd_dtype_t dtype,
@@ -304,9 +380,36 @@ int svd_greedy_select_and_verify(const void *p_logits, const int32_t *drafts, sv
                                  float *alpha, void *workspace, size_t workspace_bytes,
                                  void *hip_stream) {
   if (!selected) return SVD_EINVAL;
-  return dispatch(p_logits, nullptr, drafts, dtype, B, K, gamma, V, temp_p, temp_p, seed,
-                  row_base, true, selected, accept_len, next_token, scores, alpha, nullptr,
-                  workspace, workspace_bytes, hip_stream);
+  return dispatch(make_call(p_logits, nullptr, drafts, dtype, B, K, gamma, V, temp_p, temp_p,
+                            seed, row_base, true, selected, accept_len, next_token, scores, alpha,
+                            nullptr, workspace, workspace_bytes, hip_stream));
+}
+
+size_t svd_rows_workspace_bytes(int64_t B, int32_t K, int32_t gamma, int32_t V,
+                                int64_t n_p_rows, int64_t n_q_rows) {
+  if (!sizes_ok(B, K, gamma, V) || !pools_ok(n_p_rows, n_q_rows, true)) return 0;
+  return layout(B, K, gamma, V, n_p_rows, n_q_rows).total;
+}
+
+int svd_select_and_verify_rows(svd_rule_t rule, const void *p_rows, int64_t n_p_rows,
+                               const int32_t *p_index, const void *q_rows, int64_t n_q_rows,
+                               const int32_t *q_index, const int32_t *drafts, svd_dtype_t dtype,
+                               int64_t B, int32_t K, int32_t gamma, int32_t V, float temp_p,
+                               float temp_q, uint64_t seed, uint64_t row_base, int32_t *selected,
+                               int32_t *accept_len, int32_t *next_token, float *scores,
+                               float *alpha, void *workspace, size_t workspace_bytes,
+                               void *hip_stream) {
+  if (rule != SVD_RULE_STANDARD && rule != SVD_RULE_GREEDY) return SVD_EINVAL;
+  if (!selected || !p_index) return SVD_EINVAL;
+  const bool greedy = rule == SVD_RULE_GREEDY;
+  Call c = make_call(p_rows, greedy ? nullptr : q_rows, drafts, dtype, B, K, gamma, V, temp_p,
+                     greedy ? temp_p : temp_q, seed, row_base, greedy, selected, accept_len,
+                     next_token, scores, alpha, nullptr, workspace, workspace_bytes, hip_stream);
+  c.p_index = p_index;
+  c.q_index = greedy ? nullptr : q_index;
+  c.np = n_p_rows;
+  c.nq = greedy ? 0 : n_q_rows;
+  return dispatch(c);
 }
 
 const char *svd_strerror(int status) {
