@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.svdo_select_and_verify.argtypes = [
             vp, vp, vp, ctypes.c_int, i64, i32, i32, i32, ctypes.c_float, ctypes.c_float,
             u64, u64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+        L.svdo_window_select_and_verify.restype = ctypes.c_int
+        L.svdo_window_select_and_verify.argtypes = [
+            ctypes.c_int, vp, vp, vp, vp, i32, ctypes.c_int, i64, i32, i32, i32, ctypes.c_float,
+            ctypes.c_float, u64, u64, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
         L.svdo_greedy_select_and_verify.restype = ctypes.c_int
         L.svdo_greedy_select_and_verify.argtypes = [
             vp, vp, ctypes.c_int, i64, i32, i32, i32, ctypes.c_float, u64, u64, vp, vp, vp, vp,
@@ -258,3 +262,50 @@ def select_and_verify_rows(p_pool, p_index, q_pool, q_index, drafts, temp_p=1.0,
     return select_and_verify(p, q, d, temp_p=temp_p, temp_q=temp_q, seed=seed,
                              row_base=row_base, force_k=force_k, force_L=force_L,
                              nthreads=nthreads)
+
+
+def window_select_and_verify(p_logits, q_logits, drafts, gamma_b=None, eos=-1, greedy=False,
+                             temp_p=1.0, temp_q=None, seed=0, row_base=0, force_k=None,
+                             force_L=None, nthreads=None) -> OracleResult:
+    """Ragged, EOS-aware windows: prefix b drafts gamma_b[b] positions of the padded
+    arrays (None: all gamma); with eos >= 0 a draft's usable positions end at its first
+    drafted EOS, and an accepted window ending in EOS draws nothing (next_token -2).
+    greedy: the greedy-acceptance rule (q_logits unused, may be None)."""
+    p, dt = _logits(p_logits)
+    B, K, G1, V = p.shape
+    G = G1 - 1
+    q = None
+    if not greedy:
+        q, dq = _logits(q_logits)
+        if dq != dt or q.shape != (B, K, G, V):
+            raise ValueError("q must be [B,K,gamma,V] of p's dtype")
+    d = np.ascontiguousarray(drafts, dtype=np.int32)
+    if d.shape != (B, K, G):
+        raise ValueError("drafts shape %s, expected %s" % (d.shape, (B, K, G)))
+    gb = None if gamma_b is None else np.ascontiguousarray(gamma_b, dtype=np.int32)
+    if gb is not None and gb.shape != (B,):
+        raise ValueError("gamma_b must be [B]")
+    if temp_q is None:
+        temp_q = temp_p
+    if nthreads is None:
+        nthreads = min(os.cpu_count() or 1, 16)
+    fk = None if force_k is None else np.ascontiguousarray(force_k, dtype=np.int32)
+    fl = None if force_L is None else np.ascontiguousarray(force_L, dtype=np.int32)
+    sel = np.empty(B, np.int32)
+    L = np.empty(B, np.int32)
+    tok = np.empty(B, np.int32)
+    scores = np.full((B, K), np.nan)
+    alpha = np.full((B, K, G), np.nan)
+    am = np.full((B, G), np.nan)
+    diag = (_Diag * B)()
+    rc = lib().svdo_window_select_and_verify(
+        int(bool(greedy)), _ptr(p), _ptr(q), _ptr(d), _ptr(gb), int(eos), dt, B, K, G, V,
+        float(temp_p), float(temp_q), seed & 0xFFFFFFFFFFFFFFFF, row_base & 0xFFFFFFFFFFFFFFFF,
+        _ptr(fk), _ptr(fl), _ptr(sel), _ptr(L), _ptr(tok), _ptr(scores), _ptr(alpha), _ptr(am),
+        ctypes.cast(diag, ctypes.c_void_p), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+    dg = np.frombuffer(diag, dtype=np.float64).reshape(B, 4) if B else np.zeros((0, 4))
+    return OracleResult(sel, L, tok, scores, alpha, None, alpha.copy(),
+                        np.full((B, K, G), np.nan), am, dg[:, 0].copy(), dg[:, 1].copy(),
+                        dg[:, 2].copy(), dg[:, 3].copy())

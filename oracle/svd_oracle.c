@@ -169,6 +169,8 @@ typedef struct {
   double *scores, *alpha, *beta, *px, *qx, *accept_margin;
   svdo_diag_t *diag;
   int greedy;  /* greedy acceptance: alpha = p(x), no drafter rows */
+  const int32_t *gamma_b;  /* per-prefix window (NULL: every window is gamma) */
+  int32_t eos;             /* end-of-sequence token, or -1 */
   int nthreads, tid;
   int status;
 } job_t;
@@ -194,15 +196,33 @@ static void mark_invalid(const job_t *J, int64_t b)
 
 /* One prefix, steps in the order the pages give them. */
 static int do_prefix(const job_t *J, int64_t b, double *P, double *Q, double *R, double *a_buf,
-                     double *s_buf)
+                     double *s_buf, int32_t *m_buf)
 {
   const int32_t K = J->K, G = J->gamma, V = J->V;
   const uint64_t row = J->row_base + (uint64_t)b;
   int valid = 1;
 
+  /* The window: draft k proposes positions j < n (n = gamma_b[b], or gamma);
+   * with an end-of-sequence token, a draft's usable positions stop at its
+   * first EOS, included (DiffuSpec section 3, "Accepted prefix length":
+   * decoding ends early at an accepted EOS).  m_k = that length. */
+  const int32_t n = J->gamma_b ? J->gamma_b[b] : G;
+  if (n < 1 || n > G) {
+    mark_invalid(J, b);
+    return 0;
+  }
+  for (int32_t k = 0; k < K; ++k) {
+    m_buf[k] = n;
+    for (int32_t j = 0; j < n && J->eos >= 0; ++j)
+      if (J->drafts[((size_t)b * K + k) * G + j] == J->eos) {
+        m_buf[k] = j + 1;
+        break;
+      }
+  }
+
   /* drafted tokens must index the vocabulary */
   for (int32_t k = 0; k < K; ++k)
-    for (int32_t j = 0; j < G; ++j) {
+    for (int32_t j = 0; j < m_buf[k]; ++j) {
       int32_t x = J->drafts[((size_t)b * K + k) * G + j];
       if (x < 0 || x >= V) valid = 0;
     }
@@ -212,7 +232,7 @@ static int do_prefix(const job_t *J, int64_t b, double *P, double *Q, double *R,
     /* greedy acceptance (SpecDiff-2 section 5.2 and appendix B.4): the test
      * compares the uniform with the verifier probability of the drafted
      * token, alpha = p(x); the drafter's probabilities are not used */
-    for (int32_t j = 0; j < G && valid; ++j) {
+    for (int32_t j = 0; j < m_buf[k] && valid; ++j) {
       if (!softmax_full(p_row(J, b, k, j), J->dtype, V, J->tp, P, NULL, NULL)) {
         valid = 0;
         break;
@@ -225,7 +245,7 @@ static int do_prefix(const job_t *J, int64_t b, double *P, double *Q, double *R,
     }
   }
   for (int32_t k = 0; k < K && valid && !J->greedy; ++k) {
-    for (int32_t j = 0; j < G && valid; ++j) {
+    for (int32_t j = 0; j < m_buf[k] && valid; ++j) {
       const void *pr = p_row(J, b, k, j), *qr = q_row(J, b, k, j);
       double mp, Sp, mq, Sq;
       if (!softmax_full(pr, J->dtype, V, J->tp, P, &mp, &Sp) ||
@@ -260,7 +280,7 @@ static int do_prefix(const job_t *J, int64_t b, double *P, double *Q, double *R,
   /* 4. expected accepted streak of every draft: sum_j prod_{i<=j} alpha_i */
   for (int32_t k = 0; k < K; ++k) {
     double prod = 1.0, S = 0.0;
-    for (int32_t j = 0; j < G; ++j) {
+    for (int32_t j = 0; j < m_buf[k]; ++j) {
       prod *= a_buf[(size_t)k * G + j];
       S += prod;
     }
@@ -281,21 +301,38 @@ static int do_prefix(const job_t *J, int64_t b, double *P, double *Q, double *R,
   }
 
   /* 6. left-to-right acceptance: accept position j iff u_j < alpha_{k*,j} */
-  int32_t L = G;
-  for (int32_t j = 0; j < G; ++j) {
+  const int32_t m = m_buf[ks];
+  int32_t L = m;
+  for (int32_t j = 0; j < m; ++j) {
     double u = svdo_uniform(J->seed, row, (uint64_t)j, PURPOSE_ACCEPT);
     double a = a_buf[(size_t)ks * G + j];
     if (J->accept_margin) J->accept_margin[(size_t)b * G + j] = fabs(u - a);
-    if (!(u < a) && L == G) L = j;
+    if (!(u < a) && L == m) L = j;
   }
   if (J->force_L && J->force_L[b] >= 0) {
-    if (J->force_L[b] > G) return -1;
+    if (J->force_L[b] > m) return -1;
     L = J->force_L[b];
   }
 
-  /* 7-8. residual draw at the first rejection, or bonus draw after gamma accepts */
+  /* an accepted EOS ends the commit: nothing is drawn */
+  if (L == m && J->eos >= 0 && J->drafts[((size_t)b * K + ks) * G + m - 1] == J->eos) {
+    J->selected[b] = ks;
+    J->accept_len[b] = L;
+    J->next_token[b] = -2;
+    if (J->diag) {
+      svdo_diag_t *d = &J->diag[b];
+      d->select_gap = (K > 1) ? s_buf[ks] - second : INFINITY;
+      d->emit_margin = INFINITY;
+      d->draw_z = 0.0;
+      d->draw_t = 0.0;
+    }
+    return 0;
+  }
+
+  /* 7-8. residual draw at the first rejection, or bonus draw (p row n) after
+   * the whole window is accepted */
   double Z, u;
-  if (L < G && J->greedy) {
+  if (L < m && J->greedy) {
     /* the rejected token zeroed out (SpecDiff-2 appendix B.4): the residual
      * max(0, p - q) with q the point mass at the drafted token */
     softmax_full(p_row(J, b, ks, L), J->dtype, V, J->tp, P, NULL, NULL);
@@ -303,18 +340,18 @@ static int do_prefix(const job_t *J, int64_t b, double *P, double *Q, double *R,
     Q[J->drafts[((size_t)b * K + ks) * G + L]] = 1.0;
     Z = svdo_draw_weights(P, Q, V, R);
     u = svdo_uniform(J->seed, row, (uint64_t)L, PURPOSE_RESIDUAL);
-  } else if (L < G) {
+  } else if (L < m) {
     softmax_full(p_row(J, b, ks, L), J->dtype, V, J->tp, P, NULL, NULL);
     softmax_full(q_row(J, b, ks, L), J->dtype, V, J->tq, Q, NULL, NULL);
     Z = svdo_draw_weights(P, Q, V, R);
     u = svdo_uniform(J->seed, row, (uint64_t)L, PURPOSE_RESIDUAL);
   } else {
-    if (!softmax_full(p_row(J, b, ks, G), J->dtype, V, J->tp, P, NULL, NULL)) {
+    if (!softmax_full(p_row(J, b, ks, n), J->dtype, V, J->tp, P, NULL, NULL)) {
       mark_invalid(J, b);
       return 0;
     }
     Z = svdo_draw_weights(P, NULL, V, R);
-    u = svdo_uniform(J->seed, row, (uint64_t)G, PURPOSE_BONUS);
+    u = svdo_uniform(J->seed, row, (uint64_t)n, PURPOSE_BONUS);
   }
   double t = u * Z, lo = 0.0, hi = 0.0;
   int32_t tok = svdo_inverse_cdf(R, V, t, &lo, &hi);
@@ -342,17 +379,19 @@ static void *worker(void *arg)
   double *R = (double *)malloc(sizeof(double) * (size_t)J->V);
   double *A = (double *)malloc(sizeof(double) * (size_t)J->K * (size_t)J->gamma);
   double *S = (double *)malloc(sizeof(double) * (size_t)J->K);
-  if (!P || !Q || !R || !A || !S) {
+  int32_t *M = (int32_t *)malloc(sizeof(int32_t) * (size_t)J->K);
+  if (!P || !Q || !R || !A || !S || !M) {
     J->status = -1;
   } else {
     for (int64_t b = J->tid; b < J->B; b += J->nthreads)
-      if (do_prefix(J, b, P, Q, R, A, S) != 0) J->status = -1;
+      if (do_prefix(J, b, P, Q, R, A, S, M) != 0) J->status = -1;
   }
   free(P);
   free(Q);
   free(R);
   free(A);
   free(S);
+  free(M);
   return NULL;
 }
 
@@ -430,6 +469,7 @@ int svdo_select_and_verify(const void *p_logits, const void *q_logits, const int
   base.qx = qx;
   base.accept_margin = accept_margin;
   base.diag = diag;
+  base.eos = -1;
   base.nthreads = nthreads;
   return run_jobs(&base);
 }
@@ -469,6 +509,53 @@ int svdo_greedy_select_and_verify(const void *p_logits, const int32_t *drafts, i
   base.accept_margin = accept_margin;
   base.diag = diag;
   base.greedy = 1;
+  base.eos = -1;
+  base.nthreads = nthreads;
+  return run_jobs(&base);
+}
+
+int svdo_window_select_and_verify(int greedy, const void *p_logits, const void *q_logits,
+                                  const int32_t *drafts, const int32_t *gamma_b, int32_t eos,
+                                  int dtype, int64_t B, int32_t K, int32_t gamma, int32_t V,
+                                  float temp_p, float temp_q, uint64_t seed, uint64_t row_base,
+                                  const int32_t *force_k, const int32_t *force_L,
+                                  int32_t *selected, int32_t *accept_len, int32_t *next_token,
+                                  double *scores, double *alpha, double *accept_margin,
+                                  svdo_diag_t *diag, int nthreads)
+{
+  if (!p_logits || (!q_logits && !greedy) || !drafts || !selected || !accept_len || !next_token)
+    return -1;
+  if (dtype != SVDO_F32 && dtype != SVDO_BF16) return -1;
+  if (B < 1 || K < 1 || gamma < 1 || V < 1 || eos >= V) return -1;
+  if (!(temp_p > 0.0f) || isinf(temp_p)) return -1;
+  if (!greedy && (!(temp_q > 0.0f) || isinf(temp_q))) return -1;
+
+  job_t base;
+  memset(&base, 0, sizeof base);
+  base.p = p_logits;
+  base.q = greedy ? NULL : q_logits;
+  base.drafts = drafts;
+  base.dtype = dtype;
+  base.B = B;
+  base.K = K;
+  base.gamma = gamma;
+  base.V = V;
+  base.tp = temp_p;
+  base.tq = greedy ? temp_p : temp_q;
+  base.seed = seed;
+  base.row_base = row_base;
+  base.force_k = force_k;
+  base.force_L = force_L;
+  base.selected = selected;
+  base.accept_len = accept_len;
+  base.next_token = next_token;
+  base.scores = scores;
+  base.alpha = alpha;
+  base.accept_margin = accept_margin;
+  base.diag = diag;
+  base.greedy = greedy != 0;
+  base.gamma_b = gamma_b;
+  base.eos = eos < 0 ? -1 : eos;
   base.nthreads = nthreads;
   return run_jobs(&base);
 }

@@ -110,6 +110,31 @@ int svdo_greedy_select_and_verify(const void *p_logits, const int32_t *drafts, i
                                   int32_t *next_token, double *scores, double *alpha,
                                   double *accept_margin, svdo_diag_t *diag, int nthreads);
 
+/*
+ * Ragged, EOS-aware windows (DiffuSpec section 3, "Accepted prefix length":
+ * the committed tokens are the accepted prefix, and decoding ends early at an
+ * accepted EOS; section 4.3: the draft length k_t changes from step to step).
+ * Prefix b drafts n = gamma_b[b] positions (1 <= n <= gamma; NULL: gamma) in
+ * arrays padded to gamma.  With eos >= 0, draft k's usable length m_k stops at
+ * its first drafted EOS, included (else m_k = n).  Then
+ *   score      S_k = sum_{j < m_k} prod_{i <= j} alpha_{k,i};
+ *   acceptance over j < m_{k*}: L = the first rejection, or m_{k*};
+ *   an accepted window ending in EOS commits L tokens and draws nothing
+ *   (next_token = -2); otherwise the residual draw at L < m_{k*}, or the bonus
+ *   draw from p row n with uniform position n.
+ * Rows past m_k are never read and their alpha is not written.  An n outside
+ * [1, gamma] invalidates the prefix.  greedy: the greedy-acceptance rule (no
+ * q_logits).  Returns 0, or -1 on bad arguments.
+ */
+int svdo_window_select_and_verify(int greedy, const void *p_logits, const void *q_logits,
+                                  const int32_t *drafts, const int32_t *gamma_b, int32_t eos,
+                                  int dtype, int64_t B, int32_t K, int32_t gamma, int32_t V,
+                                  float temp_p, float temp_q, uint64_t seed, uint64_t row_base,
+                                  const int32_t *force_k, const int32_t *force_L,
+                                  int32_t *selected, int32_t *accept_len, int32_t *next_token,
+                                  double *scores, double *alpha, double *accept_margin,
+                                  svdo_diag_t *diag, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -59,8 +59,15 @@ def _slice(a, b):
     return np.ascontiguousarray(a[b:b + 1])
 
 
-def _run(orc, greedy, p, q, d, temp_p, temp_q, seed, row_base, want_beta=False, **force):
-    """One oracle call in the standard or the greedy-acceptance mode."""
+def _run(orc, greedy, p, q, d, temp_p, temp_q, seed, row_base, want_beta=False, window=None,
+         **force):
+    """One oracle call in the standard or the greedy-acceptance mode; window: dict of
+    gamma_b (aligned with p) and eos for ragged, EOS-aware windows."""
+    if window is not None:
+        return orc.window_select_and_verify(p, q, d, gamma_b=window.get("gamma_b"),
+                                            eos=window.get("eos", -1), greedy=greedy,
+                                            temp_p=temp_p, temp_q=temp_q, seed=seed,
+                                            row_base=row_base, **force)
     if greedy:
         return orc.greedy_select_and_verify(p, d, temp_p=temp_p, seed=seed, row_base=row_base,
                                             **force)
@@ -69,10 +76,12 @@ def _run(orc, greedy, p, q, d, temp_p, temp_q, seed, row_base, want_beta=False, 
 
 
 def compare(orc, host_p, host_q, host_d, gpu, temp_p, temp_q, seed, row_base=0,
-            prefixes=None, rep: ParityReport | None = None, greedy=False) -> ParityReport:
+            prefixes=None, rep: ParityReport | None = None, greedy=False,
+            window=None) -> ParityReport:
     """host_p/host_q/host_d: host arrays of the prefixes in `prefixes` (in that order);
     gpu: dict of host numpy outputs of the full batch (selected may be None for svd_verify).
     greedy: compare with the oracle's greedy-acceptance mode (host_q is then unused).
+    window: ragged, EOS-aware windows: dict(gamma_b aligned with the host arrays, eos).
     """
     rep = rep or ParityReport()
     B, K, G1, V = host_p.shape
@@ -83,7 +92,7 @@ def compare(orc, host_p, host_q, host_d, gpu, temp_p, temp_q, seed, row_base=0,
     # uniform rows follow the batch index of each prefix
     rows = np.array(idx, dtype=np.int64)
     res = _oracle_rows(orc, host_p, host_q, host_d, temp_p, temp_q, seed, row_base, rows,
-                       want_beta, greedy)
+                       want_beta, greedy, window)
     sel_tol = ALPHA_TOL * G
     for i, b in enumerate(idx):
         rep.prefixes += 1
@@ -115,6 +124,7 @@ def compare(orc, host_p, host_q, host_d, gpu, temp_p, temp_q, seed, row_base=0,
         pb = _slice(host_p, i)
         qb = None if greedy else _slice(host_q, i)
         db = _slice(host_d, i)
+        wb = _window_slice(window, i)
         row = row_base + b
         cur = res
         ci = i
@@ -126,7 +136,7 @@ def compare(orc, host_p, host_q, host_d, gpu, temp_p, temp_q, seed, row_base=0,
             if g_sel != o_sel:
                 if res.select_gap[i] < sel_tol:
                     rep.flagged["select"] += 1
-                    cur = _run(orc, greedy, pb, qb, db, temp_p, temp_q, seed, row,
+                    cur = _run(orc, greedy, pb, qb, db, temp_p, temp_q, seed, row, window=wb,
                                force_k=np.array([g_sel], np.int32))
                     ci = 0
                 else:
@@ -141,7 +151,7 @@ def compare(orc, host_p, host_q, host_d, gpu, temp_p, temp_q, seed, row_base=0,
             j = min(g_L, o_L)
             if 0 <= j < G and m[j] < ACCEPT_EPS:
                 rep.flagged["accept"] += 1
-                cur = _run(orc, greedy, pb, qb, db, temp_p, temp_q, seed, row,
+                cur = _run(orc, greedy, pb, qb, db, temp_p, temp_q, seed, row, window=wb,
                            force_k=np.array([g_sel], np.int32), force_L=np.array([g_L], np.int32))
                 ci = 0
             else:
@@ -163,15 +173,24 @@ def compare(orc, host_p, host_q, host_d, gpu, temp_p, temp_q, seed, row_base=0,
     return rep
 
 
+def _window_slice(window, i):
+    if window is None:
+        return None
+    gb = window.get("gamma_b")
+    return dict(eos=window.get("eos", -1),
+                gamma_b=None if gb is None else np.ascontiguousarray(gb[i:i + 1]))
+
+
 def _oracle_rows(orc, host_p, host_q, host_d, temp_p, temp_q, seed, row_base, rows, want_beta,
-                 greedy=False):
+                 greedy=False, window=None):
     """Oracle over a host batch whose prefix i sits at batch row rows[i]."""
     rows = np.asarray(rows)
     if len(rows) and np.all(np.diff(rows) == 1):
         return _run(orc, greedy, host_p, host_q, host_d, temp_p, temp_q, seed,
-                    row_base + int(rows[0]), want_beta)
+                    row_base + int(rows[0]), want_beta, window)
     parts = [_run(orc, greedy, _slice(host_p, i), None if greedy else _slice(host_q, i),
-                  _slice(host_d, i), temp_p, temp_q, seed, row_base + int(r), want_beta)
+                  _slice(host_d, i), temp_p, temp_q, seed, row_base + int(r), want_beta,
+                  _window_slice(window, i))
              for i, r in enumerate(rows)]
     out = parts[0]
     for f in out.__dataclass_fields__:
