@@ -183,6 +183,9 @@ def main():
     ap.add_argument("--mode", choices=("standard", "greedy"), default="standard",
                     help="acceptance rule: standard (alpha = min(1, p/q)) or greedy (alpha = p(x), "
                          "no drafter rows)")
+    ap.add_argument("--early-exit", action="store_true",
+                    help="K = 1 workloads: stream each prefix's positions only up to its first "
+                         "rejection (svd_verify_window); reported apart from the full-streaming line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (for counter calibration)")
@@ -231,9 +234,18 @@ def main():
     code = svd.SVD_BF16 if cfg.dtype == "bf16" else svd.SVD_F32
 
     greedy = args.mode == "greedy"
+    early = args.early_exit
+    if early and (pooled or K != 1):
+        sys.exit("--early-exit needs a dense workload with K = 1")
+    alpha_out = torch.empty((B, K, G), dtype=torch.float32, device=dev) if early else None
 
     def step():
-        if pooled:
+        if early:
+            rc = svd.svd_verify_window(
+                svd.SVD_RULE_GREEDY if greedy else svd.SVD_RULE_STANDARD, d["p"], d["q"],
+                d["drafts"], None, -1, 1, code, B, K, G, V, cfg.temp, cfg.temp, cfg.seed, 0, sel,
+                L, tok, None, alpha_out, ws, ws.numel(), stream.cuda_stream)
+        elif pooled:
             rc = svd.svd_select_and_verify_rows(
                 svd.SVD_RULE_GREEDY if greedy else svd.SVD_RULE_STANDARD, d["p_pool"], NP,
                 d["p_index"], d["q_pool"], NQ, d["q_index"], d["drafts"], code, B, K, G, V,
@@ -284,7 +296,15 @@ def main():
     positions = B * K * G
     L_host = L.cpu().numpy()
     bonus_rows = int((L_host == G).sum())
-    if pooled:
+    if early:
+        # positions actually streamed (alpha is NaN at the others), per rowstats launch
+        streamed = int((~torch.isnan(alpha_out)).sum().item())
+        lpd = max(launches[svd.KERNELS.index(dom)] // max(args.steps, 1), 1)
+        units = streamed / lpd
+        unit_bytes = bytes_per_row_pair(V, es, args.mode)
+        rows = 1 if greedy else 2
+        alg_bytes_step = streamed * (rows * V * es + 4) + bonus_rows * V * es + B * 12
+    elif pooled:
         units = pool_rows_read(d, args.mode)
         unit_bytes = V * es + POOL_STAT_BYTES
         # the pool rows read once, drafts and index tables, bonus rows drawn, outputs
@@ -299,7 +319,7 @@ def main():
     ms_dom = ms_kernels[di] / max(launches[di], 1)
     launch_bytes = unit_bytes * units
     achieved = launch_bytes / (ms_dom * 1e-3) / 1e9
-    traffic = measured_traffic(dom, cfg.name, args.mode)
+    traffic = None if early else measured_traffic(dom, cfg.name, args.mode)
 
     result = {
         "metric": METRIC,
@@ -314,7 +334,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "mode": args.mode, "B": B, "K": K, "gamma": G, "V": V,
+        "config": {"workload": cfg.name, "mode": args.mode, "early_exit": early,
+                   "B": B, "K": K, "gamma": G, "V": V,
                    "logits": cfg.dtype, "temperature": cfg.temp, "global_batch": B,
                    "parallelism": "single GPU"},
         "achieved_hbm_gbps": alg_bytes_step / (ms_step * 1e-3) / 1e9,

@@ -198,6 +198,39 @@ int svd_select_and_verify_rows(svd_rule_t rule, const void *p_rows, int64_t n_p_
                                float *alpha, void *workspace, size_t workspace_bytes,
                                void *hip_stream);
 
+/*
+ * Ragged, EOS-aware windows (DiffuSpec section 3, "Accepted prefix length":
+ * the committed tokens are the accepted prefix, and decoding ends early when
+ * an accepted token is EOS; section 4.3: the draft length k_t is set per step
+ * by a controller, so it differs between sequences of a batch).
+ *
+ * Arrays are laid out as for svd_select_and_verify, padded to gamma.  Prefix b
+ * drafts n_b = gamma_b[b] positions (gamma_b nullable: every n_b = gamma), and
+ * with eos >= 0 draft k's usable positions stop at its first drafted EOS,
+ * included: m_k = that length, or n_b.  Positions past m_k are not read.
+ *   scores     S_k = sum_{j < m_k} prod_{i <= j} alpha_{k,i};
+ *   acceptance over j < m_{k*}: L = the first rejection, or m_{k*};
+ *   a fully accepted window that ends in EOS commits L tokens and draws
+ *   nothing: next_token = -2;
+ *   otherwise the residual draw at L < m_{k*}, or the bonus draw from p row n_b
+ *   (uniform position n_b).
+ * rule: SVD_RULE_STANDARD or SVD_RULE_GREEDY (q_logits may then be NULL).
+ * alpha (nullable) is NaN at positions not streamed.
+ * early_exit != 0 (K = 1 only, scores NULL): positions are streamed in chunks
+ * and a prefix stops being streamed after the chunk that holds its first
+ * rejection, which skips most rows when acceptance is low; data errors in rows
+ * that are not streamed are then not detected.
+ * Errors: SVD_EINVAL also for eos >= V, early_exit with K != 1 or a non-NULL
+ * scores; an n_b outside [1, gamma] is a data error of prefix b (-1 outputs).
+ * Workspace: svd_workspace_bytes(B, K, gamma, V).
+ */
+int svd_verify_window(svd_rule_t rule, const void *p_logits, const void *q_logits,
+                      const int32_t *drafts, const int32_t *gamma_b, int32_t eos,
+                      int32_t early_exit, svd_dtype_t dtype, int64_t B, int32_t K, int32_t gamma,
+                      int32_t V, float temp_p, float temp_q, uint64_t seed, uint64_t row_base,
+                      int32_t *selected, int32_t *accept_len, int32_t *next_token, float *scores,
+                      float *alpha, void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* Static text for a status code. */
 const char *svd_strerror(int status);
 

@@ -8,10 +8,10 @@ Raw entry points (same names and argument order as the C ABI; pointer
 arguments take an int address or a tensor):
     svd_workspace_bytes, svd_verify, svd_select_and_verify, svd_greedy_verify,
     svd_greedy_select_and_verify, svd_rows_workspace_bytes, svd_select_and_verify_rows,
-    svd_strerror, svd_profile_enable, svd_profile_read
+    svd_verify_window, svd_strerror, svd_profile_enable, svd_profile_read
 Tensor conveniences that allocate the outputs and the workspace with torch:
     verify, select_and_verify, greedy_verify, greedy_select_and_verify,
-    select_and_verify_rows, workspace_bytes
+    select_and_verify_rows, verify_window, workspace_bytes
 
 Importing fails with ImportError when ``libsvd.so`` has not been built; there
 is no fallback path.
@@ -33,8 +33,8 @@ SVD_RULE_STANDARD, SVD_RULE_GREEDY = 0, 1
 
 C_EXPORTS = ("svd_workspace_bytes", "svd_verify", "svd_select_and_verify", "svd_greedy_verify",
              "svd_greedy_select_and_verify", "svd_rows_workspace_bytes",
-             "svd_select_and_verify_rows", "svd_strerror", "svd_profile_enable",
-             "svd_profile_read")
+             "svd_select_and_verify_rows", "svd_verify_window", "svd_strerror",
+             "svd_profile_enable", "svd_profile_read")
 
 
 class SvdError(RuntimeError):
@@ -72,6 +72,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.svd_select_and_verify_rows.argtypes = [ctypes.c_int, vp, i64, vp, vp, i64, vp, vp,
                                              ctypes.c_int, i64, i32, i32, i32, f32, f32, u64, u64,
                                              vp, vp, vp, vp, vp, vp, sz, vp]
+    L.svd_verify_window.restype = ctypes.c_int
+    L.svd_verify_window.argtypes = [ctypes.c_int, vp, vp, vp, vp, i32, i32, ctypes.c_int, i64, i32,
+                                    i32, i32, f32, f32, u64, u64, vp, vp, vp, vp, vp, vp, sz, vp]
     L.svd_strerror.restype = ctypes.c_char_p
     L.svd_strerror.argtypes = [ctypes.c_int]
     L.svd_profile_enable.restype = ctypes.c_int
@@ -153,6 +156,17 @@ def svd_select_and_verify_rows(rule, p_rows, n_p_rows, p_index, q_rows, n_q_rows
         float(temp_p), float(temp_q), int(seed) & _M64, int(row_base) & _M64, _addr(selected),
         _addr(accept_len), _addr(next_token), _addr(scores), _addr(alpha), _addr(workspace),
         int(workspace_bytes), _addr(hip_stream)))
+
+
+def svd_verify_window(rule, p_logits, q_logits, drafts, gamma_b, eos, early_exit, dtype, B, K,
+                      gamma, V, temp_p, temp_q, seed, row_base, selected, accept_len, next_token,
+                      scores, alpha, workspace, workspace_bytes, hip_stream) -> int:
+    return int(_lib.svd_verify_window(
+        int(rule), _addr(p_logits), _addr(q_logits), _addr(drafts), _addr(gamma_b), int(eos),
+        int(early_exit), int(dtype), int(B), int(K), int(gamma), int(V), float(temp_p),
+        float(temp_q), int(seed) & _M64, int(row_base) & _M64, _addr(selected), _addr(accept_len),
+        _addr(next_token), _addr(scores), _addr(alpha), _addr(workspace), int(workspace_bytes),
+        _addr(hip_stream)))
 
 
 def svd_strerror(status: int) -> str:
@@ -392,4 +406,44 @@ def select_and_verify_rows(p_pool, p_index, q_pool, q_index, drafts, rule="stand
         out["next_token"], out["scores"], out["alpha"], workspace, workspace.numel(), st)
     if rc != SVD_OK:
         raise SvdError(rc, "svd_select_and_verify_rows")
+    return out
+
+
+def verify_window(p, q, drafts, gamma_b=None, eos=-1, rule="standard", early_exit=False,
+                  temp_p=1.0, temp_q=None, seed=0, row_base=0, want_alpha=False,
+                  want_scores=False, workspace=None, stream=None):
+    """Ragged, EOS-aware windows: p [B,K,gamma+1,V], q [B,K,gamma,V] (None for
+    rule="greedy"), drafts [B,K,gamma] int32, gamma_b [B] int32 or None, eos a token or -1.
+    early_exit (K = 1): stream positions only up to each prefix's first rejection."""
+    import torch
+    greedy = rule == "greedy"
+    if rule not in ("standard", "greedy"):
+        raise ValueError("rule must be 'standard' or 'greedy'")
+    dev = p.device
+    tens = [(p, "p"), (drafts, "drafts")] + ([] if greedy else [(q, "q")])
+    if gamma_b is not None:
+        tens.append((gamma_b, "gamma_b"))
+    for t, n in tens:
+        _check(t, n, dev)
+    B, K, G1, V = p.shape
+    G = G1 - 1
+    if tuple(drafts.shape) != (B, K, G) or (gamma_b is not None and tuple(gamma_b.shape) != (B,)):
+        raise ValueError("drafts must be [B,K,gamma] and gamma_b [B]")
+    out = {
+        "selected": torch.empty(B, dtype=torch.int32, device=dev),
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+        "scores": torch.empty((B, K), dtype=torch.float32, device=dev) if want_scores else None,
+        "alpha": torch.empty((B, K, G), dtype=torch.float32, device=dev) if want_alpha else None,
+    }
+    ws = alloc_workspace(B, K, G, V, dev) if workspace is None else workspace
+    st = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    temp_q = temp_p if temp_q is None else temp_q
+    rc = svd_verify_window(SVD_RULE_GREEDY if greedy else SVD_RULE_STANDARD, p,
+                           None if greedy else q, drafts, gamma_b, eos, int(bool(early_exit)),
+                           _dtype_code(p), B, K, G, V, temp_p, temp_q, seed, row_base,
+                           out["selected"], out["accept_len"], out["next_token"], out["scores"],
+                           out["alpha"], ws, ws.numel(), st)
+    if rc != SVD_OK:
+        raise SvdError(rc, "svd_verify_window")
     return out

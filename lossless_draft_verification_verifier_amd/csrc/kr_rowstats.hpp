@@ -161,14 +161,28 @@ __device__ __forceinline__ void rowstats_item(const typename E::elem *__restrict
   }
 }
 
+// Workgroup w takes position j = j0 + w % jn of draft (b, k) = w / jn (the
+// whole batch: j0 = 0, jn = gamma).  Ragged or EOS-aware windows: mlen[b*K+k]
+// is the draft's usable length and later positions are skipped; positions
+// streamed in chunks: alive[b*K+k] == 0 skips a draft already rejected.  A
+// skipped position's alpha output is NaN.
 // Two 1024-thread workgroups per CU (8 waves per SIMD) need at most 64 VGPRs.
 template <typename E, bool kVec, bool kGreedy>
 __global__ __launch_bounds__(kRowBlock) __attribute__((amdgpu_waves_per_eu(8))) void kr_rowstats(
     const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
     const int32_t *__restrict__ drafts, int gamma, int V, float cp, float cq,
-    RowStats *__restrict__ stats, float *__restrict__ alpha_ws, float *__restrict__ alpha_out) {
-  rowstats_item<E, kVec, kRowBlock, kRowUnroll, kGreedy>(p, q, drafts, gamma, V, cp, cq,
-                                                         blockIdx.x, stats, alpha_ws, alpha_out);
+    RowStats *__restrict__ stats, float *__restrict__ alpha_ws, float *__restrict__ alpha_out,
+    const int32_t *__restrict__ mlen, const uint32_t *__restrict__ alive, int j0, int jn) {
+  const int64_t bk = blockIdx.x / jn;
+  const int j = j0 + (int)(blockIdx.x - bk * jn);
+  if (j >= gamma) return;
+  const int64_t rp = bk * gamma + j;
+  if ((mlen && j >= mlen[bk]) || (alive && !alive[bk])) {
+    if (alpha_out && threadIdx.x == 0) alpha_out[rp] = __builtin_nanf("");
+    return;
+  }
+  rowstats_item<E, kVec, kRowBlock, kRowUnroll, kGreedy>(p, q, drafts, gamma, V, cp, cq, rp, stats,
+                                                         alpha_ws, alpha_out);
 }
 
 }  // namespace svd

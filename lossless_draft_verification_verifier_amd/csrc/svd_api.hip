@@ -23,7 +23,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-  size_t stats, alpha, desc, segs, uncs, mass, pstat, flags, total;
+  size_t stats, alpha, desc, segs, uncs, mass, mlen, alive, pstat, flags, total;
   int nseg;
 };
 
@@ -55,6 +55,10 @@ Layout layout(int64_t B, int32_t K, int32_t G, int32_t V, int64_t np = 0, int64_
   off = align_up(off + (size_t)B * L.nseg * kUncCap * sizeof(DrawUnc));
   L.mass = off;
   off = align_up(off + (size_t)B * L.nseg * sizeof(DrawMass));
+  L.mlen = off;
+  off = align_up(off + (size_t)B * K * sizeof(int32_t));
+  L.alive = off;
+  off = align_up(off + (size_t)B * sizeof(uint32_t));
   L.pstat = off;
   off = align_up(off + (size_t)(np + nq) * sizeof(PoolStat));
   L.flags = off;
@@ -136,6 +140,11 @@ struct Batch {
   int64_t np, nq;
   PoolStat *pstat;
   uint32_t *flags;
+  bool windowed, early;  // ragged / EOS-aware windows; K == 1 streamed up to the first rejection
+  const int32_t *gamma_b;
+  int eos;
+  int32_t *mlen;
+  uint32_t *alive;
   int32_t *selected, *accept_len, *next_token;
   float *scores, *alpha, *beta;
   RowStats *stats;
@@ -152,6 +161,17 @@ struct Batch {
     if (launch(__VA_ARGS__) != hipSuccess) return SVD_EHIP;         \
     (tm).end(rec_, (kid), (stream));                                \
   } while (0)
+
+// Positions per chunk when one draft per prefix is streamed up to its first
+// rejection: enough workgroups per launch to fill the GPU about once.
+#ifndef SVD_EARLY_CHUNK
+#define SVD_EARLY_CHUNK 0
+#endif
+int early_chunk(int64_t B, int G) {
+  if (SVD_EARLY_CHUNK > 0) return std::min(SVD_EARLY_CHUNK, G);
+  const int64_t want = (512 + B - 1) / B;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, G));
+}
 
 // row statistics and alpha (and the optional overlap mass) of a batch
 template <typename E, bool kVec>
@@ -178,12 +198,44 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
                  a.cq, (const PoolStat *)a.pstat, a.stats, a.alpha_ws, a.alpha);
     return SVD_OK;
   }
-  if (a.greedy)
-    SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, true>, dim3(rp), dim3(kRowBlock), s,
-               a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, a.stats, a.alpha_ws, a.alpha);
-  else
-    SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, false>, dim3(rp), dim3(kRowBlock),
-               s, a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, a.stats, a.alpha_ws, a.alpha);
+  const int32_t *mlen = nullptr;
+  if (a.windowed) {
+    const int64_t bk = a.B * a.K;
+    SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_window, dim3((unsigned)((bk + kBlock - 1) / kBlock)),
+               dim3(kBlock), s, a.drafts, a.gamma_b, a.eos, bk, a.K, a.G, a.mlen);
+    mlen = a.mlen;
+  }
+  // the positions [j0, j0 + jn) of every draft
+  auto stream_rows = [&](int j0, int jn, const uint32_t *alive) -> int {
+    const dim3 grid((unsigned)(a.B * a.K * jn));
+    if (a.greedy)
+      SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, true>, grid, dim3(kRowBlock), s,
+                 a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, a.stats, a.alpha_ws, a.alpha, mlen,
+                 alive, j0, jn);
+    else
+      SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, false>, grid, dim3(kRowBlock), s,
+                 a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, a.stats, a.alpha_ws, a.alpha, mlen,
+                 alive, j0, jn);
+    return SVD_OK;
+  };
+  if (!a.early) {
+    const int rc = stream_rows(0, a.G, nullptr);
+    if (rc != SVD_OK) return rc;
+  } else {
+    // one draft per prefix, positions in chunks of J; a draft leaves the
+    // stream after the chunk holding its first rejection
+    const int J = early_chunk(a.B, a.G);
+    const unsigned gb = (unsigned)((a.B + kBlock - 1) / kBlock);
+    SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_fill_u32, dim3(gb), dim3(kBlock), s, a.alive, a.B, 1u);
+    for (int j0 = 0; j0 < a.G; j0 += J) {
+      const int rc = stream_rows(j0, std::min(J, a.G - j0), a.alive);
+      if (rc != SVD_OK) return rc;
+      if (j0 + J < a.G)
+        SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_advance, dim3(gb), dim3(kBlock), s,
+                   (const float *)a.alpha_ws, (const int32_t *)a.mlen, a.B, a.G, j0, J, a.seed,
+                   a.row_base, a.alive);
+    }
+  }
   if (a.beta)
     SVD_LAUNCH(tm, SVD_KERNEL_BETA, s, kr_beta<E, kVec>, dim3(rp), dim3(kBlock), s, a.p, a.q, a.G,
                a.V, a.cp, a.cq, (const RowStats *)a.stats, a.beta);
@@ -196,8 +248,11 @@ int enqueue_draw(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   const unsigned nb = (unsigned)a.B;
   const unsigned nbs = (unsigned)(a.B * a.nseg);
   SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_select, dim3(nb), dim3(64), s,
-             (const float *)a.alpha_ws, a.drafts, (int)a.greedy, a.ix.p, a.np, a.K, a.G, a.seed,
-             a.row_base, a.selected, a.accept_len, a.next_token, a.scores, a.desc);
+             (const float *)a.alpha_ws, a.drafts, (int)a.greedy, a.ix.p, a.np,
+             Window{a.windowed ? (const int32_t *)a.mlen : nullptr, a.gamma_b, a.eos,
+                    (int)a.early},
+             a.K, a.G, a.seed, a.row_base, a.selected, a.accept_len, a.next_token, a.scores,
+             a.desc);
   SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PASS, s, kr_draw_pass<E, kVec>, dim3(nbs), dim3(kBlock), s,
              a.p, a.q, a.ix, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
              (const DrawDesc *)a.desc, a.segs, a.uncs);
@@ -224,6 +279,9 @@ struct Call {
   bool greedy;
   const int32_t *p_index, *q_index;  // shared rows (null: dense layout)
   int64_t np, nq;
+  bool windowed, early;  // ragged / EOS-aware windows; stream up to the first rejection
+  const int32_t *gamma_b;
+  int32_t eos;
   int32_t *selected, *accept_len, *next_token;
   float *scores, *alpha, *beta;
   void *workspace;
@@ -256,6 +314,12 @@ int run(const Call &c) {
   a.ix = RowIndex{c.p_index, c.q_index};
   a.np = c.np;
   a.nq = c.nq;
+  a.windowed = c.windowed;
+  a.early = c.early;
+  a.gamma_b = c.gamma_b;
+  a.eos = c.windowed ? c.eos : -1;
+  a.mlen = reinterpret_cast<int32_t *>(ws + Lo.mlen);
+  a.alive = reinterpret_cast<uint32_t *>(ws + Lo.alive);
   a.pstat = reinterpret_cast<PoolStat *>(ws + Lo.pstat);
   a.flags = reinterpret_cast<uint32_t *>(ws + Lo.flags);
   a.selected = c.selected;
@@ -292,6 +356,8 @@ int dispatch(const Call &c) {
   if (c.dtype != SVD_F32 && c.dtype != SVD_BF16) return SVD_EDTYPE;
   if (!sizes_ok(c.B, c.K, c.G, c.V) || !temp_ok(c.tp) || !temp_ok(c.tq)) return SVD_EINVAL;
   if (rows && !pools_ok(c.np, c.nq, c.greedy)) return SVD_EINVAL;
+  if (c.windowed && (rows || c.beta || c.eos >= c.V)) return SVD_EINVAL;
+  if (c.early && (!c.windowed || c.K != 1 || c.scores)) return SVD_EINVAL;
   if (((uintptr_t)c.workspace) % kAlign != 0) return SVD_EINVAL;
   if (c.workspace_bytes < layout(c.B, c.K, c.G, c.V, c.np, c.nq).total) return SVD_EWORKSPACE;
   const size_t es = c.dtype == SVD_F32 ? 4 : 2;
@@ -330,6 +396,7 @@ Call make_call(const void *p, const void *q, const int32_t *drafts, svd_dtype_t 
   c.workspace = workspace;
   c.workspace_bytes = workspace_bytes;
   c.stream = stream;
+  c.eos = -1;
   return c;
 }
 
@@ -409,6 +476,25 @@ int svd_select_and_verify_rows(svd_rule_t rule, const void *p_rows, int64_t n_p_
   c.q_index = greedy ? nullptr : q_index;
   c.np = n_p_rows;
   c.nq = greedy ? 0 : n_q_rows;
+  return dispatch(c);
+}
+
+int svd_verify_window(svd_rule_t rule, const void *p_logits, const void *q_logits,
+                      const int32_t *drafts, const int32_t *gamma_b, int32_t eos,
+                      int32_t early_exit, svd_dtype_t dtype, int64_t B, int32_t K, int32_t gamma,
+                      int32_t V, float temp_p, float temp_q, uint64_t seed, uint64_t row_base,
+                      int32_t *selected, int32_t *accept_len, int32_t *next_token, float *scores,
+                      float *alpha, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  if (rule != SVD_RULE_STANDARD && rule != SVD_RULE_GREEDY) return SVD_EINVAL;
+  if (!selected) return SVD_EINVAL;
+  const bool greedy = rule == SVD_RULE_GREEDY;
+  Call c = make_call(p_logits, greedy ? nullptr : q_logits, drafts, dtype, B, K, gamma, V, temp_p,
+                     greedy ? temp_p : temp_q, seed, row_base, greedy, selected, accept_len,
+                     next_token, scores, alpha, nullptr, workspace, workspace_bytes, hip_stream);
+  c.windowed = true;
+  c.early = early_exit != 0;
+  c.gamma_b = gamma_b;
+  c.eos = eos < 0 ? -1 : eos;
   return dispatch(c);
 }
 

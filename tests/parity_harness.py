@@ -106,7 +106,12 @@ def compare(orc, host_p, host_q, host_d, gpu, temp_p, temp_q, seed, row_base=0,
                 rep.failures.append((b, "invalid prefix not reported", (g_sel, g_L, g_tok)))
             continue
         if gpu.get("alpha") is not None:
-            e = float(np.max(np.abs(gpu["alpha"][b].astype(np.float64) - res.alpha[i])))
+            ga, oa = gpu["alpha"][b].astype(np.float64), res.alpha[i]
+            # positions outside a window are NaN on both sides
+            if not np.array_equal(np.isnan(ga), np.isnan(oa)):
+                rep.failures.append((b, "alpha NaN pattern", (ga, oa)))
+            d = np.abs(ga - oa)[~np.isnan(oa)]
+            e = float(d.max()) if d.size else 0.0
             rep.max_alpha_err = max(rep.max_alpha_err, e)
             if not e <= ALPHA_TOL:
                 rep.failures.append((b, "alpha", e))
