@@ -309,3 +309,49 @@ def window_select_and_verify(p_logits, q_logits, drafts, gamma_b=None, eos=-1, g
     return OracleResult(sel, L, tok, scores, alpha, None, alpha.copy(),
                         np.full((B, K, G), np.nan), am, dg[:, 0].copy(), dg[:, 1].copy(),
                         dg[:, 2].copy(), dg[:, 3].copy())
+
+
+def cps_lattice(q_logits, temp_q=1.0, tau=0.8, m_max=15, eos=-1) -> dict:
+    """The pruned candidate lattice of every drafter row: q_logits [B, G, V]."""
+    q, dt = _logits(q_logits)
+    B, G, V = q.shape
+    cand = np.empty((B, G, m_max), np.int32)
+    logp = np.empty((B, G, m_max), np.float64)
+    n = np.empty((B, G), np.int32)
+    ln = np.empty(B, np.int32)
+    cm = np.empty((B, G), np.float64)
+    L = lib()
+    L.svdo_cps_lattice.restype = ctypes.c_int
+    L.svdo_cps_lattice.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_float, ctypes.c_double,
+                                   ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 5
+    rc = L.svdo_cps_lattice(_ptr(q), dt, B, G, V, float(temp_q), float(tau), int(m_max), int(eos),
+                            _ptr(cand), _ptr(logp), _ptr(n), _ptr(ln), _ptr(cm))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+    return {"cand": cand, "cand_logp": logp, "n_cand": n, "len": ln, "cum_margin": cm}
+
+
+def cps_beam(lat: dict, fluency=None, lam=1.0, beam=3) -> dict:
+    """Beam search over a lattice from cps_lattice; fluency [B, G, m_max, m_max] float32
+    or None."""
+    cand, logp = np.ascontiguousarray(lat["cand"]), np.ascontiguousarray(lat["cand_logp"])
+    n, ln = np.ascontiguousarray(lat["n_cand"]), np.ascontiguousarray(lat["len"])
+    B, G, M = cand.shape
+    f = None if fluency is None else np.ascontiguousarray(fluency, dtype=np.float32)
+    if f is not None and f.shape != (B, G, M, M):
+        raise ValueError("fluency must be [B, G, m_max, m_max]")
+    paths = np.empty((B, beam, G), np.int32)
+    score = np.empty((B, beam), np.float64)
+    plen = np.empty((B, beam), np.int32)
+    rm = np.empty(B, np.float64)
+    L = lib()
+    L.svdo_cps_beam.restype = ctypes.c_int
+    L.svdo_cps_beam.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_double, ctypes.c_int64,
+                                                        ctypes.c_int32, ctypes.c_int32,
+                                                        ctypes.c_int32] + [ctypes.c_void_p] * 4
+    rc = L.svdo_cps_beam(_ptr(cand), _ptr(logp), _ptr(n), _ptr(ln), _ptr(f), float(lam), B, G, M,
+                         int(beam), _ptr(paths), _ptr(score), _ptr(plen), _ptr(rm))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+    return {"paths": paths, "score": score, "path_len": plen, "rank_margin": rm}

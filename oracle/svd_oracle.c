@@ -559,3 +559,173 @@ int svdo_window_select_and_verify(int greedy, const void *p_logits, const void *
   base.nthreads = nthreads;
   return run_jobs(&base);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Causal-consistency path search (DiffuSpec section 4.2; its settings B = 3,
+ * M_max = 15, tau = 0.8 in section 5.3).  The drafter's per-position
+ * candidates form a lattice: each position keeps its most probable tokens
+ * until their cumulative mass reaches tau (at most m_max of them), and the
+ * lattice stops at the first position whose most probable token is EOS.  A
+ * left-to-right beam search then scores paths by drafter confidence plus a
+ * causal-proxy fluency term, which is an input here. */
+
+/* the order of a row's tokens: larger logit first, the lower index on a tie */
+static int before(const void *row, int dtype, int32_t a, int32_t b)
+{
+  double za = logit_at(row, dtype, a), zb = logit_at(row, dtype, b);
+  return za > zb || (za == zb && a < b);
+}
+
+int svdo_cps_lattice(const void *q_logits, int dtype, int64_t B, int32_t G, int32_t V,
+                     float temp_q, double tau, int32_t m_max, int32_t eos, int32_t *cand,
+                     double *cand_logp, int32_t *n_cand, int32_t *len, double *cum_margin)
+{
+  if (!q_logits || !cand || !cand_logp || !n_cand || !len) return -1;
+  if (B < 1 || G < 1 || V < 1 || m_max < 1 || !(tau > 0.0) || tau > 1.0) return -1;
+  if (!(temp_q > 0.0f) || isinf(temp_q)) return -1;
+  double *P = (double *)malloc(sizeof(double) * (size_t)V);
+  if (!P) return -1;
+  for (int64_t b = 0; b < B; ++b) {
+    len[b] = G;
+    for (int32_t j = 0; j < G; ++j) {
+      const size_t o = (size_t)b * G + j;
+      int32_t *c = cand + o * m_max;
+      double *lp = cand_logp + o * m_max;
+      for (int32_t i = 0; i < m_max; ++i) {
+        c[i] = -1;
+        lp[i] = -INFINITY;
+      }
+      n_cand[o] = 0;
+      if (cum_margin) cum_margin[o] = INFINITY;
+      if (j >= len[b]) continue;
+      const void *row = (const char *)q_logits + o * (size_t)V * elem_size(dtype);
+      double m, S;
+      if (!softmax_full(row, dtype, V, temp_q, P, &m, &S)) {
+        len[b] = -1;  /* invalid row: no lattice for this prefix */
+        continue;
+      }
+      /* the m_max most probable tokens, in order (selection by repeated scans) */
+      int32_t n = 0;
+      double cum = 0.0, prev_cum = 0.0;
+      for (int32_t i = 0; i < m_max && i < V; ++i) {
+        int32_t best = -1;
+        for (int32_t v = 0; v < V; ++v) {
+          int taken = 0;
+          for (int32_t t = 0; t < i; ++t) taken |= (c[t] == v);
+          if (!taken && (best < 0 || before(row, dtype, v, best))) best = v;
+        }
+        c[i] = best;
+        lp[i] = log_prob_at(row, dtype, temp_q, best, m, S);
+        prev_cum = cum;
+        cum += P[best];
+        n = i + 1;
+        if (cum >= tau) break;
+      }
+      n_cand[o] = n;
+      if (cum_margin) {
+        double mg = fabs(cum - tau);
+        if (n > 1 && fabs(prev_cum - tau) < mg) mg = fabs(prev_cum - tau);
+        cum_margin[o] = mg;
+      }
+      for (int32_t i = n; i < m_max; ++i) {
+        c[i] = -1;
+        lp[i] = -INFINITY;
+      }
+      /* the lattice stops at the first position whose most probable token is EOS */
+      if (eos >= 0 && c[0] == eos) {
+        for (int32_t i = 1; i < m_max; ++i) {
+          c[i] = -1;
+          lp[i] = -INFINITY;
+        }
+        n_cand[o] = 1;
+        if (cum_margin) cum_margin[o] = INFINITY;
+        len[b] = j + 1;
+      }
+    }
+    if (len[b] < 0)
+      for (int32_t j = 0; j < G; ++j) n_cand[(size_t)b * G + j] = 0;
+  }
+  free(P);
+  return 0;
+}
+
+int svdo_cps_beam(const int32_t *cand, const double *cand_logp, const int32_t *n_cand,
+                  const int32_t *len, const float *fluency, double lambda, int64_t B, int32_t G,
+                  int32_t m_max, int32_t beam, int32_t *paths, double *path_score,
+                  int32_t *path_len, double *rank_margin)
+{
+  if (!cand || !cand_logp || !n_cand || !len || !paths || !path_score || !path_len) return -1;
+  if (B < 1 || G < 1 || m_max < 1 || beam < 1) return -1;
+  const int32_t E = beam * m_max;  /* expansions per step, at most */
+  int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)beam * G);  /* candidate ranks */
+  int32_t *nidx = (int32_t *)malloc(sizeof(int32_t) * (size_t)beam * G);
+  double *sc = (double *)malloc(sizeof(double) * (size_t)beam);
+  double *nsc = (double *)malloc(sizeof(double) * (size_t)beam);
+  double *es = (double *)malloc(sizeof(double) * (size_t)E);
+  int32_t *ep = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+  int32_t *ei = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+  char *used = (char *)malloc((size_t)E);
+  int status = 0;
+  if (!idx || !nidx || !sc || !nsc || !es || !ep || !ei || !used) status = -1;
+  for (int64_t b = 0; b < B && status == 0; ++b) {
+    const int32_t n_len = len[b];
+    double margin = INFINITY;
+    int32_t nb = 1;  /* live paths, best first */
+    sc[0] = 0.0;
+    for (int32_t j = 0; j < n_len; ++j) {
+      const size_t o = (size_t)b * G + j;
+      const int32_t nc = n_cand[o];
+      /* every expansion (path p, candidate i), in order: path rank, then candidate rank */
+      int32_t ne = 0;
+      for (int32_t p = 0; p < nb; ++p)
+        for (int32_t i = 0; i < nc; ++i) {
+          /* the proxy's transition from the path's last candidate (the context at j = 0) */
+          const int32_t prev = (j == 0) ? 0 : idx[(size_t)p * G + j - 1];
+          const double f = fluency ? (double)fluency[(o * m_max + prev) * m_max + i] : 0.0;
+          es[ne] = sc[p] + cand_logp[o * m_max + i] + lambda * f;
+          ep[ne] = p;
+          ei[ne] = i;
+          used[ne] = 0;
+          ++ne;
+        }
+      /* keep the `beam` best, the earlier expansion on an exact tie */
+      const int32_t keep = ne < beam ? ne : beam;
+      double last = 0.0;
+      for (int32_t r = 0; r < keep; ++r) {
+        int32_t best = -1;
+        for (int32_t e = 0; e < ne; ++e)
+          if (!used[e] && (best < 0 || es[e] > es[best])) best = e;
+        if (r > 0 && last - es[best] < margin) margin = last - es[best];
+        last = es[best];
+        used[best] = 1;
+        for (int32_t t = 0; t < j; ++t) nidx[(size_t)r * G + t] = idx[(size_t)ep[best] * G + t];
+        nidx[(size_t)r * G + j] = ei[best];
+        nsc[r] = es[best];
+      }
+      if (keep < ne) {  /* the gap to the best expansion left out */
+        int32_t best = -1;
+        for (int32_t e = 0; e < ne; ++e)
+          if (!used[e] && (best < 0 || es[e] > es[best])) best = e;
+        if (last - es[best] < margin) margin = last - es[best];
+      }
+      for (int32_t r = 0; r < keep; ++r) {
+        sc[r] = nsc[r];
+        for (int32_t t = 0; t <= j; ++t) idx[(size_t)r * G + t] = nidx[(size_t)r * G + t];
+      }
+      nb = keep;
+    }
+    for (int32_t r = 0; r < beam; ++r) {
+      int32_t *out = paths + ((size_t)b * beam + r) * G;
+      for (int32_t t = 0; t < G; ++t) out[t] = -1;
+      const int live = n_len > 0 && r < nb;
+      path_len[(size_t)b * beam + r] = live ? n_len : 0;
+      path_score[(size_t)b * beam + r] = live ? sc[r] : -INFINITY;
+      if (live)
+        for (int32_t t = 0; t < n_len; ++t)
+          out[t] = cand[((size_t)b * G + t) * m_max + idx[(size_t)r * G + t]];
+    }
+    if (rank_margin) rank_margin[b] = margin;
+  }
+  free(idx); free(nidx); free(sc); free(nsc); free(es); free(ep); free(ei); free(used);
+  return status;
+}

@@ -135,6 +135,34 @@ int svdo_window_select_and_verify(int greedy, const void *p_logits, const void *
                                   double *scores, double *alpha, double *accept_margin,
                                   svdo_diag_t *diag, int nthreads);
 
+/*
+ * Causal-consistency path search (DiffuSpec section 4.2; settings in section
+ * 5.3).  svdo_cps_lattice: for each drafter row q_logits[b][j] (softmax at
+ * temp_q), the tokens in order of decreasing logit (lower index on a tie) are
+ * kept until their cumulative probability reaches tau, at most m_max of them:
+ * cand[b][j][0..n_cand), cand_logp = their log-probabilities, -1 / -inf after.
+ * The lattice of prefix b stops at the first position whose most probable
+ * token is EOS, which is then that position's only candidate: len[b] = that
+ * position + 1, else G (-1 for an invalid row).  cum_margin (nullable): the
+ * distance of the last two cumulative sums from tau.
+ * svdo_cps_beam: a left-to-right beam search of width `beam` over the lattice.
+ * A path's score is the sum over its positions of cand_logp plus lambda times
+ * fluency[b][j][a][i], the causal proxy's score of candidate i at position j
+ * after candidate a at position j - 1 (a = 0 at j = 0: after the context);
+ * fluency may be NULL (0).  Each step keeps the `beam` best expansions, the
+ * earlier one (path rank, then candidate rank) on an exact tie.  Outputs:
+ * paths[b][beam][G] tokens (-1 padded), path_score, path_len (0 for a missing
+ * path), rank_margin[b] = the smallest score gap between consecutive kept
+ * expansions, or between the last kept and the best dropped one.
+ */
+int svdo_cps_lattice(const void *q_logits, int dtype, int64_t B, int32_t G, int32_t V,
+                     float temp_q, double tau, int32_t m_max, int32_t eos, int32_t *cand,
+                     double *cand_logp, int32_t *n_cand, int32_t *len, double *cum_margin);
+int svdo_cps_beam(const int32_t *cand, const double *cand_logp, const int32_t *n_cand,
+                  const int32_t *len, const float *fluency, double lambda, int64_t B, int32_t G,
+                  int32_t m_max, int32_t beam, int32_t *paths, double *path_score,
+                  int32_t *path_len, double *rank_margin);
+
 #ifdef __cplusplus
 }
 #endif
