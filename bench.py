@@ -26,8 +26,10 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "verified draft positions/sec and achieved HBM GB/s (V=152064, bf16 logits)"
 # sources whose text decides each kernel's memory traffic
 KERNEL_SOURCES = {"rowstats": ["svd_device.hpp", "kr_rowstats.hpp"],
-                  "pool_stats": ["svd_device.hpp", "kr_rowstats.hpp", "kr_rows.hpp"]}
-KERNEL_SYMBOL = {"rowstats": "kr_rowstats", "pool_stats": "kr_pool_stats"}
+                  "pool_stats": ["svd_device.hpp", "kr_rowstats.hpp", "kr_rows.hpp"],
+                  "lattice": ["svd_device.hpp", "kr_rowstats.hpp", "kr_cps.hpp"]}
+KERNEL_SYMBOL = {"rowstats": "kr_rowstats", "pool_stats": "kr_pool_stats",
+                 "lattice": "kr_lattice"}
 
 
 def traffic_file(kernel: str, mode: str = "standard") -> str:
@@ -174,6 +176,83 @@ def calibrate_copy(torch, steps):
                       "launches": steps}), flush=True)
 
 
+CPS_TAU, CPS_MMAX, CPS_BEAM, CPS_LAMBDA = 0.8, 15, 3, 0.5
+
+
+def bench_cps(args, torch, svd, W):
+    """Causal-consistency path search over one drafter row per (prefix, position): the
+    shared drafter rows of the shared_marginal workload (B = 16, gamma = 16)."""
+    cfg = W.get_config("shared_marginal")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = W.generate_pooled(cfg, device=dev)
+    B, G, V = cfg.B, cfg.gamma, cfg.V
+    q = d["q_pool"].view(B, G, V)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.data_seed + 5)
+    flu = torch.randn((B, G, CPS_MMAX, CPS_MMAX), generator=g, device=dev) * 0.3
+    es = 2 if cfg.dtype == "bf16" else 4
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        lat = svd.cps_lattice(q, temp_q=cfg.temp, tau=CPS_TAU, m_max=CPS_MMAX, stream=stream.cuda_stream)
+        return lat, svd.cps_beam(lat, flu, lam=CPS_LAMBDA, beam=CPS_BEAM, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    svd.svd_profile_read()
+    svd.svd_profile_enable(["lattice"])
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        lat, bm = step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    svd.svd_profile_enable(())
+    ms, n = svd.svd_profile_read()
+    svd.svd_profile_enable("all")
+    for _ in range(min(args.steps, 10)):
+        step()
+    torch.cuda.synchronize()
+    svd.svd_profile_enable(())
+    ms_all, n_all = svd.svd_profile_read()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    li = svd.KERNELS.index("lattice")
+    ms_lat = ms[li] / max(n[li], 1)
+    rows = B * G
+    unit = V * es + CPS_MMAX * 8 + 8
+    achieved = unit * rows / (ms_lat * 1e-3) / 1e9
+    result = {
+        "metric": "drafter rows/s through the causal-consistency path search (V=152064, bf16)",
+        "value": rows / (ms_step * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "cps_" + cfg.name, "B": B, "gamma": G, "V": V, "tau": CPS_TAU,
+                   "m_max": CPS_MMAX, "beam": CPS_BEAM},
+        "kernel_ms": {k: ms_all[i] / max(n_all[i], 1) for i, k in enumerate(svd.KERNELS)
+                      if n_all[i]},
+        "roofline": {"kernel": "kr_lattice", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "bytes_per_unit": unit, "units_per_launch": rows},
+        "mean_lattice_width": float(lat["n_cand"].float().mean().item()),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        hq = W.to_host(q)
+        t0 = time.perf_counter()
+        reps = 0
+        while reps == 0 or time.perf_counter() - t0 < 10.0:
+            ol = oracle.cps_lattice(hq, temp_q=cfg.temp, tau=CPS_TAU, m_max=CPS_MMAX)
+            oracle.cps_beam(ol, flu.cpu().numpy(), lam=CPS_LAMBDA, beam=CPS_BEAM)
+            reps += 1
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": rows * reps / dt, "unit": "rows/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": "the %d drafter rows %d times, %.1f s" % (rows, reps, dt)}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +265,9 @@ def main():
     ap.add_argument("--early-exit", action="store_true",
                     help="K = 1 workloads: stream each prefix's positions only up to its first "
                          "rejection (svd_verify_window); reported apart from the full-streaming line")
+    ap.add_argument("--cps", action="store_true",
+                    help="time the causal-consistency path search instead (lattice of the "
+                         "workload's drafter rows, then a beam of 3; tau 0.8, M_max 15)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (for counter calibration)")
@@ -213,6 +295,10 @@ def main():
 
     import lossless_draft_verification_verifier_amd as svd
     import workloads as W
+
+    if args.cps:
+        bench_cps(args, torch, svd, W)
+        return
 
     cfg = W.get_config(args.workload)
     dev = torch.device("cuda:0")

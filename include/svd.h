@@ -231,6 +231,54 @@ int svd_verify_window(svd_rule_t rule, const void *p_logits, const void *q_logit
                       int32_t *selected, int32_t *accept_len, int32_t *next_token, float *scores,
                       float *alpha, void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * Causal-consistency path search (DiffuSpec section 4.2: the diffusion
+ * drafter's per-position candidates form a lattice; each position keeps its
+ * candidates by cumulative probability mass, the lattice stops at the first
+ * EOS, and a left-to-right beam search scores paths by drafter confidence
+ * plus a causal-proxy fluency; section 5.3 settles on beam 3, M_max 15 and
+ * tau 0.8).  The top paths are the drafts a call of svd_select_and_verify_rows
+ * (the shared drafter rows are the marginals the lattice came from) ranks and
+ * verifies.
+ *
+ * svd_cps_lattice: for every drafter row q_logits[B][G][V] (softmax at
+ * temp_q), the tokens in order of decreasing probability (the lower index on
+ * a tie) are kept until their cumulative mass reaches tau, at most m_max
+ * (1..16) of them:
+ *   cand      [B][G][m_max] out  candidate tokens, -1 after the kept ones
+ *   cand_logp [B][G][m_max] out  their log-probabilities (natural log), -inf after
+ *   n_cand    [B][G]        out  kept candidates (0 past the lattice)
+ *   len       [B]           out  lattice length: the first position whose most
+ *                                probable token is eos, included (that position
+ *                                then keeps only eos), else G; -1 when a row
+ *                                before it holds a NaN or +inf, or is all -inf
+ * eos < 0: no EOS.  Workspace: svd_cps_workspace_bytes(B, G) bytes, 256-byte
+ * aligned.  Probabilities are fp32; a cut at tau can differ from an exact one
+ * when a running sum lies within ~1e-6 of tau.
+ *
+ * svd_cps_beam: a beam search of width beam (1..8) over a lattice (G <= 1024).
+ * A path's score is the sum over its positions of cand_logp plus lambda times
+ *   fluency [B][G][m_max][m_max] (nullable: 0)  the causal proxy's score of
+ *   candidate i at position j after candidate a at position j-1 (a = 0 at
+ *   j = 0: after the context),
+ * computed in fp64.  Every step keeps the beam best expansions (path rank, then
+ * candidate rank order breaks exact ties).  Outputs, best first:
+ *   paths      [B][beam][G] out  tokens, -1 padded
+ *   path_score [B][beam]    out  -inf for a missing path
+ *   path_len   [B][beam]    out  len[b], or 0 for a missing path
+ * A prefix with len[b] outside [1, G] or an n_cand outside [1, m_max] before
+ * len[b] gets no paths.
+ */
+size_t svd_cps_workspace_bytes(int64_t B, int32_t G);
+int svd_cps_lattice(const void *q_logits, svd_dtype_t dtype, int64_t B, int32_t G, int32_t V,
+                    float temp_q, float tau, int32_t m_max, int32_t eos, int32_t *cand,
+                    float *cand_logp, int32_t *n_cand, int32_t *len, void *workspace,
+                    size_t workspace_bytes, void *hip_stream);
+int svd_cps_beam(const int32_t *cand, const float *cand_logp, const int32_t *n_cand,
+                 const int32_t *len, const float *fluency, float lambda, int64_t B, int32_t G,
+                 int32_t m_max, int32_t beam, int32_t *paths, float *path_score,
+                 int32_t *path_len, void *hip_stream);
+
 /* Static text for a status code. */
 const char *svd_strerror(int status);
 
@@ -256,7 +304,10 @@ enum {
   SVD_KERNEL_MARK = 6,       /* shared rows: flags of the pool rows read               */
   SVD_KERNEL_POOL_STATS = 7, /* shared rows: statistics once per pool row read          */
   SVD_KERNEL_ALPHA_ROWS = 8, /* shared rows: alpha per scored position                  */
-  SVD_KERNEL_COUNT = 9
+  SVD_KERNEL_LATTICE = 9,    /* candidate lattice of the drafter rows (and its length)  */
+  SVD_KERNEL_BEAM = 10,      /* beam search over the lattice                            */
+  SVD_KERNEL_LATTICE_LEN = 11, /* lattice length and cleared tail                       */
+  SVD_KERNEL_COUNT = 12
 };
 int svd_profile_enable(unsigned kernel_mask);
 int svd_profile_read(double *ms, int64_t *launches, int n);

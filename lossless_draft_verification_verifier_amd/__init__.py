@@ -8,10 +8,11 @@ Raw entry points (same names and argument order as the C ABI; pointer
 arguments take an int address or a tensor):
     svd_workspace_bytes, svd_verify, svd_select_and_verify, svd_greedy_verify,
     svd_greedy_select_and_verify, svd_rows_workspace_bytes, svd_select_and_verify_rows,
-    svd_verify_window, svd_strerror, svd_profile_enable, svd_profile_read
+    svd_verify_window, svd_cps_workspace_bytes, svd_cps_lattice, svd_cps_beam, svd_strerror,
+    svd_profile_enable, svd_profile_read
 Tensor conveniences that allocate the outputs and the workspace with torch:
     verify, select_and_verify, greedy_verify, greedy_select_and_verify,
-    select_and_verify_rows, verify_window, workspace_bytes
+    select_and_verify_rows, verify_window, cps_lattice, cps_beam, workspace_bytes
 
 Importing fails with ImportError when ``libsvd.so`` has not been built; there
 is no fallback path.
@@ -28,13 +29,14 @@ SVD_F32, SVD_BF16 = 0, 1
 SVD_OK, SVD_EINVAL, SVD_EDTYPE, SVD_EWORKSPACE, SVD_EHIP = 0, -1, -2, -3, -4
 SVD_MAX_K, SVD_MAX_GAMMA = 64, 4096
 KERNELS = ("rowstats", "select", "draw_pass", "draw_fix", "draw_pick", "beta", "mark",
-           "pool_stats", "alpha_rows")
+           "pool_stats", "alpha_rows", "lattice", "beam", "lattice_len")
 SVD_RULE_STANDARD, SVD_RULE_GREEDY = 0, 1
 
 C_EXPORTS = ("svd_workspace_bytes", "svd_verify", "svd_select_and_verify", "svd_greedy_verify",
              "svd_greedy_select_and_verify", "svd_rows_workspace_bytes",
-             "svd_select_and_verify_rows", "svd_verify_window", "svd_strerror",
-             "svd_profile_enable", "svd_profile_read")
+             "svd_select_and_verify_rows", "svd_verify_window", "svd_cps_workspace_bytes",
+             "svd_cps_lattice", "svd_cps_beam", "svd_strerror", "svd_profile_enable",
+             "svd_profile_read")
 
 
 class SvdError(RuntimeError):
@@ -75,6 +77,13 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.svd_verify_window.restype = ctypes.c_int
     L.svd_verify_window.argtypes = [ctypes.c_int, vp, vp, vp, vp, i32, i32, ctypes.c_int, i64, i32,
                                     i32, i32, f32, f32, u64, u64, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.svd_cps_workspace_bytes.restype = sz
+    L.svd_cps_workspace_bytes.argtypes = [i64, i32]
+    L.svd_cps_lattice.restype = ctypes.c_int
+    L.svd_cps_lattice.argtypes = [vp, ctypes.c_int, i64, i32, i32, f32, f32, i32, i32, vp, vp, vp,
+                                  vp, vp, sz, vp]
+    L.svd_cps_beam.restype = ctypes.c_int
+    L.svd_cps_beam.argtypes = [vp, vp, vp, vp, vp, f32, i64, i32, i32, i32, vp, vp, vp, vp]
     L.svd_strerror.restype = ctypes.c_char_p
     L.svd_strerror.argtypes = [ctypes.c_int]
     L.svd_profile_enable.restype = ctypes.c_int
@@ -166,6 +175,26 @@ def svd_verify_window(rule, p_logits, q_logits, drafts, gamma_b, eos, early_exit
         int(early_exit), int(dtype), int(B), int(K), int(gamma), int(V), float(temp_p),
         float(temp_q), int(seed) & _M64, int(row_base) & _M64, _addr(selected), _addr(accept_len),
         _addr(next_token), _addr(scores), _addr(alpha), _addr(workspace), int(workspace_bytes),
+        _addr(hip_stream)))
+
+
+def svd_cps_workspace_bytes(B: int, G: int) -> int:
+    return int(_lib.svd_cps_workspace_bytes(B, G))
+
+
+def svd_cps_lattice(q_logits, dtype, B, G, V, temp_q, tau, m_max, eos, cand, cand_logp, n_cand,
+                    length, workspace, workspace_bytes, hip_stream) -> int:
+    return int(_lib.svd_cps_lattice(
+        _addr(q_logits), int(dtype), int(B), int(G), int(V), float(temp_q), float(tau),
+        int(m_max), int(eos), _addr(cand), _addr(cand_logp), _addr(n_cand), _addr(length),
+        _addr(workspace), int(workspace_bytes), _addr(hip_stream)))
+
+
+def svd_cps_beam(cand, cand_logp, n_cand, length, fluency, lam, B, G, m_max, beam, paths,
+                 path_score, path_len, hip_stream) -> int:
+    return int(_lib.svd_cps_beam(
+        _addr(cand), _addr(cand_logp), _addr(n_cand), _addr(length), _addr(fluency), float(lam),
+        int(B), int(G), int(m_max), int(beam), _addr(paths), _addr(path_score), _addr(path_len),
         _addr(hip_stream)))
 
 
@@ -446,4 +475,47 @@ def verify_window(p, q, drafts, gamma_b=None, eos=-1, rule="standard", early_exi
                            out["alpha"], ws, ws.numel(), st)
     if rc != SVD_OK:
         raise SvdError(rc, "svd_verify_window")
+    return out
+
+
+def cps_lattice(q, temp_q=1.0, tau=0.8, m_max=15, eos=-1, stream=None):
+    """Candidate lattice of drafter logits q [B, G, V] (bf16 or fp32)."""
+    import torch
+    dev = q.device
+    _check(q, "q", dev)
+    B, G, V = q.shape
+    out = {"cand": torch.empty((B, G, m_max), dtype=torch.int32, device=dev),
+           "cand_logp": torch.empty((B, G, m_max), dtype=torch.float32, device=dev),
+           "n_cand": torch.empty((B, G), dtype=torch.int32, device=dev),
+           "len": torch.empty(B, dtype=torch.int32, device=dev)}
+    n = svd_cps_workspace_bytes(B, G)
+    if n == 0:
+        raise ValueError("sizes out of range")
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    rc = svd_cps_lattice(q, _dtype_code(q), B, G, V, temp_q, tau, m_max, eos, out["cand"],
+                         out["cand_logp"], out["n_cand"], out["len"], ws, n, st)
+    if rc != SVD_OK:
+        raise SvdError(rc, "svd_cps_lattice")
+    return out
+
+
+def cps_beam(lat, fluency=None, lam=1.0, beam=3, stream=None):
+    """Beam search over a lattice from cps_lattice; fluency [B, G, m_max, m_max] fp32 or None."""
+    import torch
+    cand = lat["cand"]
+    dev = cand.device
+    B, G, M = cand.shape
+    if fluency is not None:
+        _check(fluency, "fluency", dev)
+        if fluency.dtype != torch.float32 or tuple(fluency.shape) != (B, G, M, M):
+            raise ValueError("fluency must be float32 [B, G, m_max, m_max]")
+    out = {"paths": torch.empty((B, beam, G), dtype=torch.int32, device=dev),
+           "score": torch.empty((B, beam), dtype=torch.float32, device=dev),
+           "path_len": torch.empty((B, beam), dtype=torch.int32, device=dev)}
+    st = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    rc = svd_cps_beam(cand, lat["cand_logp"], lat["n_cand"], lat["len"], fluency, lam, B, G, M,
+                      beam, out["paths"], out["score"], out["path_len"], st)
+    if rc != SVD_OK:
+        raise SvdError(rc, "svd_cps_beam")
     return out

@@ -10,6 +10,7 @@
 
 #include "svd.h"
 #include "kr_beta.hpp"
+#include "kr_cps.hpp"
 #include "kr_draw.hpp"
 #include "kr_rows.hpp"
 #include "kr_rowstats.hpp"
@@ -496,6 +497,70 @@ int svd_verify_window(svd_rule_t rule, const void *p_logits, const void *q_logit
   c.gamma_b = gamma_b;
   c.eos = eos < 0 ? -1 : eos;
   return dispatch(c);
+}
+
+size_t svd_cps_workspace_bytes(int64_t B, int32_t G) {
+  if (B < 1 || G < 1 || G > SVD_MAX_GAMMA || B >= ((int64_t)1 << 31) / G) return 0;
+  return align_up((size_t)B * G * sizeof(uint32_t));
+}
+
+int svd_cps_lattice(const void *q_logits, svd_dtype_t dtype, int64_t B, int32_t G, int32_t V,
+                    float temp_q, float tau, int32_t m_max, int32_t eos, int32_t *cand,
+                    float *cand_logp, int32_t *n_cand, int32_t *len, void *workspace,
+                    size_t workspace_bytes, void *hip_stream) {
+  if (!q_logits || !cand || !cand_logp || !n_cand || !len || !workspace) return SVD_EINVAL;
+  if (dtype != SVD_F32 && dtype != SVD_BF16) return SVD_EDTYPE;
+  if (V < 1 || !temp_ok(temp_q) || !(tau > 0.0f) || !(tau <= 1.0f) || m_max < 1 ||
+      m_max > kCpsMax || eos >= V)
+    return SVD_EINVAL;
+  const size_t need = svd_cps_workspace_bytes(B, G);
+  if (need == 0 || ((uintptr_t)workspace) % kAlign != 0) return SVD_EINVAL;
+  if (workspace_bytes < need) return SVD_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  uint32_t *flags = static_cast<uint32_t *>(workspace);
+  const float c = (float)(1.4426950408889634 / (double)temp_q);
+  const size_t es = dtype == SVD_F32 ? 4 : 2;
+  const bool vec = ((size_t)V * es) % 16 == 0 && ((uintptr_t)q_logits) % 16 == 0;
+  const dim3 grid((unsigned)(B * G));
+  const int e = eos < 0 ? -1 : eos;
+  CallTimer tm;
+  if (dtype == SVD_BF16) {
+    const auto *q = static_cast<const BF16::elem *>(q_logits);
+    if (vec)
+      SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<BF16, true>, grid, dim3(kRowBlock), s, q, V,
+                 c, tau, m_max, e, cand, cand_logp, n_cand, flags);
+    else
+      SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<BF16, false>, grid, dim3(kRowBlock), s, q,
+                 V, c, tau, m_max, e, cand, cand_logp, n_cand, flags);
+  } else {
+    const auto *q = static_cast<const F32::elem *>(q_logits);
+    if (vec)
+      SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<F32, true>, grid, dim3(kRowBlock), s, q, V,
+                 c, tau, m_max, e, cand, cand_logp, n_cand, flags);
+    else
+      SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<F32, false>, grid, dim3(kRowBlock), s, q, V,
+                 c, tau, m_max, e, cand, cand_logp, n_cand, flags);
+  }
+  SVD_LAUNCH(tm, SVD_KERNEL_LATTICE_LEN, s, kr_lattice_len, dim3((unsigned)((B + kBlock - 1) / kBlock)),
+             dim3(kBlock), s, (const uint32_t *)flags, B, G, m_max, cand, cand_logp, n_cand, len);
+  return SVD_OK;
+}
+
+int svd_cps_beam(const int32_t *cand, const float *cand_logp, const int32_t *n_cand,
+                 const int32_t *len, const float *fluency, float lambda, int64_t B, int32_t G,
+                 int32_t m_max, int32_t beam, int32_t *paths, float *path_score,
+                 int32_t *path_len, void *hip_stream) {
+  if (!cand || !cand_logp || !n_cand || !len || !paths || !path_score || !path_len)
+    return SVD_EINVAL;
+  if (B < 1 || B >= ((int64_t)1 << 31) || G < 1 || G > kCpsMaxG || m_max < 1 ||
+      m_max > kCpsMax || beam < 1 || beam > kCpsBeam || !std::isfinite(lambda))
+    return SVD_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  CallTimer tm;
+  SVD_LAUNCH(tm, SVD_KERNEL_BEAM, s, kr_cps_beam, dim3((unsigned)B), dim3(64), s, cand, cand_logp,
+             n_cand, len, fluency, lambda, (int)G, (int)m_max, (int)beam, paths, path_score,
+             path_len);
+  return SVD_OK;
 }
 
 const char *svd_strerror(int status) {

@@ -1,0 +1,154 @@
+"""GPU parity of the causal-consistency path search (svd_cps_lattice,
+svd_cps_beam) against the oracle: the candidate order is exact (it is the order
+of the logits), the cut at tau is exact unless a running sum lies within
+CUM_EPS of tau, log-probabilities agree to fp32 accuracy, and the beam paths
+are exact unless two expansions' scores lie within RANK_EPS."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+CUM_EPS = 1e-5
+RANK_EPS = 1e-4
+
+
+def _rows(seed, B, G, V, dt, scale=2.0, eos=-1, eos_at=()):
+    rng = np.random.default_rng(seed)
+    z = (rng.standard_normal((B, G, V)) * scale).astype(np.float32)
+    z[:, :, rng.integers(0, V, 3)] += 3.0  # a few strong tokens
+    for b, j in eos_at:
+        z[b, j, eos] = z[b, j].max() + 2.0
+    t = torch.from_numpy(z)
+    if dt == "bf16":
+        t = t.to(torch.bfloat16)
+        host_z = t.view(torch.int16).numpy().view(np.uint16)
+    else:
+        host_z = z
+    return t.cuda(), host_z
+
+
+def _check_lattice(g, o, m_max):
+    B, G = o["n_cand"].shape
+    flagged = 0
+    assert np.array_equal(g["len"], o["len"])
+    for b in range(B):
+        for j in range(G):
+            n_g, n_o = int(g["n_cand"][b, j]), int(o["n_cand"][b, j])
+            if n_g != n_o:
+                assert o["cum_margin"][b, j] < CUM_EPS, (b, j, n_g, n_o, o["cum_margin"][b, j])
+                flagged += 1
+            n = min(n_g, n_o)
+            assert np.array_equal(g["cand"][b, j, :n], o["cand"][b, j, :n])
+            lo = o["cand_logp"][b, j, :n]
+            assert np.all(np.abs(g["cand_logp"][b, j, :n] - lo) <= 2e-6 * np.maximum(1, np.abs(lo)))
+            assert np.all(g["cand"][b, j, n_g:] == -1)
+    return flagged
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("V,B,G,tau,m_max", [(1000, 4, 8, 0.8, 15), (1001, 3, 5, 0.5, 4),
+                                             (37, 2, 6, 0.95, 16), (8, 2, 3, 0.99, 16),
+                                             (20000, 2, 4, 0.8, 1)])
+def test_lattice_matches_oracle(dt, V, B, G, tau, m_max):
+    svd = require_gpu()
+    say("lattice", dt, V, B, G, tau, m_max)
+    q, hz = _rows(V + G, B, G, V, dt)
+    g = host(svd.cps_lattice(q, temp_q=0.9, tau=tau, m_max=m_max))
+    o = oracle.cps_lattice(hz, temp_q=0.9, tau=tau, m_max=m_max)
+    assert _check_lattice(g, o, m_max) <= 1
+
+
+def test_lattice_eos_and_invalid_rows():
+    svd = require_gpu()
+    q, hz = _rows(3, 4, 7, 500, "bf16", eos=11, eos_at=[(0, 2), (0, 5), (2, 6)])
+    q[3, 1, 40] = float("nan")
+    hz = hz.copy()
+    hz[3, 1, 40] = 0x7FC0
+    g = host(svd.cps_lattice(q, tau=0.8, m_max=15, eos=11))
+    o = oracle.cps_lattice(hz, tau=0.8, m_max=15, eos=11)
+    assert list(g["len"]) == list(o["len"]) == [3, 7, 7, -1]
+    _check_lattice(g, o, 15)
+
+
+def test_full_vocabulary_rows():
+    svd = require_gpu()
+    q, hz = _rows(5, 2, 3, 152064, "bf16", scale=2.0)
+    g = host(svd.cps_lattice(q, tau=0.8, m_max=15))
+    o = oracle.cps_lattice(hz, tau=0.8, m_max=15)
+    _check_lattice(g, o, 15)
+
+
+@pytest.mark.parametrize("beam", [1, 3, 8])
+def test_beam_matches_oracle_on_the_same_lattice(beam):
+    svd = require_gpu()
+    B, G, M = 12, 10, 6
+    q, hz = _rows(7, B, G, 300, "f32", scale=1.0)
+    o = oracle.cps_lattice(hz, tau=0.9, m_max=M)
+    o["cand_logp"] = o["cand_logp"].astype(np.float32).astype(np.float64)  # the GPU's inputs
+    f = np.random.default_rng(8).standard_normal((B, G, M, M)).astype(np.float32)
+    ob = oracle.cps_beam(o, f, lam=0.7, beam=beam)
+    lat = {k: torch.from_numpy(np.ascontiguousarray(v if k != "cand_logp" else v.astype(np.float32))).cuda()
+           for k, v in o.items() if k in ("cand", "cand_logp", "n_cand", "len")}
+    g = host(svd.cps_beam(lat, torch.from_numpy(f).cuda(), lam=0.7, beam=beam))
+    for b in range(B):
+        if ob["rank_margin"][b] < 1e-9:
+            continue
+        assert np.array_equal(g["paths"][b], ob["paths"][b]), b
+        assert np.array_equal(g["path_len"][b], ob["path_len"][b])
+        live = ob["path_len"][b] > 0
+        assert np.allclose(g["score"][b][live], ob["score"][b][live], atol=1e-4)
+
+
+def test_lattice_then_beam_end_to_end():
+    svd = require_gpu()
+    B, G, V, M = 8, 12, 5000, 15
+    q, hz = _rows(9, B, G, V, "bf16", scale=1.5, eos=3, eos_at=[(1, 7)])
+    f = (np.random.default_rng(2).standard_normal((B, G, M, M)) * 0.3).astype(np.float32)
+    gl = svd.cps_lattice(q, tau=0.8, m_max=M, eos=3)
+    g = host(svd.cps_beam(gl, torch.from_numpy(f).cuda(), lam=0.5, beam=3))
+    ol = oracle.cps_lattice(hz, tau=0.8, m_max=M, eos=3)
+    ob = oracle.cps_beam(ol, f, lam=0.5, beam=3)
+    compared = 0
+    for b in range(B):
+        if np.min(ol["cum_margin"][b]) < CUM_EPS or ob["rank_margin"][b] < RANK_EPS:
+            continue
+        compared += 1
+        assert np.array_equal(g["paths"][b], ob["paths"][b]), b
+        assert np.allclose(g["score"][b], ob["score"][b], atol=1e-3)
+    assert compared >= B - 2
+    assert g["path_len"][1, 0] == 8 and g["paths"][1, 0, 7] == 3  # stopped at the EOS
+
+
+def test_beam_rejects_unusable_inputs():
+    svd = require_gpu()
+    B, G, M = 3, 4, 4
+    lat = {"cand": torch.zeros((B, G, M), dtype=torch.int32, device="cuda"),
+           "cand_logp": torch.zeros((B, G, M), dtype=torch.float32, device="cuda"),
+           "n_cand": torch.tensor([[1, 2, 1, 1], [1, 5, 1, 1], [1, 1, 1, 1]], dtype=torch.int32,
+                                  device="cuda"),
+           "len": torch.tensor([4, 4, 9], dtype=torch.int32, device="cuda")}
+    g = host(svd.cps_beam(lat, None, beam=2))
+    assert list(g["path_len"][:, 0]) == [4, 0, 0]  # n_cand 5 > m_max, len 9 > G
+    assert np.all(g["paths"][1:] == -1)
+    assert svd.svd_cps_beam(lat["cand"], lat["cand_logp"], lat["n_cand"], lat["len"], None, 1.0,
+                            B, 2000, M, 2, lat["cand"], lat["cand_logp"], lat["n_cand"],
+                            None) == svd.SVD_EINVAL
+
+
+def test_lattice_with_many_ties_at_the_top():
+    # more tokens tie at the threshold than the candidate list holds: the
+    # per-thread sorted lists take over; the lowest indices win the tie
+    svd = require_gpu()
+    q, hz = _rows(11, 2, 3, 3000, "f32")
+    hz = hz.copy()
+    hz[0, :, 100:700] = 9.0
+    hz[1, 1, ::2] = 7.0
+    q = torch.from_numpy(hz).cuda()
+    g = host(svd.cps_lattice(q, tau=0.99, m_max=16))
+    o = oracle.cps_lattice(hz, tau=0.99, m_max=16)
+    _check_lattice(g, o, 16)
+    assert list(g["cand"][0, 0, :3]) == [100, 101, 102]
