@@ -307,7 +307,8 @@ enum {
   SVD_KERNEL_LATTICE = 9,    /* candidate lattice of the drafter rows (and its length)  */
   SVD_KERNEL_BEAM = 10,      /* beam search over the lattice                            */
   SVD_KERNEL_LATTICE_LEN = 11, /* lattice length and cleared tail                       */
-  SVD_KERNEL_COUNT = 12
+  SVD_KERNEL_COMBINE = 12,   /* split rows: merge of the slices' statistics, alpha      */
+  SVD_KERNEL_COUNT = 13
 };
 int svd_profile_enable(unsigned kernel_mask);
 int svd_profile_read(double *ms, int64_t *launches, int n);

@@ -37,6 +37,7 @@
 namespace svd {
 
 constexpr int kUncCap = 32;            // uncertain tokens kept per segment
+constexpr int kPickSegs = 256;         // segment records the pick stages in LDS
 constexpr double kClassMargin = 2e-4;  // relative margin of the p > q test
 
 // ---------------------------------------------------------------------------
@@ -455,19 +456,27 @@ __device__ __forceinline__ void draw_pick_item(
     const DrawDesc d, const RowStats st, const DrawSeg *__restrict__ segs,
     const DrawUnc *__restrict__ uncs, DrawMass *__restrict__ mass,
     int32_t *__restrict__ selected, int32_t *__restrict__ accept_len,
-    int32_t *__restrict__ next_token, int64_t b) {
+    int32_t *__restrict__ next_token, int64_t b, bool inline_fix) {
   constexpr int NW = NT / 64;
   constexpr int kRun = kDrawSeg / NT;  // tokens per thread in the scan of one segment
   __shared__ Exp64Table tab;
   __shared__ double ldsd[NW + 1];
   __shared__ int ldsi[NW + 1];
+  __shared__ DrawSeg segl[kPickSegs];   // the prefix's segment records, when they fit
+  __shared__ DrawMass massl[kPickSegs];
   const int tid = threadIdx.x;
   if (!d.valid) return;
   exp64_table_init(tab);
+  // the serial loops below read the segment records from LDS (global memory
+  // for vocabularies of more than kPickSegs segments)
+  const bool staged = nseg <= kPickSegs;
+  if (staged)
+    for (int s = tid; s < nseg; s += NT) segl[s] = segs[b * nseg + s];
   __syncthreads();
   const DrawRows<E> rows = draw_rows<E>(p, q, ix, K, gamma, V, b, d);
-  const DrawSeg *S = segs + b * nseg;
-  DrawMass *ms = mass + b * nseg;
+  const DrawSeg *S = staged ? segl : segs + b * nseg;
+  DrawMass *msg = mass + b * nseg;  // the fix kernel's masses
+  DrawMass *ms = staged ? massl : msg;
   const bool residual = d.two != 0;
   DrawWeight<E> W;
   if (!draw_setup<E>(rows, d, st, S, nseg, tp, tq, W)) {
@@ -482,7 +491,10 @@ __device__ __forceinline__ void draw_pick_item(
   // per-segment masses of the other segments
   for (int s = tid; s < nseg; s += NT) {
     const DrawSeg g = S[s];
-    if (residual && g.n_unc < 0) continue;
+    if (residual && g.n_unc < 0) {  // recomputed by the fix kernel, or just below
+      if (staged && !inline_fix) ms[s] = msg[s];
+      continue;
+    }
     DrawMass m{};
     m.last_p = g.last_p;
     if (residual) {
@@ -510,6 +522,16 @@ __device__ __forceinline__ void draw_pick_item(
     ms[s] = m;
   }
   __syncthreads();
+  if (inline_fix && residual) {  // few prefixes: overflowed segments settled here
+    for (int s = 0; s < nseg; ++s) {
+      const DrawSeg g = S[s];
+      if (g.n_unc >= 0) continue;
+      DrawMass m{};
+      segment_mass_exact<E, kVec, NT>(W, g, V, s, tab, ldsd, ldsi, m);
+      if (tid == 0) ms[s] = m;
+    }
+    __syncthreads();
+  }
 
   double zr = 0.0;
   for (int s = 0; s < nseg; ++s) zr += ms[s].zr;
@@ -597,12 +619,12 @@ __global__ __launch_bounds__(kBlock) void kr_draw_pick(
     const RowStats *__restrict__ stats, const DrawDesc *__restrict__ desc,
     const DrawSeg *__restrict__ segs, const DrawUnc *__restrict__ uncs,
     DrawMass *__restrict__ mass, int32_t *__restrict__ selected,
-    int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token) {
+    int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token, int inline_fix) {
   const int64_t b = blockIdx.x;
   const DrawDesc d = desc[b];
   draw_pick_item<E, kVec, kBlock>(p, q, ix, K, gamma, V, nseg, tp, tq, seed, row_base, d,
                                   drawn_stats(stats, d, K, gamma, b), segs, uncs, mass, selected,
-                                  accept_len, next_token, b);
+                                  accept_len, next_token, b, inline_fix != 0);
 }
 
 }  // namespace svd

@@ -185,4 +185,90 @@ __global__ __launch_bounds__(kRowBlock) __attribute__((amdgpu_waves_per_eu(8))) 
                                                          alpha_ws, alpha_out);
 }
 
+// ---------------------------------------------------------------------------
+// Split rows.  A launch with few row pairs (a single sequence, or the later
+// chunks of an early exit) cannot fill the GPU with one workgroup per pair, so
+// each pair's vocabulary is cut into S slices of whole 16-byte vectors, one
+// 256-thread workgroup per slice writes a partial (max, sum) record of both
+// rows, and kr_rowstats_combine merges the S records of a pair in slice order
+// and forms alpha.
+
+constexpr int kSplitBlock = 256;
+
+struct PartStats {  // one (row pair, slice)
+  float mp, sp, mq, sq;
+};
+
+// Workgroup w: slice w % S of launch row r = w / S, i.e. position j0 + r % jn
+// of draft r / jn; skipping as in kr_rowstats.
+template <typename E, bool kVec, bool kGreedy>
+__global__ __launch_bounds__(kSplitBlock) void kr_rowstats_split(
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int gamma,
+    int V, float cp, float cq, int S, int slice, const int32_t *__restrict__ mlen,
+    const uint32_t *__restrict__ alive, int j0, int jn, PartStats *__restrict__ part) {
+  __shared__ float lds[2 * (kSplitBlock / 64)];
+  const int64_t r = blockIdx.x / S;
+  const int sl = (int)(blockIdx.x - r * S);
+  const int64_t bk = r / jn;
+  const int j = j0 + (int)(r - bk * jn);
+  if (j >= gamma || (mlen && j >= mlen[bk]) || (alive && !alive[bk])) return;
+  const int lo = sl * slice, hi = min(V, lo + slice);  // slice: whole vectors
+  const typename E::elem *prow = p + (bk * (gamma + 1) + j) * (int64_t)V + lo;
+  float mp, sp, mq = 0.0f, sq = 1.0f;
+  row_ms<E, kVec, kSplitBlock, kRowUnroll>(prow, hi - lo, cp, mp, sp, lds);
+  if constexpr (!kGreedy) {
+    const typename E::elem *qrow = q + (bk * gamma + j) * (int64_t)V + lo;
+    row_ms<E, kVec, kSplitBlock, kRowUnroll>(qrow, hi - lo, cq, mq, sq, lds);
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = PartStats{mp, sp, mq, sq};
+}
+
+// One wave per launch row: lane sl holds slice sl's record (lane sl + 64k
+// folds slices past 64 in first), a butterfly merges the lanes in a fixed
+// pattern, and lane 0 forms alpha.
+template <typename E, bool kGreedy>
+__global__ __launch_bounds__(kBlock) void kr_rowstats_combine(
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
+    const int32_t *__restrict__ drafts, int64_t rows, int gamma, int V, float cp, float cq, int S,
+    const int32_t *__restrict__ mlen, const uint32_t *__restrict__ alive, int j0, int jn,
+    const PartStats *__restrict__ part, RowStats *__restrict__ stats,
+    float *__restrict__ alpha_ws, float *__restrict__ alpha_out) {
+  const int64_t r = ((int64_t)blockIdx.x * kBlock + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;  // whole waves
+  const int64_t bk = r / jn;
+  const int j = j0 + (int)(r - bk * jn);
+  if (j >= gamma) return;
+  const int64_t rp = bk * gamma + j;
+  if ((mlen && j >= mlen[bk]) || (alive && !alive[bk])) {
+    if (alpha_out && lane == 0) alpha_out[rp] = __builtin_nanf("");
+    return;
+  }
+  PartStats a{kNegInf, 0.0f, kNegInf, 0.0f};
+  for (int sl = lane; sl < S; sl += 64) {
+    const PartStats b = part[r * S + sl];
+    ms_merge(a.mp, a.sp, b.mp, b.sp, cp);
+    if constexpr (!kGreedy) ms_merge(a.mq, a.sq, b.mq, b.sq, cq);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    ms_merge(a.mp, a.sp, __shfl_xor(a.mp, off, 64), __shfl_xor(a.sp, off, 64), cp);
+    if constexpr (!kGreedy)
+      ms_merge(a.mq, a.sq, __shfl_xor(a.mq, off, 64), __shfl_xor(a.sq, off, 64), cq);
+  }
+  if (lane != 0) return;
+  if constexpr (kGreedy) {
+    a.mq = 0.0f;
+    a.sq = 1.0f;
+  }
+  const int32_t x = drafts[rp];
+  float al = __builtin_nanf("");
+  if (x >= 0 && x < V)
+    al = acceptance<kGreedy>(E::at(p + (bk * (gamma + 1) + j) * (int64_t)V, x), a.mp, a.sp, cp,
+                             kGreedy ? 0.0f : E::at(q + rp * (int64_t)V, x), a.mq, a.sq, cq);
+  stats[rp] = RowStats{a.mp, a.sp, a.mq, a.sq};
+  alpha_ws[rp] = al;
+  if (alpha_out) alpha_out[rp] = al;
+}
+
 }  // namespace svd

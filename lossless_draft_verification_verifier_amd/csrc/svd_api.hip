@@ -24,9 +24,14 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-  size_t stats, alpha, desc, segs, uncs, mass, mlen, alive, pstat, flags, total;
+  size_t stats, alpha, desc, segs, uncs, mass, mlen, alive, part, pstat, flags, total;
   int nseg;
 };
+
+// Split rows: at most this many (row pair, slice) records per launch.
+constexpr int kPartCap = 4096;
+constexpr int64_t kSplitRows = 1024;    // launches with fewer row pairs are split
+constexpr int64_t kSplitTarget = 2048;  // slice workgroups to aim for
 
 bool sizes_ok(int64_t B, int32_t K, int32_t G, int32_t V) {
   if (B < 1 || K < 1 || G < 1 || V < 1) return false;
@@ -60,6 +65,8 @@ Layout layout(int64_t B, int32_t K, int32_t G, int32_t V, int64_t np = 0, int64_
   off = align_up(off + (size_t)B * K * sizeof(int32_t));
   L.alive = off;
   off = align_up(off + (size_t)B * sizeof(uint32_t));
+  L.part = off;
+  off = align_up(off + (size_t)kPartCap * sizeof(PartStats));
   L.pstat = off;
   off = align_up(off + (size_t)(np + nq) * sizeof(PoolStat));
   L.flags = off;
@@ -146,6 +153,8 @@ struct Batch {
   int eos;
   int32_t *mlen;
   uint32_t *alive;
+  PartStats *part;
+  bool vec;  // 16-byte loads
   int32_t *selected, *accept_len, *next_token;
   float *scores, *alpha, *beta;
   RowStats *stats;
@@ -162,6 +171,9 @@ struct Batch {
     if (launch(__VA_ARGS__) != hipSuccess) return SVD_EHIP;         \
     (tm).end(rec_, (kid), (stream));                                \
   } while (0)
+
+// Batches below this size settle overflowed draw segments in the pick.
+constexpr int64_t kInlineFixBatch = 64;
 
 // Positions per chunk when one draft per prefix is streamed up to its first
 // rejection: enough workgroups per launch to fill the GPU about once.
@@ -208,7 +220,39 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   }
   // the positions [j0, j0 + jn) of every draft
   auto stream_rows = [&](int j0, int jn, const uint32_t *alive) -> int {
-    const dim3 grid((unsigned)(a.B * a.K * jn));
+    const int64_t rows = a.B * a.K * jn;
+    int S = 1, slice = a.V;
+    if (rows < kSplitRows) {
+      const int unit = a.vec ? E::kPerVec : 1;  // elements per load
+      const int64_t units = a.V / unit;
+      const int64_t most = std::max<int64_t>(1, units / (2 * kSplitBlock));
+      const int64_t want = std::min<int64_t>((kSplitTarget + rows - 1) / rows, kPartCap / rows);
+      const int64_t s_try = std::max<int64_t>(1, std::min(most, want));
+      slice = (int)((units + s_try - 1) / s_try) * unit;
+      S = (a.V + slice - 1) / slice;
+    }
+    if (S > 1) {
+      const dim3 grid((unsigned)(rows * S));
+      if (a.greedy)
+        SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats_split<E, kVec, true>, grid,
+                   dim3(kSplitBlock), s, a.p, a.q, a.G, a.V, a.cp, a.cq, S, slice, mlen, alive, j0,
+                   jn, a.part);
+      else
+        SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats_split<E, kVec, false>, grid,
+                   dim3(kSplitBlock), s, a.p, a.q, a.G, a.V, a.cp, a.cq, S, slice, mlen, alive, j0,
+                   jn, a.part);
+      const dim3 gc((unsigned)((rows * 64 + kBlock - 1) / kBlock));  // a wave per row
+      if (a.greedy)
+        SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_rowstats_combine<E, true>, gc, dim3(kBlock), s,
+                   a.p, a.q, a.drafts, rows, a.G, a.V, a.cp, a.cq, S, mlen, alive, j0, jn,
+                   (const PartStats *)a.part, a.stats, a.alpha_ws, a.alpha);
+      else
+        SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_rowstats_combine<E, false>, gc, dim3(kBlock), s,
+                   a.p, a.q, a.drafts, rows, a.G, a.V, a.cp, a.cq, S, mlen, alive, j0, jn,
+                   (const PartStats *)a.part, a.stats, a.alpha_ws, a.alpha);
+      return SVD_OK;
+    }
+    const dim3 grid((unsigned)rows);
     if (a.greedy)
       SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, true>, grid, dim3(kRowBlock), s,
                  a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, a.stats, a.alpha_ws, a.alpha, mlen,
@@ -257,14 +301,18 @@ int enqueue_draw(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PASS, s, kr_draw_pass<E, kVec>, dim3(nbs), dim3(kBlock), s,
              a.p, a.q, a.ix, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
              (const DrawDesc *)a.desc, a.segs, a.uncs);
-  if (!a.greedy)  // only residuals max(0, p - q) can leave uncertain tokens
+  // only residuals max(0, p - q) can leave uncertain tokens; a small batch
+  // settles overflowed segments in the pick rather than in a launch of its own
+  const bool inline_fix = a.B < kInlineFixBatch;
+  if (!a.greedy && !inline_fix)
     SVD_LAUNCH(tm, SVD_KERNEL_DRAW_FIX, s, kr_draw_fix<E, kVec>, dim3(nbs), dim3(kBlock), s, a.p,
                a.q, a.ix, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
                (const DrawDesc *)a.desc, (const DrawSeg *)a.segs, a.mass);
   SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PICK, s, kr_draw_pick<E, kVec>, dim3(nb), dim3(kBlock), s, a.p,
              a.q, a.ix, a.K, a.G, a.V, a.nseg, a.tp, a.tq, a.seed, a.row_base,
              (const RowStats *)a.stats, (const DrawDesc *)a.desc, (const DrawSeg *)a.segs,
-             (const DrawUnc *)a.uncs, a.mass, a.selected, a.accept_len, a.next_token);
+             (const DrawUnc *)a.uncs, a.mass, a.selected, a.accept_len, a.next_token,
+             (int)inline_fix);
   return SVD_OK;
 }
 
@@ -320,6 +368,8 @@ int run(const Call &c) {
   a.gamma_b = c.gamma_b;
   a.eos = c.windowed ? c.eos : -1;
   a.mlen = reinterpret_cast<int32_t *>(ws + Lo.mlen);
+  a.part = reinterpret_cast<PartStats *>(ws + Lo.part);
+  a.vec = kVec;
   a.alive = reinterpret_cast<uint32_t *>(ws + Lo.alive);
   a.pstat = reinterpret_cast<PoolStat *>(ws + Lo.pstat);
   a.flags = reinterpret_cast<uint32_t *>(ws + Lo.flags);

@@ -85,13 +85,15 @@ def test_many_prefixes_flag_rates(orc):
     assert rep.flag_rate() < 1e-3
 
 
-def test_residual_inside_the_margin_everywhere(orc):
+@pytest.mark.parametrize("B", [8, 80])
+def test_residual_inside_the_margin_everywhere(orc, B):
     # q equals p except at the drafted token, raised by 2: every other token has
     # p_v / q_v = S_q / S_p, within the classification margin of 1, so every
     # segment's list of uncertain tokens overflows and is recomputed exactly
+    # (in the pick for a small batch, by the fix kernel for a large one)
     svd = require_gpu()
     import torch
-    B, G, V = 8, 3, 20000
+    G, V = 3, 20000
     gen_ = torch.Generator(device="cuda").manual_seed(77)
     zp = torch.randn((B, 1, G + 1, V), generator=gen_, device="cuda") * 2.0
     zq = zp[:, :, :G].clone()
@@ -100,7 +102,7 @@ def test_residual_inside_the_margin_everywhere(orc):
     d = {"p": zp.contiguous(), "q": zq.contiguous(), "drafts": x.contiguous()}
     g = run_select(svd, d, 1.0, 5)
     say("accept lengths", g["accept_len"])
-    assert (g["accept_len"] < G).sum() >= 4
+    assert (g["accept_len"] < G).sum() >= B // 2
     rep = compare(orc, *host_inputs(d), g, 1.0, 1.0, 5)
     say(rep.summary())
     assert rep.ok(), rep.failures
