@@ -24,7 +24,7 @@
 //   exact tie), backpointers in LDS, paths rebuilt at the end.
 #pragma once
 
-#include "kr_rowstats.hpp"
+#include "kr_rowstats.hpp"  // row_ms helpers, kSplitBlock
 
 namespace svd {
 
@@ -32,6 +32,7 @@ constexpr int kCpsMax = 16;      // candidates per position, at most
 constexpr int kCpsBeam = 8;      // beam width, at most
 constexpr int kCpsMaxG = 1024;   // positions of a beam search, at most
 constexpr int kNoIndex = 0x7fffffff;
+constexpr int kBeamChunk = 16;   // positions of lattice data a beam loads at once
 
 // (va, ia) comes before (vb, ib)
 __device__ __forceinline__ bool ahead(float va, int ia, float vb, int ib) {
@@ -102,77 +103,107 @@ __device__ __forceinline__ void wave_pop16(float (&lv)[N], int (&li)[N], float &
 enum : uint32_t { kRowInvalid = 1u, kRowEosTop = 2u };
 
 constexpr int kCandCap = 512;  // LDS list of tokens at or above the threshold
+constexpr int kLatticeMaxSlices = 64;  // slices of one row (one per lane of the merge)
 
 // visit the logits of a row with kRowBlock threads: f(index, value)
-template <typename E, bool kVec, typename F>
-__device__ __forceinline__ void visit_row(const typename E::elem *z, int V, F &&f) {
+// Visit z[0, n) with NT threads: f(index, value); kLatticeUnroll 16-byte
+// loads in flight per thread on the vector path.
+constexpr int kLatticeUnroll = 4;
+
+template <typename E, bool kVec, int NT, typename F>
+__device__ __forceinline__ void visit_row(const typename E::elem *z, int n, F &&f) {
   const int tid = threadIdx.x;
   if constexpr (kVec) {
-    constexpr int P = E::kPerVec;
+    constexpr int P = E::kPerVec, U = kLatticeUnroll;
     const vec16 *vz = reinterpret_cast<const vec16 *>(z);
-    for (int i = tid; i < V / P; i += kRowBlock) {
+    const int nv = n / P;
+    int i = tid;
+    for (; i + (U - 1) * NT < nv; i += U * NT) {
+      vec16 w[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) w[u] = vz[i + u * NT];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float x[P];
+        E::unpack(w[u], x);
+#pragma unroll
+        for (int e = 0; e < P; ++e) f((i + u * NT) * P + e, x[e]);
+      }
+    }
+    for (; i < nv; i += NT) {
       float x[P];
       E::unpack(vz[i], x);
 #pragma unroll
       for (int e = 0; e < P; ++e) f(i * P + e, x[e]);
     }
   } else {
-    for (int i = tid; i < V; i += kRowBlock) f(i, E::at(z, i));
+    for (int i = tid; i < n; i += NT) f(i, E::at(z, i));
   }
 }
 
-template <typename E, bool kVec>
-__global__ __launch_bounds__(kRowBlock) void kr_lattice(
-    const typename E::elem *__restrict__ q, int V, float c, float tau, int m_max, int eos,
-    int32_t *__restrict__ cand, float *__restrict__ cand_logp, int32_t *__restrict__ n_cand,
-    uint32_t *__restrict__ flags) {
-  constexpr int NW = kRowBlock / 64;
-  __shared__ float lds[2 * NW];
+// The 16 best (logit, index) pairs of z[lo, hi) and the slice's (max, sum),
+// by NT threads.  Results: (m, s) and, in lanes 0..15 of wave 0, the r-th best
+// pair in (bv, bi); other threads return with undefined values.
+template <typename E, bool kVec, int NT>
+__device__ __forceinline__ void lattice_slice(const typename E::elem *row, int lo, int hi, float c,
+                                              float &m_out, float &s_out, float &bv, int &bi) {
+  constexpr int NW = NT / 64;
+  __shared__ float lds[2 * NW + 2];
   __shared__ float wv[NW * kCpsMax];
   __shared__ int wi[NW * kCpsMax];
   __shared__ float cv[kCandCap];
   __shared__ int cix[kCandCap];
   __shared__ int n_found;
   __shared__ float thr_s;
-  const int64_t row = blockIdx.x;  // b * G + j
-  const typename E::elem *z = q + row * (int64_t)V;
+  const typename E::elem *z = row + lo;  // 16-byte aligned when kVec
+  const int n = hi - lo;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
-  // 1. one streaming pass: (max, sum) of the row and this thread's largest logit
+  // 1. one streaming pass: (max, sum) and this thread's largest logit
   float m = kNegInf, s = 0.0f, tmax = kNegInf;
   int tidx = kNoIndex;
   if constexpr (kVec) {
-    constexpr int P = E::kPerVec;
+    constexpr int P = E::kPerVec, U = kLatticeUnroll;
     const vec16 *vz = reinterpret_cast<const vec16 *>(z);
-    for (int i = tid; i < V / P; i += kRowBlock) {
+    const int nv = n / P;
+    auto fold = [&](const vec16 &wv16, int i) {
       float x[P];
-      E::unpack(stream_load(vz + i), x);
+      E::unpack(wv16, x);
       ms_fold<P>(m, s, x, c);
 #pragma unroll
       for (int e = 0; e < P; ++e)
-        if (ahead(x[e], i * P + e, tmax, tidx)) {
+        if (ahead(x[e], lo + i * P + e, tmax, tidx)) {
           tmax = x[e];
-          tidx = i * P + e;
+          tidx = lo + i * P + e;
         }
+    };
+    int i = tid;
+    for (; i + (U - 1) * NT < nv; i += U * NT) {
+      vec16 w[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) w[u] = vz[i + u * NT];  // kept for the second pass: cached
+#pragma unroll
+      for (int u = 0; u < U; ++u) fold(w[u], i + u * NT);
     }
+    for (; i < nv; i += NT) fold(vz[i], i);
   } else {
-    for (int i = tid; i < V; i += kRowBlock) {
+    for (int i = tid; i < n; i += NT) {
       float x = E::at(z, i);
       ms_fold<1>(m, s, &x, c);
-      if (ahead(x, i, tmax, tidx)) {
+      if (ahead(x, lo + i, tmax, tidx)) {
         tmax = x;
-        tidx = i;
+        tidx = lo + i;
       }
     }
   }
   block_ms<NW>(m, s, c, lds);  // valid in thread 0
   if (tid == 0) {
-    lds[0] = m;
-    lds[1] = s;
+    lds[2 * NW] = m;
+    lds[2 * NW + 1] = s;
     n_found = 0;
   }
-  // 2. the 16th largest of the threads' maxima bounds the row's 16th largest
-  //    logit from below: every one of the row's 16 best is at least that
+  // 2. the 16th largest of the threads' maxima bounds the slice's 16th largest
+  //    logit from below: every one of its 16 best is at least that
   {
     float lv[1] = {tmax};
     int li[1] = {tidx};
@@ -186,16 +217,18 @@ __global__ __launch_bounds__(kRowBlock) void kr_lattice(
   }
   __syncthreads();
   if (w == 0) {
-    float lv[4];
-    int li[4];
+    constexpr int PER = (NW * kCpsMax + 63) / 64;  // entries per lane
+    float lv[PER];
+    int li[PER];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      lv[t] = wv[4 * lane + t];
-      li[t] = wi[4 * lane + t];
+    for (int t = 0; t < PER; ++t) {
+      const int k = PER * lane + t;  // consecutive entries of one wave's sorted list
+      lv[t] = k < NW * kCpsMax ? wv[k] : kNegInf;
+      li[t] = k < NW * kCpsMax ? wi[k] : kNoIndex;
     }
     float v16;
     int i16;
-    wave_pop16<4>(lv, li, v16, i16);
+    wave_pop16<PER>(lv, li, v16, i16);
     const float t16 = __shfl(v16, kCpsMax - 1, 64);
     const int n16 = __shfl(i16, kCpsMax - 1, 64);
     if (lane == 0) thr_s = n16 == kNoIndex ? kNegInf : t16;  // fewer than 16 tokens: all
@@ -203,19 +236,19 @@ __global__ __launch_bounds__(kRowBlock) void kr_lattice(
   __syncthreads();
   // 3. second pass: every token at or above the bound into an LDS list
   const float thr = thr_s;
-  visit_row<E, kVec>(z, V, [&](int i, float x) {
+  visit_row<E, kVec, NT>(z, n, [&](int i, float x) {
     if (x >= thr) {
       const int k = atomicAdd(&n_found, 1);
       if (k < kCandCap) {
         cv[k] = x;
-        cix[k] = i;
+        cix[k] = lo + i;
       }
     }
   });
   __syncthreads();
   const int nf = n_found;
   if (nf > kCandCap) {
-    // many tokens tie at the bound: sorted per-thread lists over the whole row
+    // many tokens tie at the bound: sorted per-thread lists over the whole slice
     float tv[kCpsMax];
     int ti[kCpsMax];
 #pragma unroll
@@ -223,7 +256,7 @@ __global__ __launch_bounds__(kRowBlock) void kr_lattice(
       tv[k] = kNegInf;
       ti[k] = kNoIndex;
     }
-    visit_row<E, kVec>(z, V, [&](int i, float x) { top_insert(tv, ti, x, i); });
+    visit_row<E, kVec, NT>(z, n, [&](int i, float x) { top_insert(tv, ti, x, lo + i); });
     float v16;
     int i16;
     wave_pop16<kCpsMax>(tv, ti, v16, i16);
@@ -233,19 +266,20 @@ __global__ __launch_bounds__(kRowBlock) void kr_lattice(
     }
     __syncthreads();
   }
+  m_out = lds[2 * NW];
+  s_out = lds[2 * NW + 1];
   if (w != 0) return;
-  const float rm = lds[0], rs = lds[1];
-  float bv;
-  int bi;
   if (nf > kCandCap) {
-    float lv[4];
-    int li[4];
+    constexpr int PER = (NW * kCpsMax + 63) / 64;
+    float lv[PER];
+    int li[PER];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      lv[t] = wv[4 * lane + t];
-      li[t] = wi[4 * lane + t];
+    for (int t = 0; t < PER; ++t) {
+      const int k = PER * lane + t;
+      lv[t] = k < NW * kCpsMax ? wv[k] : kNegInf;
+      li[t] = k < NW * kCpsMax ? wi[k] : kNoIndex;
     }
-    wave_pop16<4>(lv, li, bv, bi);
+    wave_pop16<PER>(lv, li, bv, bi);
   } else {
     // lane l sorts the list entries l, l + 64, ... (at most 8), then the wave pops
     float lv[kCandCap / 64];
@@ -276,7 +310,18 @@ __global__ __launch_bounds__(kRowBlock) void kr_lattice(
     }
     wave_pop16<kCandCap / 64>(lv, li, bv, bi);
   }
-  // probabilities of the 16 best, their running sum in rank order, the cut at tau
+}
+
+// Wave 0 with the row's 16 best pairs (lane r holds the r-th in bv, bi) and its
+// (max, sum): probabilities, their running sum in rank order, the cut at tau,
+// the outputs of the row.
+__device__ __forceinline__ void lattice_finish(int64_t row, float rm, float rs, float bv, int bi,
+                                               float c, float tau, int m_max, int eos,
+                                               int32_t *__restrict__ cand,
+                                               float *__restrict__ cand_logp,
+                                               int32_t *__restrict__ n_cand,
+                                               uint32_t *__restrict__ flags) {
+  const int lane = threadIdx.x & 63;
   const bool real = lane < kCpsMax && bi != kNoIndex;
   const float lg2 = (bv - rm) * c - log2f(rs);  // log2 p
   float p = real ? exp2f(lg2) : 0.0f;
@@ -289,45 +334,127 @@ __global__ __launch_bounds__(kRowBlock) void kr_lattice(
   const bool reached = real && lane < m_max && cum >= tau;
   const uint64_t hit = __ballot(reached);
   const uint64_t avail = __ballot(real && lane < m_max);
-  const int n = hit ? __ffsll((unsigned long long)hit) : __popcll(avail);
+  const int n = hit ? __ffsll((unsigned long long)hit) : __popcll(avail);  // first rank reaching tau, + 1
   if (lane < m_max) {
     const int64_t o = row * m_max + lane;
     cand[o] = lane < n ? bi : -1;
     cand_logp[o] = lane < n ? lg2 * 0.6931471805599453f : kNegInf;
   }
+  const int b0 = __shfl(bi, 0, 64);
   if (lane == 0) {
     n_cand[row] = n;
     uint32_t f = 0u;
     if (rs != rs || rm == kNegInf) f |= kRowInvalid;
-    if (eos >= 0 && bi == eos) f |= kRowEosTop;
+    if (eos >= 0 && b0 == eos) f |= kRowEosTop;
     flags[row] = f;
   }
 }
 
+// one workgroup per drafter row
+template <typename E, bool kVec>
+__global__ __launch_bounds__(kRowBlock) void kr_lattice(
+    const typename E::elem *__restrict__ q, int V, float c, float tau, int m_max, int eos,
+    int32_t *__restrict__ cand, float *__restrict__ cand_logp, int32_t *__restrict__ n_cand,
+    uint32_t *__restrict__ flags) {
+  const int64_t row = blockIdx.x;  // b * G + j
+  float m, s, bv;
+  int bi;
+  lattice_slice<E, kVec, kRowBlock>(q + row * (int64_t)V, 0, V, c, m, s, bv, bi);
+  if (threadIdx.x >= 64) return;
+  lattice_finish(row, m, s, bv, bi, c, tau, m_max, eos, cand, cand_logp, n_cand, flags);
+}
+
+// Split rows, as for the row statistics: slice sl of row r in workgroup
+// r * S + sl, a record of the slice's (max, sum) and 16 best pairs, then one
+// wave per row merges the S records.
+struct LatticePart {
+  float m, s;
+  float v[kCpsMax];
+  int i[kCpsMax];
+};
+
+template <typename E, bool kVec>
+__global__ __launch_bounds__(kSplitBlock) void kr_lattice_split(
+    const typename E::elem *__restrict__ q, int V, float c, int S, int slice,
+    LatticePart *__restrict__ part) {
+  const int64_t r = blockIdx.x / S;
+  const int sl = (int)(blockIdx.x - r * S);
+  const int lo = sl * slice, hi = min(V, lo + slice);  // slice: whole vectors
+  float m, s, bv;
+  int bi;
+  lattice_slice<E, kVec, kSplitBlock>(q + r * (int64_t)V, lo, hi, c, m, s, bv, bi);
+  if (threadIdx.x >= kCpsMax) return;
+  LatticePart *o = part + blockIdx.x;
+  if (threadIdx.x == 0) {
+    o->m = m;
+    o->s = s;
+  }
+  o->v[threadIdx.x] = bv;
+  o->i[threadIdx.x] = bi;
+}
+
+__global__ __launch_bounds__(kBlock) void kr_lattice_combine(
+    int64_t rows, float c, float tau, int m_max, int eos, int S,
+    const LatticePart *__restrict__ part, int32_t *__restrict__ cand,
+    float *__restrict__ cand_logp, int32_t *__restrict__ n_cand, uint32_t *__restrict__ flags) {
+  const int64_t row = ((int64_t)blockIdx.x * kBlock + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;  // whole waves
+  // lane sl holds slice sl's sorted list (S <= 64)
+  float lv[kCpsMax];
+  int li[kCpsMax];
+  float m = kNegInf, s = 0.0f;
+  if (lane < S) {
+    const LatticePart *pp = part + row * S + lane;
+    m = pp->m;
+    s = pp->s;
+#pragma unroll
+    for (int k = 0; k < kCpsMax; ++k) {
+      lv[k] = pp->v[k];
+      li[k] = pp->i[k];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kCpsMax; ++k) {
+      lv[k] = kNegInf;
+      li[k] = kNoIndex;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1)
+    ms_merge(m, s, __shfl_xor(m, off, 64), __shfl_xor(s, off, 64), c);
+  float bv;
+  int bi;
+  wave_pop16<kCpsMax>(lv, li, bv, bi);
+  lattice_finish(row, m, s, bv, bi, c, tau, m_max, eos, cand, cand_logp, n_cand, flags);
+}
+
+// One wave per prefix: the first row flagged invalid or with EOS on top.
 __global__ __launch_bounds__(kBlock) void kr_lattice_len(const uint32_t *__restrict__ flags,
                                                          int64_t B, int G, int m_max,
                                                          int32_t *__restrict__ cand,
                                                          float *__restrict__ cand_logp,
                                                          int32_t *__restrict__ n_cand,
                                                          int32_t *__restrict__ len) {
-  const int64_t b = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (b >= B) return;
-  int L = G;
-  bool eos_end = false;
-  for (int j = 0; j < G; ++j) {
-    const uint32_t f = flags[b * G + j];
-    if (f & kRowInvalid) {
-      L = -1;
-      break;
-    }
-    if (f & kRowEosTop) {
-      L = j + 1;
-      eos_end = true;
-      break;
+  const int64_t b = ((int64_t)blockIdx.x * kBlock + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (b >= B) return;  // whole waves
+  int first = G;  // first flagged row
+  uint32_t ff = 0u;
+  for (int j0 = 0; j0 < G && first == G; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t f = j < G ? flags[b * G + j] : 0u;
+    const uint64_t hit = __ballot(f != 0u);
+    if (hit) {
+      const int k = __ffsll((unsigned long long)hit) - 1;
+      first = j0 + k;
+      ff = __shfl(f, k, 64);
     }
   }
-  len[b] = L;
-  for (int j = 0; j < G; ++j) {
+  const int L = first == G ? G : ((ff & kRowInvalid) ? -1 : first + 1);
+  const bool eos_end = first < G && !(ff & kRowInvalid);
+  if (lane == 0) len[b] = L;
+  for (int j = lane; j < G; j += 64) {
     const int64_t o = b * G + j;
     int keep = n_cand[o];
     if (L < 0 || j >= L) keep = 0;
@@ -337,6 +464,24 @@ __global__ __launch_bounds__(kBlock) void kr_lattice_len(const uint32_t *__restr
     for (int i = keep; i < m_max; ++i) {
       cand[o * m_max + i] = -1;
       cand_logp[o * m_max + i] = kNegInf;
+    }
+  }
+}
+
+// n floats from global memory into LDS by one wave, 16 loads in flight per lane
+__device__ __forceinline__ void copy_to_lds(float *dst, const float *__restrict__ src, int n) {
+  const int lane = threadIdx.x & 63;
+  for (int t0 = 0; t0 < n; t0 += 64 * 16) {
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int t = t0 + k * 64 + lane;
+      v[k] = t < n ? src[t] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int t = t0 + k * 64 + lane;
+      if (t < n) dst[t] = v[k];
     }
   }
 }
@@ -361,8 +506,13 @@ __global__ __launch_bounds__(64) void kr_cps_beam(
     int32_t *__restrict__ paths, float *__restrict__ path_score, int32_t *__restrict__ path_len) {
   __shared__ uint8_t bp[kCpsMaxG][kCpsBeam];  // parent rank of rank r at position j
   __shared__ uint8_t ci[kCpsMaxG][kCpsBeam];  // candidate rank of rank r at position j
+  __shared__ uint8_t rk[kCpsMaxG][kCpsBeam];  // final path r's candidate rank at position j
   __shared__ double sc[kCpsBeam], nsc[kCpsBeam];
   __shared__ int pc[kCpsBeam], npc[kCpsBeam];
+  // the lattice of kBeamChunk positions at a time, loaded together
+  __shared__ int nc_s[kBeamChunk];
+  __shared__ float lp_s[kBeamChunk * kCpsMax];
+  __shared__ float fl_s[kBeamChunk * kCpsMax * kCpsMax];
   const int64_t b = blockIdx.x;
   const int lane = threadIdx.x;
   int L = len[b];
@@ -382,15 +532,23 @@ __global__ __launch_bounds__(64) void kr_cps_beam(
   }
   __syncthreads();
   for (int j = 0; ok && j < L; ++j) {
-    const int64_t o = b * G + j;
-    const int nc = n_cand[o];
+    const int jj = j % kBeamChunk;
+    if (jj == 0) {  // the next chunk of positions into LDS
+      const int n = min(kBeamChunk, L - j);
+      const int64_t o0 = b * G + j;
+      if (lane < n) nc_s[lane] = n_cand[o0 + lane];
+      copy_to_lds(lp_s, cand_logp + o0 * m_max, n * m_max);
+      if (fluency) copy_to_lds(fl_s, fluency + o0 * m_max * m_max, n * m_max * m_max);
+      __syncthreads();
+    }
+    const int nc = nc_s[jj];
     const int ne = nb * nc;
     double s0 = -INFINITY, s1 = -INFINITY;
     auto score = [&](int e) -> double {
       const int p = e / nc, i = e - p * nc;
       const int prev = j == 0 ? 0 : pc[p];
-      const double f = fluency ? (double)fluency[(o * m_max + prev) * m_max + i] : 0.0;
-      return sc[p] + (double)cand_logp[o * m_max + i] + (double)lambda * f;
+      const double f = fluency ? (double)fl_s[(jj * m_max + prev) * m_max + i] : 0.0;
+      return sc[p] + (double)lp_s[jj * m_max + i] + (double)lambda * f;
     };
     const int e0 = lane, e1 = lane + 64;
     if (e0 < ne) s0 = score(e0);
@@ -428,20 +586,25 @@ __global__ __launch_bounds__(64) void kr_cps_beam(
     nb = keep;
     __syncthreads();
   }
-  // rebuild the paths from the backpointers
-  if (lane < beam) {
-    int32_t *out = paths + (b * beam + lane) * (int64_t)G;
-    const bool live = ok && lane < nb;
+  // rebuild the paths: each live rank follows its backpointers in LDS and
+  // records its candidate ranks, then the whole wave gathers the tokens
+  const int live_n = ok ? nb : 0;
+  if (lane < live_n) {
     int rr = lane;
-    for (int j = G - 1; j >= 0; --j) {
-      int32_t tok = -1;
-      if (live && j < L) {
-        const int i = ci[j][rr];
-        tok = cand[(b * G + j) * m_max + i];
-        rr = bp[j][rr];
-      }
-      out[j] = tok;
+    for (int j = L - 1; j >= 0; --j) {
+      rk[j][lane] = ci[j][rr];
+      rr = bp[j][rr];
     }
+  }
+  __syncthreads();
+  for (int t = lane; t < beam * G; t += 64) {
+    const int r = t / G, j = t - r * G;
+    int32_t tok = -1;
+    if (r < live_n && j < L) tok = cand[(b * G + j) * m_max + rk[j][r]];
+    paths[(b * beam + r) * (int64_t)G + j] = tok;
+  }
+  if (lane < beam) {
+    const bool live = lane < live_n;
     path_score[b * beam + lane] = live ? (float)sc[lane] : kNegInf;
     path_len[b * beam + lane] = live ? L : 0;
   }

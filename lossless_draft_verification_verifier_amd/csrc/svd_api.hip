@@ -172,6 +172,10 @@ struct Batch {
     (tm).end(rec_, (kid), (stream));                                \
   } while (0)
 
+// Lattice launches of fewer rows are split (a whole row per workgroup keeps
+// up four loads in flight per thread and does its selection once).
+constexpr int64_t kLatticeSplitRows = 128;
+
 // Batches below this size settle overflowed draw segments in the pick.
 constexpr int64_t kInlineFixBatch = 64;
 
@@ -551,7 +555,8 @@ int svd_verify_window(svd_rule_t rule, const void *p_logits, const void *q_logit
 
 size_t svd_cps_workspace_bytes(int64_t B, int32_t G) {
   if (B < 1 || G < 1 || G > SVD_MAX_GAMMA || B >= ((int64_t)1 << 31) / G) return 0;
-  return align_up((size_t)B * G * sizeof(uint32_t));
+  // row flags, then the records of split rows
+  return align_up((size_t)B * G * sizeof(uint32_t)) + (size_t)kPartCap * sizeof(LatticePart);
 }
 
 int svd_cps_lattice(const void *q_logits, svd_dtype_t dtype, int64_t B, int32_t G, int32_t V,
@@ -568,13 +573,50 @@ int svd_cps_lattice(const void *q_logits, svd_dtype_t dtype, int64_t B, int32_t 
   if (workspace_bytes < need) return SVD_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   uint32_t *flags = static_cast<uint32_t *>(workspace);
+  LatticePart *part = reinterpret_cast<LatticePart *>(static_cast<char *>(workspace) +
+                                                      align_up((size_t)B * G * sizeof(uint32_t)));
   const float c = (float)(1.4426950408889634 / (double)temp_q);
   const size_t es = dtype == SVD_F32 ? 4 : 2;
   const bool vec = ((size_t)V * es) % 16 == 0 && ((uintptr_t)q_logits) % 16 == 0;
   const dim3 grid((unsigned)(B * G));
   const int e = eos < 0 ? -1 : eos;
   CallTimer tm;
-  if (dtype == SVD_BF16) {
+  // few rows: slices of whole vectors, then one wave per row merges them
+  const int64_t rows = B * G;
+  int S = 1, slice = V;
+  if (rows < kLatticeSplitRows) {
+    const int unit = vec ? (int)(16 / es) : 1;
+    const int64_t units = V / unit;
+    const int64_t most = std::min<int64_t>(std::max<int64_t>(1, units / (2 * kSplitBlock)),
+                                           kLatticeMaxSlices);
+    const int64_t want = std::min<int64_t>((kSplitTarget + rows - 1) / rows, kPartCap / rows);
+    const int64_t s_try = std::max<int64_t>(1, std::min(most, want));
+    slice = (int)((units + s_try - 1) / s_try) * unit;
+    S = (V + slice - 1) / slice;
+  }
+  if (S > 1) {
+    const dim3 gs((unsigned)(rows * S));
+    if (dtype == SVD_BF16) {
+      const auto *q = static_cast<const BF16::elem *>(q_logits);
+      if (vec)
+        SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice_split<BF16, true>, gs, dim3(kSplitBlock),
+                   s, q, V, c, S, slice, part);
+      else
+        SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice_split<BF16, false>, gs,
+                   dim3(kSplitBlock), s, q, V, c, S, slice, part);
+    } else {
+      const auto *q = static_cast<const F32::elem *>(q_logits);
+      if (vec)
+        SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice_split<F32, true>, gs, dim3(kSplitBlock),
+                   s, q, V, c, S, slice, part);
+      else
+        SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice_split<F32, false>, gs, dim3(kSplitBlock),
+                   s, q, V, c, S, slice, part);
+    }
+    SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_lattice_combine,
+               dim3((unsigned)((rows * 64 + kBlock - 1) / kBlock)), dim3(kBlock), s, rows, c, tau,
+               m_max, e, S, (const LatticePart *)part, cand, cand_logp, n_cand, flags);
+  } else if (dtype == SVD_BF16) {
     const auto *q = static_cast<const BF16::elem *>(q_logits);
     if (vec)
       SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<BF16, true>, grid, dim3(kRowBlock), s, q, V,
@@ -591,7 +633,8 @@ int svd_cps_lattice(const void *q_logits, svd_dtype_t dtype, int64_t B, int32_t 
       SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<F32, false>, grid, dim3(kRowBlock), s, q, V,
                  c, tau, m_max, e, cand, cand_logp, n_cand, flags);
   }
-  SVD_LAUNCH(tm, SVD_KERNEL_LATTICE_LEN, s, kr_lattice_len, dim3((unsigned)((B + kBlock - 1) / kBlock)),
+  SVD_LAUNCH(tm, SVD_KERNEL_LATTICE_LEN, s, kr_lattice_len,
+             dim3((unsigned)((B * 64 + kBlock - 1) / kBlock)),
              dim3(kBlock), s, (const uint32_t *)flags, B, G, m_max, cand, cand_logp, n_cand, len);
   return SVD_OK;
 }

@@ -152,3 +152,17 @@ def test_lattice_with_many_ties_at_the_top():
     o = oracle.cps_lattice(hz, tau=0.99, m_max=16)
     _check_lattice(g, o, 16)
     assert list(g["cand"][0, 0, :3]) == [100, 101, 102]
+
+
+def test_split_rows_with_ties_inside_one_slice():
+    # few rows: each row is cut into slices; 600 tied tokens fill one slice's
+    # candidate list, whose sorted per-thread lists take over
+    svd = require_gpu()
+    q, hz = _rows(13, 1, 2, 40000, "f32")
+    hz = hz.copy()
+    hz[0, 0, 5000:5600] = 9.0
+    q = torch.from_numpy(hz).cuda()
+    g = host(svd.cps_lattice(q, tau=0.99, m_max=16))
+    o = oracle.cps_lattice(hz, tau=0.99, m_max=16)
+    _check_lattice(g, o, 16)
+    assert list(g["cand"][0, 0, :2]) == [5000, 5001]
