@@ -298,7 +298,7 @@ enum {
   SVD_KERNEL_ROWSTATS = 0,   /* row statistics + alpha (streams every scored row pair) */
   SVD_KERNEL_SELECT = 1,     /* streak scores, argmax, first rejection                 */
   SVD_KERNEL_DRAW_PASS = 2,  /* fp64 pass over the drawn row pair                       */
-  SVD_KERNEL_DRAW_FIX = 3,   /* exact mass of segments with many near-equal p/q ratios  */
+  SVD_KERNEL_DRAW_FIX = 3,   /* reserved (no launch: the pick settles overflowed lists) */
   SVD_KERNEL_DRAW_PICK = 4,  /* fp64 masses and inverse CDF                             */
   SVD_KERNEL_BETA = 5,       /* optional overlap mass                                   */
   SVD_KERNEL_MARK = 6,       /* shared rows: flags of the pool rows read               */

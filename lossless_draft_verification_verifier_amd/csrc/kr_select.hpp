@@ -34,12 +34,18 @@ struct Window {
 
 // Run by the 64 lanes of one wave (lane = threadIdx.x & 63); every lane gets
 // the decision.  Lane 0 writes selected / accept_len (and -1 next_token for an
-// invalid prefix), lane k writes scores[k].  p_index (nullable): the verifier
-// rows come from a pool of np rows, and a bonus row outside it makes the
-// prefix invalid.
+// invalid prefix), lane k writes scores[k].  p_index / q_index (nullable): the
+// rows come from pools, p of np rows, and a bonus row outside it makes the
+// prefix invalid.  The returned record names the rows the draw reads and,
+// for a residual draw, their statistics; the loads that settle it are issued
+// together with those of the acceptance test.
+constexpr int kSelChunk = 16;  // alpha loads in flight per lane in the scores
+
 __device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alpha_ws,
+                                                  const RowStats *__restrict__ stats,
                                                   const int32_t *__restrict__ drafts, bool greedy,
-                                                  const int32_t *__restrict__ p_index, int64_t np,
+                                                  const int32_t *__restrict__ p_index,
+                                                  const int32_t *__restrict__ q_index, int64_t np,
                                                   const Window win, int K, int gamma,
                                                   uint64_t seed, uint64_t row_base, int64_t b,
                                                   int32_t *__restrict__ selected,
@@ -57,11 +63,18 @@ __device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alph
     bad |= m < 1;
     double prod = 1.0;
     S = 0.0;
-    for (int j = 0; j < m; ++j) {
-      const float aj = alpha_ws[base + j];
-      bad |= (aj != aj);
-      prod *= (double)aj;
-      S += prod;
+    for (int j0 = 0; j0 < m; j0 += kSelChunk) {
+      float a[kSelChunk];
+#pragma unroll
+      for (int i = 0; i < kSelChunk; ++i) a[i] = (j0 + i < m) ? alpha_ws[base + j0 + i] : 1.0f;
+#pragma unroll
+      for (int i = 0; i < kSelChunk; ++i) {
+        if (j0 + i < m) {
+          bad |= (a[i] != a[i]);
+          prod *= (double)a[i];
+          S += prod;
+        }
+      }
     }
     if (scores) scores[b * K + lane] = (float)S;
   }
@@ -82,31 +95,55 @@ __device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alph
   }
 
   const int m = invalid ? 0 : usable(bk);
+  const int64_t row_k = (int64_t)b * K + bk;  // the kept draft's rows
+  const int64_t base = row_k * gamma;
   int L = m;
+  RowStats st{0.0f, 1.0f, 0.0f, 1.0f};
+  int xL = -1;
+  int64_t prow = 0, qrow = 0;
   if (!invalid) {
-    const int64_t base = ((int64_t)b * K + bk) * gamma;
     const uint64_t row = row_base + (uint64_t)b;
     for (int j0 = 0; j0 < m; j0 += 64) {
       const int j = j0 + lane;
       bool rej = false;
-      if (j < m)
-        rej = !(counter_uniform(seed, row, (uint64_t)j, kAccept) < (double)alpha_ws[base + j]);
+      float aj = 0.0f;
+      RowStats sj{0.0f, 1.0f, 0.0f, 1.0f};
+      int xj = -1, pj = 0, qj = 0;
+      if (j < m) {
+        aj = alpha_ws[base + j];
+        if (greedy) xj = drafts[base + j];
+        else sj = stats[base + j];
+        if (p_index) pj = p_index[row_k * (gamma + 1) + j];
+        if (q_index && !greedy) qj = q_index[base + j];
+        rej = !(counter_uniform(seed, row, (uint64_t)j, kAccept) < (double)aj);
+      }
       const uint64_t mask = __ballot(rej);
       if (mask) {
-        L = j0 + __ffsll((unsigned long long)mask) - 1;
+        const int src = __ffsll((unsigned long long)mask) - 1;
+        L = j0 + src;
+        st = RowStats{__shfl(sj.mp, src, 64), __shfl(sj.sp, src, 64), __shfl(sj.mq, src, 64),
+                      __shfl(sj.sq, src, 64)};
+        xL = __shfl(xj, src, 64);
+        prow = p_index ? (int64_t)__shfl(pj, src, 64) : row_k * (gamma + 1) + L;
+        qrow = q_index ? (int64_t)__shfl(qj, src, 64) : base + L;
+        // streamed up to the first rejection only: its alpha is the one that can be NaN
+        const float aL = __shfl(aj, src, 64);
+        if (win.first_only) invalid = aL != aL;
         break;
       }
     }
-    // streamed up to the first rejection only: its alpha is the one that can be NaN
-    if (win.first_only && L < m) invalid = alpha_ws[base + L] != alpha_ws[base + L];
   }
 
   // an accepted window that ends in EOS commits without a draw
-  const bool eos_end = !invalid && L == m && win.eos >= 0 &&
-                       drafts[((int64_t)b * K + bk) * gamma + m - 1] == win.eos;
-  if (!invalid && !eos_end && L == m && p_index) {
-    const int32_t pi = p_index[((int64_t)b * K + bk) * (gamma + 1) + n];
-    invalid = pi < 0 || pi >= np;
+  const bool eos_end = !invalid && L == m && win.eos >= 0 && drafts[base + m - 1] == win.eos;
+  if (!invalid && !eos_end && L == m) {
+    if (p_index) {
+      const int32_t pi = p_index[row_k * (gamma + 1) + n];
+      invalid = pi < 0 || pi >= np;
+      prow = pi;
+    } else {
+      prow = row_k * (gamma + 1) + n;
+    }
   }
 
   if (lane == 0) {
@@ -120,22 +157,38 @@ __device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alph
       if (eos_end) next_token[b] = -2;
     }
   }
-  if (invalid || eos_end) return DrawDesc{0, 0, 0, 0, 0, -1};
-  if (L == m) return DrawDesc{bk, n, (int)kBonus, 1, 0, -1};
-  if (greedy)
-    return DrawDesc{bk, L, (int)kResidual, 1, 0, drafts[((int64_t)b * K + bk) * gamma + L]};
-  return DrawDesc{bk, L, (int)kResidual, 1, 1, -1};
+  DrawDesc d{};
+  d.excl = -1;
+  if (invalid || eos_end) return d;
+  d.valid = 1;
+  d.prow = prow;
+  if (L == m) {
+    d.pos = n;
+    d.purpose = (int)kBonus;
+    return d;
+  }
+  d.pos = L;
+  d.purpose = (int)kResidual;
+  if (greedy) {
+    d.excl = xL;
+    return d;
+  }
+  d.two = 1;
+  d.qrow = qrow;
+  d.st = st;
+  return d;
 }
 
 __global__ __launch_bounds__(64) void kr_select(
-    const float *__restrict__ alpha_ws, const int32_t *__restrict__ drafts, int greedy,
-    const int32_t *__restrict__ p_index, int64_t np, const Window win, int K, int gamma,
+    const float *__restrict__ alpha_ws, const RowStats *__restrict__ stats,
+    const int32_t *__restrict__ drafts, int greedy, const int32_t *__restrict__ p_index,
+    const int32_t *__restrict__ q_index, int64_t np, const Window win, int K, int gamma,
     uint64_t seed, uint64_t row_base, int32_t *__restrict__ selected,
     int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token,
     float *__restrict__ scores, DrawDesc *__restrict__ desc) {
-  const DrawDesc d = select_prefix(alpha_ws, drafts, greedy != 0, p_index, np, win, K, gamma,
-                                   seed, row_base, blockIdx.x, selected, accept_len, next_token,
-                                   scores);
+  const DrawDesc d = select_prefix(alpha_ws, stats, drafts, greedy != 0, p_index, q_index, np,
+                                   win, K, gamma, seed, row_base, blockIdx.x, selected,
+                                   accept_len, next_token, scores);
   if (threadIdx.x == 0) desc[blockIdx.x] = d;
 }
 

@@ -134,6 +134,13 @@ struct CallTimer {
   }
 };
 
+// Index tables of the shared-row layout ([B][K][gamma+1] and [B][K][gamma]);
+// null tables mean the dense layout.
+struct RowIndex {
+  const int32_t *p;
+  const int32_t *q;
+};
+
 // Everything the launch chain reads and writes.
 template <typename E>
 struct Batch {
@@ -175,9 +182,6 @@ struct Batch {
 // Lattice launches of fewer rows are split (a whole row per workgroup keeps
 // up four loads in flight per thread and does its selection once).
 constexpr int64_t kLatticeSplitRows = 128;
-
-// Batches below this size settle overflowed draw segments in the pick.
-constexpr int64_t kInlineFixBatch = 64;
 
 // Positions per chunk when one draft per prefix is streamed up to its first
 // rejection: enough workgroups per launch to fill the GPU about once.
@@ -297,26 +301,18 @@ int enqueue_draw(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   const unsigned nb = (unsigned)a.B;
   const unsigned nbs = (unsigned)(a.B * a.nseg);
   SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_select, dim3(nb), dim3(64), s,
-             (const float *)a.alpha_ws, a.drafts, (int)a.greedy, a.ix.p, a.np,
+             (const float *)a.alpha_ws, (const RowStats *)a.stats, a.drafts, (int)a.greedy,
+             a.ix.p, a.greedy ? nullptr : a.ix.q, a.np,
              Window{a.windowed ? (const int32_t *)a.mlen : nullptr, a.gamma_b, a.eos,
                     (int)a.early},
              a.K, a.G, a.seed, a.row_base, a.selected, a.accept_len, a.next_token, a.scores,
              a.desc);
   SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PASS, s, kr_draw_pass<E, kVec>, dim3(nbs), dim3(kBlock), s,
-             a.p, a.q, a.ix, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
-             (const DrawDesc *)a.desc, a.segs, a.uncs);
-  // only residuals max(0, p - q) can leave uncertain tokens; a small batch
-  // settles overflowed segments in the pick rather than in a launch of its own
-  const bool inline_fix = a.B < kInlineFixBatch;
-  if (!a.greedy && !inline_fix)
-    SVD_LAUNCH(tm, SVD_KERNEL_DRAW_FIX, s, kr_draw_fix<E, kVec>, dim3(nbs), dim3(kBlock), s, a.p,
-               a.q, a.ix, a.K, a.G, a.V, a.nseg, a.tp, a.tq, (const RowStats *)a.stats,
-               (const DrawDesc *)a.desc, (const DrawSeg *)a.segs, a.mass);
-  SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PICK, s, kr_draw_pick<E, kVec>, dim3(nb), dim3(kBlock), s, a.p,
-             a.q, a.ix, a.K, a.G, a.V, a.nseg, a.tp, a.tq, a.seed, a.row_base,
-             (const RowStats *)a.stats, (const DrawDesc *)a.desc, (const DrawSeg *)a.segs,
-             (const DrawUnc *)a.uncs, a.mass, a.selected, a.accept_len, a.next_token,
-             (int)inline_fix);
+             a.p, a.q, a.V, a.nseg, a.tp, a.tq, (const DrawDesc *)a.desc, a.segs, a.uncs);
+  SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PICK, s, kr_draw_pick<E, kVec>, dim3(nb), dim3(kPickBlock), s,
+             a.p, a.q, a.V, a.nseg, a.tp, a.tq, a.seed, a.row_base, (const DrawDesc *)a.desc,
+             (const DrawSeg *)a.segs, (const DrawUnc *)a.uncs, a.mass, a.selected, a.accept_len,
+             a.next_token);
   return SVD_OK;
 }
 

@@ -211,13 +211,16 @@ struct RowStats {      // one scored row pair
   float mq, sq;        // the same for the q row
 };
 
-struct DrawDesc {      // one prefix: which rows the draw reads
-  int k;               // kept draft
-  int pos;             // accepted length L (rejection) or gamma (bonus)
+struct DrawDesc {      // one prefix: what the draw reads, settled by the selection
+  int64_t prow;        // the drawn p row: row index into the p logits (or the p pool)
+  int64_t qrow;        // residual draws: the q row, likewise; 0 otherwise
+  RowStats st;         // residual draws: statistics of the drawn row pair
+  int pos;             // accepted length L (rejection) or the window (bonus)
   int purpose;         // kResidual or kBonus: the uniform's purpose
-  int valid;           // 0: prefix invalid, nothing to draw
-  int two;             // 1: residual max(0, p - q) of row pair (k, pos); 0: p row (k, pos)
+  int valid;           // 0: prefix invalid or committed without a draw
+  int two;             // 1: residual max(0, p - q) of the row pair; 0: p row alone
   int excl;            // p-row draw: a token of weight zero (the rejected one), or -1
+  int pad;
 };
 
 }  // namespace svd

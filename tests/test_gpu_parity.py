@@ -85,25 +85,89 @@ def test_many_prefixes_flag_rates(orc):
     assert rep.flag_rate() < 1e-3
 
 
-@pytest.mark.parametrize("B", [8, 80])
-def test_residual_inside_the_margin_everywhere(orc, B):
-    # q equals p except at the drafted token, raised by 2: every other token has
-    # p_v / q_v = S_q / S_p, within the classification margin of 1, so every
-    # segment's list of uncertain tokens overflows and is recomputed exactly
-    # (in the pick for a small batch, by the fix kernel for a large one)
-    svd = require_gpu()
+def _margin_case(B, seed):
+    # q equals p except at the drafted token (a median one), raised by 2, so
+    # most drafts are rejected at position 0 and S_q / S_p is within the
+    # classification margin of 1
     import torch
     G, V = 3, 20000
-    gen_ = torch.Generator(device="cuda").manual_seed(77)
+    gen_ = torch.Generator(device="cuda").manual_seed(seed)
     zp = torch.randn((B, 1, G + 1, V), generator=gen_, device="cuda") * 2.0
     zq = zp[:, :, :G].clone()
-    x = torch.argsort(zp[:, :, :G], dim=-1)[..., V // 2].to(torch.int32)  # a median token
+    x = torch.argsort(zp[:, :, :G], dim=-1)[..., V // 2].to(torch.int32)
     zq.scatter_add_(-1, x.long().unsqueeze(-1), torch.full((B, 1, G, 1), 2.0, device="cuda"))
-    d = {"p": zp.contiguous(), "q": zq.contiguous(), "drafts": x.contiguous()}
+    return G, {"p": zp.contiguous(), "q": zq.contiguous(), "drafts": x.contiguous()}
+
+
+@pytest.mark.parametrize("B", [8, 80])
+def test_residual_inside_the_margin_everywhere(orc, B):
+    # at one temperature every other token has w_p == w_q exactly: the margin
+    # tokens settle as one sum whose sign is that of 1/S_p - 1/S_q
+    svd = require_gpu()
+    G, d = _margin_case(B, 77)
     g = run_select(svd, d, 1.0, 5)
     say("accept lengths", g["accept_len"])
     assert (g["accept_len"] < G).sum() >= B // 2
     rep = compare(orc, *host_inputs(d), g, 1.0, 1.0, 5)
+    say(rep.summary())
+    assert rep.ok(), rep.failures
+
+
+@pytest.mark.parametrize("shift", [1e-3, -1e-2])
+def test_equal_logit_class_with_distinct_maxima(orc, shift):
+    # the case above with q's maximum logit also moved by a small shift: the
+    # tokens of equal logits share one ratio exp(M_q - M_p) S_q / S_p != 1,
+    # inside the margin, and settle as one class of that ratio's sign
+    svd = require_gpu()
+    import torch
+    G, d = _margin_case(40, 79)
+    q = d["q"]
+    top = torch.argmax(q, dim=-1, keepdim=True)
+    q.scatter_add_(-1, top, torch.full(top.shape, shift, device="cuda"))
+    g = run_select(svd, d, 1.0, 7)
+    say("accept lengths", g["accept_len"])
+    assert (g["accept_len"] < G).sum() >= 20
+    rep = compare(orc, *host_inputs(d), g, 1.0, 1.0, 7)
+    say(rep.summary())
+    assert rep.ok(), rep.failures
+
+
+@pytest.mark.parametrize("B", [8, 80])
+def test_margin_classes_of_one_logit_difference(orc, B):
+    # the case above with 2 % of q's logits lowered by 2^-14 and 1 % by 2^-13:
+    # each difference is one class of about 60-160 margin tokens per segment,
+    # more than a segment keeps singly, merged class by class
+    svd = require_gpu()
+    import torch
+    G, d = _margin_case(B, 80)
+    q = d["q"]
+    g_ = torch.Generator(device="cuda").manual_seed(81)
+    u = torch.rand(q.shape, generator=g_, device="cuda")
+    q.sub_(torch.where(u < 0.02, 2.0 ** -14, torch.where(u < 0.03, 2.0 ** -13, 0.0)))
+    g = run_select(svd, d, 1.0, 8)
+    say("accept lengths", g["accept_len"])
+    assert (g["accept_len"] < G).sum() >= B // 2
+    rep = compare(orc, *host_inputs(d), g, 1.0, 1.0, 8)
+    say(rep.summary())
+    assert rep.ok(), rep.failures
+
+
+@pytest.mark.parametrize("B", [8, 80])
+def test_residual_margin_lists_overflow(orc, B):
+    # the same rows with q read at a temperature 2^-17 above p's: every p/q ratio
+    # is within the margin and almost none is exactly 1, so every segment's
+    # list of uncertain tokens overflows and the pick recomputes its mass exactly
+    svd = require_gpu()
+    import torch
+    G, d = _margin_case(B, 78)
+    tq = 1.0 + 2.0 ** -17
+    out = svd.select_and_verify(d["p"], d["q"], d["drafts"], temp_p=1.0, temp_q=tq, seed=6,
+                                want_alpha=True, want_scores=True)
+    torch.cuda.synchronize()
+    g = {k: (None if v is None else v.cpu().numpy()) for k, v in out.items()}
+    say("accept lengths", g["accept_len"])
+    assert (g["accept_len"] < G).sum() >= B // 2
+    rep = compare(orc, *host_inputs(d), g, 1.0, tq, 6)
     say(rep.summary())
     assert rep.ok(), rep.failures
 
