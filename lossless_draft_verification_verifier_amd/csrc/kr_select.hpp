@@ -111,8 +111,8 @@ __device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alph
       int xj = -1, pj = 0, qj = 0;
       if (j < m) {
         aj = alpha_ws[base + j];
+        sj = stats[base + j];
         if (greedy) xj = drafts[base + j];
-        else sj = stats[base + j];
         if (p_index) pj = p_index[row_k * (gamma + 1) + j];
         if (q_index && !greedy) qj = q_index[base + j];
         rej = !(counter_uniform(seed, row, (uint64_t)j, kAccept) < (double)aj);
@@ -169,13 +169,14 @@ __device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alph
   }
   d.pos = L;
   d.purpose = (int)kResidual;
+  d.st = st;
+  d.known = 1;
   if (greedy) {
     d.excl = xL;
     return d;
   }
   d.two = 1;
   d.qrow = qrow;
-  d.st = st;
   return d;
 }
 

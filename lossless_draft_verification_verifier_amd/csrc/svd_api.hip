@@ -307,7 +307,7 @@ int enqueue_draw(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
                     (int)a.early},
              a.K, a.G, a.seed, a.row_base, a.selected, a.accept_len, a.next_token, a.scores,
              a.desc);
-  SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PASS, s, kr_draw_pass<E, kVec>, dim3(nbs), dim3(kBlock), s,
+  SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PASS, s, kr_draw_pass<E, kVec>, dim3(nbs), dim3(kPassBlock), s,
              a.p, a.q, a.V, a.nseg, a.tp, a.tq, (const DrawDesc *)a.desc, a.segs, a.uncs);
   SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PICK, s, kr_draw_pick<E, kVec>, dim3(nb), dim3(kPickBlock), s,
              a.p, a.q, a.V, a.nseg, a.tp, a.tq, a.seed, a.row_base, (const DrawDesc *)a.desc,
