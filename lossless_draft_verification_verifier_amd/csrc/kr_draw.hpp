@@ -57,56 +57,26 @@ constexpr int kUncCap = SVD_UNC_CAP;   // uncertain tokens kept per segment
 #define SVD_PICK_BLOCK 256
 #endif
 constexpr int kPickBlock = SVD_PICK_BLOCK;  // threads of a pick workgroup
-constexpr int kUncList = 512;          // margin tokens a pass workgroup collects
+constexpr int kUncList = 256;          // margin tokens a pass workgroup collects
 constexpr int kPickSegs = 256;         // segment records the pick stages in LDS
 constexpr int kPickUncSegs = 32;       // segments whose uncertain lists the pick stages
 constexpr double kClassMargin = 2e-4;  // relative margin of the p > q test
-#ifndef SVD_PASS_TOK
-#define SVD_PASS_TOK 4                 // tokens per thread and step of the pass
-#endif
-#ifndef SVD_PASS_BLOCK
-#define SVD_PASS_BLOCK 256
-#endif
-constexpr int kPassBlock = SVD_PASS_BLOCK;
+constexpr int kPassBlock = 256;        // threads of a pass workgroup
 
 // ---------------------------------------------------------------------------
 // exp(x) in fp64 for x <= 0 (a few ulp above 0 is fine; x must not be NaN):
-// x = n ln2/64 + r with |r| <= ln2/128, n rounded to nearest by the 1.5 * 2^52
-// shifter in one fma (its low word is n); r by a Cody-Waite split of ln2/64
-// (n ln2_hi is exact for |n| < 2^17); exp(r) by its degree-5 Taylor
-// polynomial (the next term is below 4e-17); 2^(n mod 64 / 64) from a 64-entry
-// table; then ldexp by n div 64.
+// x = n ln2/256 + r with |r| <= ln2/512, n rounded to nearest by the
+// 1.5 * 2^52 shifter in one fma (its low word is n); r by a Cody-Waite split
+// of ln2/256 whose 34-bit head makes n ln2_hi exact for |n| < 2^19; exp(r) by
+// its degree-4 Taylor polynomial (the next term is below 4e-17);
+// 2^(n mod 256 / 256) from a 256-entry table in LDS; then ldexp by n div 256.
 
-#ifndef SVD_EXP_TAB
-#define SVD_EXP_TAB 256
-#endif
-constexpr int kExpTab = SVD_EXP_TAB;  // table entries: 64 (degree-5 polynomial) or 256 (degree 4)
+constexpr int kExpTab = 256;
 
-struct Exp64Table {
+struct ExpTable {
   double t[kExpTab];
 };
 
-#if SVD_EXP_TAB == 64
-// 2^(j/64), j = 0..63, correctly rounded to double.
-__constant__ double kExp2Frac[64] = {
-    0x1.0000000000000p+0, 0x1.02c9a3e778061p+0, 0x1.059b0d3158574p+0, 0x1.0874518759bc8p+0,
-    0x1.0b5586cf9890fp+0, 0x1.0e3ec32d3d1a2p+0, 0x1.11301d0125b51p+0, 0x1.1429aaea92de0p+0,
-    0x1.172b83c7d517bp+0, 0x1.1a35beb6fcb75p+0, 0x1.1d4873168b9aap+0, 0x1.2063b88628cd6p+0,
-    0x1.2387a6e756238p+0, 0x1.26b4565e27cddp+0, 0x1.29e9df51fdee1p+0, 0x1.2d285a6e4030bp+0,
-    0x1.306fe0a31b715p+0, 0x1.33c08b26416ffp+0, 0x1.371a7373aa9cbp+0, 0x1.3a7db34e59ff7p+0,
-    0x1.3dea64c123422p+0, 0x1.4160a21f72e2ap+0, 0x1.44e086061892dp+0, 0x1.486a2b5c13cd0p+0,
-    0x1.4bfdad5362a27p+0, 0x1.4f9b2769d2ca7p+0, 0x1.5342b569d4f82p+0, 0x1.56f4736b527dap+0,
-    0x1.5ab07dd485429p+0, 0x1.5e76f15ad2148p+0, 0x1.6247eb03a5585p+0, 0x1.6623882552225p+0,
-    0x1.6a09e667f3bcdp+0, 0x1.6dfb23c651a2fp+0, 0x1.71f75e8ec5f74p+0, 0x1.75feb564267c9p+0,
-    0x1.7a11473eb0187p+0, 0x1.7e2f336cf4e62p+0, 0x1.82589994cce13p+0, 0x1.868d99b4492edp+0,
-    0x1.8ace5422aa0dbp+0, 0x1.8f1ae99157736p+0, 0x1.93737b0cdc5e5p+0, 0x1.97d829fde4e50p+0,
-    0x1.9c49182a3f090p+0, 0x1.a0c667b5de565p+0, 0x1.a5503b23e255dp+0, 0x1.a9e6b5579fdbfp+0,
-    0x1.ae89f995ad3adp+0, 0x1.b33a2b84f15fbp+0, 0x1.b7f76f2fb5e47p+0, 0x1.bcc1e904bc1d2p+0,
-    0x1.c199bdd85529cp+0, 0x1.c67f12e57d14bp+0, 0x1.cb720dcef9069p+0, 0x1.d072d4a07897cp+0,
-    0x1.d5818dcfba487p+0, 0x1.da9e603db3285p+0, 0x1.dfc97337b9b5fp+0, 0x1.e502ee78b3ff6p+0,
-    0x1.ea4afa2a490dap+0, 0x1.efa1bee615a27p+0, 0x1.f50765b6e4540p+0, 0x1.fa7c1819e90d8p+0,
-};
-#else
 // 2^(j/256), j = 0..255, correctly rounded to double.
 __constant__ double kExp2Frac[256] = {
     0x1.0000000000000p+0  , 0x1.00b1afa5abcbfp+0  , 0x1.0163da9fb3335p+0  , 0x1.02168143b0281p+0,
@@ -174,34 +144,19 @@ __constant__ double kExp2Frac[256] = {
     0x1.f50765b6e4540p+0  , 0x1.f6632798844f8p+0  , 0x1.f7bfdad9cbe14p+0  , 0x1.f91d802243c89p+0,
     0x1.fa7c1819e90d8p+0  , 0x1.fbdba3692d514p+0  , 0x1.fd3c22b8f71f1p+0  , 0x1.fe9d96b2a23d9p+0,
 };
-#endif
 
 template <int NT>
-__device__ __forceinline__ void exp64_table_init(Exp64Table &tab) {
+__device__ __forceinline__ void exp_table_init(ExpTable &tab) {
   for (int i = threadIdx.x; i < kExpTab; i += NT) tab.t[i] = kExp2Frac[i];
 }
 
-__device__ __forceinline__ double exp_nonpos(double x, const Exp64Table &tab) {
+__device__ __forceinline__ double exp_nonpos(double x, const ExpTable &tab) {
   constexpr double kShift = 0x1.8p52;
   x = fmax(x, -760.0);  // exp(-760) is 0 in double; also maps -inf
-#if SVD_EXP_TAB == 64
-  const double y = __builtin_fma(x, 92.33248261689366, kShift);  // 64 / ln 2
-  const double n = y - kShift;
-  const int ni = (int)(uint32_t)__builtin_bit_cast(uint64_t, y);
-  double r = __builtin_fma(-n, 0x1.62e42fefa0000p-7, x);
-  r = __builtin_fma(-n, 0x1.cf79abc9e3b3ap-46, r);
-  double p = 1.0 / 120.0;
-  p = __builtin_fma(p, r, 1.0 / 24.0);
-  p = __builtin_fma(p, r, 1.0 / 6.0);
-  p = __builtin_fma(p, r, 0.5);
-  p = __builtin_fma(p, r, 1.0);
-  p = __builtin_fma(p, r, 1.0);
-  return ldexp(tab.t[ni & 63] * p, ni >> 6);
-#else
   const double y = __builtin_fma(x, 369.3299304675746, kShift);  // 256 / ln 2
   const double n = y - kShift;
   const int ni = (int)(uint32_t)__builtin_bit_cast(uint64_t, y);
-  double r = __builtin_fma(-n, 0x1.62e42fef80000p-9, x);  // 34-bit head: exact for |n| < 2^19
+  double r = __builtin_fma(-n, 0x1.62e42fef80000p-9, x);
   r = __builtin_fma(-n, 0x1.1cf79abc9e3b4p-44, r);
   double p = 1.0 / 24.0;
   p = __builtin_fma(p, r, 1.0 / 6.0);
@@ -209,7 +164,6 @@ __device__ __forceinline__ double exp_nonpos(double x, const Exp64Table &tab) {
   p = __builtin_fma(p, r, 1.0);
   p = __builtin_fma(p, r, 1.0);
   return ldexp(tab.t[ni & 255] * p, ni >> 8);
-#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -263,10 +217,11 @@ __device__ __forceinline__ void load_unit(const typename E::elem *row, int i, fl
   }
 }
 
-// tokens per unit of the pass: at most SVD_PASS_TOK, within one vector
+// tokens per unit of the residual pass: four (fewer registers than a whole
+// bf16 vector, so more waves)
 template <typename E, bool kVec>
 constexpr int pass_unit() {
-  return kVec ? (E::kPerVec < SVD_PASS_TOK ? E::kPerVec : SVD_PASS_TOK) : 1;
+  return kVec ? 4 : 1;
 }
 
 // Visit the logits of [lo, hi) of one or two rows with NT threads, P tokens
@@ -305,147 +260,121 @@ __device__ __forceinline__ void block_sums(double (&x)[N], double *lds /* N*NW *
   __syncthreads();
 }
 
-// Segment seg of one prefix in the draw's fp64 pass.
+// ---------------------------------------------------------------------------
+// The pass: one workgroup per (prefix, segment), one record per segment.
+
+template <int NT>
+struct PassShared {
+  ExpTable tab;
+  double red[6 * (NT / 64)];
+  float redf[NT / 64 + 1];
+  int redi[NT / 64 + 1];
+  int n_unc;
+  DrawUnc unc[kUncList];
+  double ukey[kUncList];  // the margin tokens' logit differences
+  int uord[kUncList];
+};
+
+// One segment of a residual draw: the six sums of this thread in acc and the
+// margin tokens in the workgroup's list.
 template <typename E, bool kVec, int NT>
-__device__ __forceinline__ void draw_pass_item(const typename E::elem *__restrict__ p,
-                                               const typename E::elem *__restrict__ q, int V,
-                                               int nseg, float tp, float tq, const DrawDesc d,
-                                               DrawSeg *__restrict__ segs,
-                                               DrawUnc *__restrict__ uncs, int64_t b, int seg) {
-  constexpr int NW = NT / 64;
-  __shared__ Exp64Table tab;
-  __shared__ float ldsf[NW + 1];
-  __shared__ double ldsd[6 * NW];
-  __shared__ int ldsi[NW + 1];
-  __shared__ int n_unc;
-  __shared__ DrawUnc unc[kUncList];
-  __shared__ double ukey[kUncList];  // the tokens' logit differences
-  __shared__ int uord[kUncList];
-  if (!d.valid) return;
-  exp64_table_init<NT>(tab);
-  const typename E::elem *rp = p + d.prow * (int64_t)V;
-  const double invTp = 1.0 / (double)tp, invTq = 1.0 / (double)tq;
-  if (threadIdx.x == 0) n_unc = 0;
-  __syncthreads();
-  const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
-  double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};  // sp, sq, ap, aq, ep, eq
-  int bad = 0;
-  float mseg = kNegInf;
-  if (d.two) {
-    const typename E::elem *rq = q + d.qrow * (int64_t)V;
-    const double Mp = (double)d.st.mp / (double)tp, Mq = (double)d.st.mq / (double)tq;
-    const double rho = (double)d.st.sp / (double)d.st.sq;  // fp32 estimate of S_p / S_q
-    const double up = rho * (1.0 + kClassMargin), dn = rho * (1.0 - kClassMargin);
-    const bool same_t = tp == tq;
-    double sp = 0.0, sq = 0.0, ap = 0.0, aq = 0.0, ep = 0.0, eq = 0.0;
-    // one vector of tokens at a time; the margin tokens of the vector are
-    // settled after it, behind one branch
-    constexpr int P = pass_unit<E, kVec>();
-    for (int i = lo / P + (int)threadIdx.x; i < (hi + P - 1) / P; i += NT) {
-      float xp[P], xq[P];
-      load_unit<E, kVec, P>(rp, i, xp);
-      load_unit<E, kVec, P>(rq, i, xq);
-      uint32_t margin = 0;
+__device__ __forceinline__ void pass_residual(PassShared<NT> &S, const typename E::elem *rp,
+                                              const typename E::elem *rq, int lo, int hi,
+                                              double invTp, double Mp, double invTq, double Mq,
+                                              double up, double dn, bool same_t,
+                                              double (&acc)[6]) {
+  double sp = 0.0, sq = 0.0, ap = 0.0, aq = 0.0, ep = 0.0, eq = 0.0;
+  // one unit of tokens at a time; its margin tokens are settled after it,
+  // behind one branch
+  constexpr int P = pass_unit<E, kVec>();
+  for (int i = lo / P + (int)threadIdx.x; i < (hi + P - 1) / P; i += NT) {
+    float xp[P], xq[P];
+    load_unit<E, kVec, P>(rp, i, xp);
+    load_unit<E, kVec, P>(rq, i, xq);
+    uint32_t margin = 0;
 #pragma unroll
-      for (int e = 0; e < P; ++e) {
-        const double wp = exp_nonpos(__builtin_fma((double)xp[e], invTp, -Mp), tab);
-        const double wq = exp_nonpos(__builtin_fma((double)xq[e], invTq, -Mq), tab);
-        sp += wp;
-        sq += wq;
-        const bool pos = wp > up * wq;
-        const double f = pos ? 1.0 : 0.0;
-        ap = __builtin_fma(f, wp, ap);
-        aq = __builtin_fma(f, wq, aq);
-        margin |= (uint32_t)(!pos && wp > dn * wq) << e;
-      }
-      if (margin) {  // rare: the weights are recomputed (the same bits) rather than kept
+    for (int e = 0; e < P; ++e) {
+      const double wp = exp_nonpos(__builtin_fma((double)xp[e], invTp, -Mp), S.tab);
+      const double wq = exp_nonpos(__builtin_fma((double)xq[e], invTq, -Mq), S.tab);
+      sp += wp;
+      sq += wq;
+      const bool pos = wp > up * wq;
+      const double f = pos ? 1.0 : 0.0;
+      ap = __builtin_fma(f, wp, ap);
+      aq = __builtin_fma(f, wq, aq);
+      margin |= (uint32_t)(!pos && wp > dn * wq) << e;
+    }
+    if (margin) {  // rare: the weights are recomputed (the same bits) rather than kept
 #pragma unroll 1
-        for (int e = 0; e < P; ++e) {
-          if (!((margin >> e) & 1u)) continue;
-          const double wp = exp_nonpos(__builtin_fma((double)xp[e], invTp, -Mp), tab);
-          const double wq = exp_nonpos(__builtin_fma((double)xq[e], invTq, -Mq), tab);
-          if (same_t && xp[e] == xq[e]) {
-            ep += wp;
-            eq += wq;
-          } else {
-            const int k = atomicAdd(&n_unc, 1);
-            if (k < kUncList) {
-              unc[k] = DrawUnc{wp, wq, i * P + e, 0};
-              ukey[k] = (double)xp[e] - (double)xq[e];
-            }
+      for (int e = 0; e < P; ++e) {
+        if (!((margin >> e) & 1u)) continue;
+        const double wp = exp_nonpos(__builtin_fma((double)xp[e], invTp, -Mp), S.tab);
+        const double wq = exp_nonpos(__builtin_fma((double)xq[e], invTq, -Mq), S.tab);
+        if (same_t && xp[e] == xq[e]) {
+          ep += wp;
+          eq += wq;
+        } else {
+          const int k = atomicAdd(&S.n_unc, 1);
+          if (k < kUncList) {
+            S.unc[k] = DrawUnc{wp, wq, i * P + e, 0};
+            S.ukey[k] = (double)xp[e] - (double)xq[e];
           }
         }
       }
     }
-    acc[0] = sp;
-    acc[1] = sq;
-    acc[2] = ap;
-    acc[3] = aq;
-    acc[4] = ep;
-    acc[5] = eq;
-  } else {
-    // the row max: known for a scored row, else this segment's (bonus row)
-    if (d.known) {
-      mseg = d.st.mp;
-    } else {
-      float m = kNegInf;
-      visit_segment<E, kVec, false, NT>(rp, rp, lo, hi, [&](int, float zp, float) {
-        m = fmaxf(m, zp);
-        bad |= (zp != zp);
-      });
-      mseg = block_max<NW>(m, ldsf);
-      bad = block_max_i<NW>(bad, ldsi);
-    }
-    const double M = (double)fmaxf(mseg, kLowest) / (double)tp;
-    const int excl = d.excl;  // sp: every token; ap: all but the excluded one
-    double sp = 0.0, ap = 0.0;
-    visit_segment<E, kVec, false, NT>(rp, rp, lo, hi, [&](int v, float zp, float) {
-      const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -M), tab);
-      sp += wp;
-      ap = __builtin_fma(v != excl ? 1.0 : 0.0, wp, ap);
-    });
-    acc[0] = sp;
-    acc[2] = ap;
   }
-  block_sums<NW, 6>(acc, ldsd);
-  const int64_t so = b * nseg + seg;
-  const int n = n_unc;
+  acc[0] = sp;
+  acc[1] = sq;
+  acc[2] = ap;
+  acc[3] = aq;
+  acc[4] = ep;
+  acc[5] = eq;
+}
+
+// The end of a segment: workgroup sums, the margin list (merged by class
+// when longer than kUncCap) and the record.
+template <int NT>
+__device__ __forceinline__ void pass_finish(PassShared<NT> &S, double (&acc)[6], float mseg,
+                                            int bad, bool classes, DrawSeg *__restrict__ segs,
+                                            DrawUnc *__restrict__ uncs, int64_t so) {
+  block_sums<NT / 64, 6>(acc, S.red);
+  const int n = S.n_unc;
   int nout = -1;  // entries written; -1: the list overflowed
   if (n <= kUncCap) {
     // margin tokens in token order (distinct tokens: the ranks are a permutation)
     if ((int)threadIdx.x < n) {
-      const DrawUnc e = unc[threadIdx.x];
+      const DrawUnc e = S.unc[threadIdx.x];
       int rank = 0;
-      for (int i = 0; i < n; ++i) rank += (unc[i].v < e.v);
+      for (int i = 0; i < n; ++i) rank += (S.unc[i].v < e.v);
       uncs[so * kUncCap + rank] = e;
     }
     nout = n;
-  } else if (n <= kUncList && d.two && tp == tq) {
+  } else if (n <= kUncList && classes) {
     // merge by class: order by (difference, token), then each class's first
     // entry sums its class in that order
     for (int i = threadIdx.x; i < n; i += NT) {
-      const double ki = ukey[i];
-      const int vi = unc[i].v;
+      const double ki = S.ukey[i];
+      const int vi = S.unc[i].v;
       int r = 0;
-      for (int j = 0; j < n; ++j) r += (ukey[j] < ki) || (ukey[j] == ki && unc[j].v < vi);
-      uord[r] = i;
+      for (int j = 0; j < n; ++j) r += (S.ukey[j] < ki) || (S.ukey[j] == ki && S.unc[j].v < vi);
+      S.uord[r] = i;
     }
     __syncthreads();
     for (int r = threadIdx.x; r < n; r += NT) {
-      const int i = uord[r];
-      if (r > 0 && ukey[uord[r - 1]] == ukey[i]) continue;  // not the first of its class
+      const int i = S.uord[r];
+      if (r > 0 && S.ukey[S.uord[r - 1]] == S.ukey[i]) continue;  // not the first of its class
       int g = 0;
-      for (int c = 1; c <= r; ++c) g += ukey[uord[c]] != ukey[uord[c - 1]];
+      for (int c = 1; c <= r; ++c) g += S.ukey[S.uord[c]] != S.ukey[S.uord[c - 1]];
       if (g >= kUncCap) continue;
       double swp = 0.0, swq = 0.0;
-      for (int c = r; c < n && ukey[uord[c]] == ukey[i]; ++c) {
-        swp += unc[uord[c]].wp;
-        swq += unc[uord[c]].wq;
+      for (int c = r; c < n && S.ukey[S.uord[c]] == S.ukey[i]; ++c) {
+        swp += S.unc[S.uord[c]].wp;
+        swq += S.unc[S.uord[c]].wq;
       }
-      uncs[so * kUncCap + g] = DrawUnc{swp, swq, unc[i].v, 0};
+      uncs[so * kUncCap + g] = DrawUnc{swp, swq, S.unc[i].v, 0};
     }
     int ng = 1;
-    for (int c = 1; c < n; ++c) ng += ukey[uord[c]] != ukey[uord[c - 1]];
+    for (int c = 1; c < n; ++c) ng += S.ukey[S.uord[c]] != S.ukey[S.uord[c - 1]];
     nout = ng <= kUncCap ? ng : -1;
   }
   if (threadIdx.x == 0) {
@@ -464,17 +393,57 @@ __device__ __forceinline__ void draw_pass_item(const typename E::elem *__restric
 }
 
 template <typename E, bool kVec>
-__global__ __launch_bounds__(kPassBlock)
-#ifdef SVD_PASS_WAVES
-__attribute__((amdgpu_waves_per_eu(SVD_PASS_WAVES)))
-#endif
-void kr_draw_pass(
+__global__ __launch_bounds__(kPassBlock) __attribute__((amdgpu_waves_per_eu(6))) void kr_draw_pass(
     const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int V,
     int nseg, float tp, float tq, const DrawDesc *__restrict__ desc,
     DrawSeg *__restrict__ segs, DrawUnc *__restrict__ uncs) {
+  constexpr int NT = kPassBlock;
+  __shared__ PassShared<NT> S;
   const int64_t b = blockIdx.x / nseg;
-  draw_pass_item<E, kVec, kPassBlock>(p, q, V, nseg, tp, tq, desc[b], segs, uncs, b,
-                                  (int)(blockIdx.x - b * nseg));
+  const int seg = (int)(blockIdx.x - b * nseg);
+  const DrawDesc d = desc[b];
+  if (!d.valid) return;
+  exp_table_init<NT>(S.tab);
+  if (threadIdx.x == 0) S.n_unc = 0;
+  __syncthreads();
+  const typename E::elem *rp = p + d.prow * (int64_t)V;
+  const double invTp = 1.0 / (double)tp, invTq = 1.0 / (double)tq;
+  const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
+  const int64_t so = b * nseg + seg;
+  double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  if (d.two) {
+    const typename E::elem *rq = q + d.qrow * (int64_t)V;
+    const double rho = (double)d.st.sp / (double)d.st.sq;  // fp32 estimate of S_p / S_q
+    const double up = rho * (1.0 + kClassMargin), dn = rho * (1.0 - kClassMargin);
+    pass_residual<E, kVec, NT>(S, rp, rq, lo, hi, invTp, (double)d.st.mp / (double)tp, invTq,
+                               (double)d.st.mq / (double)tq, up, dn, tp == tq, acc);
+    pass_finish<NT>(S, acc, kNegInf, 0, tp == tq, segs, uncs, so);
+    return;
+  }
+  // p row: its max is known when it was scored (greedy rejection); a bonus
+  // row takes this segment's max from a first sweep
+  float mseg = d.st.mp;
+  int bad = 0;
+  if (!d.known) {
+    float m = kNegInf;
+    visit_segment<E, kVec, false, NT>(rp, rp, lo, hi, [&](int, float zp, float) {
+      m = fmaxf(m, zp);
+      bad |= (zp != zp);
+    });
+    mseg = block_max<NT / 64>(m, S.redf);
+    bad = block_max_i<NT / 64>(bad, S.redi);
+  }
+  const double M = (double)fmaxf(mseg, kLowest) / (double)tp;
+  const int excl = d.excl;  // sp: every token; ap: all but the excluded one
+  double sp = 0.0, ap = 0.0;
+  visit_segment<E, kVec, false, NT>(rp, rp, lo, hi, [&](int v, float zp, float) {
+    const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -M), S.tab);
+    sp += wp;
+    ap = __builtin_fma(v != excl ? 1.0 : 0.0, wp, ap);
+  });
+  acc[0] = sp;
+  acc[2] = ap;
+  pass_finish<NT>(S, acc, mseg, bad, false, segs, uncs, so);
 }
 
 // Exact weights of the draw.
@@ -485,7 +454,7 @@ struct DrawWeight {
   bool resid;  // max(0, p - q); otherwise p with token excl zeroed
   int excl;
   // weight of token v from its two logits
-  __device__ __forceinline__ double from(int v, float zp, float zq, const Exp64Table &tab) const {
+  __device__ __forceinline__ double from(int v, float zp, float zq, const ExpTable &tab) const {
     const double pv = exp_nonpos(__builtin_fma((double)zp, invTp, -Mp), tab) * invSp;
     if (!resid) return v == excl ? 0.0 : pv;
     const double qv = exp_nonpos(__builtin_fma((double)zq, invTq, -Mq), tab) * invSq;
@@ -541,7 +510,7 @@ __device__ __forceinline__ bool draw_setup(const typename E::elem *rp,
 // The weights of the kRun consecutive tokens from a of a segment ending at hi.
 template <typename E, bool kVec, int kRun>
 __device__ __forceinline__ void run_weights(const DrawWeight<E> &W, int a, int hi,
-                                            const Exp64Table &tab, double (&w)[kRun]) {
+                                            const ExpTable &tab, double (&w)[kRun]) {
   if constexpr (kVec) {
     constexpr int P = E::kPerVec;
     static_assert(kRun % P == 0, "a run is whole 16-byte vectors");
@@ -571,7 +540,7 @@ __device__ __forceinline__ void run_weights(const DrawWeight<E> &W, int a, int h
 // Exact residual mass of one segment (all NT threads); valid in thread 0.
 template <typename E, bool kVec, int NT>
 __device__ __forceinline__ double segment_mass_exact(const DrawWeight<E> &W, int V, int seg,
-                                                     const Exp64Table &tab, double *ldsd) {
+                                                     const ExpTable &tab, double *ldsd) {
   const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
   double z = 0.0;
   visit_segment<E, kVec, true, NT>(W.p, W.q, lo, hi, [&](int v, float zp, float zq) {
@@ -613,7 +582,7 @@ __global__ __launch_bounds__(kPickBlock) void kr_draw_pick(
     int32_t *__restrict__ next_token) {
   constexpr int NT = kPickBlock, NW = NT / 64;
   constexpr int kRun = kDrawSeg / NT;  // tokens per thread in the scan of one segment
-  __shared__ Exp64Table tab;
+  __shared__ ExpTable tab;
   __shared__ double ldsd[NW + 1];
   __shared__ int ldsi[NW + 1];
   __shared__ DrawSeg segl[kPickSegs];  // the prefix's records, when they fit
@@ -623,7 +592,7 @@ __global__ __launch_bounds__(kPickBlock) void kr_draw_pick(
   const int tid = threadIdx.x;
   const DrawDesc d = desc[b];
   if (!d.valid) return;
-  exp64_table_init<NT>(tab);
+  exp_table_init<NT>(tab);
   const bool staged = nseg <= kPickSegs;
   const bool unc_staged = nseg <= kPickUncSegs;
   if (staged)

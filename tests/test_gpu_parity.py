@@ -184,3 +184,32 @@ def test_bonus_draws_across_segments(orc, V):
         assert np.all(g["accept_len"] == 3)
         rep = compare(orc, *host_inputs(d), g, 0.9, 0.9, seed)
         assert rep.ok(), rep.failures
+
+
+@pytest.mark.parametrize("temp", [1.0, 0.7])
+def test_bf16_weight_tables_edge_logits(orc, temp):
+    # a batch large enough for the draw pass's bf16 weight tables (groups of
+    # several segments per workgroup), over rows whose logits leave the tables'
+    # range: -inf (masked tokens), near-zero magnitudes and large magnitudes,
+    # with a ragged last segment; the oracle checks a sample of prefixes
+    svd = require_gpu()
+    import torch
+    B, G, V = 512, 2, 3 * 8192 + 5
+    g_ = torch.Generator(device="cuda").manual_seed(90)
+    zp = torch.randn((B, 1, G + 1, V), generator=g_, device="cuda") * 2.0
+    u = torch.rand((B, 1, G + 1, V), generator=g_, device="cuda")
+    zp = torch.where(u < 0.01, torch.full_like(zp, float("-inf")), zp)
+    zp = torch.where((u >= 0.01) & (u < 0.02), zp * 1e-5, zp)
+    zp = torch.where((u >= 0.02) & (u < 0.021), zp * 25.0, zp)
+    zq = zp[:, :, :G] + 0.75 * torch.randn((B, 1, G, V), generator=g_, device="cuda")
+    zp, zq = zp.to(torch.bfloat16), zq.to(torch.bfloat16)
+    gum = -torch.log(-torch.log(torch.rand((B, 1, G, V), generator=g_, device="cuda")))
+    x = torch.argmax(zq.float() / temp + gum, dim=-1).to(torch.int32)
+    d = {"p": zp.contiguous(), "q": zq.contiguous(), "drafts": x.contiguous()}
+    g = run_select(svd, d, temp, 12)
+    idx = list(range(0, B, 16))
+    hp, hq, hd = host_inputs(d, idx)
+    rep = compare(orc, hp, hq, hd, g, temp, temp, 12, prefixes=idx)
+    say(rep.summary())
+    assert rep.ok(), rep.failures
+    assert rep.invalid == 0
