@@ -41,17 +41,36 @@ struct Window {
 // together with those of the acceptance test.
 constexpr int kSelChunk = 16;  // alpha loads in flight per lane in the scores
 
-__device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alpha_ws,
-                                                  const RowStats *__restrict__ stats,
-                                                  const int32_t *__restrict__ drafts, bool greedy,
-                                                  const int32_t *__restrict__ p_index,
-                                                  const int32_t *__restrict__ q_index, int64_t np,
-                                                  const Window win, int K, int gamma,
-                                                  uint64_t seed, uint64_t row_base, int64_t b,
-                                                  int32_t *__restrict__ selected,
-                                                  int32_t *__restrict__ accept_len,
-                                                  int32_t *__restrict__ next_token,
-                                                  float *__restrict__ scores) {
+// Everything the selection reads and writes.
+struct SelectArgs {
+  const float *alpha_ws;
+  const RowStats *stats;
+  const int32_t *drafts;
+  int greedy;
+  const int32_t *p_index, *q_index;  // nullable: shared-row pools
+  int64_t np;
+  Window win;
+  int K, gamma;
+  uint64_t seed, row_base;
+  int32_t *selected, *accept_len, *next_token;
+  float *scores;
+};
+
+__device__ __forceinline__ DrawDesc select_prefix(const SelectArgs &A, int64_t b) {
+  const float *__restrict__ alpha_ws = A.alpha_ws;
+  const RowStats *__restrict__ stats = A.stats;
+  const int32_t *__restrict__ drafts = A.drafts;
+  const bool greedy = A.greedy != 0;
+  const int32_t *__restrict__ p_index = A.p_index;
+  const int32_t *__restrict__ q_index = A.q_index;
+  const int64_t np = A.np;
+  const Window win = A.win;
+  const int K = A.K, gamma = A.gamma;
+  const uint64_t seed = A.seed, row_base = A.row_base;
+  int32_t *__restrict__ selected = A.selected;
+  int32_t *__restrict__ accept_len = A.accept_len;
+  int32_t *__restrict__ next_token = A.next_token;
+  float *__restrict__ scores = A.scores;
   const int lane = threadIdx.x & 63;
   const int n = win.gamma_b ? win.gamma_b[b] : gamma;  // the window (bonus row n)
   auto usable = [&](int k) { return win.mlen ? win.mlen[(int64_t)b * K + k] : gamma; };
@@ -180,16 +199,9 @@ __device__ __forceinline__ DrawDesc select_prefix(const float *__restrict__ alph
   return d;
 }
 
-__global__ __launch_bounds__(64) void kr_select(
-    const float *__restrict__ alpha_ws, const RowStats *__restrict__ stats,
-    const int32_t *__restrict__ drafts, int greedy, const int32_t *__restrict__ p_index,
-    const int32_t *__restrict__ q_index, int64_t np, const Window win, int K, int gamma,
-    uint64_t seed, uint64_t row_base, int32_t *__restrict__ selected,
-    int32_t *__restrict__ accept_len, int32_t *__restrict__ next_token,
-    float *__restrict__ scores, DrawDesc *__restrict__ desc) {
-  const DrawDesc d = select_prefix(alpha_ws, stats, drafts, greedy != 0, p_index, q_index, np,
-                                   win, K, gamma, seed, row_base, blockIdx.x, selected,
-                                   accept_len, next_token, scores);
+__global__ __launch_bounds__(64) void kr_select(const SelectArgs sel,
+                                                 DrawDesc *__restrict__ desc) {
+  const DrawDesc d = select_prefix(sel, blockIdx.x);
   if (threadIdx.x == 0) desc[blockIdx.x] = d;
 }
 

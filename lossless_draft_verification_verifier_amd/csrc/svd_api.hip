@@ -300,13 +300,13 @@ template <typename E, bool kVec>
 int enqueue_draw(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   const unsigned nb = (unsigned)a.B;
   const unsigned nbs = (unsigned)(a.B * a.nseg);
-  SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_select, dim3(nb), dim3(64), s,
-             (const float *)a.alpha_ws, (const RowStats *)a.stats, a.drafts, (int)a.greedy,
-             a.ix.p, a.greedy ? nullptr : a.ix.q, a.np,
-             Window{a.windowed ? (const int32_t *)a.mlen : nullptr, a.gamma_b, a.eos,
-                    (int)a.early},
-             a.K, a.G, a.seed, a.row_base, a.selected, a.accept_len, a.next_token, a.scores,
-             a.desc);
+  const SelectArgs sel{(const float *)a.alpha_ws, (const RowStats *)a.stats, a.drafts,
+                       (int)a.greedy, a.ix.p, a.greedy ? nullptr : a.ix.q, a.np,
+                       Window{a.windowed ? (const int32_t *)a.mlen : nullptr, a.gamma_b, a.eos,
+                              (int)a.early},
+                       a.K, a.G, a.seed, a.row_base, a.selected, a.accept_len, a.next_token,
+                       a.scores};
+  SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_select, dim3(nb), dim3(64), s, sel, a.desc);
   SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PASS, s, kr_draw_pass<E, kVec>, dim3(nbs), dim3(kPassBlock), s,
              a.p, a.q, a.V, a.nseg, a.tp, a.tq, (const DrawDesc *)a.desc, a.segs, a.uncs);
   SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PICK, s, kr_draw_pick<E, kVec>, dim3(nb), dim3(kPickBlock), s,

@@ -64,24 +64,27 @@ def test_row_base_shifts_uniform_rows(orc):
     assert rep.ok(), rep.failures
 
 
-def test_minus_inf_logits_and_data_errors(orc):
+@pytest.mark.parametrize("K,V", [(2, 1000), (1, 20000)])
+def test_minus_inf_logits_and_data_errors(orc, K, V):
+    # (1, 20000): one draft per prefix, rows of three draw segments
     svd = require_gpu()
-    cfg = W.Config(94, "custom", B=8, K=2, gamma=4, V=1000, dtype="f32", sigma0=1.0,
+    cfg = W.Config(94, "custom", B=8, K=K, gamma=4, V=V, dtype="f32", sigma0=1.0,
                    sigma_step=0.0, temp=1.0, boost=6.0, boost_prob=1.0)
     d = gen(cfg, data_seed=8)
     p, q, dr = d["p"], d["q"], d["drafts"]
-    p[0, :, :, 500:] = -float("inf")          # legal: half the vocabulary has p = 0
+    k = K - 1
+    p[0, :, :, V // 2:] = -float("inf")       # legal: half the vocabulary has p = 0
     q[1, 0, 2, dr[1, 0, 2]] = -float("inf")   # q(x) = 0 -> alpha = 1
-    p[2, 1, 1, dr[2, 1, 1]] = -float("inf")   # p(x) = 0 -> alpha = 0
-    p[3, 1, 2, 17] = float("nan")             # invalid
+    p[2, k, 1, dr[2, k, 1]] = -float("inf")   # p(x) = 0 -> alpha = 0
+    p[3, k, 2, 17] = float("nan")             # invalid
     q[4, 0, 0, 3] = float("inf")              # invalid
-    dr[5, 1, 3] = 1000                        # token out of range
+    dr[5, k, 3] = V                           # token out of range
     p[6, 0, 1, :] = -float("inf")             # all -inf row
     dr[7, 0, 0] = -5
     g = host(svd.select_and_verify(p, q, dr, seed=4, want_alpha=True, want_scores=True))
     for b in (3, 4, 5, 6, 7):
         assert g["selected"][b] == -1 and g["accept_len"][b] == -1 and g["next_token"][b] == -1
-    assert g["alpha"][1, 0, 2] == 1.0 and g["alpha"][2, 1, 1] == 0.0
+    assert g["alpha"][1, 0, 2] == 1.0 and g["alpha"][2, k, 1] == 0.0
     rep = compare(orc, *host_inputs(d), g, 1.0, 1.0, 4)
     say(rep.summary())
     assert rep.ok(), rep.failures
