@@ -45,7 +45,7 @@
 // token order, so the result is deterministic.
 #pragma once
 
-#include "svd_device.hpp"
+#include "kr_select.hpp"
 
 namespace svd {
 

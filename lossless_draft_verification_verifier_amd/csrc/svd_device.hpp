@@ -211,16 +211,4 @@ struct RowStats {      // one scored row pair
   float mq, sq;        // the same for the q row
 };
 
-struct DrawDesc {      // one prefix: what the draw reads, settled by the selection
-  int64_t prow;        // the drawn p row: row index into the p logits (or the p pool)
-  int64_t qrow;        // residual draws: the q row, likewise; 0 otherwise
-  RowStats st;         // statistics of the drawn row pair (when known)
-  int pos;             // accepted length L (rejection) or the window (bonus)
-  int purpose;         // kResidual or kBonus: the uniform's purpose
-  int valid;           // 0: prefix invalid or committed without a draw
-  int two;             // 1: residual max(0, p - q) of the row pair; 0: p row alone
-  int excl;            // p-row draw: a token of weight zero (the rejected one), or -1
-  int known;           // 1: st.mp is the drawn p row's max (a scored row); 0: bonus row
-};
-
 }  // namespace svd

@@ -187,11 +187,10 @@ def test_bonus_draws_across_segments(orc, V):
 
 
 @pytest.mark.parametrize("temp", [1.0, 0.7])
-def test_bf16_weight_tables_edge_logits(orc, temp):
-    # a batch large enough for the draw pass's bf16 weight tables (groups of
-    # several segments per workgroup), over rows whose logits leave the tables'
-    # range: -inf (masked tokens), near-zero magnitudes and large magnitudes,
-    # with a ragged last segment; the oracle checks a sample of prefixes
+def test_large_batch_edge_logits(orc, temp):
+    # 512 prefixes over rows with -inf (masked tokens), near-zero and large
+    # logit magnitudes, a ragged last draw segment; the oracle checks a sample
+    # of prefixes
     svd = require_gpu()
     import torch
     B, G, V = 512, 2, 3 * 8192 + 5
