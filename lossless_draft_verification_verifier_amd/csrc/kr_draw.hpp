@@ -49,14 +49,8 @@
 
 namespace svd {
 
-#ifndef SVD_UNC_CAP
-#define SVD_UNC_CAP 32
-#endif
-constexpr int kUncCap = SVD_UNC_CAP;   // uncertain tokens kept per segment
-#ifndef SVD_PICK_BLOCK
-#define SVD_PICK_BLOCK 256
-#endif
-constexpr int kPickBlock = SVD_PICK_BLOCK;  // threads of a pick workgroup
+constexpr int kUncCap = 32;            // uncertain tokens kept per segment
+constexpr int kPickBlock = 256;        // threads of a pick workgroup
 constexpr int kUncList = 256;          // margin tokens a pass workgroup collects
 constexpr int kPickSegs = 256;         // segment records the pick stages in LDS
 constexpr int kPickUncSegs = 32;       // segments whose uncertain lists the pick stages
