@@ -457,13 +457,28 @@ struct DrawWeight {
   }
 };
 
-// Exact row normalisers of the draw from the pass's segment sums, in segment
-// order.  Returns false for an invalid bonus row.
+// Fixed-order reductions over the 64 lanes of a wave (an xor butterfly:
+// every lane ends with the same bits).
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Exact row normalisers of the draw from the pass's segment sums; every wave
+// computes them (lane l adds segments l, l + 64, ..., then the lanes are
+// summed).  Returns false for an invalid bonus row.
 template <typename E>
 __device__ __forceinline__ bool draw_setup(const typename E::elem *rp,
                                            const typename E::elem *rq, const DrawDesc &d,
                                            const DrawSeg *S, int nseg, float tp, float tq,
                                            DrawWeight<E> &W) {
+  const int lane = threadIdx.x & 63;
   W.p = rp;
   W.q = rq;
   W.invTp = 1.0 / (double)tp;
@@ -476,25 +491,30 @@ __device__ __forceinline__ bool draw_setup(const typename E::elem *rp,
   if (W.resid) {
     W.Mp = (double)d.st.mp / (double)tp;
     W.Mq = (double)d.st.mq / (double)tq;
-    Sq = 0.0;
-    for (int s = 0; s < nseg; ++s) {
-      Sp += S[s].sp;
-      Sq += S[s].sq;
+    double a = 0.0, c = 0.0;
+    for (int s = lane; s < nseg; s += 64) {
+      a += S[s].sp;
+      c += S[s].sq;
     }
+    Sp = wave_sum_d(a);
+    Sq = wave_sum_d(c);
   } else {
-    float mr = kNegInf;
+    float m = kNegInf;
     int bad = 0;
-    for (int s = 0; s < nseg; ++s) {
-      mr = fmaxf(mr, S[s].mseg);
+    for (int s = lane; s < nseg; s += 64) {
+      m = fmaxf(m, S[s].mseg);
       bad |= S[s].bad;
     }
-    if (bad || mr == kNegInf || mr == -kNegInf) return false;
+    const float mr = wave_max_f(m);
+    if (__any(bad) || mr == kNegInf || mr == -kNegInf) return false;
     W.Mp = (double)mr / (double)tp;
     W.Mq = 0.0;
-    for (int s = 0; s < nseg; ++s) {
+    double a = 0.0;
+    for (int s = lane; s < nseg; s += 64) {
       const double Ms = (double)fmaxf(S[s].mseg, kLowest) / (double)tp;
-      Sp += (S[s].mseg == mr) ? S[s].sp : S[s].sp * exp(Ms - W.Mp);
+      a += (S[s].mseg == mr) ? S[s].sp : S[s].sp * exp(Ms - W.Mp);
     }
+    Sp = wave_sum_d(a);
   }
   W.invSp = 1.0 / Sp;
   W.invSq = 1.0 / Sq;
@@ -583,17 +603,19 @@ __global__ __launch_bounds__(kPickBlock) void kr_draw_pick(
   __shared__ DrawMass massl[kPickSegs];
   __shared__ DrawUnc uncl[kPickUncSegs * kUncCap];
   const int64_t b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const DrawDesc d = desc[b];
-  if (!d.valid) return;
-  exp_table_init<NT>(tab);
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the records are staged together with the descriptor's load (a prefix
+  // without a draw has stale records, which it never reads)
   const bool staged = nseg <= kPickSegs;
   const bool unc_staged = nseg <= kPickUncSegs;
   if (staged)
     for (int s = tid; s < nseg; s += NT) segl[s] = segs[b * nseg + s];
-  if (unc_staged && d.two)  // every slot: the lists' lengths are not known yet
+  if (unc_staged)  // every slot: the lists' lengths are not known yet
     for (int i = tid; i < nseg * kUncCap; i += NT) uncl[i] = uncs[b * nseg * kUncCap + i];
+  const DrawDesc d = desc[b];
+  exp_table_init<NT>(tab);
   __syncthreads();
+  if (!d.valid) return;
   const DrawSeg *S = staged ? segl : segs + b * nseg;
   const DrawUnc *U = unc_staged ? uncl : uncs + b * nseg * kUncCap;
   DrawMass *ms = staged ? massl : mass + b * nseg;
@@ -637,7 +659,9 @@ __global__ __launch_bounds__(kPickBlock) void kr_draw_pick(
     ms[s] = m;
   }
   __syncthreads();
-  if (residual) {  // segments whose list overflowed: exact, all threads
+  int overflow = 0;
+  for (int s = lane; s < nseg; s += 64) overflow |= residual && S[s].n_unc < 0;
+  if (__any(overflow)) {  // segments whose list overflowed: exact, all threads
     for (int s = 0; s < nseg; ++s) {
       if (S[s].n_unc >= 0) continue;
       const double z = segment_mass_exact<E, kVec, NT>(W, V, s, tab, ldsd);
@@ -646,28 +670,48 @@ __global__ __launch_bounds__(kPickBlock) void kr_draw_pick(
     }
   }
 
-  double zr = 0.0;
-  for (int s = 0; s < nseg; ++s) zr += ms[s].zr;
+  double zl = 0.0;
+  for (int s = lane; s < nseg; s += 64) zl += ms[s].zr;
+  const double zr = wave_sum_d(zl);
   const bool use_r = zr > 0.0;  // a residual without mass draws from p
   W.resid = residual && use_r;
   if (!use_r) W.excl = -1;
   double Z = zr;
   if (!use_r) {
-    Z = 0.0;
-    for (int s = 0; s < nseg; ++s) Z += ms[s].zp;
+    zl = 0.0;
+    for (int s = lane; s < nseg; s += 64) zl += ms[s].zp;
+    Z = wave_sum_d(zl);
   }
   const double t = counter_uniform(seed, row_base + (uint64_t)b, (uint64_t)d.pos,
                                    (uint64_t)d.purpose) * Z;
 
+  // the segment that holds t: the first whose inclusive prefix sum of masses
+  // exceeds it (a scan over lanes, or a serial one past 64 segments)
   double cum = 0.0;
   int s0 = -1;
-  for (int s = 0; s < nseg; ++s) {
-    const double w = use_r ? ms[s].zr : ms[s].zp;
-    if (cum + w > t) {
-      s0 = s;
-      break;
+  if (nseg <= 64) {
+    const double w = lane < nseg ? (use_r ? ms[lane].zr : ms[lane].zp) : 0.0;
+    double incl = w;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
     }
-    cum += w;
+    const double excl = __shfl_up(incl, 1, 64);
+    const uint64_t hit = __ballot(lane < nseg && incl > t);
+    if (hit) {
+      s0 = __ffsll((unsigned long long)hit) - 1;
+      cum = __shfl(lane == 0 ? 0.0 : excl, s0, 64);
+    }
+  } else {
+    for (int s = 0; s < nseg; ++s) {
+      const double w = use_r ? ms[s].zr : ms[s].zp;
+      if (cum + w > t) {
+        s0 = s;
+        break;
+      }
+      cum += w;
+    }
   }
   int tok = -1;
   if (s0 >= 0) {
