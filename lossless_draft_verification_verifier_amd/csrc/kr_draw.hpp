@@ -50,7 +50,7 @@
 namespace svd {
 
 constexpr int kUncCap = 32;            // uncertain tokens kept per segment
-constexpr int kPickBlock = 256;        // threads of a pick workgroup
+constexpr int kPickBlock = 512;        // threads of a pick workgroup
 constexpr int kUncList = 256;          // margin tokens a pass workgroup collects
 constexpr int kPickSegs = 256;         // segment records the pick stages in LDS
 constexpr int kPickUncSegs = 32;       // segments whose uncertain lists the pick stages
