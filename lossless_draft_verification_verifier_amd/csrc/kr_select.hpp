@@ -86,9 +86,12 @@ __device__ __forceinline__ DrawDesc select_prefix(const SelectArgs &A, int64_t b
   const int lane = threadIdx.x & 63;
   const int n = win.gamma_b ? win.gamma_b[b] : gamma;  // the window (bonus row n)
   auto usable = [&](int k) { return win.mlen ? win.mlen[(int64_t)b * K + k] : gamma; };
+  // one draft and no scores asked for: its alpha is read once, by the
+  // acceptance test below (which then also finds a NaN), saving a round trip
+  const bool lean = K == 1 && !scores && gamma <= 64 && !win.first_only;
   double S = -1.0;
   bool bad = false;
-  if (lane < K && !win.first_only) {
+  if (lane < K && !win.first_only && !lean) {
     const int64_t base = ((int64_t)b * K + lane) * gamma;
     const int m = usable(lane);
     bad |= m < 1;
@@ -109,7 +112,7 @@ __device__ __forceinline__ DrawDesc select_prefix(const SelectArgs &A, int64_t b
     }
     if (scores) scores[b * K + lane] = (float)S;
   }
-  bool invalid = __any(bad) || (win.first_only && usable(0) < 1);
+  bool invalid = __any(bad) || ((win.first_only || lean) && usable(0) < 1);
 
   // argmax over lanes, the lower index on an exact tie (a total order, so
   // every lane of the butterfly ends with the same winner)
@@ -147,6 +150,10 @@ __device__ __forceinline__ DrawDesc select_prefix(const SelectArgs &A, int64_t b
         if (p_index) pj = p_index[row_k * (gamma + 1) + j];
         if (q_index && !greedy) qj = q_index[base + j];
         rej = !(counter_uniform(seed, row, (uint64_t)j, kAccept) < (double)aj);
+      }
+      if (lean && __any(aj != aj)) {  // the whole window is this one chunk
+        invalid = true;
+        break;
       }
       const uint64_t mask = __ballot(rej);
       if (mask) {

@@ -64,9 +64,10 @@ def test_row_base_shifts_uniform_rows(orc):
     assert rep.ok(), rep.failures
 
 
-@pytest.mark.parametrize("K,V", [(2, 1000), (1, 20000)])
-def test_minus_inf_logits_and_data_errors(orc, K, V):
-    # (1, 20000): one draft per prefix, rows of three draw segments
+@pytest.mark.parametrize("K,V,scores", [(2, 1000, True), (1, 20000, True), (1, 20000, False)])
+def test_minus_inf_logits_and_data_errors(orc, K, V, scores):
+    # (1, 20000): one draft per prefix, rows of three draw segments; without
+    # scores the selection reads a single draft's alpha once
     svd = require_gpu()
     cfg = W.Config(94, "custom", B=8, K=K, gamma=4, V=V, dtype="f32", sigma0=1.0,
                    sigma_step=0.0, temp=1.0, boost=6.0, boost_prob=1.0)
@@ -81,7 +82,7 @@ def test_minus_inf_logits_and_data_errors(orc, K, V):
     dr[5, k, 3] = V                           # token out of range
     p[6, 0, 1, :] = -float("inf")             # all -inf row
     dr[7, 0, 0] = -5
-    g = host(svd.select_and_verify(p, q, dr, seed=4, want_alpha=True, want_scores=True))
+    g = host(svd.select_and_verify(p, q, dr, seed=4, want_alpha=True, want_scores=scores))
     for b in (3, 4, 5, 6, 7):
         assert g["selected"][b] == -1 and g["accept_len"][b] == -1 and g["next_token"][b] == -1
     assert g["alpha"][1, 0, 2] == 1.0 and g["alpha"][2, k, 1] == 0.0
