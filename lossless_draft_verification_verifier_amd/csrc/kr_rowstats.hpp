@@ -223,18 +223,16 @@ __global__ __launch_bounds__(kSplitBlock) void kr_rowstats_split(
   if (threadIdx.x == 0) part[blockIdx.x] = PartStats{mp, sp, mq, sq};
 }
 
-// One wave per launch row: lane sl holds slice sl's record (lane sl + 64k
-// folds slices past 64 in first), a butterfly merges the lanes in a fixed
-// pattern, and lane 0 forms alpha.
+// One launch row r merged by one wave: lane sl holds slice sl's record (lane
+// sl + 64k folds slices past 64 in first), a butterfly merges the lanes in a
+// fixed pattern, and lane 0 forms alpha.
 template <typename E, bool kGreedy>
-__global__ __launch_bounds__(kBlock) void kr_rowstats_combine(
+__device__ __forceinline__ void combine_row(
     const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
     const int32_t *__restrict__ drafts, int64_t rows, int gamma, int V, float cp, float cq, int S,
     const int32_t *__restrict__ mlen, const uint32_t *__restrict__ alive, int j0, int jn,
     const PartStats *__restrict__ part, RowStats *__restrict__ stats,
-    float *__restrict__ alpha_ws, float *__restrict__ alpha_out) {
-  const int64_t r = ((int64_t)blockIdx.x * kBlock + threadIdx.x) >> 6;
-  const int lane = threadIdx.x & 63;
+    float *__restrict__ alpha_ws, float *__restrict__ alpha_out, int64_t r, int lane) {
   if (r >= rows) return;  // whole waves
   const int64_t bk = r / jn;
   const int j = j0 + (int)(r - bk * jn);
@@ -269,6 +267,19 @@ __global__ __launch_bounds__(kBlock) void kr_rowstats_combine(
   stats[rp] = RowStats{a.mp, a.sp, a.mq, a.sq};
   alpha_ws[rp] = al;
   if (alpha_out) alpha_out[rp] = al;
+}
+
+// One wave per launch row.
+template <typename E, bool kGreedy>
+__global__ __launch_bounds__(kBlock) void kr_rowstats_combine(
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
+    const int32_t *__restrict__ drafts, int64_t rows, int gamma, int V, float cp, float cq, int S,
+    const int32_t *__restrict__ mlen, const uint32_t *__restrict__ alive, int j0, int jn,
+    const PartStats *__restrict__ part, RowStats *__restrict__ stats,
+    float *__restrict__ alpha_ws, float *__restrict__ alpha_out) {
+  const int64_t r = ((int64_t)blockIdx.x * kBlock + threadIdx.x) >> 6;
+  combine_row<E, kGreedy>(p, q, drafts, rows, gamma, V, cp, cq, S, mlen, alive, j0, jn, part,
+                          stats, alpha_ws, alpha_out, r, threadIdx.x & 63);
 }
 
 }  // namespace svd

@@ -14,7 +14,7 @@
 // appendix B.4).
 #pragma once
 
-#include "svd_device.hpp"
+#include "kr_rowstats.hpp"
 
 namespace svd {
 
@@ -222,6 +222,32 @@ __global__ __launch_bounds__(64) void kr_select(const SelectArgs sel,
                                                  DrawDesc *__restrict__ desc) {
   const DrawDesc d = select_prefix(sel, blockIdx.x);
   if (threadIdx.x == 0) desc[blockIdx.x] = d;
+}
+
+// A batch of few scored rows per prefix (K * gamma <= kFuseRows) streamed as
+// split rows in one launch: one workgroup per prefix merges its rows' slice
+// records, a wave per row, then its wave 0 selects, so the selection takes no
+// launch of its own.
+constexpr int kFuseRows = 16;
+
+template <typename E, bool kGreedy>
+__global__ __launch_bounds__(64 * kFuseRows) void kr_combine_select(
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int V,
+    float cp, float cq, int S, const PartStats *__restrict__ part, RowStats *stats,
+    float *alpha_ws, float *__restrict__ alpha_out, const SelectArgs sel,
+    DrawDesc *__restrict__ desc) {
+  // sel.stats and sel.alpha_ws are stats and alpha_ws, read back after the barrier
+  const int64_t b = blockIdx.x;
+  const int64_t kg = (int64_t)sel.K * sel.gamma;  // this prefix's rows
+  const int64_t rows = (int64_t)gridDim.x * kg;
+  combine_row<E, kGreedy>(p, q, sel.drafts, rows, sel.gamma, V, cp, cq, S, sel.win.mlen, nullptr,
+                          0, sel.gamma, part, stats, alpha_ws, alpha_out,
+                          b * kg + (threadIdx.x >> 6), threadIdx.x & 63);
+  __syncthreads();  // the rows' alpha and statistics, visible to wave 0
+  if (threadIdx.x < 64) {
+    const DrawDesc d = select_prefix(sel, b);
+    if (threadIdx.x == 0) desc[b] = d;
+  }
 }
 
 // Usable length of every draft: its window, cut after its first EOS; -1 for a

@@ -162,6 +162,7 @@ struct Batch {
   uint32_t *alive;
   PartStats *part;
   bool vec;  // 16-byte loads
+  bool fuse_select;  // the selection runs in the split rows' merge (kr_combine_select)
   int32_t *selected, *accept_len, *next_token;
   float *scores, *alpha, *beta;
   RowStats *stats;
@@ -192,6 +193,33 @@ int early_chunk(int64_t B, int G) {
   if (SVD_EARLY_CHUNK > 0) return std::min(SVD_EARLY_CHUNK, G);
   const int64_t want = (512 + B - 1) / B;
   return (int)std::max<int64_t>(1, std::min<int64_t>(want, G));
+}
+
+// Split rows: slices per row pair (1: not split) and the slice length for a
+// launch of `rows` row pairs.
+template <typename E>
+void split_plan(const Batch<E> &a, int64_t rows, int &S, int &slice) {
+  S = 1;
+  slice = a.V;
+  if (rows >= kSplitRows) return;
+  const int unit = a.vec ? E::kPerVec : 1;  // elements per load
+  const int64_t units = a.V / unit;
+  const int64_t most = std::max<int64_t>(1, units / (2 * kSplitBlock));
+  const int64_t want = std::min<int64_t>((kSplitTarget + rows - 1) / rows, kPartCap / rows);
+  const int64_t s_try = std::max<int64_t>(1, std::min(most, want));
+  slice = (int)((units + s_try - 1) / s_try) * unit;
+  S = (a.V + slice - 1) / slice;
+}
+
+// the selection's arguments for a batch
+template <typename E>
+SelectArgs make_select(const Batch<E> &a) {
+  return SelectArgs{(const float *)a.alpha_ws, (const RowStats *)a.stats, a.drafts,
+                    (int)a.greedy, a.ix.p, a.greedy ? nullptr : a.ix.q, a.np,
+                    Window{a.windowed ? (const int32_t *)a.mlen : nullptr, a.gamma_b, a.eos,
+                           (int)a.early},
+                    a.K, a.G, a.seed, a.row_base, a.selected, a.accept_len, a.next_token,
+                    a.scores};
 }
 
 // row statistics and alpha (and the optional overlap mass) of a batch
@@ -229,16 +257,8 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   // the positions [j0, j0 + jn) of every draft
   auto stream_rows = [&](int j0, int jn, const uint32_t *alive) -> int {
     const int64_t rows = a.B * a.K * jn;
-    int S = 1, slice = a.V;
-    if (rows < kSplitRows) {
-      const int unit = a.vec ? E::kPerVec : 1;  // elements per load
-      const int64_t units = a.V / unit;
-      const int64_t most = std::max<int64_t>(1, units / (2 * kSplitBlock));
-      const int64_t want = std::min<int64_t>((kSplitTarget + rows - 1) / rows, kPartCap / rows);
-      const int64_t s_try = std::max<int64_t>(1, std::min(most, want));
-      slice = (int)((units + s_try - 1) / s_try) * unit;
-      S = (a.V + slice - 1) / slice;
-    }
+    int S, slice;
+    split_plan<E>(a, rows, S, slice);
     if (S > 1) {
       const dim3 grid((unsigned)(rows * S));
       if (a.greedy)
@@ -249,6 +269,19 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
         SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats_split<E, kVec, false>, grid,
                    dim3(kSplitBlock), s, a.p, a.q, a.G, a.V, a.cp, a.cq, S, slice, mlen, alive, j0,
                    jn, a.part);
+      if (a.fuse_select) {  // the whole window at once, few rows per prefix
+        const SelectArgs sel = make_select(a);
+        const dim3 gb((unsigned)a.B), tb((unsigned)(64 * a.K * a.G));
+        if (a.greedy)
+          SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_combine_select<E, true>, gb, tb, s, a.p, a.q,
+                     a.V, a.cp, a.cq, S, (const PartStats *)a.part, a.stats, a.alpha_ws, a.alpha,
+                     sel, a.desc);
+        else
+          SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_combine_select<E, false>, gb, tb, s, a.p,
+                     a.q, a.V, a.cp, a.cq, S, (const PartStats *)a.part, a.stats, a.alpha_ws,
+                     a.alpha, sel, a.desc);
+        return SVD_OK;
+      }
       const dim3 gc((unsigned)((rows * 64 + kBlock - 1) / kBlock));  // a wave per row
       if (a.greedy)
         SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_rowstats_combine<E, true>, gc, dim3(kBlock), s,
@@ -300,13 +333,8 @@ template <typename E, bool kVec>
 int enqueue_draw(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   const unsigned nb = (unsigned)a.B;
   const unsigned nbs = (unsigned)(a.B * a.nseg);
-  const SelectArgs sel{(const float *)a.alpha_ws, (const RowStats *)a.stats, a.drafts,
-                       (int)a.greedy, a.ix.p, a.greedy ? nullptr : a.ix.q, a.np,
-                       Window{a.windowed ? (const int32_t *)a.mlen : nullptr, a.gamma_b, a.eos,
-                              (int)a.early},
-                       a.K, a.G, a.seed, a.row_base, a.selected, a.accept_len, a.next_token,
-                       a.scores};
-  SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_select, dim3(nb), dim3(64), s, sel, a.desc);
+  if (!a.fuse_select)
+    SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_select, dim3(nb), dim3(64), s, make_select(a), a.desc);
   SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PASS, s, kr_draw_pass<E, kVec>, dim3(nbs), dim3(kPassBlock), s,
              a.p, a.q, a.V, a.nseg, a.tp, a.tq, (const DrawDesc *)a.desc, a.segs, a.uncs);
   SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PICK, s, kr_draw_pick<E, kVec>, dim3(nb), dim3(kPickBlock), s,
@@ -385,6 +413,11 @@ int run(const Call &c) {
   a.segs = reinterpret_cast<DrawSeg *>(ws + Lo.segs);
   a.uncs = reinterpret_cast<DrawUnc *>(ws + Lo.uncs);
   a.mass = reinterpret_cast<DrawMass *>(ws + Lo.mass);
+  // few rows per prefix, dense, the whole window in one split launch: the
+  // selection joins the merge of the split rows
+  int S_all, slice_all;
+  split_plan<E>(a, a.B * a.K * a.G, S_all, slice_all);
+  a.fuse_select = !a.ix.p && !a.early && S_all > 1 && a.K * a.G <= kFuseRows;
 
   hipStream_t stream = static_cast<hipStream_t>(c.stream);
   CallTimer tm;
