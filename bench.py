@@ -130,7 +130,7 @@ def bytes_per_row_pair(V: int, es: int, mode: str = "standard") -> int:
     return rows * V * es + 4 + 16 + 4
 
 
-def cpu_baseline(d, cfg, seed, mode="standard", pooled=False, seconds=10.0):
+def cpu_baseline(d, cfg, seed, mode="standard", pooled=False, seconds=10.0, want_beta=False):
     """The oracle, untuned, on the same batch, repeated until about `seconds`
     of wall time have passed (at least once)."""
     import oracle
@@ -150,7 +150,8 @@ def cpu_baseline(d, cfg, seed, mode="standard", pooled=False, seconds=10.0):
         elif mode == "greedy":
             oracle.greedy_select_and_verify(hp, hd, temp_p=cfg.temp, seed=seed, nthreads=threads)
         else:
-            oracle.select_and_verify(hp, hq, hd, temp_p=cfg.temp, seed=seed, nthreads=threads)
+            oracle.select_and_verify(hp, hq, hd, temp_p=cfg.temp, seed=seed, nthreads=threads,
+                                     want_beta=want_beta)
         dt += time.perf_counter() - t0
         reps += 1
     positions = cfg.B * cfg.K * cfg.gamma
@@ -273,6 +274,9 @@ def main():
     ap.add_argument("--cps", action="store_true",
                     help="time the causal-consistency path search instead (lattice of the "
                          "workload's drafter rows, then a beam of 3; tau 0.8, M_max 15)")
+    ap.add_argument("--beta", action="store_true",
+                    help="also ask for the overlap mass beta (a second pass over every scored "
+                         "row pair; dense workloads, standard rule)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (for counter calibration)")
@@ -329,6 +333,9 @@ def main():
     if early and (pooled or K != 1):
         sys.exit("--early-exit needs a dense workload with K = 1")
     alpha_out = torch.empty((B, K, G), dtype=torch.float32, device=dev) if early else None
+    if args.beta and (early or pooled or greedy):
+        sys.exit("--beta needs a dense workload and the standard rule")
+    beta_out = torch.empty((B, K, G), dtype=torch.float32, device=dev) if args.beta else None
 
     def step():
         if early:
@@ -349,7 +356,7 @@ def main():
         else:
             rc = svd.svd_select_and_verify(d["p"], d["q"], d["drafts"], code, B, K, G, V,
                                            cfg.temp, cfg.temp, cfg.seed, 0, sel, L, tok, None,
-                                           None, None, ws, ws.numel(), stream.cuda_stream)
+                                           None, beta_out, ws, ws.numel(), stream.cuda_stream)
         if rc != svd.SVD_OK:
             raise svd.SvdError(rc, "select_and_verify (%s)" % args.mode)
 
@@ -445,8 +452,15 @@ def main():
         "mat": float(L_host.mean() + 1.0),
         "wall_s": wall,
     }
+    if args.beta:  # the second pass over every scored row pair (logit bytes of both rows)
+        bi = svd.KERNELS.index("beta")
+        ms_beta = ms_all[bi] / max(launches_all[bi], 1)
+        gbps = positions * 2 * V * es / (ms_beta * 1e-3) / 1e9
+        result["beta"] = {"kernel": "kr_beta", "ms": ms_beta, "achieved": gbps, "unit": "GB/s",
+                          "frac": gbps / HBM_PEAK_GBPS}
+        result["config"]["beta"] = True
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(d, cfg, cfg.seed, args.mode, pooled)
+        result["cpu_baseline"] = cpu_baseline(d, cfg, cfg.seed, args.mode, pooled, want_beta=args.beta)
     print(json.dumps(result), flush=True)
 
 
