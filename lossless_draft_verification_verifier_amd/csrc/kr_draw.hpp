@@ -13,8 +13,8 @@
 // launches:
 //
 // kr_draw_pass (prefix, vocabulary segment of kDrawSeg tokens), one fp64 pass:
-//   residual draw: with the exact row maxima from the row-statistics kernel,
-//     w_p = exp(z_p/T_p - M_p) and w_q likewise; the segment sums of w_p and
+//   residual draw: with the exact row maxima m_p, m_q from the row-statistics
+//     kernel, w_p = exp((z_p - m_p)/T_p) and w_q likewise; the segment sums of w_p and
 //     w_q give the exact normalisers S_p, S_q.  Whether p_v > q_v, i.e.
 //     w_p > (S_p/S_q) w_q, is decided against the fp32 ratio from the
 //     row-statistics kernel with a relative margin kClassMargin far above its
@@ -23,7 +23,7 @@
 //     (sum w_p)/S_p - (sum w_q)/S_q.  The rare tokens inside the margin are
 //     settled once S_p and S_q are known.  At equal temperatures the ratio
 //     p_v / q_v of a token depends only on the logit difference
-//     d = z_p - z_q (it is exp(d/T + M_q - M_p) S_q / S_p up to rounding), and
+//     d = z_p - z_q (it is exp((d - m_p + m_q)/T) S_q / S_p up to rounding), and
 //     bf16 logits put hundreds of tokens on each difference, so a margin
 //     token's difference is its class: tokens with d = 0 go to two more sums,
 //     the others are collected in LDS and, when more than kUncCap, merged
@@ -31,7 +31,7 @@
 //     differ from it is within 1e-12 of p_v = q_v, where its weight is below
 //     rounding.  At most kUncCap entries (single tokens or classes) are kept
 //     per segment.
-//   p-row draw (bonus, or greedy rejection): the sums of exp(z/T - m) with
+//   p-row draw (bonus, or greedy rejection): the sums of exp((z - m)/T) with
 //     and without the excluded token, m the row max when the row was scored
 //     (greedy rejection), else the segment max from a first sweep (bonus row).
 // kr_draw_pick (prefix, kPickBlock threads): exact normalisers and segment
@@ -58,12 +58,15 @@ constexpr double kClassMargin = 2e-4;  // relative margin of the p > q test
 constexpr int kPassBlock = 256;        // threads of a pass workgroup
 
 // ---------------------------------------------------------------------------
-// exp(x) in fp64 for x <= 0 (a few ulp above 0 is fine; x must not be NaN):
-// x = n ln2/256 + r with |r| <= ln2/512, n rounded to nearest by the
-// 1.5 * 2^52 shifter in one fma (its low word is n); r by a Cody-Waite split
-// of ln2/256 whose 34-bit head makes n ln2_hi exact for |n| < 2^19; exp(r) by
-// its degree-4 Taylor polynomial (the next term is below 4e-17);
-// 2^(n mod 256 / 256) from a 256-entry table in LDS; then ldexp by n div 256.
+// 2^(x/256) in fp64 for x <= 0 (a few ulp above 0 is fine; x must not be
+// NaN).  The argument comes in 1/256ths of a power of two, so that rounding
+// it to the nearest integer n is one add of the 1.5 * 2^52 shifter (its low
+// word is n) and r = x - n is exact (both are multiples of the ulp of x and
+// |r| <= 1/2).  2^(r/256) = exp(r ln2/256) by its degree-4 Taylor
+// polynomial (the next term is below 4e-17); 2^(n mod 256 / 256) from a
+// 256-entry table in LDS; then ldexp by n div 256.  A row's argument
+// x = c z - M takes c = 256 log2(e)/T and M = c m, which are 256 times their
+// values in base 2 exactly, so one fma forms it.
 
 constexpr int kExpTab = 256;
 
@@ -144,20 +147,32 @@ __device__ __forceinline__ void exp_table_init(ExpTable &tab) {
   for (int i = threadIdx.x; i < kExpTab; i += NT) tab.t[i] = kExp2Frac[i];
 }
 
-__device__ __forceinline__ double exp_nonpos(double x, const ExpTable &tab) {
+__device__ __forceinline__ double exp2_256(double x, const ExpTable &tab) {
   constexpr double kShift = 0x1.8p52;
-  x = fmax(x, -760.0);  // exp(-760) is 0 in double; also maps -inf
-  const double y = __builtin_fma(x, 369.3299304675746, kShift);  // 256 / ln 2
+  x = fmax(x, -281600.0);  // 2^-1100 is 0 in double; also maps -inf
+  const double y = x + kShift;
   const double n = y - kShift;
   const int ni = (int)(uint32_t)__builtin_bit_cast(uint64_t, y);
-  double r = __builtin_fma(-n, 0x1.62e42fef80000p-9, x);
-  r = __builtin_fma(-n, 0x1.1cf79abc9e3b4p-44, r);
-  double p = 1.0 / 24.0;
-  p = __builtin_fma(p, r, 1.0 / 6.0);
-  p = __builtin_fma(p, r, 0.5);
-  p = __builtin_fma(p, r, 1.0);
+  const double r = x - n;
+  // (ln 2 / 256)^k / k!, correctly rounded
+  double p = __builtin_fma(0x1.3b2ab6fba4e77p-39, r, 0x1.c6b08d704a0c0p-29);
+  p = __builtin_fma(p, r, 0x1.ebfbdff82c58fp-19);
+  p = __builtin_fma(p, r, 0x1.62e42fefa39efp-9);
   p = __builtin_fma(p, r, 1.0);
   return ldexp(tab.t[ni & 255] * p, ni >> 8);
+}
+
+constexpr double kLog2e256 = 0x1.71547652b82fep+8;  // 256 log2(e), log2(e) correctly rounded
+
+// exponent scale of a row at temperature t: exp(z/t) = 2^(z c / 256)
+__device__ __forceinline__ double exp2_scale(float t) { return kLog2e256 / (double)t; }
+
+// a wave-uniform double moved to scalar registers
+__device__ __forceinline__ double uniform_d(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 // ---------------------------------------------------------------------------
@@ -274,9 +289,16 @@ struct PassShared {
 template <typename E, bool kVec, int NT>
 __device__ __forceinline__ void pass_residual(PassShared<NT> &S, const typename E::elem *rp,
                                               const typename E::elem *rq, int lo, int hi,
-                                              double invTp, double Mp, double invTq, double Mq,
+                                              double cp, double Mp, double cq, double Mq,
                                               double up, double dn, bool same_t,
                                               double (&acc)[6]) {
+  // wave-uniform operands in scalar registers
+  cp = uniform_d(cp);
+  Mp = uniform_d(Mp);
+  cq = uniform_d(cq);
+  Mq = uniform_d(Mq);
+  up = uniform_d(up);
+  dn = uniform_d(dn);
   double sp = 0.0, sq = 0.0, ap = 0.0, aq = 0.0, ep = 0.0, eq = 0.0;
   // one unit of tokens at a time; its margin tokens are settled after it,
   // behind one branch
@@ -288,8 +310,8 @@ __device__ __forceinline__ void pass_residual(PassShared<NT> &S, const typename 
     uint32_t margin = 0;
 #pragma unroll
     for (int e = 0; e < P; ++e) {
-      const double wp = exp_nonpos(__builtin_fma((double)xp[e], invTp, -Mp), S.tab);
-      const double wq = exp_nonpos(__builtin_fma((double)xq[e], invTq, -Mq), S.tab);
+      const double wp = exp2_256(__builtin_fma((double)xp[e], cp, -Mp), S.tab);
+      const double wq = exp2_256(__builtin_fma((double)xq[e], cq, -Mq), S.tab);
       sp += wp;
       sq += wq;
       const bool pos = wp > up * wq;
@@ -302,8 +324,8 @@ __device__ __forceinline__ void pass_residual(PassShared<NT> &S, const typename 
 #pragma unroll 1
       for (int e = 0; e < P; ++e) {
         if (!((margin >> e) & 1u)) continue;
-        const double wp = exp_nonpos(__builtin_fma((double)xp[e], invTp, -Mp), S.tab);
-        const double wq = exp_nonpos(__builtin_fma((double)xq[e], invTq, -Mq), S.tab);
+        const double wp = exp2_256(__builtin_fma((double)xp[e], cp, -Mp), S.tab);
+        const double wq = exp2_256(__builtin_fma((double)xq[e], cq, -Mq), S.tab);
         if (same_t && xp[e] == xq[e]) {
           ep += wp;
           eq += wq;
@@ -401,7 +423,7 @@ __global__ __launch_bounds__(kPassBlock) __attribute__((amdgpu_waves_per_eu(6)))
   if (threadIdx.x == 0) S.n_unc = 0;
   __syncthreads();
   const typename E::elem *rp = p + d.prow * (int64_t)V;
-  const double invTp = 1.0 / (double)tp, invTq = 1.0 / (double)tq;
+  const double cp = exp2_scale(tp), cq = exp2_scale(tq);
   const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
   const int64_t so = b * nseg + seg;
   double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
@@ -409,8 +431,8 @@ __global__ __launch_bounds__(kPassBlock) __attribute__((amdgpu_waves_per_eu(6)))
     const typename E::elem *rq = q + d.qrow * (int64_t)V;
     const double rho = (double)d.st.sp / (double)d.st.sq;  // fp32 estimate of S_p / S_q
     const double up = rho * (1.0 + kClassMargin), dn = rho * (1.0 - kClassMargin);
-    pass_residual<E, kVec, NT>(S, rp, rq, lo, hi, invTp, (double)d.st.mp / (double)tp, invTq,
-                               (double)d.st.mq / (double)tq, up, dn, tp == tq, acc);
+    pass_residual<E, kVec, NT>(S, rp, rq, lo, hi, cp, (double)d.st.mp * cp, cq,
+                               (double)d.st.mq * cq, up, dn, tp == tq, acc);
     pass_finish<NT>(S, acc, kNegInf, 0, tp == tq, segs, uncs, so);
     return;
   }
@@ -427,11 +449,11 @@ __global__ __launch_bounds__(kPassBlock) __attribute__((amdgpu_waves_per_eu(6)))
     mseg = block_max<NT / 64>(m, S.redf);
     bad = block_max_i<NT / 64>(bad, S.redi);
   }
-  const double M = (double)fmaxf(mseg, kLowest) / (double)tp;
+  const double M = (double)fmaxf(mseg, kLowest) * cp;
   const int excl = d.excl;  // sp: every token; ap: all but the excluded one
   double sp = 0.0, ap = 0.0;
   visit_segment<E, kVec, false, NT>(rp, rp, lo, hi, [&](int v, float zp, float) {
-    const double wp = exp_nonpos(__builtin_fma((double)zp, invTp, -M), S.tab);
+    const double wp = exp2_256(__builtin_fma((double)zp, cp, -M), S.tab);
     sp += wp;
     ap = __builtin_fma(v != excl ? 1.0 : 0.0, wp, ap);
   });
@@ -444,14 +466,14 @@ __global__ __launch_bounds__(kPassBlock) __attribute__((amdgpu_waves_per_eu(6)))
 template <typename E>
 struct DrawWeight {
   const typename E::elem *p, *q;
-  double invTp, invTq, Mp, Mq, invSp, invSq;
+  double cp, cq, Mp, Mq, invSp, invSq;  // weight 2^((c z - M)/256) = exp((z - m)/T)
   bool resid;  // max(0, p - q); otherwise p with token excl zeroed
   int excl;
   // weight of token v from its two logits
   __device__ __forceinline__ double from(int v, float zp, float zq, const ExpTable &tab) const {
-    const double pv = exp_nonpos(__builtin_fma((double)zp, invTp, -Mp), tab) * invSp;
+    const double pv = exp2_256(__builtin_fma((double)zp, cp, -Mp), tab) * invSp;
     if (!resid) return v == excl ? 0.0 : pv;
-    const double qv = exp_nonpos(__builtin_fma((double)zq, invTq, -Mq), tab) * invSq;
+    const double qv = exp2_256(__builtin_fma((double)zq, cq, -Mq), tab) * invSq;
     const double dd = pv - qv;
     return dd > 0.0 ? dd : 0.0;
   }
@@ -481,16 +503,16 @@ __device__ __forceinline__ bool draw_setup(const typename E::elem *rp,
   const int lane = threadIdx.x & 63;
   W.p = rp;
   W.q = rq;
-  W.invTp = 1.0 / (double)tp;
-  W.invTq = 1.0 / (double)tq;
+  W.cp = exp2_scale(tp);
+  W.cq = exp2_scale(tq);
   W.resid = d.two != 0;
   W.excl = d.excl;
   double Sp = 0.0, Sq = 1.0;
   // segment sums relative to one max (residual rows and scored p rows) or to
   // their segments' maxima (bonus rows)
   if (W.resid) {
-    W.Mp = (double)d.st.mp / (double)tp;
-    W.Mq = (double)d.st.mq / (double)tq;
+    W.Mp = (double)d.st.mp * W.cp;
+    W.Mq = (double)d.st.mq * W.cq;
     double a = 0.0, c = 0.0;
     for (int s = lane; s < nseg; s += 64) {
       a += S[s].sp;
@@ -507,12 +529,12 @@ __device__ __forceinline__ bool draw_setup(const typename E::elem *rp,
     }
     const float mr = wave_max_f(m);
     if (__any(bad) || mr == kNegInf || mr == -kNegInf) return false;
-    W.Mp = (double)mr / (double)tp;
+    W.Mp = (double)mr * W.cp;
     W.Mq = 0.0;
     double a = 0.0;
     for (int s = lane; s < nseg; s += 64) {
-      const double Ms = (double)fmaxf(S[s].mseg, kLowest) / (double)tp;
-      a += (S[s].mseg == mr) ? S[s].sp : S[s].sp * exp(Ms - W.Mp);
+      const double Ms = (double)fmaxf(S[s].mseg, kLowest) * W.cp;
+      a += (S[s].mseg == mr) ? S[s].sp : S[s].sp * exp2((Ms - W.Mp) * 0x1.0p-8);
     }
     Sp = wave_sum_d(a);
   }
@@ -651,8 +673,8 @@ __global__ __launch_bounds__(kPickBlock) void kr_draw_pick(
         m.zr = z;
       }
     } else {  // p row: zp with every token, zr without the excluded one
-      const double Ms = (double)fmaxf(g.mseg, kLowest) / (double)tp;
-      const double scale = (g.mseg == kNegInf) ? 0.0 : exp(Ms - W.Mp);
+      const double Ms = (double)fmaxf(g.mseg, kLowest) * W.cp;
+      const double scale = (g.mseg == kNegInf) ? 0.0 : exp2((Ms - W.Mp) * 0x1.0p-8);
       m.zp = g.sp * scale * W.invSp;
       m.zr = g.ap * scale * W.invSp;
     }
