@@ -27,9 +27,11 @@ PROFILE_EVERY = 10  # timed steps per step whose dominant-kernel launches carry 
 METRIC = "verified draft positions/sec and achieved HBM GB/s (V=152064, bf16 logits)"
 # sources whose text decides each kernel's memory traffic
 KERNEL_SOURCES = {"rowstats": ["svd_device.hpp", "kr_rowstats.hpp"],
+                  "rowstats_split": ["svd_device.hpp", "kr_rowstats.hpp"],
                   "pool_stats": ["svd_device.hpp", "kr_rowstats.hpp", "kr_rows.hpp"],
                   "lattice": ["svd_device.hpp", "kr_rowstats.hpp", "kr_cps.hpp"]}
-KERNEL_SYMBOL = {"rowstats": "kr_rowstats", "pool_stats": "kr_pool_stats",
+KERNEL_SYMBOL = {"rowstats": "kr_rowstats", "rowstats_split": "kr_rowstats_split",
+                 "pool_stats": "kr_pool_stats",
                  "lattice": "kr_lattice"}
 
 
@@ -368,7 +370,9 @@ def main():
     # timed region: K steps; HIP events around the dominant kernel's launches,
     # recorded on the stream the kernel is launched on, in every PROFILE_EVERY-th
     # step (each timing event costs the step a queue drain, ~17 us)
+    # (row pairs split into slices stream through kr_rowstats_split instead)
     dom = "pool_stats" if pooled else "rowstats"
+    timed = [dom] if pooled else ["rowstats", "rowstats_split"]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -377,7 +381,7 @@ def main():
     for i in range(args.steps):
         sampled = i % PROFILE_EVERY == 0
         if sampled:
-            svd.svd_profile_enable([dom])
+            svd.svd_profile_enable(timed)
         step()
         if sampled:
             svd.svd_profile_enable(())
@@ -386,6 +390,8 @@ def main():
     wall = time.perf_counter() - t0
     ms_kernels, launches = svd.svd_profile_read()
     ms_step = ev0.elapsed_time(ev1) / args.steps
+    if not pooled and launches[svd.KERNELS.index("rowstats")] == 0:
+        dom = "rowstats_split"
 
     # after the timed region: a few steps with every kernel timed, for the breakdown
     svd.svd_profile_enable("all")

@@ -262,11 +262,11 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
     if (S > 1) {
       const dim3 grid((unsigned)(rows * S));
       if (a.greedy)
-        SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats_split<E, kVec, true>, grid,
+        SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS_SPLIT, s, kr_rowstats_split<E, kVec, true>, grid,
                    dim3(kSplitBlock), s, a.p, a.q, a.G, a.V, a.cp, a.cq, S, slice, mlen, alive, j0,
                    jn, a.part);
       else
-        SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats_split<E, kVec, false>, grid,
+        SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS_SPLIT, s, kr_rowstats_split<E, kVec, false>, grid,
                    dim3(kSplitBlock), s, a.p, a.q, a.G, a.V, a.cp, a.cq, S, slice, mlen, alive, j0,
                    jn, a.part);
       if (a.fuse_select) {  // the whole window at once, few rows per prefix

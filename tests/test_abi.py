@@ -139,3 +139,13 @@ def test_binding_fails_loudly_without_library(tmp_path):
     code = "import sys; sys.path.insert(0, %r); import svdcopy" % str(tmp_path)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
     assert r.returncode != 0 and "libsvd.so is not built" in r.stderr
+
+
+def test_profile_kernel_names_follow_the_header(svd):
+    # the binding's KERNELS tuple is indexed by the header's SVD_KERNEL_* ids
+    text = open(HEADER).read()
+    ids = {m.group(1).lower(): int(m.group(2))
+           for m in re.finditer(r"SVD_KERNEL_([A-Z_]+) = (\d+)", text)}
+    count = ids.pop("count")
+    assert len(svd.KERNELS) == count
+    assert {name: i for i, name in enumerate(svd.KERNELS)} == ids
