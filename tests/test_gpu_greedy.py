@@ -28,6 +28,8 @@ CASES = [
     (1, 64, 2, 512, "bf16", 2.0),
     (2, 1, 1, 1, "f32", 1.0),            # V = 1: p(x) = 1, always accepted
     (3, 2, 2, 2, "bf16", 1.0),
+    (4, 2, 5, 9000, "bf16", 0.05),       # nearly one-hot rows: weights down to the exp's clamp
+    (4, 2, 5, 9000, "bf16", 40.0),       # nearly uniform rows
 ]
 
 

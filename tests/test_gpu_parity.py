@@ -48,6 +48,26 @@ def test_small_shapes_match_oracle(orc, case, seed):
     assert rep.invalid == 0
 
 
+@pytest.mark.parametrize("temp", [0.05, 0.2, 8.0, 40.0])
+def test_extreme_temperatures(orc, temp):
+    # 0.05: nearly one-hot rows, draw weights down to 2^-500 and below the
+    # exp's underflow clamp; 40: nearly uniform rows, p and q close, so the
+    # residual is small and most tokens sit near the p > q margin
+    svd = require_gpu()
+    B, K, G, V = 6, 2, 5, 9000
+    say("temp", temp)
+    cfg = W.Config(99, "custom", B=B, K=K, gamma=G, V=V, dtype="bf16", sigma0=0.5,
+                   sigma_step=0.05, temp=temp, boost=6.0, boost_prob=0.8)
+    d = gen(cfg, data_seed=int(temp * 100) + 3)
+    g = run_select(svd, d, temp, 9, want_beta=True)
+    check_ranges(g, K, G, V)
+    hp, hq, hd = host_inputs(d)
+    rep = compare(orc, hp, hq, hd, g, temp, temp, 9)
+    say(rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    assert rep.invalid == 0
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_tiny_workload_matches_oracle(orc, seed):
     svd = require_gpu()
