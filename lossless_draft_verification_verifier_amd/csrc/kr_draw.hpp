@@ -12,7 +12,7 @@
 // (DrawDesc).  The rows are recomputed from the logits in fp64, in two
 // launches:
 //
-// kr_draw_pass (prefix, vocabulary segment of kDrawSeg tokens), one fp64 pass:
+// kr_draw_pass (prefix, vocabulary segment of SEG tokens), one fp64 pass:
 //   residual draw: with the exact row maxima m_p, m_q from the row-statistics
 //     kernel, w_p = exp((z_p - m_p)/T_p) and w_q likewise; the segment sums of w_p and
 //     w_q give the exact normalisers S_p, S_q.  Whether p_v > q_v, i.e.
@@ -36,11 +36,14 @@
 //     (greedy rejection), else the segment max from a first sweep (bonus row).
 // kr_draw_pick (prefix, kPickBlock threads): exact normalisers and segment
 //   masses (a segment whose uncertain list overflowed is recomputed here, all
-//   threads on one segment), the segment that holds t, then each thread takes
-//   kRun consecutive tokens of that segment into registers and a workgroup
-//   prefix sum over the threads' totals locates the token.  The rare fallback
-//   (t at or past the total) scans segments from the end for the last token
-//   with weight.
+//   threads on one segment), the segment that holds t (a scan over lanes that
+//   hold one segment each, or a run of consecutive segments each when there
+//   are more than 64), then each thread takes kRun consecutive tokens of that
+//   segment into registers and a workgroup prefix sum over the threads' totals
+//   locates the token.  The rare fallback (t at or past the total) scans
+//   segments from the end for the last token with weight.
+// SEG is kDrawSeg, or kDrawSegSmall when the batch has too few prefixes to
+// fill the GPU with segments of kDrawSeg tokens.
 // Every reduction has a fixed order and the uncertain tokens are summed in
 // token order, so the result is deterministic.
 #pragma once
@@ -408,7 +411,7 @@ __device__ __forceinline__ void pass_finish(PassShared<NT> &S, double (&acc)[6],
   }
 }
 
-template <typename E, bool kVec>
+template <typename E, bool kVec, int SEG>
 __global__ __launch_bounds__(kPassBlock) __attribute__((amdgpu_waves_per_eu(6))) void kr_draw_pass(
     const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int V,
     int nseg, float tp, float tq, const DrawDesc *__restrict__ desc,
@@ -424,7 +427,7 @@ __global__ __launch_bounds__(kPassBlock) __attribute__((amdgpu_waves_per_eu(6)))
   __syncthreads();
   const typename E::elem *rp = p + d.prow * (int64_t)V;
   const double cp = exp2_scale(tp), cq = exp2_scale(tq);
-  const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
+  const int lo = seg * SEG, hi = min(V, lo + SEG);
   const int64_t so = b * nseg + seg;
   double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
   if (d.two) {
@@ -574,10 +577,10 @@ __device__ __forceinline__ void run_weights(const DrawWeight<E> &W, int a, int h
 }
 
 // Exact residual mass of one segment (all NT threads); valid in thread 0.
-template <typename E, bool kVec, int NT>
+template <typename E, bool kVec, int NT, int SEG>
 __device__ __forceinline__ double segment_mass_exact(const DrawWeight<E> &W, int V, int seg,
                                                      const ExpTable &tab, double *ldsd) {
-  const int lo = seg * kDrawSeg, hi = min(V, lo + kDrawSeg);
+  const int lo = seg * SEG, hi = min(V, lo + SEG);
   double z = 0.0;
   visit_segment<E, kVec, true, NT>(W.p, W.q, lo, hi, [&](int v, float zp, float zq) {
     z += W.from(v, zp, zq, tab);
@@ -608,7 +611,7 @@ __device__ __forceinline__ double block_exclusive_scan(double x, double *lds /* 
 // The pick: one workgroup of kPickBlock threads per prefix.  mass is global
 // scratch for the segment masses of vocabularies with more than kPickSegs
 // segments.
-template <typename E, bool kVec>
+template <typename E, bool kVec, int SEG>
 __global__ __launch_bounds__(kPickBlock) void kr_draw_pick(
     const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int V,
     int nseg, float tp, float tq, uint64_t seed, uint64_t row_base,
@@ -617,7 +620,9 @@ __global__ __launch_bounds__(kPickBlock) void kr_draw_pick(
     int32_t *__restrict__ selected, int32_t *__restrict__ accept_len,
     int32_t *__restrict__ next_token) {
   constexpr int NT = kPickBlock, NW = NT / 64;
-  constexpr int kRun = kDrawSeg / NT;  // tokens per thread in the scan of one segment
+  // tokens per thread in the scan of one segment (whole 16-byte vectors); in a
+  // segment shorter than NT * kRun the threads past its end hold no tokens
+  constexpr int kRun = SEG / NT > 8 ? SEG / NT : 8;
   __shared__ ExpTable tab;
   __shared__ double ldsd[NW + 1];
   __shared__ int ldsi[NW + 1];
@@ -686,7 +691,7 @@ __global__ __launch_bounds__(kPickBlock) void kr_draw_pick(
   if (__any(overflow)) {  // segments whose list overflowed: exact, all threads
     for (int s = 0; s < nseg; ++s) {
       if (S[s].n_unc >= 0) continue;
-      const double z = segment_mass_exact<E, kVec, NT>(W, V, s, tab, ldsd);
+      const double z = segment_mass_exact<E, kVec, NT, SEG>(W, V, s, tab, ldsd);
       if (tid == 0) ms[s].zr = z;
       __syncthreads();
     }
@@ -726,21 +731,40 @@ __global__ __launch_bounds__(kPickBlock) void kr_draw_pick(
       cum = __shfl(lane == 0 ? 0.0 : excl, s0, 64);
     }
   } else {
-    for (int s = 0; s < nseg; ++s) {
-      const double w = use_r ? ms[s].zr : ms[s].zp;
-      if (cum + w > t) {
-        s0 = s;
-        break;
+    // lane l holds the run of segments [l c, l c + c); the first lane whose
+    // inclusive sum exceeds t names the run, and a walk from the run's start
+    // finds the segment (it goes on past the run if rounding moved the hit)
+    const int c = (nseg + 63) >> 6;
+    const int r0 = lane * c, r1 = min(nseg, r0 + c);
+    double w = 0.0;
+    for (int s = r0; s < r1; ++s) w += use_r ? ms[s].zr : ms[s].zp;
+    double incl = w;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const double excl = __shfl_up(incl, 1, 64);
+    const uint64_t hit = __ballot(r0 < nseg && incl > t);
+    if (hit) {
+      const int l0 = __ffsll((unsigned long long)hit) - 1;
+      cum = __shfl(lane == 0 ? 0.0 : excl, l0, 64);
+      for (int s = l0 * c; s < nseg; ++s) {
+        const double ws = use_r ? ms[s].zr : ms[s].zp;
+        if (cum + ws > t) {
+          s0 = s;
+          break;
+        }
+        cum += ws;
       }
-      cum += w;
     }
   }
   int tok = -1;
   if (s0 >= 0) {
     for (int s = s0; s < nseg; ++s) {
       // thread tid owns tokens [a, a + kRun) of the segment, kept in registers
-      const int hi = min(V, (s + 1) * kDrawSeg);
-      const int a = s * kDrawSeg + tid * kRun;
+      const int hi = min(V, (s + 1) * SEG);
+      const int a = s * SEG + tid * kRun;
       double w[kRun];
       run_weights<E, kVec, kRun>(W, a, hi, tab, w);
       double loc = 0.0;
@@ -763,8 +787,8 @@ __global__ __launch_bounds__(kPickBlock) void kr_draw_pick(
   }
   // t at or past the total through rounding: the last token with weight
   for (int s = nseg - 1; s >= 0 && tok < 0; --s) {
-    const int hi = min(V, (s + 1) * kDrawSeg);
-    const int a = s * kDrawSeg + tid * kRun;
+    const int hi = min(V, (s + 1) * SEG);
+    const int a = s * SEG + tid * kRun;
     double w[kRun];
     run_weights<E, kVec, kRun>(W, a, hi, tab, w);
     int last = -1;

@@ -25,8 +25,18 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
   size_t stats, alpha, desc, segs, uncs, mass, mlen, alive, part, pstat, flags, total;
-  int nseg;
+  int seg, nseg;
 };
+
+// Tokens per draw segment: the pass runs one workgroup per (prefix, segment)
+// and about 1536 of them are resident at once, so a batch that would fill
+// fewer than half of those with segments of kDrawSeg tokens takes segments of
+// kDrawSegSmall (a shorter serial run per workgroup, more workgroups).
+constexpr int64_t kDrawSmallBelow = 768;
+int draw_seg(int64_t B, int32_t V) {
+  const int64_t nbig = ((int64_t)V + kDrawSeg - 1) / kDrawSeg;
+  return B * nbig < kDrawSmallBelow ? kDrawSegSmall : kDrawSeg;
+}
 
 // Split rows: at most this many (row pair, slice) records per launch.
 constexpr int kPartCap = 4096;
@@ -36,7 +46,8 @@ constexpr int64_t kSplitTarget = 2048;  // slice workgroups to aim for
 bool sizes_ok(int64_t B, int32_t K, int32_t G, int32_t V) {
   if (B < 1 || K < 1 || G < 1 || V < 1) return false;
   if (K > SVD_MAX_K || G > SVD_MAX_GAMMA) return false;
-  const int64_t nseg = ((int64_t)V + kDrawSeg - 1) / kDrawSeg;
+  const int seg = draw_seg(B, V);
+  const int64_t nseg = ((int64_t)V + seg - 1) / seg;
   const int64_t lim = (int64_t)1 << 31;
   if (B >= lim / ((int64_t)K * G)) return false;  // B*K*gamma workgroups
   if (B >= lim / nseg) return false;              // B*nseg workgroups
@@ -47,7 +58,8 @@ bool sizes_ok(int64_t B, int32_t K, int32_t G, int32_t V) {
 Layout layout(int64_t B, int32_t K, int32_t G, int32_t V, int64_t np = 0, int64_t nq = 0) {
   Layout L{};
   const size_t rp = (size_t)B * K * G;
-  L.nseg = (int)(((int64_t)V + kDrawSeg - 1) / kDrawSeg);
+  L.seg = draw_seg(B, V);
+  L.nseg = (int)(((int64_t)V + L.seg - 1) / L.seg);
   size_t off = 0;
   L.stats = off;
   off = align_up(off + rp * sizeof(RowStats));
@@ -147,7 +159,7 @@ struct Batch {
   const typename E::elem *p, *q;
   const int32_t *drafts;
   int64_t B;
-  int K, G, V, nseg;
+  int K, G, V, seg, nseg;
   float tp, tq, cp, cq;
   uint64_t seed, row_base;
   bool greedy;  // greedy acceptance: alpha = p(x), q unused
@@ -328,20 +340,30 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   return SVD_OK;
 }
 
+// the draw's pass and pick, in segments of SEG tokens
+template <typename E, bool kVec, int SEG>
+int enqueue_pass_pick(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
+  const unsigned nb = (unsigned)a.B;
+  const unsigned nbs = (unsigned)(a.B * a.nseg);
+  SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PASS, s, kr_draw_pass<E, kVec, SEG>, dim3(nbs),
+             dim3(kPassBlock), s, a.p, a.q, a.V, a.nseg, a.tp, a.tq, (const DrawDesc *)a.desc,
+             a.segs, a.uncs);
+  SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PICK, s, kr_draw_pick<E, kVec, SEG>, dim3(nb),
+             dim3(kPickBlock), s, a.p, a.q, a.V, a.nseg, a.tp, a.tq, a.seed, a.row_base,
+             (const DrawDesc *)a.desc, (const DrawSeg *)a.segs, (const DrawUnc *)a.uncs, a.mass,
+             a.selected, a.accept_len, a.next_token);
+  return SVD_OK;
+}
+
 // selection, first rejection and the draw of a batch whose statistics are done
 template <typename E, bool kVec>
 int enqueue_draw(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   const unsigned nb = (unsigned)a.B;
-  const unsigned nbs = (unsigned)(a.B * a.nseg);
   if (!a.fuse_select)
     SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_select, dim3(nb), dim3(64), s, make_select(a), a.desc);
-  SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PASS, s, kr_draw_pass<E, kVec>, dim3(nbs), dim3(kPassBlock), s,
-             a.p, a.q, a.V, a.nseg, a.tp, a.tq, (const DrawDesc *)a.desc, a.segs, a.uncs);
-  SVD_LAUNCH(tm, SVD_KERNEL_DRAW_PICK, s, kr_draw_pick<E, kVec>, dim3(nb), dim3(kPickBlock), s,
-             a.p, a.q, a.V, a.nseg, a.tp, a.tq, a.seed, a.row_base, (const DrawDesc *)a.desc,
-             (const DrawSeg *)a.segs, (const DrawUnc *)a.uncs, a.mass, a.selected, a.accept_len,
-             a.next_token);
-  return SVD_OK;
+  if (a.seg == kDrawSeg)
+    return enqueue_pass_pick<E, kVec, kDrawSeg>(a, s, tm);
+  return enqueue_pass_pick<E, kVec, kDrawSegSmall>(a, s, tm);
 }
 
 // The arguments of one entry-point call.
@@ -379,6 +401,7 @@ int run(const Call &c) {
   a.K = c.K;
   a.G = c.G;
   a.V = c.V;
+  a.seg = Lo.seg;
   a.nseg = Lo.nseg;
   a.tp = c.tp;
   a.tq = c.tq;

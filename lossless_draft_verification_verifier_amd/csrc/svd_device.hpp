@@ -10,6 +10,7 @@ namespace svd {
 constexpr int kBlock = 256;         // threads per workgroup (4 waves of 64)
 constexpr int kWaves = kBlock / 64;
 constexpr int kDrawSeg = 8192;      // vocabulary segment of the fp64 draw
+constexpr int kDrawSegSmall = 1024; // the same for batches too small to fill the GPU
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLowest = -3.40282347e38f;
 

@@ -25,6 +25,9 @@ CASES = [
     (3, 1, 70, 2048, "bf16", 1.0),       # gamma beyond one wave of 64
     (1, 64, 2, 512, "bf16", 2.0),        # K at its limit
     (17, 2, 4, 3000, "f32", 0.5),
+    (800, 1, 2, 8193, "bf16", 1.0),      # a batch drawn in segments of 8192: one-token second segment
+    (3, 2, 4, 1032, "bf16", 1.0),        # segments of 1024: an 8-token second segment
+    (2, 1, 3, 70008, "bf16", 0.7),       # 69 segments of 1024: runs of segments per lane in the pick
     (2, 1, 1, 1, "f32", 1.0),            # V = 1: every row is one token
     (3, 2, 2, 2, "bf16", 1.0),
 ]
@@ -105,6 +108,11 @@ def test_many_prefixes_flag_rates(orc):
     assert rep.flag_rate() < 1e-3
 
 
+# 8 prefixes of 20000 tokens are drawn in segments of 1024 tokens, 400 in
+# segments of 8192 (the draw cuts rows finer when a batch is small)
+MARGIN_BATCHES = [8, 400]
+
+
 def _margin_case(B, seed):
     # q equals p except at the drafted token (a median one), raised by 2, so
     # most drafts are rejected at position 0 and S_q / S_p is within the
@@ -119,7 +127,7 @@ def _margin_case(B, seed):
     return G, {"p": zp.contiguous(), "q": zq.contiguous(), "drafts": x.contiguous()}
 
 
-@pytest.mark.parametrize("B", [8, 80])
+@pytest.mark.parametrize("B", MARGIN_BATCHES)
 def test_residual_inside_the_margin_everywhere(orc, B):
     # at one temperature every other token has w_p == w_q exactly: the margin
     # tokens settle as one sum whose sign is that of 1/S_p - 1/S_q
@@ -152,7 +160,7 @@ def test_equal_logit_class_with_distinct_maxima(orc, shift):
     assert rep.ok(), rep.failures
 
 
-@pytest.mark.parametrize("B", [8, 80])
+@pytest.mark.parametrize("B", MARGIN_BATCHES)
 def test_margin_classes_of_one_logit_difference(orc, B):
     # the case above with 2 % of q's logits lowered by 2^-14 and 1 % by 2^-13:
     # each difference is one class of about 60-160 margin tokens per segment,
@@ -172,7 +180,7 @@ def test_margin_classes_of_one_logit_difference(orc, B):
     assert rep.ok(), rep.failures
 
 
-@pytest.mark.parametrize("B", [8, 80])
+@pytest.mark.parametrize("B", MARGIN_BATCHES)
 def test_residual_margin_lists_overflow(orc, B):
     # the same rows with q read at a temperature 2^-17 above p's: every p/q ratio
     # is within the margin and almost none is exactly 1, so every segment's
