@@ -42,3 +42,9 @@ def test_tiny_workload_chi_square_on_gpu(orc):
     rep = compare(orc, hp, hq, dr[:m], g, cfg.temp, cfg.temp, cfg.seed)
     say(rep.summary())
     assert rep.ok(), rep.failures[:5]
+    # mismatches excused as near-ties stay under 0.01 % of the decisions of
+    # each kind (50000 draws and selections, over 10^5 acceptance tests)
+    for kind in ("accept", "emit"):
+        say(kind, "decisions", rep.decisions[kind], "excused", rep.flagged[kind],
+            "near-ties", rep.near_ties[kind])
+        assert rep.flagged[kind] < 1e-4 * rep.decisions[kind]
