@@ -283,3 +283,60 @@ __global__ __launch_bounds__(kBlock) void kr_rowstats_combine(
 }
 
 }  // namespace svd
+
+namespace svd {
+
+// ---------------------------------------------------------------------------
+// Early exit over a live list.  One draft per prefix is streamed in chunks of
+// J positions; the prefixes not yet rejected form a list (live, its length in
+// a device counter) that the merge of each chunk rebuilds for the next.  A
+// chunk's launch has a fixed grid of kLiveGrid workgroups and cuts each of
+// its n * J rows into as many slices as fill that grid, so the later chunks,
+// with few prefixes left, still spread over every CU.  The slicing depends
+// only on n, so a row's statistics do not depend on which prefixes are live.
+constexpr int kLiveGrid = 2048;
+
+struct LivePlan {
+  int S;      // slices per row
+  int slice;  // elements per slice (whole loads)
+};
+
+// units: loads per row (V / elements per load); Smax: most slices per row
+__device__ __forceinline__ LivePlan live_plan(int64_t rows, int units, int unit, int Smax) {
+  int64_t s = rows > 0 ? kLiveGrid / rows : 1;
+  s = s < 1 ? 1 : (s > Smax ? Smax : s);
+  const int su = (int)((units + s - 1) / s);  // loads per slice
+  return LivePlan{(units + su - 1) / su, su * unit};
+}
+
+// Workgroup w: slice w % S of row r = w / S, i.e. position j0 + r % J of the
+// prefix live[r / J]; positions past the prefix's usable length are skipped.
+template <typename E, bool kVec, bool kGreedy>
+__global__ __launch_bounds__(kSplitBlock) void kr_rowstats_live(
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q, int gamma,
+    int V, float cp, float cq, int units, int unit, int Smax, const int32_t *__restrict__ mlen,
+    const int32_t *__restrict__ live, const uint32_t *__restrict__ count, int j0, int J,
+    PartStats *__restrict__ part) {
+  __shared__ float lds[2 * (kSplitBlock / 64)];
+  const int64_t rows = (int64_t)*count * J;
+  const LivePlan L = live_plan(rows, units, unit, Smax);
+  const int64_t item = blockIdx.x;
+  if (item >= rows * L.S) return;
+  const int64_t r = item / L.S;
+  const int sl = (int)(item - r * L.S);
+  const int64_t w = r / J;
+  const int j = j0 + (int)(r - w * J);
+  const int64_t b = live[w];
+  if (j >= gamma || j >= mlen[b]) return;
+  const int lo = sl * L.slice, hi = min(V, lo + L.slice);
+  const typename E::elem *prow = p + (b * (gamma + 1) + j) * (int64_t)V + lo;
+  float mp, sp, mq = 0.0f, sq = 1.0f;
+  row_ms<E, kVec, kSplitBlock, kRowUnroll>(prow, hi - lo, cp, mp, sp, lds);
+  if constexpr (!kGreedy) {
+    const typename E::elem *qrow = q + (b * gamma + j) * (int64_t)V + lo;
+    row_ms<E, kVec, kSplitBlock, kRowUnroll>(qrow, hi - lo, cq, mq, sq, lds);
+  }
+  if (threadIdx.x == 0) part[item] = PartStats{mp, sp, mq, sq};
+}
+
+}  // namespace svd

@@ -251,13 +251,20 @@ __global__ __launch_bounds__(64 * kFuseRows) void kr_combine_select(
 }
 
 // Usable length of every draft: its window, cut after its first EOS; -1 for a
-// window outside [1, gamma].
+// window outside [1, gamma].  Early exit over a live list (counts non-null,
+// one draft per prefix): the first chunk's list holds every prefix, and the
+// ncounts chunk counters start at {BK, 0, 0, ...}; the grid covers
+// max(BK, ncounts) threads.
 __global__ __launch_bounds__(kBlock) void kr_window(const int32_t *__restrict__ drafts,
                                                     const int32_t *__restrict__ gamma_b, int eos,
                                                     int64_t BK, int K, int gamma,
-                                                    int32_t *__restrict__ mlen) {
+                                                    int32_t *__restrict__ mlen,
+                                                    int32_t *__restrict__ live,
+                                                    uint32_t *__restrict__ counts, int ncounts) {
   const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;  // b * K + k
+  if (counts && i < ncounts) counts[i] = i == 0 ? (uint32_t)BK : 0u;
   if (i >= BK) return;
+  if (counts) live[i] = (int32_t)i;
   const int n = gamma_b ? gamma_b[i / K] : gamma;
   int m = (n < 1 || n > gamma) ? -1 : n;
   for (int j = 0; j < m && eos >= 0; ++j)
@@ -284,6 +291,77 @@ __global__ __launch_bounds__(kBlock) void kr_advance(const float *__restrict__ a
       alive[b] = 0u;
       return;
     }
+}
+
+// Early exit over a live list: the merge of chunk [j0, j0 + J), one wave per
+// live prefix (lanes over the slices of each row, as in combine_row), then
+// the chunk's acceptance tests in order.  A prefix with every test passed and
+// positions left joins the next chunk's list; one that leaves the stream
+// marks the alpha of its later positions NaN (not streamed).  The next list's
+// order follows the atomic counter, which changes no result: each row is
+// merged in slice order.
+template <typename E, bool kGreedy>
+__global__ __launch_bounds__(kBlock) void kr_combine_advance(
+    const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
+    const int32_t *__restrict__ drafts, int gamma, int V, float cp, float cq, int units, int unit,
+    int Smax, const int32_t *__restrict__ mlen, const int32_t *__restrict__ live,
+    const uint32_t *__restrict__ count, int j0, int J, const PartStats *__restrict__ part,
+    RowStats *__restrict__ stats, float *__restrict__ alpha_ws, float *__restrict__ alpha_out,
+    uint64_t seed, uint64_t row_base, int32_t *__restrict__ live_next,
+    uint32_t *__restrict__ count_next) {
+  const int64_t n = *count;
+  const int64_t w = ((int64_t)blockIdx.x * kBlock + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (w >= n) return;  // whole waves
+  const LivePlan L = live_plan(n * J, units, unit, Smax);
+  const int64_t b = live[w];
+  const int m = mlen[b];
+  bool rejected = false;
+  for (int jj = 0; jj < J; ++jj) {
+    const int j = j0 + jj;
+    if (j >= gamma) break;
+    const int64_t rp = b * gamma + j;
+    if (j >= m) {
+      if (alpha_out && lane == 0) alpha_out[rp] = __builtin_nanf("");
+      continue;
+    }
+    const int64_t r = w * J + jj;
+    PartStats a{kNegInf, 0.0f, kNegInf, 0.0f};
+    for (int sl = lane; sl < L.S; sl += 64) {
+      const PartStats c = part[r * L.S + sl];
+      ms_merge(a.mp, a.sp, c.mp, c.sp, cp);
+      if constexpr (!kGreedy) ms_merge(a.mq, a.sq, c.mq, c.sq, cq);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      ms_merge(a.mp, a.sp, __shfl_xor(a.mp, off, 64), __shfl_xor(a.sp, off, 64), cp);
+      if constexpr (!kGreedy)
+        ms_merge(a.mq, a.sq, __shfl_xor(a.mq, off, 64), __shfl_xor(a.sq, off, 64), cq);
+    }
+    if constexpr (kGreedy) {
+      a.mq = 0.0f;
+      a.sq = 1.0f;
+    }
+    const int32_t x = drafts[rp];
+    float al = __builtin_nanf("");
+    if (x >= 0 && x < V)
+      al = acceptance<kGreedy>(E::at(p + (b * (gamma + 1) + j) * (int64_t)V, x), a.mp, a.sp, cp,
+                               kGreedy ? 0.0f : E::at(q + rp * (int64_t)V, x), a.mq, a.sq, cq);
+    if (lane == 0) {
+      stats[rp] = RowStats{a.mp, a.sp, a.mq, a.sq};
+      alpha_ws[rp] = al;
+      if (alpha_out) alpha_out[rp] = al;
+    }
+    if (!rejected)
+      rejected = !(counter_uniform(seed, row_base + (uint64_t)b, (uint64_t)j, kAccept) <
+                   (double)al);
+  }
+  const int jn = j0 + J;  // the next chunk's first position
+  if (!rejected && jn < m && jn < gamma) {
+    if (lane == 0) live_next[atomicAdd(count_next, 1u)] = (int32_t)b;
+  } else if (alpha_out) {
+    for (int j = jn + lane; j < gamma; j += 64) alpha_out[b * gamma + j] = __builtin_nanf("");
+  }
 }
 
 }  // namespace svd

@@ -24,7 +24,8 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-  size_t stats, alpha, desc, segs, uncs, mass, mlen, alive, part, pstat, flags, total;
+  size_t stats, alpha, desc, segs, uncs, mass, mlen, alive, live, counts, part, pstat, flags,
+      total;
   int seg, nseg;
 };
 
@@ -40,6 +41,8 @@ int draw_seg(int64_t B, int32_t V) {
 
 // Split rows: at most this many (row pair, slice) records per launch.
 constexpr int kPartCap = 4096;
+static_assert(kLiveGrid <= kPartCap, "a live-list launch writes up to kLiveGrid records");
+constexpr int kLiveCounts = SVD_MAX_GAMMA + 1;  // chunk counters of an early exit
 constexpr int64_t kSplitRows = 1024;    // launches with fewer row pairs are split
 constexpr int64_t kSplitTarget = 2048;  // slice workgroups to aim for
 
@@ -77,6 +80,10 @@ Layout layout(int64_t B, int32_t K, int32_t G, int32_t V, int64_t np = 0, int64_
   off = align_up(off + (size_t)B * K * sizeof(int32_t));
   L.alive = off;
   off = align_up(off + (size_t)B * sizeof(uint32_t));
+  L.live = off;  // early exit: two lists of live prefixes, and a counter per chunk
+  off = align_up(off + (size_t)2 * B * sizeof(int32_t));
+  L.counts = off;
+  off = align_up(off + (size_t)kLiveCounts * sizeof(uint32_t));
   L.part = off;
   off = align_up(off + (size_t)kPartCap * sizeof(PartStats));
   L.pstat = off;
@@ -172,6 +179,8 @@ struct Batch {
   int eos;
   int32_t *mlen;
   uint32_t *alive;
+  int32_t *live;     // early exit: two lists of B prefixes
+  uint32_t *counts;  // early exit: live prefixes per chunk
   PartStats *part;
   bool vec;  // 16-byte loads
   bool fuse_select;  // the selection runs in the split rows' merge (kr_combine_select)
@@ -259,12 +268,51 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
                  a.cq, (const PoolStat *)a.pstat, a.stats, a.alpha_ws, a.alpha);
     return SVD_OK;
   }
+  // early exit over a live list: the batch's chunks are split rows (few row
+  // pairs per chunk) and the rows can be cut in more than one slice
+  const int J = a.early ? early_chunk(a.B, a.G) : a.G;
+  const int unit = a.vec ? E::kPerVec : 1;  // elements per load
+  const int units = a.V / unit;
+  const int smax = (int)std::max<int64_t>(1, units / (2 * kSplitBlock));
+  const bool live = a.early && a.B * J < kSplitRows && smax > 1;
+  const int nchunks = (a.G + J - 1) / J;
   const int32_t *mlen = nullptr;
   if (a.windowed) {
     const int64_t bk = a.B * a.K;
-    SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_window, dim3((unsigned)((bk + kBlock - 1) / kBlock)),
-               dim3(kBlock), s, a.drafts, a.gamma_b, a.eos, bk, a.K, a.G, a.mlen);
+    const int64_t nt = live ? std::max<int64_t>(bk, nchunks + 1) : bk;
+    SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_window, dim3((unsigned)((nt + kBlock - 1) / kBlock)),
+               dim3(kBlock), s, a.drafts, a.gamma_b, a.eos, bk, a.K, a.G, a.mlen,
+               live ? a.live : nullptr, live ? a.counts : nullptr, live ? nchunks + 1 : 0);
     mlen = a.mlen;
+  }
+  if (live) {
+    // chunk c reads list c % 2 and its counter c, and writes the next ones
+    const unsigned gw = (unsigned)((a.B * 64 + kBlock - 1) / kBlock);  // a wave per prefix
+    for (int c = 0; c < nchunks; ++c) {
+      const int j0 = c * J;
+      const int32_t *cur = a.live + (c % 2) * a.B;
+      int32_t *next = a.live + ((c + 1) % 2) * a.B;
+      const uint32_t *cnt = a.counts + c;
+      uint32_t *cnt_next = c + 1 < nchunks ? a.counts + c + 1 : nullptr;
+      if (a.greedy) {
+        SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS_SPLIT, s, kr_rowstats_live<E, kVec, true>,
+                   dim3(kLiveGrid), dim3(kSplitBlock), s, a.p, a.q, a.G, a.V, a.cp, a.cq, units,
+                   unit, smax, mlen, cur, cnt, j0, J, a.part);
+        SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_combine_advance<E, true>, dim3(gw),
+                   dim3(kBlock), s, a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, units, unit, smax,
+                   mlen, cur, cnt, j0, J, (const PartStats *)a.part, a.stats, a.alpha_ws,
+                   a.alpha, a.seed, a.row_base, next, cnt_next);
+      } else {
+        SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS_SPLIT, s, kr_rowstats_live<E, kVec, false>,
+                   dim3(kLiveGrid), dim3(kSplitBlock), s, a.p, a.q, a.G, a.V, a.cp, a.cq, units,
+                   unit, smax, mlen, cur, cnt, j0, J, a.part);
+        SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_combine_advance<E, false>, dim3(gw),
+                   dim3(kBlock), s, a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, units, unit, smax,
+                   mlen, cur, cnt, j0, J, (const PartStats *)a.part, a.stats, a.alpha_ws,
+                   a.alpha, a.seed, a.row_base, next, cnt_next);
+      }
+    }
+    return SVD_OK;
   }
   // the positions [j0, j0 + jn) of every draft
   auto stream_rows = [&](int j0, int jn, const uint32_t *alive) -> int {
@@ -322,7 +370,6 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   } else {
     // one draft per prefix, positions in chunks of J; a draft leaves the
     // stream after the chunk holding its first rejection
-    const int J = early_chunk(a.B, a.G);
     const unsigned gb = (unsigned)((a.B + kBlock - 1) / kBlock);
     SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_fill_u32, dim3(gb), dim3(kBlock), s, a.alive, a.B, 1u);
     for (int j0 = 0; j0 < a.G; j0 += J) {
@@ -422,6 +469,8 @@ int run(const Call &c) {
   a.part = reinterpret_cast<PartStats *>(ws + Lo.part);
   a.vec = kVec;
   a.alive = reinterpret_cast<uint32_t *>(ws + Lo.alive);
+  a.live = reinterpret_cast<int32_t *>(ws + Lo.live);
+  a.counts = reinterpret_cast<uint32_t *>(ws + Lo.counts);
   a.pstat = reinterpret_cast<PoolStat *>(ws + Lo.pstat);
   a.flags = reinterpret_cast<uint32_t *>(ws + Lo.flags);
   a.selected = c.selected;

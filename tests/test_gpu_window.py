@@ -80,19 +80,36 @@ def test_ragged_eos_windows_match_oracle(orc, rule, case):
 
 
 @pytest.mark.parametrize("rule", ["standard", "greedy"])
-def test_early_exit_equals_full_streaming(orc, rule):
+@pytest.mark.parametrize("V,dt", [(4096, "bf16"), (20000, "bf16"), (20000, "f32")])
+def test_early_exit_equals_full_streaming(orc, rule, V, dt):
+    # V = 4096 (bf16): a row is too short to cut, chunks stream whole rows, so
+    # alpha is bitwise that of full streaming; V = 20000: chunks follow the
+    # live list with rows cut into slices, alpha within the parity tolerance
     svd = require_gpu()
-    cfg, d = _inputs(300, 1, 12, 4096, "bf16", seed=9, sigma=1.2)
-    gb = torch.from_numpy(np.random.default_rng(1).integers(4, 13, 300).astype(np.int32)).cuda()
+    B, G = 300, 12
+    say("early exit", rule, V, dt)
+    cfg, d = _inputs(B, 1, G, V, dt, seed=9, sigma=1.2)
+    gb = torch.from_numpy(np.random.default_rng(1).integers(4, 13, B).astype(np.int32)).cuda()
     a = _call(svd, d, rule, gb, 17, True, cfg.temp, 6, scores=False)
     b = _call(svd, d, rule, gb, 17, False, cfg.temp, 6, scores=False)
     for k in ("selected", "accept_len", "next_token"):
         assert np.array_equal(a[k], b[k]), k
-    # every position up to the first rejection was streamed, with the same alpha
+    # every position up to the first rejection was streamed, with the same alpha,
+    # and nothing past the chunk of J = ceil(512 / B) positions that holds it
     L = a["accept_len"]
-    for i in range(300):
-        n = min(int(L[i]) + 1, int(gb[i]))
-        assert np.array_equal(a["alpha"][i, 0, :n], b["alpha"][i, 0, :n], equal_nan=True)
+    J = min(G, -(-512 // B))
+    hd = W.to_host(d["drafts"])
+    for i in range(B):
+        hits = np.nonzero(hd[i, 0, :int(gb[i])] == 17)[0]
+        m = int(hits[0]) + 1 if len(hits) else int(gb[i])
+        n = min(int(L[i]) + 1, m)
+        if V == 4096:
+            assert np.array_equal(a["alpha"][i, 0, :n], b["alpha"][i, 0, :n], equal_nan=True)
+        else:
+            assert np.all(np.abs(a["alpha"][i, 0, :n] - b["alpha"][i, 0, :n]) <= 1e-5)
+        end = min(m, (min(int(L[i]), m - 1) // J + 1) * J)
+        assert not np.any(np.isnan(a["alpha"][i, 0, :end])), i
+        assert np.all(np.isnan(a["alpha"][i, 0, end:])), i
     streamed = np.sum(~np.isnan(a["alpha"]))
     say("positions streamed with early exit: %d of %d" % (streamed, np.sum(~np.isnan(b["alpha"]))))
     assert streamed < 0.8 * np.sum(~np.isnan(b["alpha"]))
@@ -112,7 +129,7 @@ def test_full_size_batched_serving_early_exit(orc):
                                       seed=cfg.seed))
     for k in ("accept_len", "next_token"):
         assert np.array_equal(g[k], full[k]), k
-    idx = [0, 100, 255]
+    idx = list(range(256))
     hp, hq, hd = (W.to_host(d[k].index_select(0, torch.tensor(idx, device="cuda")))
                   for k in ("p", "q", "drafts"))
     rep = compare(orc, hp, hq, hd, dict(g, alpha=None), cfg.temp, cfg.temp, cfg.seed,
