@@ -294,7 +294,10 @@ namespace svd {
 // its n * J rows into as many slices as fill that grid, so the later chunks,
 // with few prefixes left, still spread over every CU.  The slicing depends
 // only on n, so a row's statistics do not depend on which prefixes are live.
-constexpr int kLiveGrid = 2048;
+#ifndef SVD_LIVE_GRID
+#define SVD_LIVE_GRID 2048
+#endif
+constexpr int kLiveGrid = SVD_LIVE_GRID;
 
 struct LivePlan {
   int S;      // slices per row
