@@ -28,9 +28,11 @@ METRIC = "verified draft positions/sec and achieved HBM GB/s (V=152064, bf16 log
 # sources whose text decides each kernel's memory traffic
 KERNEL_SOURCES = {"rowstats": ["svd_device.hpp", "kr_rowstats.hpp"],
                   "rowstats_split": ["svd_device.hpp", "kr_rowstats.hpp"],
+                  "rowstats_live": ["svd_device.hpp", "kr_rowstats.hpp"],
                   "pool_stats": ["svd_device.hpp", "kr_rowstats.hpp", "kr_rows.hpp"],
                   "lattice": ["svd_device.hpp", "kr_rowstats.hpp", "kr_cps.hpp"]}
 KERNEL_SYMBOL = {"rowstats": "kr_rowstats", "rowstats_split": "kr_rowstats_split",
+                 "rowstats_live": "kr_rowstats_live",
                  "pool_stats": "kr_pool_stats",
                  "lattice": "kr_lattice"}
 
@@ -370,9 +372,10 @@ def main():
     # timed region: K steps; HIP events around the dominant kernel's launches,
     # recorded on the stream the kernel is launched on, in every PROFILE_EVERY-th
     # step (each timing event costs the step a queue drain, ~17 us)
-    # (row pairs split into slices stream through kr_rowstats_split instead)
+    # (row pairs split into slices stream through kr_rowstats_split instead, and
+    # the chunks of an early exit over a live list through kr_rowstats_live)
     dom = "pool_stats" if pooled else "rowstats"
-    timed = [dom] if pooled else ["rowstats", "rowstats_split"]
+    timed = [dom] if pooled else ["rowstats", "rowstats_split", "rowstats_live"]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -392,6 +395,8 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     if not pooled and launches[svd.KERNELS.index("rowstats")] == 0:
         dom = "rowstats_split"
+        if launches[svd.KERNELS.index(dom)] == 0:
+            dom = "rowstats_live"
 
     # after the timed region: a few steps with every kernel timed, for the breakdown
     svd.svd_profile_enable("all")

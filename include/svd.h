@@ -309,7 +309,8 @@ enum {
   SVD_KERNEL_LATTICE_LEN = 11, /* lattice length and cleared tail                       */
   SVD_KERNEL_COMBINE = 12,   /* split rows: merge of the slices' statistics, alpha      */
   SVD_KERNEL_ROWSTATS_SPLIT = 13, /* split rows: statistics of each slice of a row pair  */
-  SVD_KERNEL_COUNT = 14
+  SVD_KERNEL_ROWSTATS_LIVE = 14,  /* early exit: slices of the live prefixes' row pairs   */
+  SVD_KERNEL_COUNT = 15
 };
 int svd_profile_enable(unsigned kernel_mask);
 int svd_profile_read(double *ms, int64_t *launches, int n);

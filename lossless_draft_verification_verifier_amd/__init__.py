@@ -30,7 +30,7 @@ SVD_OK, SVD_EINVAL, SVD_EDTYPE, SVD_EWORKSPACE, SVD_EHIP = 0, -1, -2, -3, -4
 SVD_MAX_K, SVD_MAX_GAMMA = 64, 4096
 KERNELS = ("rowstats", "select", "draw_pass", "draw_fix", "draw_pick", "beta", "mark",
            "pool_stats", "alpha_rows", "lattice", "beam", "lattice_len", "combine",
-           "rowstats_split")
+           "rowstats_split", "rowstats_live")
 SVD_RULE_STANDARD, SVD_RULE_GREEDY = 0, 1
 
 C_EXPORTS = ("svd_workspace_bytes", "svd_verify", "svd_select_and_verify", "svd_greedy_verify",

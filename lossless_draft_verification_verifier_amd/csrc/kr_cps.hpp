@@ -20,8 +20,9 @@
 // kr_lattice_len (one thread per prefix): the lattice length (first position
 //   whose best token is EOS, included) and the cleared tail.
 // kr_cps_beam (one wave per prefix): expansions (path rank, candidate rank) in
-//   fp64, the best `beam` popped one at a time (the earlier expansion on an
-//   exact tie), backpointers in LDS, paths rebuilt at the end.
+//   fp64, each ranked against all the step's expansions in LDS (the earlier
+//   expansion on an exact tie, a NaN score as -inf), the best `beam` kept by
+//   rank, backpointers in LDS, paths rebuilt at the end.
 #pragma once
 
 #include "kr_rowstats.hpp"  // row_ms helpers, kSplitBlock
@@ -486,17 +487,15 @@ __device__ __forceinline__ void copy_to_lds(float *dst, const float *__restrict_
   }
 }
 
-// best (score, expansion) over the wave: larger score, then the smaller expansion
-__device__ __forceinline__ void wave_best_d(double &s, int &e) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const double os = __shfl_xor(s, off, 64);
-    const int oe = __shfl_xor(e, off, 64);
-    if (os > s || (os == s && oe < e)) {
-      s = os;
-      e = oe;
-    }
+// rank of expansion e with score v among the n scores in es: how many come
+// before it (a larger score, or an equal one at a smaller expansion)
+__device__ __forceinline__ int expansion_rank(const double *es, int n, double v, int e) {
+  int r = 0;
+  for (int k = 0; k < n; ++k) {
+    const double x = es[k];
+    r += (x > v) | ((x == v) & (k < e));
   }
+  return r;
 }
 
 __global__ __launch_bounds__(64) void kr_cps_beam(
@@ -508,6 +507,7 @@ __global__ __launch_bounds__(64) void kr_cps_beam(
   __shared__ uint8_t ci[kCpsMaxG][kCpsBeam];  // candidate rank of rank r at position j
   __shared__ uint8_t rk[kCpsMaxG][kCpsBeam];  // final path r's candidate rank at position j
   __shared__ double sc[kCpsBeam], nsc[kCpsBeam];
+  __shared__ double es[kCpsBeam * kCpsMax];  // the step's expansion scores
   __shared__ int pc[kCpsBeam], npc[kCpsBeam];
   // the lattice of kBeamChunk positions at a time, loaded together
   __shared__ int nc_s[kBeamChunk];
@@ -551,33 +551,31 @@ __global__ __launch_bounds__(64) void kr_cps_beam(
       return sc[p] + (double)lp_s[jj * m_max + i] + (double)lambda * f;
     };
     const int e0 = lane, e1 = lane + 64;
-    if (e0 < ne) s0 = score(e0);
-    if (e1 < ne) s1 = score(e1);
-    bool u0 = e0 >= ne, u1 = e1 >= ne;  // used (or absent)
-    const int keep = ne < beam ? ne : beam;
-    for (int r = 0; r < keep; ++r) {
-      // this lane's best unused expansion, then the wave's
-      double s = -INFINITY;
-      int e = kNoIndex;
-      if (!u0) {
-        s = s0;
-        e = e0;
-      }
-      if (!u1 && (e == kNoIndex || s1 > s)) {
-        s = s1;
-        e = e1;
-      }
-      wave_best_d(s, e);
-      if (e == e0) u0 = true;
-      if (e == e1) u1 = true;
-      if (lane == 0) {
-        const int p = e / nc, i = e - p * nc;
-        nsc[r] = s;
-        npc[r] = i;
-        bp[j][r] = (uint8_t)p;
-        ci[j][r] = (uint8_t)i;
-      }
+    // a NaN score ranks as -inf, so the ranks are a permutation
+    if (e0 < ne) {
+      s0 = score(e0);
+      s0 = s0 != s0 ? -INFINITY : s0;
+      es[e0] = s0;
     }
+    if (e1 < ne) {
+      s1 = score(e1);
+      s1 = s1 != s1 ? -INFINITY : s1;
+      es[e1] = s1;
+    }
+    __syncthreads();
+    const int keep = ne < beam ? ne : beam;
+    // an expansion ranked below keep takes that slot of the new beam
+    auto place = [&](int e, double v) {
+      const int r = expansion_rank(es, ne, v, e);
+      if (r >= keep) return;
+      const int p = e / nc, i = e - p * nc;
+      nsc[r] = v;
+      npc[r] = i;
+      bp[j][r] = (uint8_t)p;
+      ci[j][r] = (uint8_t)i;
+    };
+    if (e0 < ne) place(e0, s0);
+    if (e1 < ne) place(e1, s1);
     __syncthreads();
     if (lane < keep) {
       sc[lane] = nsc[lane];

@@ -295,7 +295,7 @@ namespace svd {
 // with few prefixes left, still spread over every CU.  The slicing depends
 // only on n, so a row's statistics do not depend on which prefixes are live.
 #ifndef SVD_LIVE_GRID
-#define SVD_LIVE_GRID 2048
+#define SVD_LIVE_GRID 1024
 #endif
 constexpr int kLiveGrid = SVD_LIVE_GRID;
 

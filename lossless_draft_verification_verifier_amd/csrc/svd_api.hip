@@ -295,7 +295,7 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
       const uint32_t *cnt = a.counts + c;
       uint32_t *cnt_next = c + 1 < nchunks ? a.counts + c + 1 : nullptr;
       if (a.greedy) {
-        SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS_SPLIT, s, kr_rowstats_live<E, kVec, true>,
+        SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS_LIVE, s, kr_rowstats_live<E, kVec, true>,
                    dim3(kLiveGrid), dim3(kSplitBlock), s, a.p, a.q, a.G, a.V, a.cp, a.cq, units,
                    unit, smax, mlen, cur, cnt, j0, J, a.part);
         SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_combine_advance<E, true>, dim3(gw),
@@ -303,7 +303,7 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
                    mlen, cur, cnt, j0, J, (const PartStats *)a.part, a.stats, a.alpha_ws,
                    a.alpha, a.seed, a.row_base, next, cnt_next);
       } else {
-        SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS_SPLIT, s, kr_rowstats_live<E, kVec, false>,
+        SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS_LIVE, s, kr_rowstats_live<E, kVec, false>,
                    dim3(kLiveGrid), dim3(kSplitBlock), s, a.p, a.q, a.G, a.V, a.cp, a.cq, units,
                    unit, smax, mlen, cur, cnt, j0, J, a.part);
         SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_combine_advance<E, false>, dim3(gw),

@@ -683,6 +683,8 @@ int svdo_cps_beam(const int32_t *cand, const double *cand_logp, const int32_t *n
           const int32_t prev = (j == 0) ? 0 : idx[(size_t)p * G + j - 1];
           const double f = fluency ? (double)fluency[(o * m_max + prev) * m_max + i] : 0.0;
           es[ne] = sc[p] + cand_logp[o * m_max + i] + lambda * f;
+          /* a score made NaN by the proxy ranks below every other one */
+          if (isnan(es[ne])) es[ne] = -INFINITY;
           ep[ne] = p;
           ei[ne] = i;
           used[ne] = 0;

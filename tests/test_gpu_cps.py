@@ -82,14 +82,18 @@ def test_full_vocabulary_rows():
     _check_lattice(g, o, 15)
 
 
-@pytest.mark.parametrize("beam", [1, 3, 8])
-def test_beam_matches_oracle_on_the_same_lattice(beam):
+@pytest.mark.parametrize("beam,holes", [(1, False), (3, False), (8, False), (3, True)])
+def test_beam_matches_oracle_on_the_same_lattice(beam, holes):
+    # holes: 5 % of the proxy scores NaN, which rank their expansions last
     svd = require_gpu()
     B, G, M = 12, 10, 6
     q, hz = _rows(7, B, G, 300, "f32", scale=1.0)
     o = oracle.cps_lattice(hz, tau=0.9, m_max=M)
     o["cand_logp"] = o["cand_logp"].astype(np.float32).astype(np.float64)  # the GPU's inputs
-    f = np.random.default_rng(8).standard_normal((B, G, M, M)).astype(np.float32)
+    rng = np.random.default_rng(8)
+    f = rng.standard_normal((B, G, M, M)).astype(np.float32)
+    if holes:
+        f[rng.random(f.shape) < 0.05] = np.nan
     ob = oracle.cps_beam(o, f, lam=0.7, beam=beam)
     lat = {k: torch.from_numpy(np.ascontiguousarray(v if k != "cand_logp" else v.astype(np.float32))).cuda()
            for k, v in o.items() if k in ("cand", "cand_logp", "n_cand", "len")}

@@ -112,3 +112,24 @@ def test_exact_ties_keep_the_earlier_expansion():
     res = oracle.cps_beam(lat, None, beam=3)
     assert res["paths"][0].tolist() == [[5, 8], [5, 9], [6, 8]]
     assert res["rank_margin"][0] == 0.0
+
+
+def test_nan_proxy_scores_rank_last():
+    # a proxy score of NaN makes its expansion unusable: it ranks below every
+    # finite one, as if the score were -inf
+    lat = {"cand": np.array([[[5, 6], [8, 9]]], np.int32),
+           "cand_logp": np.full((1, 2, 2), -1.0), "n_cand": np.array([[2, 2]], np.int32),
+           "len": np.array([2], np.int32)}
+    f = np.zeros((1, 2, 2, 2), np.float32)
+    f[0, 0, 0, 0] = np.nan  # candidate 0 after the context
+    res = oracle.cps_beam(lat, f, lam=0.5, beam=2)
+    assert res["paths"][0].tolist() == [[6, 8], [6, 9]]
+    # on random lattices, NaN entries act as -inf entries
+    z = _rows(6, 3, 4, 50, scale=1.0)
+    lat = oracle.cps_lattice(z, tau=0.9, m_max=4)
+    rng = np.random.default_rng(7)
+    f = rng.standard_normal((3, 4, 4, 4)).astype(np.float32)
+    hole = rng.random(f.shape) < 0.1
+    a = oracle.cps_beam(lat, np.where(hole, np.float32(np.nan), f), lam=0.5, beam=3)
+    b = oracle.cps_beam(lat, np.where(hole, np.float32(-np.inf), f), lam=0.5, beam=3)
+    assert np.array_equal(a["paths"], b["paths"]) and np.array_equal(a["score"], b["score"])
