@@ -409,10 +409,15 @@ def main():
     positions = B * K * G
     L_host = L.cpu().numpy()
     bonus_rows = int((L_host == G).sum())
+    stream_ids = [svd.KERNELS.index(k) for k in timed]
     if early:
-        # positions actually streamed (alpha is NaN at the others), per rowstats launch
+        # positions actually streamed (alpha is NaN at the others), over every
+        # streaming launch of a step (the first chunk may stream whole rows,
+        # the later ones slices of the live rows)
         streamed = int((~torch.isnan(alpha_out)).sum().item())
-        lpd = max(launches[svd.KERNELS.index(dom)] // len(range(0, args.steps, PROFILE_EVERY)), 1)
+        stream_ids = [i for i in stream_ids if launches[i]]
+        samples = len(range(0, args.steps, PROFILE_EVERY))
+        lpd = max(sum(launches[i] for i in stream_ids) / samples, 1)
         units = streamed / lpd
         unit_bytes = bytes_per_row_pair(V, es, args.mode)
         rows = 1 if greedy else 2
@@ -428,8 +433,13 @@ def main():
         unit_bytes = bytes_per_row_pair(V, es, args.mode)
         rows = 1 if greedy else 2
         alg_bytes_step = positions * (rows * V * es + 4) + bonus_rows * V * es + B * 12
-    di = svd.KERNELS.index(dom)
-    ms_dom = ms_kernels[di] / max(launches[di], 1)
+    if early:
+        ms_dom = sum(ms_kernels[i] for i in stream_ids) / max(sum(launches[i] for i in stream_ids), 1)
+        dom_name = " + ".join(KERNEL_SYMBOL[svd.KERNELS[i]] for i in stream_ids)
+    else:
+        di = svd.KERNELS.index(dom)
+        ms_dom = ms_kernels[di] / max(launches[di], 1)
+        dom_name = KERNEL_SYMBOL[dom]
     launch_bytes = unit_bytes * units
     achieved = launch_bytes / (ms_dom * 1e-3) / 1e9
     traffic = None if early else measured_traffic(dom, cfg.name, args.mode)
@@ -455,7 +465,7 @@ def main():
         "hbm_frac_step": alg_bytes_step / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "kernel_ms": {k: ms_all[i] / max(launches_all[i], 1) for i, k in enumerate(svd.KERNELS)
                       if launches_all[i]},
-        "roofline": {"kernel": KERNEL_SYMBOL[dom], "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": dom_name, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_unit": unit_bytes,
                      "units_per_launch": units},

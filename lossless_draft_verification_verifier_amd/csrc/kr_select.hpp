@@ -294,8 +294,9 @@ __global__ __launch_bounds__(kBlock) void kr_advance(const float *__restrict__ a
 }
 
 // Early exit over a live list: the merge of chunk [j0, j0 + J), one wave per
-// live prefix (lanes over the slices of each row, as in combine_row), then
-// the chunk's acceptance tests in order.  A prefix with every test passed and
+// live prefix (lanes over the slices of each row, as in combine_row; part
+// null: the chunk streamed whole rows and alpha is written), then the
+// chunk's acceptance tests in order.  A prefix with every test passed and
 // positions left joins the next chunk's list; one that leaves the stream
 // marks the alpha of its later positions NaN (not streamed).  The next list's
 // order follows the atomic counter, which changes no result: each row is
@@ -323,6 +324,12 @@ __global__ __launch_bounds__(kBlock) void kr_combine_advance(
     const int64_t rp = b * gamma + j;
     if (j >= m) {
       if (alpha_out && lane == 0) alpha_out[rp] = __builtin_nanf("");
+      continue;
+    }
+    if (!part) {  // whole rows: alpha is written already
+      if (!rejected)
+        rejected = !(counter_uniform(seed, row_base + (uint64_t)b, (uint64_t)j, kAccept) <
+                     (double)alpha_ws[rp]);
       continue;
     }
     const int64_t r = w * J + jj;

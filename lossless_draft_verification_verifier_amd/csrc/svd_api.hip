@@ -43,6 +43,7 @@ int draw_seg(int64_t B, int32_t V) {
 constexpr int kPartCap = 4096;
 static_assert(kLiveGrid <= kPartCap, "a live-list launch writes up to kLiveGrid records");
 constexpr int kLiveCounts = SVD_MAX_GAMMA + 1;  // chunk counters of an early exit
+constexpr int64_t kLiveWholeRows = 512;  // a first chunk of this many row pairs streams whole rows
 constexpr int64_t kSplitRows = 1024;    // launches with fewer row pairs are split
 constexpr int64_t kSplitTarget = 2048;  // slice workgroups to aim for
 
@@ -294,6 +295,31 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
       int32_t *next = a.live + ((c + 1) % 2) * a.B;
       const uint32_t *cnt = a.counts + c;
       uint32_t *cnt_next = c + 1 < nchunks ? a.counts + c + 1 : nullptr;
+      // the first chunk holds every prefix: with enough row pairs to give each
+      // CU two, it streams whole rows (kr_rowstats), and the merge only tests
+      const bool whole = c == 0 && a.B * J >= kLiveWholeRows;
+      const PartStats *part = whole ? nullptr : a.part;
+      if (whole) {
+        if (a.greedy)
+          SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, true>,
+                     dim3((unsigned)(a.B * J)), dim3(kRowBlock), s, a.p, a.q, a.drafts, a.G, a.V,
+                     a.cp, a.cq, a.stats, a.alpha_ws, a.alpha, mlen, nullptr, 0, J);
+        else
+          SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, false>,
+                     dim3((unsigned)(a.B * J)), dim3(kRowBlock), s, a.p, a.q, a.drafts, a.G, a.V,
+                     a.cp, a.cq, a.stats, a.alpha_ws, a.alpha, mlen, nullptr, 0, J);
+        if (a.greedy)
+          SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_combine_advance<E, true>, dim3(gw),
+                     dim3(kBlock), s, a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, units, unit, smax,
+                     mlen, cur, cnt, j0, J, part, a.stats, a.alpha_ws, a.alpha, a.seed,
+                     a.row_base, next, cnt_next);
+        else
+          SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_combine_advance<E, false>, dim3(gw),
+                     dim3(kBlock), s, a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, units, unit, smax,
+                     mlen, cur, cnt, j0, J, part, a.stats, a.alpha_ws, a.alpha, a.seed,
+                     a.row_base, next, cnt_next);
+        continue;
+      }
       if (a.greedy) {
         SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS_LIVE, s, kr_rowstats_live<E, kVec, true>,
                    dim3(kLiveGrid), dim3(kSplitBlock), s, a.p, a.q, a.G, a.V, a.cp, a.cq, units,
