@@ -154,6 +154,10 @@ __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int l
   __shared__ int wi[NW * kCpsMax];
   __shared__ float cv[kCandCap];
   __shared__ int cix[kCandCap];
+  __shared__ float av[NT];  // every thread's largest logit
+  __shared__ int ai[NT];
+  __shared__ float sv[kCpsMax];  // the 16 best of the candidate list, by rank
+  __shared__ int si[kCpsMax];
   __shared__ int n_found;
   __shared__ float thr_s;
   const typename E::elem *z = row + lo;  // 16-byte aligned when kVec
@@ -203,36 +207,45 @@ __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int l
     lds[2 * NW + 1] = s;
     n_found = 0;
   }
-  // 2. the 16th largest of the threads' maxima bounds the slice's 16th largest
-  //    logit from below: every one of its 16 best is at least that
-  {
-    float lv[1] = {tmax};
-    int li[1] = {tidx};
-    float v16;
-    int i16;
-    wave_pop16<1>(lv, li, v16, i16);
-    if (lane < kCpsMax) {
-      wv[w * kCpsMax + lane] = v16;
-      wi[w * kCpsMax + lane] = i16;
+  // 2. the 16th largest of the threads' maxima (in (logit, index) order)
+  //    bounds the slice's 16th largest logit from below: every one of its 16
+  //    best is at least that.  Each wave ranks its 64 maxima against each
+  //    other and keeps its 16 best in rank slots; then four threads rank each
+  //    of those NW * 16 against a quarter of them each.  Every key is unique
+  //    (a token index), and threads without a token take no slot.
+  av[tid] = tmax;
+  ai[tid] = tidx;
+  for (int k = tid; k < NW * kCpsMax; k += NT) {
+    wv[k] = kNegInf;
+    wi[k] = kNoIndex;
+  }
+  if (tid < kCpsMax) {
+    sv[tid] = kNegInf;
+    si[tid] = kNoIndex;
+  }
+  if (tid == 0) thr_s = kNegInf;  // fewer than 16 tokens: all of them
+  __syncthreads();
+  if (tidx != kNoIndex) {
+    int r = 0;
+#pragma unroll 8
+    for (int k = w * 64; k < w * 64 + 64; ++k) r += ahead(av[k], ai[k], tmax, tidx);
+    if (r < kCpsMax) {
+      wv[w * kCpsMax + r] = tmax;
+      wi[w * kCpsMax + r] = tidx;
     }
   }
   __syncthreads();
-  if (w == 0) {
-    constexpr int PER = (NW * kCpsMax + 63) / 64;  // entries per lane
-    float lv[PER];
-    int li[PER];
-#pragma unroll
-    for (int t = 0; t < PER; ++t) {
-      const int k = PER * lane + t;  // consecutive entries of one wave's sorted list
-      lv[t] = k < NW * kCpsMax ? wv[k] : kNegInf;
-      li[t] = k < NW * kCpsMax ? wi[k] : kNoIndex;
-    }
-    float v16;
-    int i16;
-    wave_pop16<PER>(lv, li, v16, i16);
-    const float t16 = __shfl(v16, kCpsMax - 1, 64);
-    const int n16 = __shfl(i16, kCpsMax - 1, 64);
-    if (lane == 0) thr_s = n16 == kNoIndex ? kNegInf : t16;  // fewer than 16 tokens: all
+  {
+    constexpr int NE = NW * kCpsMax;  // NT / 4: four threads per entry
+    const int e = tid >> 2, k0 = (tid & 3) * (NE / 4);
+    const float ve = wv[e];
+    const int ie = wi[e];
+    int r = 0;
+#pragma unroll 8
+    for (int k = k0; k < k0 + NE / 4; ++k) r += ahead(wv[k], wi[k], ve, ie);
+    r += __shfl_xor(r, 1, 64);
+    r += __shfl_xor(r, 2, 64);
+    if ((tid & 3) == 0 && ie != kNoIndex && r == kCpsMax - 1) thr_s = ve;
   }
   __syncthreads();
   // 3. second pass: every token at or above the bound into an LDS list
@@ -265,8 +278,22 @@ __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int l
       wv[w * kCpsMax + lane] = v16;
       wi[w * kCpsMax + lane] = i16;
     }
-    __syncthreads();
+  } else {
+    // every listed token counts the ones ahead of it; the 16 best take their
+    // rank slots (token indices are unique)
+    for (int t = tid; t < nf; t += NT) {
+      const float v = cv[t];
+      const int i = cix[t];
+      int r = 0;
+#pragma unroll 4
+      for (int k = 0; k < nf; ++k) r += ahead(cv[k], cix[k], v, i);
+      if (r < kCpsMax) {
+        sv[r] = v;
+        si[r] = i;
+      }
+    }
   }
+  __syncthreads();
   m_out = lds[2 * NW];
   s_out = lds[2 * NW + 1];
   if (w != 0) return;
@@ -282,34 +309,8 @@ __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int l
     }
     wave_pop16<PER>(lv, li, bv, bi);
   } else {
-    // lane l sorts the list entries l, l + 64, ... (at most 8), then the wave pops
-    float lv[kCandCap / 64];
-    int li[kCandCap / 64];
-#pragma unroll
-    for (int t = 0; t < kCandCap / 64; ++t) {
-      lv[t] = kNegInf;
-      li[t] = kNoIndex;
-    }
-#pragma unroll
-    for (int t = 0; t < kCandCap / 64; ++t) {
-      const int k = lane + 64 * t;
-      if (k < nf) {
-        float v = cv[k];
-        int i = cix[k];
-#pragma unroll
-        for (int u = 0; u < kCandCap / 64; ++u) {  // insertion into the sorted list
-          if (ahead(v, i, lv[u], li[u])) {
-            const float tvv = lv[u];
-            const int tii = li[u];
-            lv[u] = v;
-            li[u] = i;
-            v = tvv;
-            i = tii;
-          }
-        }
-      }
-    }
-    wave_pop16<kCandCap / 64>(lv, li, bv, bi);
+    bv = lane < kCpsMax ? sv[lane] : kNegInf;
+    bi = lane < kCpsMax ? si[lane] : kNoIndex;
   }
 }
 
