@@ -296,7 +296,7 @@ def main():
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the verification path shards by prefix with no "
-              "exchange, and multi-GPU runs are not part of this build (got --gpus %d)"
+              "exchange, and this benchmark runs on a single GPU (got --gpus %d)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 

@@ -1,6 +1,6 @@
 """Comparison of the HIP library's outputs with the oracle's.
 
-Rules (the readings behind them are listed in the design doc):
+Rules (each follows a reading of the pages where they leave the point open):
   * alpha and beta within ALPHA_TOL absolute; scores within ALPHA_TOL * gamma;
   * selected draft, accepted length and drawn token bit-exact, except where the
     oracle marks the decision as a near-tie:
