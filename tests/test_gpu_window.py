@@ -80,16 +80,19 @@ def test_ragged_eos_windows_match_oracle(orc, rule, case):
 
 
 @pytest.mark.parametrize("rule", ["standard", "greedy"])
-@pytest.mark.parametrize("V,dt", [(4096, "bf16"), (20000, "bf16"), (20000, "f32")])
-def test_early_exit_equals_full_streaming(orc, rule, V, dt):
+@pytest.mark.parametrize("B,V,dt", [(300, 4096, "bf16"), (300, 20000, "bf16"), (300, 20000, "f32"),
+                                    (300, 20001, "bf16"), (20, 20000, "bf16")])
+def test_early_exit_equals_full_streaming(orc, rule, B, V, dt):
     # V = 4096 (bf16): a row is too short to cut, chunks stream whole rows, so
     # alpha is bitwise that of full streaming; V = 20000: chunks follow the
-    # live list with rows cut into slices, alpha within the parity tolerance
+    # live list (whole rows for the first chunk, slices of the live rows
+    # after it), alpha within the parity tolerance; V = 20001: the same on
+    # the element-wise path; B = 20: one chunk of every position, in slices
     svd = require_gpu()
-    B, G = 300, 12
+    G = 12
     say("early exit", rule, V, dt)
     cfg, d = _inputs(B, 1, G, V, dt, seed=9, sigma=1.2)
-    gb = torch.from_numpy(np.random.default_rng(1).integers(4, 13, B).astype(np.int32)).cuda()
+    gb = torch.from_numpy(np.random.default_rng(1).integers(4, G + 1, B).astype(np.int32)).cuda()
     a = _call(svd, d, rule, gb, 17, True, cfg.temp, 6, scores=False)
     b = _call(svd, d, rule, gb, 17, False, cfg.temp, 6, scores=False)
     for k in ("selected", "accept_len", "next_token"):
@@ -112,7 +115,10 @@ def test_early_exit_equals_full_streaming(orc, rule, V, dt):
         assert np.all(np.isnan(a["alpha"][i, 0, end:])), i
     streamed = np.sum(~np.isnan(a["alpha"]))
     say("positions streamed with early exit: %d of %d" % (streamed, np.sum(~np.isnan(b["alpha"]))))
-    assert streamed < 0.8 * np.sum(~np.isnan(b["alpha"]))
+    if J < G:
+        assert streamed < 0.8 * np.sum(~np.isnan(b["alpha"]))
+    else:  # one chunk: every usable position is streamed
+        assert streamed == np.sum(~np.isnan(b["alpha"]))
     # alpha past the chunk of the first rejection is not streamed (NaN): decisions only
     rep = compare(orc, W.to_host(d["p"]), W.to_host(d["q"]), W.to_host(d["drafts"]),
                   dict(a, alpha=None), cfg.temp, cfg.temp, 6, greedy=rule == "greedy",
