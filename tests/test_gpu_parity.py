@@ -240,3 +240,28 @@ def test_large_batch_edge_logits(orc, temp):
     say(rep.summary())
     assert rep.ok(), rep.failures
     assert rep.invalid == 0
+
+
+@pytest.mark.parametrize("B,V", [(2, 300000), (30, 2_200_000)])
+@pytest.mark.parametrize("bonus", [False, True])
+def test_more_draw_segments_than_the_pick_stages(orc, B, V, bonus):
+    # more than 256 draw segments per row (2 prefixes of 300000 tokens in
+    # segments of 1024: 293; 30 of 2.2M in segments of 8192: 269): the pick
+    # reads the segment records and keeps the masses in global memory and
+    # scans runs of five segments per lane; bonus: q = p, every prefix draws
+    # from its bonus row
+    svd = require_gpu()
+    say("segments", B, V, "bonus", bonus)
+    cfg = W.Config(91, "custom", B=B, K=1, gamma=3, V=V, dtype="bf16", sigma0=1.0,
+                   sigma_step=0.0, temp=0.9, boost=8.0, boost_prob=1.0)
+    d = gen(cfg, data_seed=V + B)
+    if bonus:
+        d["q"].copy_(d["p"][:, :, :3])
+    g = run_select(svd, d, 0.9, 4)
+    check_ranges(g, 1, 3, V)
+    if bonus:
+        assert np.all(g["accept_len"] == 3)
+    rep = compare(orc, *host_inputs(d), g, 0.9, 0.9, 4)
+    say(rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    assert rep.invalid == 0
