@@ -51,7 +51,11 @@
  *     temperature that is not finite and positive; SVD_EDTYPE for an unknown
  *     dtype; SVD_EWORKSPACE for a workspace below svd_workspace_bytes();
  *     SVD_EHIP when a kernel launch fails.  Nothing is enqueued when the
- *     return code is not SVD_OK.
+ *     return code is SVD_EINVAL, SVD_EDTYPE or SVD_EWORKSPACE; after
+ *     SVD_EHIP the launches before the failing one may have been enqueued.
+ *   - Every flag, counter and list in the workspace is written by the
+ *     call's own kernels before it is read (no memset, no host copy), so a
+ *     call can be captured in a HIP graph and replayed.
  *   - Errors in the data go to the outputs: a drafted token outside [0, V),
  *     or a NaN or +inf logit, or an all -inf row, among the rows a prefix
  *     reads, sets that prefix's selected / accept_len / next_token to -1
