@@ -294,6 +294,10 @@ def main():
     ap.add_argument("--beta", action="store_true",
                     help="also ask for the overlap mass beta (a second pass over every scored "
                          "row pair; dense workloads, standard rule)")
+    ap.add_argument("--vocab-shards", type=int, default=1,
+                    help="one GPU's share of a vocabulary-sharded verifier: the workload with "
+                         "V / N columns per row (the statistics exchange between shards is not "
+                         "part of the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (for counter calibration)")
@@ -327,6 +331,10 @@ def main():
         return
 
     cfg = W.get_config(args.workload)
+    if args.vocab_shards > 1:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, V=cfg.V // args.vocab_shards,
+                                  name="%s_vshard%d" % (cfg.name, args.vocab_shards))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pooled = cfg.layout == "pooled"
@@ -481,7 +489,8 @@ def main():
         "config": {"workload": cfg.name, "mode": args.mode, "early_exit": early,
                    "B": B, "K": K, "gamma": G, "V": V,
                    "logits": cfg.dtype, "temperature": cfg.temp, "global_batch": B,
-                   "parallelism": "single GPU", "input_copies": ncopy},
+                   "parallelism": "single GPU", "input_copies": ncopy,
+                   "vocab_shards": args.vocab_shards},
         "achieved_hbm_gbps": alg_bytes_step / (ms_step * 1e-3) / 1e9,
         "hbm_frac_step": alg_bytes_step / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "kernel_ms": {k: ms_all[i] / max(launches_all[i], 1) for i, k in enumerate(svd.KERNELS)

@@ -46,18 +46,21 @@ __global__ __launch_bounds__(kBlock) void kr_mark_rows(const int32_t *__restrict
   }
 }
 
-template <typename E, bool kVec>
-__global__ __launch_bounds__(kRowBlock) __attribute__((amdgpu_waves_per_eu(8))) void kr_pool_stats(
+// NT threads per row: kRowBlock, or kShortRowBlock for rows of fewer than
+// kShortRowBytes, as for kr_rowstats (the same reduction, so identity
+// indices reproduce the dense statistics bit for bit)
+template <typename E, bool kVec, int NT = kRowBlock>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void kr_pool_stats(
     const typename E::elem *__restrict__ p_pool, const typename E::elem *__restrict__ q_pool,
     int64_t np, int V, float cp, float cq, const uint32_t *__restrict__ flags,
     PoolStat *__restrict__ pstat) {
-  __shared__ float lds[2 * (kRowBlock / 64)];
+  __shared__ float lds[2 * (NT / 64)];
   const int64_t r = blockIdx.x;  // p rows first, then q rows
   if (!flags[r]) return;
   const bool is_p = r < np;
   const typename E::elem *row = is_p ? p_pool + r * (int64_t)V : q_pool + (r - np) * (int64_t)V;
   float m, s;
-  row_ms<E, kVec, kRowBlock, kRowUnroll>(row, V, is_p ? cp : cq, m, s, lds);
+  row_ms<E, kVec, NT, kRowUnroll>(row, V, is_p ? cp : cq, m, s, lds);
   if (threadIdx.x == 0) pstat[r] = PoolStat{m, s};
 }
 

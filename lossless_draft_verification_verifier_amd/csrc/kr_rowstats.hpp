@@ -167,8 +167,13 @@ __device__ __forceinline__ void rowstats_item(const typename E::elem *__restrict
 // streamed in chunks: alive[b*K+k] == 0 skips a draft already rejected.  A
 // skipped position's alpha output is NaN.
 // Two 1024-thread workgroups per CU (8 waves per SIMD) need at most 64 VGPRs.
-template <typename E, bool kVec, bool kGreedy>
-__global__ __launch_bounds__(kRowBlock) __attribute__((amdgpu_waves_per_eu(8))) void kr_rowstats(
+// Rows of fewer than kShortRowBytes take NT = kShortRowBlock threads (eight
+// workgroups per CU), so that a thread still has several loads per row.
+constexpr int kShortRowBlock = 256;
+constexpr int64_t kShortRowBytes = 128 * 1024;
+
+template <typename E, bool kVec, bool kGreedy, int NT = kRowBlock>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void kr_rowstats(
     const typename E::elem *__restrict__ p, const typename E::elem *__restrict__ q,
     const int32_t *__restrict__ drafts, int gamma, int V, float cp, float cq,
     RowStats *__restrict__ stats, float *__restrict__ alpha_ws, float *__restrict__ alpha_out,
@@ -181,8 +186,8 @@ __global__ __launch_bounds__(kRowBlock) __attribute__((amdgpu_waves_per_eu(8))) 
     if (alpha_out && threadIdx.x == 0) alpha_out[rp] = __builtin_nanf("");
     return;
   }
-  rowstats_item<E, kVec, kRowBlock, kRowUnroll, kGreedy>(p, q, drafts, gamma, V, cp, cq, rp, stats,
-                                                         alpha_ws, alpha_out);
+  rowstats_item<E, kVec, NT, kRowUnroll, kGreedy>(p, q, drafts, gamma, V, cp, cq, rp, stats,
+                                                  alpha_ws, alpha_out);
 }
 
 // ---------------------------------------------------------------------------

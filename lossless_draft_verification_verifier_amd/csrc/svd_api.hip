@@ -244,6 +244,31 @@ SelectArgs make_select(const Batch<E> &a) {
                     a.scores};
 }
 
+// one workgroup per row pair (positions [j0, j0 + jn) of every draft); short
+// rows take smaller workgroups
+template <typename E, bool kVec, bool kGreedy, int NT>
+int launch_rowstats_nt(const Batch<E> &a, hipStream_t s, CallTimer &tm, unsigned grid,
+                       const int32_t *mlen, const uint32_t *alive, int j0, int jn) {
+  SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, kGreedy, NT>, dim3(grid), dim3(NT),
+             s, a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, a.stats, a.alpha_ws, a.alpha, mlen,
+             alive, j0, jn);
+  return SVD_OK;
+}
+template <typename E, bool kVec>
+int launch_rowstats(const Batch<E> &a, hipStream_t s, CallTimer &tm, unsigned grid,
+                    const int32_t *mlen, const uint32_t *alive, int j0, int jn) {
+  const bool short_rows = (int64_t)a.V * (int64_t)sizeof(typename E::elem) < kShortRowBytes;
+  if (a.greedy)
+    return short_rows
+               ? launch_rowstats_nt<E, kVec, true, kShortRowBlock>(a, s, tm, grid, mlen, alive,
+                                                                   j0, jn)
+               : launch_rowstats_nt<E, kVec, true, kRowBlock>(a, s, tm, grid, mlen, alive, j0, jn);
+  return short_rows
+             ? launch_rowstats_nt<E, kVec, false, kShortRowBlock>(a, s, tm, grid, mlen, alive, j0,
+                                                                  jn)
+             : launch_rowstats_nt<E, kVec, false, kRowBlock>(a, s, tm, grid, mlen, alive, j0, jn);
+}
+
 // row statistics and alpha (and the optional overlap mass) of a batch
 template <typename E, bool kVec>
 int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
@@ -256,9 +281,14 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
                0u);
     SVD_LAUNCH(tm, SVD_KERNEL_MARK, s, kr_mark_rows, dim3(gp), dim3(kBlock), s, a.ix.p,
                a.greedy ? nullptr : a.ix.q, (int64_t)rp, a.G, a.np, a.nq, a.flags);
-    SVD_LAUNCH(tm, SVD_KERNEL_POOL_STATS, s, kr_pool_stats<E, kVec>, dim3((unsigned)nrows),
-               dim3(kRowBlock), s, a.p, a.q, a.np, a.V, a.cp, a.cq, (const uint32_t *)a.flags,
-               a.pstat);
+    if ((int64_t)a.V * (int64_t)sizeof(typename E::elem) < kShortRowBytes)
+      SVD_LAUNCH(tm, SVD_KERNEL_POOL_STATS, s, kr_pool_stats<E, kVec, kShortRowBlock>,
+                 dim3((unsigned)nrows), dim3(kShortRowBlock), s, a.p, a.q, a.np, a.V, a.cp, a.cq,
+                 (const uint32_t *)a.flags, a.pstat);
+    else
+      SVD_LAUNCH(tm, SVD_KERNEL_POOL_STATS, s, kr_pool_stats<E, kVec>, dim3((unsigned)nrows),
+                 dim3(kRowBlock), s, a.p, a.q, a.np, a.V, a.cp, a.cq, (const uint32_t *)a.flags,
+                 a.pstat);
     if (a.greedy)
       SVD_LAUNCH(tm, SVD_KERNEL_ALPHA_ROWS, s, kr_alpha_rows<E, true>, dim3(gp), dim3(kBlock), s,
                  a.p, a.q, a.ix.p, a.ix.q, a.drafts, (int64_t)rp, a.G, a.V, a.np, a.nq, a.cp,
@@ -300,14 +330,11 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
       const bool whole = c == 0 && a.B * J >= kLiveWholeRows;
       const PartStats *part = whole ? nullptr : a.part;
       if (whole) {
-        if (a.greedy)
-          SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, true>,
-                     dim3((unsigned)(a.B * J)), dim3(kRowBlock), s, a.p, a.q, a.drafts, a.G, a.V,
-                     a.cp, a.cq, a.stats, a.alpha_ws, a.alpha, mlen, nullptr, 0, J);
-        else
-          SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, false>,
-                     dim3((unsigned)(a.B * J)), dim3(kRowBlock), s, a.p, a.q, a.drafts, a.G, a.V,
-                     a.cp, a.cq, a.stats, a.alpha_ws, a.alpha, mlen, nullptr, 0, J);
+        {
+          const int rc = launch_rowstats<E, kVec>(a, s, tm, (unsigned)(a.B * J), mlen, nullptr, 0,
+                                                  J);
+          if (rc != SVD_OK) return rc;
+        }
         if (a.greedy)
           SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_combine_advance<E, true>, dim3(gw),
                      dim3(kBlock), s, a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, units, unit, smax,
@@ -379,16 +406,7 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
                    (const PartStats *)a.part, a.stats, a.alpha_ws, a.alpha);
       return SVD_OK;
     }
-    const dim3 grid((unsigned)rows);
-    if (a.greedy)
-      SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, true>, grid, dim3(kRowBlock), s,
-                 a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, a.stats, a.alpha_ws, a.alpha, mlen,
-                 alive, j0, jn);
-    else
-      SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS, s, kr_rowstats<E, kVec, false>, grid, dim3(kRowBlock), s,
-                 a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, a.stats, a.alpha_ws, a.alpha, mlen,
-                 alive, j0, jn);
-    return SVD_OK;
+    return launch_rowstats<E, kVec>(a, s, tm, (unsigned)rows, mlen, alive, j0, jn);
   };
   if (!a.early) {
     const int rc = stream_rows(0, a.G, nullptr);
