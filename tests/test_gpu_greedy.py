@@ -26,6 +26,7 @@ CASES = [
     (2, 8, 16, 20000, "bf16", 1.0),
     (3, 1, 70, 2048, "bf16", 1.0),
     (1, 64, 2, 512, "bf16", 2.0),
+    (2, 2, 4096, 64, "f32", 1.0),        # gamma at its limit
     (800, 1, 2, 8193, "bf16", 1.0),      # drawn in segments of 8192
     (2, 1, 3, 70008, "bf16", 0.7),       # 69 segments of 1024
     (2, 1, 1, 1, "f32", 1.0),            # V = 1: p(x) = 1, always accepted

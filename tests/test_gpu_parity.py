@@ -24,6 +24,7 @@ CASES = [
     (2, 8, 16, 20000, "bf16", 1.0),
     (3, 1, 70, 2048, "bf16", 1.0),       # gamma beyond one wave of 64
     (1, 64, 2, 512, "bf16", 2.0),        # K at its limit
+    (2, 2, 4096, 64, "f32", 1.0),        # gamma at its limit
     (17, 2, 4, 3000, "f32", 0.5),
     (800, 1, 2, 8193, "bf16", 1.0),      # a batch drawn in segments of 8192: one-token second segment
     (3, 2, 4, 1032, "bf16", 1.0),        # segments of 1024: an 8-token second segment
