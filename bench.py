@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
-PROFILE_EVERY = 10  # timed steps per step whose dominant-kernel launches carry HIP events
+SETTLE_MS = 100.0  # GPU time of untimed warm-up before the timed steps (the clock settles)
 METRIC = "verified draft positions/sec and achieved HBM GB/s (V=152064, bf16 logits)"
 # sources whose text decides each kernel's memory traffic
 KERNEL_SOURCES = {"rowstats": ["svd_device.hpp", "kr_rowstats.hpp"],
@@ -35,6 +35,46 @@ KERNEL_SYMBOL = {"rowstats": "kr_rowstats", "rowstats_split": "kr_rowstats_split
                  "rowstats_live": "kr_rowstats_live",
                  "pool_stats": "kr_pool_stats",
                  "lattice": "kr_lattice"}
+
+
+def settle(torch, stream, step, warmup, settle_ms):
+    """Untimed warm-up, in the open: at least `warmup` steps, continued until at
+    least `settle_ms` of GPU time has passed since the first one, so that the
+    timed steps run on a settled clock.  Returns the GPU time and steps spent."""
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    n = 0
+    for _ in range(warmup):
+        step()
+        n += 1
+    while True:
+        ev1.record(stream)
+        ev1.synchronize()
+        elapsed = ev0.elapsed_time(ev1)
+        if elapsed >= settle_ms or n >= 1_000_000:
+            return {"settle_ms": elapsed, "steps": n}
+        for _ in range(16):
+            step()
+            n += 1
+
+
+def kernel_samples(steps: int) -> int:
+    """Steps whose dominant-kernel launches are timed: at least 5, whatever --steps is."""
+    return max(5, min(steps, 20))
+
+
+def time_kernels(torch, tl, fn, kernels, n):
+    """(ms per kernel, launches per kernel) over n calls of fn, with the timing
+    build recording HIP events around the launches of `kernels`."""
+    torch.cuda.synchronize()
+    tl.svd_profile_read()  # clear
+    tl.svd_profile_enable(kernels)
+    for _ in range(n):
+        fn()
+    tl.svd_profile_enable(())
+    torch.cuda.synchronize()
+    return tl.svd_profile_read()
 
 
 def traffic_file(kernel: str, mode: str = "standard") -> str:
@@ -134,36 +174,91 @@ def bytes_per_row_pair(V: int, es: int, mode: str = "standard") -> int:
     return rows * V * es + 4 + 16 + 4
 
 
-def cpu_baseline(d, cfg, seed, mode="standard", pooled=False, seconds=10.0, want_beta=False):
-    """The oracle, untuned, on the same batch, repeated until about `seconds`
-    of wall time have passed (at least once)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    """Threads for the oracle: the CPUs this process may run on, at most 16 (one
+    GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _oracle_run(d, cfg, seed, mode, pooled, want_beta, threads, nprefix=None):
+    """One untuned oracle pass over the batch (or its first nprefix prefixes)."""
     import oracle
     import workloads as W
-    threads = max(1, min(16, os.cpu_count() or 1))
+    cut = (lambda t: t[:nprefix]) if nprefix else (lambda t: t)
     if pooled:
         hp, hq = W.to_host(d["p_pool"]), W.to_host(d["q_pool"])
-        pi, qi, hd = W.to_host(d["p_index"]), W.to_host(d["q_index"]), W.to_host(d["drafts"])
-    else:
-        hp, hq, hd = W.to_host(d["p"]), W.to_host(d["q"]), W.to_host(d["drafts"])
+        pi, qi = W.to_host(cut(d["p_index"])), W.to_host(cut(d["q_index"]))
+        hd = W.to_host(cut(d["drafts"]))
+        return lambda: oracle.select_and_verify_rows(hp, pi, hq, qi, hd, temp_p=cfg.temp,
+                                                     seed=seed, greedy=mode == "greedy",
+                                                     nthreads=threads)
+    hp, hd = W.to_host(cut(d["p"])), W.to_host(cut(d["drafts"]))
+    if mode == "greedy":
+        return lambda: oracle.greedy_select_and_verify(hp, hd, temp_p=cfg.temp, seed=seed,
+                                                       nthreads=threads)
+    hq = W.to_host(cut(d["q"]))
+    return lambda: oracle.select_and_verify(hp, hq, hd, temp_p=cfg.temp, seed=seed,
+                                            nthreads=threads, want_beta=want_beta)
+
+
+def _time_oracle(run, seconds):
     reps, dt = 0, 0.0
     while reps == 0 or dt < seconds:
         t0 = time.perf_counter()
-        if pooled:
-            oracle.select_and_verify_rows(hp, pi, hq, qi, hd, temp_p=cfg.temp, seed=seed,
-                                          greedy=mode == "greedy", nthreads=threads)
-        elif mode == "greedy":
-            oracle.greedy_select_and_verify(hp, hd, temp_p=cfg.temp, seed=seed, nthreads=threads)
-        else:
-            oracle.select_and_verify(hp, hq, hd, temp_p=cfg.temp, seed=seed, nthreads=threads,
-                                     want_beta=want_beta)
+        run()
         dt += time.perf_counter() - t0
         reps += 1
+    return reps, dt
+
+
+# single-threaded samples of a batch larger than this many positions take the
+# first few prefixes only, and the batch's rate is extrapolated from them
+SINGLE_THREAD_MAX_POSITIONS = 4096
+
+
+def cpu_baseline(d, cfg, seed, mode="standard", pooled=False, seconds=10.0, want_beta=False):
+    """The oracle, untuned, timed on the host: the same batch on the host's
+    thread share (repeated until about `seconds` of wall time have passed, at
+    least once), and on one thread (the whole batch, or its first prefixes when
+    the batch is large, then extrapolated to the batch)."""
+    threads = host_threads()
     positions = cfg.B * cfg.K * cfg.gamma
+    reps, dt = _time_oracle(_oracle_run(d, cfg, seed, mode, pooled, want_beta, threads), seconds)
+    per_prefix = cfg.K * cfg.gamma
+    n1 = cfg.B
+    if positions > SINGLE_THREAD_MAX_POSITIONS:
+        n1 = max(1, min(cfg.B, SINGLE_THREAD_MAX_POSITIONS // per_prefix, 4))
+    reps1, dt1 = _time_oracle(_oracle_run(d, cfg, seed, mode, pooled, want_beta, 1,
+                                          nprefix=n1 if n1 < cfg.B else None), seconds)
+    rate1 = n1 * per_prefix * reps1 / dt1
+    single = {"value": rate1, "unit": "positions/s", "threads": 1, "seconds": dt1,
+              "sample": "%s%d of the %d prefixes (%d positions) %d times, %.1f s wall" % (
+                  "" if n1 == cfg.B else "the first ", n1, cfg.B, n1 * per_prefix, reps1, dt1),
+              "extrapolated": n1 < cfg.B}
+    if n1 < cfg.B:
+        single["batch_seconds_extrapolated"] = positions / rate1
     return {"value": positions * reps / dt, "unit": "positions/s", "cores": threads,
             "kind": "oracle",
             "sample": "the full %s batch (%d prefixes, %d positions) %d times, %.1f s wall on %d "
                       "threads" % (cfg.name, cfg.B, positions, reps, dt, threads),
-            "seconds": dt}
+            "seconds": dt, "single_thread": single, "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count(), "threads_note": "the host's CPUs this process may use, "
+            "at most 16 (one GPU's share of the host)"}
 
 
 COPY_BYTES = 1 << 30
@@ -211,34 +306,25 @@ def bench_cps(args, torch, svd, W):
     qs = [q] + [q.clone() for _ in range(ncopy - 1)]
     calls = [0]
 
-    def step():
+    def step(lib=None):
         qc = qs[calls[0] % ncopy]
         calls[0] += 1
-        lat = svd.cps_lattice(qc, temp_q=cfg.temp, tau=CPS_TAU, m_max=CPS_MMAX, stream=stream.cuda_stream)
-        return lat, svd.cps_beam(lat, flu, lam=CPS_LAMBDA, beam=CPS_BEAM, stream=stream.cuda_stream)
+        lat = svd.cps_lattice(qc, temp_q=cfg.temp, tau=CPS_TAU, m_max=CPS_MMAX,
+                              stream=stream.cuda_stream, lib=lib)
+        return lat, svd.cps_beam(lat, flu, lam=CPS_LAMBDA, beam=CPS_BEAM,
+                                 stream=stream.cuda_stream, lib=lib)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    svd.svd_profile_read()
+    warm = settle(torch, stream, step, args.warmup, args.settle_ms)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
-    for i in range(args.steps):
-        sampled = i % PROFILE_EVERY == 0
-        if sampled:
-            svd.svd_profile_enable(["lattice"])
+    for _ in range(args.steps):
         lat, bm = step()
-        if sampled:
-            svd.svd_profile_enable(())
     ev1.record(stream)
     torch.cuda.synchronize()
-    ms, n = svd.svd_profile_read()
-    svd.svd_profile_enable("all")
-    for _ in range(min(args.steps, 10)):
-        step()
-    torch.cuda.synchronize()
-    svd.svd_profile_enable(())
-    ms_all, n_all = svd.svd_profile_read()
+    tl = svd.timing_library()
+    nsamp = kernel_samples(args.steps)
+    ms, n = time_kernels(torch, tl, lambda: step(tl), ["lattice"], nsamp)
+    ms_all, n_all = time_kernels(torch, tl, lambda: step(tl), "all", min(args.steps, 10))
     ms_step = ev0.elapsed_time(ev1) / args.steps
     li = svd.KERNELS.index("lattice")
     ms_lat = ms[li] / max(n[li], 1)
@@ -250,13 +336,15 @@ def bench_cps(args, torch, svd, W):
         "value": rows / (ms_step * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "settle_ms": warm["settle_ms"], "warmup_steps_run": warm["steps"],
         "config": {"workload": "cps_" + cfg.name, "B": B, "gamma": G, "V": V, "tau": CPS_TAU,
                    "m_max": CPS_MMAX, "beam": CPS_BEAM, "input_copies": ncopy},
         "kernel_ms": {k: ms_all[i] / max(n_all[i], 1) for i, k in enumerate(svd.KERNELS)
                       if n_all[i]},
         "roofline": {"kernel": "kr_lattice", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "bytes_per_unit": unit, "units_per_launch": rows},
+                     "traffic": None, "bytes_per_unit": unit, "units_per_launch": rows,
+                     "ms_per_launch": ms_lat, "sampled_steps": nsamp},
         "mean_lattice_width": float(lat["n_cand"].float().mean().item()),
     }
     if not args.no_cpu_baseline:
@@ -280,7 +368,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first; the GPU clock needs ~30 ms of load to settle")
+                    help="untimed steps first (continued until --settle-ms of GPU time)")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="least GPU time of warm-up before the timed steps, so that they run on "
+                         "a settled clock (reported as settle_ms)")
     ap.add_argument("--workload", default="batched_serving")
     ap.add_argument("--mode", choices=("standard", "greedy"), default="standard",
                     help="acceptance rule: standard (alpha = min(1, p/q)) or greedy (alpha = p(x), "
@@ -368,72 +459,64 @@ def main():
     ds = [d] + [dict(d, **{k: d[k].clone() for k in keys}) for _ in range(ncopy - 1)]
     calls = [0]
 
-    def step():
+    def step(lib=svd._default):
         d = ds[calls[0] % ncopy]
         calls[0] += 1
         if early:
-            rc = svd.svd_verify_window(
+            rc = lib.svd_verify_window(
                 svd.SVD_RULE_GREEDY if greedy else svd.SVD_RULE_STANDARD, d["p"], d["q"],
                 d["drafts"], None, -1, 1, code, B, K, G, V, cfg.temp, cfg.temp, cfg.seed, 0, sel,
                 L, tok, None, alpha_out, ws, ws.numel(), stream.cuda_stream)
         elif pooled:
-            rc = svd.svd_select_and_verify_rows(
+            rc = lib.svd_select_and_verify_rows(
                 svd.SVD_RULE_GREEDY if greedy else svd.SVD_RULE_STANDARD, d["p_pool"], NP,
                 d["p_index"], d["q_pool"], NQ, d["q_index"], d["drafts"], code, B, K, G, V,
                 cfg.temp, cfg.temp, cfg.seed, 0, sel, L, tok, None, None, ws, ws.numel(),
                 stream.cuda_stream)
         elif greedy:
-            rc = svd.svd_greedy_select_and_verify(d["p"], d["drafts"], code, B, K, G, V, cfg.temp,
+            rc = lib.svd_greedy_select_and_verify(d["p"], d["drafts"], code, B, K, G, V, cfg.temp,
                                                   cfg.seed, 0, sel, L, tok, None, None, ws,
                                                   ws.numel(), stream.cuda_stream)
         else:
-            rc = svd.svd_select_and_verify(d["p"], d["q"], d["drafts"], code, B, K, G, V,
+            rc = lib.svd_select_and_verify(d["p"], d["q"], d["drafts"], code, B, K, G, V,
                                            cfg.temp, cfg.temp, cfg.seed, 0, sel, L, tok, None,
                                            None, beta_out, ws, ws.numel(), stream.cuda_stream)
         if rc != svd.SVD_OK:
             raise svd.SvdError(rc, "select_and_verify (%s)" % args.mode)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    svd.svd_profile_read()  # clear
+    warm = settle(torch, stream, step, args.warmup, args.settle_ms)
 
-    # timed region: K steps; HIP events around the dominant kernel's launches,
-    # recorded on the stream the kernel is launched on, in every PROFILE_EVERY-th
-    # step (each timing event costs the step a queue drain, ~17 us)
-    # (row pairs split into slices stream through kr_rowstats_split instead, and
-    # the chunks of an early exit over a live list through kr_rowstats_live)
-    dom = "pool_stats" if pooled else "rowstats"
-    timed = [dom] if pooled else ["rowstats", "rowstats_split", "rowstats_live"]
+    # timed region: exactly --steps calls of the product library, between two
+    # events on the call's stream; nothing else is recorded inside it
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
-    for i in range(args.steps):
-        sampled = i % PROFILE_EVERY == 0
-        if sampled:
-            svd.svd_profile_enable(timed)
+    for _ in range(args.steps):
         step()
-        if sampled:
-            svd.svd_profile_enable(())
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_kernels, launches = svd.svd_profile_read()
     ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # right after it, on the settled clock: the dominant kernel's launches timed
+    # with HIP events (recorded by the timing build on the stream the kernel is
+    # launched on) in kernel_samples(--steps) more steps of the same inputs
+    # (row pairs split into slices stream through kr_rowstats_split instead, and
+    # the chunks of an early exit over a live list through kr_rowstats_live)
+    tl = svd.timing_library()
+    dom = "pool_stats" if pooled else "rowstats"
+    timed = [dom] if pooled else ["rowstats", "rowstats_split", "rowstats_live"]
+    nsamp = kernel_samples(args.steps)
+    ms_kernels, launches = time_kernels(torch, tl, lambda: step(tl), timed, nsamp)
     if not pooled and launches[svd.KERNELS.index("rowstats")] == 0:
         dom = "rowstats_split"
         if launches[svd.KERNELS.index(dom)] == 0:
             dom = "rowstats_live"
 
-    # after the timed region: a few steps with every kernel timed, for the breakdown
-    svd.svd_profile_enable("all")
-    for _ in range(min(args.steps, 10)):
-        step()
-    torch.cuda.synchronize()
-    svd.svd_profile_enable(())
-    ms_all, launches_all = svd.svd_profile_read()
+    # then a few steps with every kernel timed, for the breakdown
+    ms_all, launches_all = time_kernels(torch, tl, lambda: step(tl), "all", min(args.steps, 10))
 
     positions = B * K * G
     L_host = L.cpu().numpy()
@@ -445,8 +528,7 @@ def main():
         # the later ones slices of the live rows)
         streamed = int((~torch.isnan(alpha_out)).sum().item())
         stream_ids = [i for i in stream_ids if launches[i]]
-        samples = len(range(0, args.steps, PROFILE_EVERY))
-        lpd = max(sum(launches[i] for i in stream_ids) / samples, 1)
+        lpd = max(sum(launches[i] for i in stream_ids) / nsamp, 1)
         units = streamed / lpd
         unit_bytes = bytes_per_row_pair(V, es, args.mode)
         rows = 1 if greedy else 2
@@ -486,6 +568,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
+        "settle_ms": warm["settle_ms"],
+        "warmup_steps_run": warm["steps"],
         "config": {"workload": cfg.name, "mode": args.mode, "early_exit": early,
                    "B": B, "K": K, "gamma": G, "V": V,
                    "logits": cfg.dtype, "temperature": cfg.temp, "global_batch": B,
@@ -498,7 +582,10 @@ def main():
         "roofline": {"kernel": dom_name, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_unit": unit_bytes,
-                     "units_per_launch": units},
+                     "units_per_launch": units, "ms_per_launch": ms_dom,
+                     "sampled_steps": nsamp,
+                     "timing": "HIP events around the kernel's launches (timing build, same "
+                               "kernels) in %d steps right after the timed region" % nsamp},
         "mean_accept_len": float(L_host.mean()),
         "mat": float(L_host.mean() + 1.0),
         "wall_s": wall,

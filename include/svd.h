@@ -48,7 +48,8 @@
  *     concurrently; calls that share a workspace must be ordered.
  *   - The return code reports only what the host can check: SVD_EINVAL for a
  *     NULL required pointer, a size below 1 or above the limits below, or a
- *     temperature that is not finite and positive; SVD_EDTYPE for an unknown
+ *     temperature that is not finite and positive or is so small (below about
+ *     4.2e-39) that log2(e)/T overflows fp32; SVD_EDTYPE for an unknown
  *     dtype; SVD_EWORKSPACE for a workspace below svd_workspace_bytes();
  *     SVD_EHIP when a kernel launch fails.  Nothing is enqueued when the
  *     return code is SVD_EINVAL, SVD_EDTYPE or SVD_EWORKSPACE; after
@@ -204,9 +205,9 @@ int svd_select_and_verify_rows(svd_rule_t rule, const void *p_rows, int64_t n_p_
 
 /*
  * Ragged, EOS-aware windows (DiffuSpec section 3, "Accepted prefix length":
- * the committed tokens are the accepted prefix, and decoding ends early when
- * an accepted token is EOS; section 4.3: the draft length k_t is set per step
- * by a controller, so it differs between sequences of a batch).
+ * a step commits the kept draft's accepted tokens, and an accepted EOS ends
+ * the sequence with no draw; section 4.3: a controller picks each step's
+ * draft length k_t, so sequences of one batch have windows of their own).
  *
  * Arrays are laid out as for svd_select_and_verify, padded to gamma.  Prefix b
  * drafts n_b = gamma_b[b] positions (gamma_b nullable: every n_b = gamma), and
@@ -285,39 +286,6 @@ int svd_cps_beam(const int32_t *cand, const float *cand_logp, const int32_t *n_c
 
 /* Static text for a status code. */
 const char *svd_strerror(int status);
-
-/*
- * Kernel timing for benchmarks and profiling.  svd_profile_enable(mask) turns
- * timing on for the kernels whose bit (1 << SVD_KERNEL_*) is set in mask, and
- * off for all with mask 0.  While on, every call records a HIP event before
- * and after each timed launch, on the stream that launch goes to (creating the
- * events on first use).  svd_profile_read() waits for the recorded events,
- * adds up the elapsed milliseconds per kernel into ms[0..n) (index:
- * SVD_KERNEL_*), writes the number of timed launches per kernel into
- * launches[0..n) (nullable), clears the record and returns SVD_OK.  Not
- * thread-safe; at most 4096 calls are recorded between reads (later ones are
- * not timed).
- */
-enum {
-  SVD_KERNEL_ROWSTATS = 0,   /* row statistics + alpha (streams every scored row pair) */
-  SVD_KERNEL_SELECT = 1,     /* streak scores, argmax, first rejection                 */
-  SVD_KERNEL_DRAW_PASS = 2,  /* fp64 pass over the drawn row pair                       */
-  SVD_KERNEL_DRAW_FIX = 3,   /* reserved (no launch: the pick settles overflowed lists) */
-  SVD_KERNEL_DRAW_PICK = 4,  /* fp64 masses and inverse CDF                             */
-  SVD_KERNEL_BETA = 5,       /* optional overlap mass                                   */
-  SVD_KERNEL_MARK = 6,       /* shared rows: flags of the pool rows read               */
-  SVD_KERNEL_POOL_STATS = 7, /* shared rows: statistics once per pool row read          */
-  SVD_KERNEL_ALPHA_ROWS = 8, /* shared rows: alpha per scored position                  */
-  SVD_KERNEL_LATTICE = 9,    /* candidate lattice of the drafter rows (and its length)  */
-  SVD_KERNEL_BEAM = 10,      /* beam search over the lattice                            */
-  SVD_KERNEL_LATTICE_LEN = 11, /* lattice length and cleared tail                       */
-  SVD_KERNEL_COMBINE = 12,   /* split rows: merge of the slices' statistics, alpha      */
-  SVD_KERNEL_ROWSTATS_SPLIT = 13, /* split rows: statistics of each slice of a row pair  */
-  SVD_KERNEL_ROWSTATS_LIVE = 14,  /* early exit: slices of the live prefixes' row pairs   */
-  SVD_KERNEL_COUNT = 15
-};
-int svd_profile_enable(unsigned kernel_mask);
-int svd_profile_read(double *ms, int64_t *launches, int n);
 
 #ifdef __cplusplus
 }

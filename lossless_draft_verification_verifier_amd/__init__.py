@@ -8,11 +8,13 @@ Raw entry points (same names and argument order as the C ABI; pointer
 arguments take an int address or a tensor):
     svd_workspace_bytes, svd_verify, svd_select_and_verify, svd_greedy_verify,
     svd_greedy_select_and_verify, svd_rows_workspace_bytes, svd_select_and_verify_rows,
-    svd_verify_window, svd_cps_workspace_bytes, svd_cps_lattice, svd_cps_beam, svd_strerror,
-    svd_profile_enable, svd_profile_read
+    svd_verify_window, svd_cps_workspace_bytes, svd_cps_lattice, svd_cps_beam, svd_strerror
 Tensor conveniences that allocate the outputs and the workspace with torch:
     verify, select_and_verify, greedy_verify, greedy_select_and_verify,
     select_and_verify_rows, verify_window, cps_lattice, cps_beam, workspace_bytes
+Kernel timing: timing_library() loads ``libsvd_timed.so`` (the same kernels with
+HIP-event timing compiled in, ``include/svd_timing.h``) as a Library whose raw
+entry points are those above plus svd_profile_enable and svd_profile_read.
 
 Importing fails with ImportError when ``libsvd.so`` has not been built; there
 is no fallback path.
@@ -24,20 +26,24 @@ import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsvd.so")
+TIMED_LIB_PATH = os.path.join(_PKG, "libsvd_timed.so")
 
 SVD_F32, SVD_BF16 = 0, 1
 SVD_OK, SVD_EINVAL, SVD_EDTYPE, SVD_EWORKSPACE, SVD_EHIP = 0, -1, -2, -3, -4
 SVD_MAX_K, SVD_MAX_GAMMA = 64, 4096
-KERNELS = ("rowstats", "select", "draw_pass", "draw_fix", "draw_pick", "beta", "mark",
-           "pool_stats", "alpha_rows", "lattice", "beam", "lattice_len", "combine",
-           "rowstats_split", "rowstats_live")
+# kernel ids of the timing build (SVD_KERNEL_* in include/svd_timing.h)
+KERNELS = ("rowstats", "select", "draw_pass", "draw_pick", "beta", "mark", "pool_stats",
+           "alpha_rows", "lattice", "beam", "lattice_len", "combine", "rowstats_split",
+           "rowstats_live", "adl")
 SVD_RULE_STANDARD, SVD_RULE_GREEDY = 0, 1
 
 C_EXPORTS = ("svd_workspace_bytes", "svd_verify", "svd_select_and_verify", "svd_greedy_verify",
              "svd_greedy_select_and_verify", "svd_rows_workspace_bytes",
              "svd_select_and_verify_rows", "svd_verify_window", "svd_cps_workspace_bytes",
-             "svd_cps_lattice", "svd_cps_beam", "svd_strerror", "svd_profile_enable",
-             "svd_profile_read")
+             "svd_cps_lattice", "svd_cps_beam", "svd_strerror")
+TIMING_EXPORTS = ("svd_profile_enable", "svd_profile_read")
+
+_M64 = 0xFFFFFFFFFFFFFFFF
 
 
 class SvdError(RuntimeError):
@@ -46,13 +52,7 @@ class SvdError(RuntimeError):
         super().__init__("%s failed: %s (status %d)" % (where, svd_strerror(status), status))
 
 
-def _load(path: str = LIB_PATH) -> ctypes.CDLL:
-    if not os.path.exists(path):
-        raise ImportError(
-            "libsvd.so is not built (expected at %s); build it with "
-            "__graft_entry__.build() or python -m lossless_draft_verification_verifier_amd._build"
-            % path)
-    L = ctypes.CDLL(path)
+def _declare(L: ctypes.CDLL, timing: bool) -> ctypes.CDLL:
     vp, i32, i64, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                   ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t)
     L.svd_workspace_bytes.restype = sz
@@ -87,15 +87,12 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.svd_cps_beam.argtypes = [vp, vp, vp, vp, vp, f32, i64, i32, i32, i32, vp, vp, vp, vp]
     L.svd_strerror.restype = ctypes.c_char_p
     L.svd_strerror.argtypes = [ctypes.c_int]
-    L.svd_profile_enable.restype = ctypes.c_int
-    L.svd_profile_enable.argtypes = [ctypes.c_uint]
-    L.svd_profile_read.restype = ctypes.c_int
-    L.svd_profile_read.argtypes = [vp, vp, ctypes.c_int]
+    if timing:
+        L.svd_profile_enable.restype = ctypes.c_int
+        L.svd_profile_enable.argtypes = [ctypes.c_uint]
+        L.svd_profile_read.restype = ctypes.c_int
+        L.svd_profile_read.argtypes = [vp, vp, ctypes.c_int]
     return L
-
-
-_lib = _load()
-_M64 = 0xFFFFFFFFFFFFFFFF
 
 
 def _addr(x):
@@ -107,122 +104,154 @@ def _addr(x):
     return x.data_ptr()
 
 
-# --------------------------------------------------------------------------
-# Raw C ABI (argument marshalling only)
+class Library:
+    """The raw C ABI of one built library (argument marshalling only)."""
 
-def svd_workspace_bytes(B: int, K: int, gamma: int, V: int) -> int:
-    return int(_lib.svd_workspace_bytes(B, K, gamma, V))
+    def __init__(self, path: str = LIB_PATH, timing: bool = False):
+        if not os.path.exists(path):
+            raise ImportError(
+                "%s is not built (expected at %s); build it with __graft_entry__.build() or "
+                "python -m lossless_draft_verification_verifier_amd._build"
+                % (os.path.basename(path), path))
+        self.path = path
+        self.timing = timing
+        self._lib = _declare(ctypes.CDLL(path), timing)
+
+    def svd_workspace_bytes(self, B: int, K: int, gamma: int, V: int) -> int:
+        return int(self._lib.svd_workspace_bytes(B, K, gamma, V))
+
+    def svd_verify(self, p_logits, q_logits, draft, dtype, B, gamma, V, temp_p, temp_q, seed,
+                   row_base, accept_len, next_token, alpha, beta, workspace, workspace_bytes,
+                   hip_stream) -> int:
+        return int(self._lib.svd_verify(
+            _addr(p_logits), _addr(q_logits), _addr(draft), int(dtype), int(B), int(gamma),
+            int(V), float(temp_p), float(temp_q), int(seed) & _M64, int(row_base) & _M64,
+            _addr(accept_len), _addr(next_token), _addr(alpha), _addr(beta), _addr(workspace),
+            int(workspace_bytes), _addr(hip_stream)))
+
+    def svd_select_and_verify(self, p_logits, q_logits, drafts, dtype, B, K, gamma, V, temp_p,
+                              temp_q, seed, row_base, selected, accept_len, next_token, scores,
+                              alpha, beta, workspace, workspace_bytes, hip_stream) -> int:
+        return int(self._lib.svd_select_and_verify(
+            _addr(p_logits), _addr(q_logits), _addr(drafts), int(dtype), int(B), int(K),
+            int(gamma), int(V), float(temp_p), float(temp_q), int(seed) & _M64,
+            int(row_base) & _M64, _addr(selected), _addr(accept_len), _addr(next_token),
+            _addr(scores), _addr(alpha), _addr(beta), _addr(workspace), int(workspace_bytes),
+            _addr(hip_stream)))
+
+    def svd_greedy_verify(self, p_logits, draft, dtype, B, gamma, V, temp_p, seed, row_base,
+                          accept_len, next_token, alpha, workspace, workspace_bytes,
+                          hip_stream) -> int:
+        return int(self._lib.svd_greedy_verify(
+            _addr(p_logits), _addr(draft), int(dtype), int(B), int(gamma), int(V), float(temp_p),
+            int(seed) & _M64, int(row_base) & _M64, _addr(accept_len), _addr(next_token),
+            _addr(alpha), _addr(workspace), int(workspace_bytes), _addr(hip_stream)))
+
+    def svd_greedy_select_and_verify(self, p_logits, drafts, dtype, B, K, gamma, V, temp_p, seed,
+                                     row_base, selected, accept_len, next_token, scores, alpha,
+                                     workspace, workspace_bytes, hip_stream) -> int:
+        return int(self._lib.svd_greedy_select_and_verify(
+            _addr(p_logits), _addr(drafts), int(dtype), int(B), int(K), int(gamma), int(V),
+            float(temp_p), int(seed) & _M64, int(row_base) & _M64, _addr(selected),
+            _addr(accept_len), _addr(next_token), _addr(scores), _addr(alpha), _addr(workspace),
+            int(workspace_bytes), _addr(hip_stream)))
+
+    def svd_rows_workspace_bytes(self, B: int, K: int, gamma: int, V: int, n_p_rows: int,
+                                 n_q_rows: int) -> int:
+        return int(self._lib.svd_rows_workspace_bytes(B, K, gamma, V, n_p_rows, n_q_rows))
+
+    def svd_select_and_verify_rows(self, rule, p_rows, n_p_rows, p_index, q_rows, n_q_rows,
+                                   q_index, drafts, dtype, B, K, gamma, V, temp_p, temp_q, seed,
+                                   row_base, selected, accept_len, next_token, scores, alpha,
+                                   workspace, workspace_bytes, hip_stream) -> int:
+        return int(self._lib.svd_select_and_verify_rows(
+            int(rule), _addr(p_rows), int(n_p_rows), _addr(p_index), _addr(q_rows),
+            int(n_q_rows), _addr(q_index), _addr(drafts), int(dtype), int(B), int(K), int(gamma),
+            int(V), float(temp_p), float(temp_q), int(seed) & _M64, int(row_base) & _M64,
+            _addr(selected), _addr(accept_len), _addr(next_token), _addr(scores), _addr(alpha),
+            _addr(workspace), int(workspace_bytes), _addr(hip_stream)))
+
+    def svd_verify_window(self, rule, p_logits, q_logits, drafts, gamma_b, eos, early_exit, dtype,
+                          B, K, gamma, V, temp_p, temp_q, seed, row_base, selected, accept_len,
+                          next_token, scores, alpha, workspace, workspace_bytes,
+                          hip_stream) -> int:
+        return int(self._lib.svd_verify_window(
+            int(rule), _addr(p_logits), _addr(q_logits), _addr(drafts), _addr(gamma_b), int(eos),
+            int(early_exit), int(dtype), int(B), int(K), int(gamma), int(V), float(temp_p),
+            float(temp_q), int(seed) & _M64, int(row_base) & _M64, _addr(selected),
+            _addr(accept_len), _addr(next_token), _addr(scores), _addr(alpha), _addr(workspace),
+            int(workspace_bytes), _addr(hip_stream)))
+
+    def svd_cps_workspace_bytes(self, B: int, G: int) -> int:
+        return int(self._lib.svd_cps_workspace_bytes(B, G))
+
+    def svd_cps_lattice(self, q_logits, dtype, B, G, V, temp_q, tau, m_max, eos, cand, cand_logp,
+                        n_cand, length, workspace, workspace_bytes, hip_stream) -> int:
+        return int(self._lib.svd_cps_lattice(
+            _addr(q_logits), int(dtype), int(B), int(G), int(V), float(temp_q), float(tau),
+            int(m_max), int(eos), _addr(cand), _addr(cand_logp), _addr(n_cand), _addr(length),
+            _addr(workspace), int(workspace_bytes), _addr(hip_stream)))
+
+    def svd_cps_beam(self, cand, cand_logp, n_cand, length, fluency, lam, B, G, m_max, beam,
+                     paths, path_score, path_len, hip_stream) -> int:
+        return int(self._lib.svd_cps_beam(
+            _addr(cand), _addr(cand_logp), _addr(n_cand), _addr(length), _addr(fluency),
+            float(lam), int(B), int(G), int(m_max), int(beam), _addr(paths), _addr(path_score),
+            _addr(path_len), _addr(hip_stream)))
+
+    def svd_strerror(self, status: int) -> str:
+        return self._lib.svd_strerror(int(status)).decode()
+
+    # -- the timing build only ------------------------------------------------
+    def svd_profile_enable(self, kernels=()) -> int:
+        """Time the named kernels (names from KERNELS; "all" for every one) in
+        later calls; an empty selection stops timing."""
+        if not self.timing:
+            raise RuntimeError("kernel timing needs the timing build (timing_library())")
+        if kernels == "all":
+            kernels = KERNELS
+        mask = 0
+        for k in kernels:
+            mask |= 1 << KERNELS.index(k)
+        return int(self._lib.svd_profile_enable(mask))
+
+    def svd_profile_read(self):
+        """(milliseconds per kernel, launches per kernel), indexed like KERNELS."""
+        if not self.timing:
+            raise RuntimeError("kernel timing needs the timing build (timing_library())")
+        n = len(KERNELS)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int64 * n)()
+        st = self._lib.svd_profile_read(ctypes.cast(ms, ctypes.c_void_p),
+                                        ctypes.cast(cnt, ctypes.c_void_p), n)
+        if st != SVD_OK:
+            raise SvdError(st, "svd_profile_read")
+        return list(ms), list(cnt)
 
 
-def svd_verify(p_logits, q_logits, draft, dtype, B, gamma, V, temp_p, temp_q, seed, row_base,
-               accept_len, next_token, alpha, beta, workspace, workspace_bytes, hip_stream) -> int:
-    return int(_lib.svd_verify(
-        _addr(p_logits), _addr(q_logits), _addr(draft), int(dtype), int(B), int(gamma), int(V),
-        float(temp_p), float(temp_q), int(seed) & _M64, int(row_base) & _M64, _addr(accept_len),
-        _addr(next_token), _addr(alpha), _addr(beta), _addr(workspace), int(workspace_bytes),
-        _addr(hip_stream)))
+_default = Library(LIB_PATH)
+_timed = []
 
 
-def svd_select_and_verify(p_logits, q_logits, drafts, dtype, B, K, gamma, V, temp_p, temp_q,
-                          seed, row_base, selected, accept_len, next_token, scores, alpha, beta,
-                          workspace, workspace_bytes, hip_stream) -> int:
-    return int(_lib.svd_select_and_verify(
-        _addr(p_logits), _addr(q_logits), _addr(drafts), int(dtype), int(B), int(K), int(gamma),
-        int(V), float(temp_p), float(temp_q), int(seed) & _M64, int(row_base) & _M64,
-        _addr(selected), _addr(accept_len), _addr(next_token), _addr(scores), _addr(alpha),
-        _addr(beta), _addr(workspace), int(workspace_bytes), _addr(hip_stream)))
+def timing_library() -> Library:
+    """The timing build, loaded once (ImportError when it is not built)."""
+    if not _timed:
+        _timed.append(Library(TIMED_LIB_PATH, timing=True))
+    return _timed[0]
 
 
-def svd_greedy_verify(p_logits, draft, dtype, B, gamma, V, temp_p, seed, row_base, accept_len,
-                      next_token, alpha, workspace, workspace_bytes, hip_stream) -> int:
-    return int(_lib.svd_greedy_verify(
-        _addr(p_logits), _addr(draft), int(dtype), int(B), int(gamma), int(V), float(temp_p),
-        int(seed) & _M64, int(row_base) & _M64, _addr(accept_len), _addr(next_token),
-        _addr(alpha), _addr(workspace), int(workspace_bytes), _addr(hip_stream)))
-
-
-def svd_greedy_select_and_verify(p_logits, drafts, dtype, B, K, gamma, V, temp_p, seed, row_base,
-                                 selected, accept_len, next_token, scores, alpha, workspace,
-                                 workspace_bytes, hip_stream) -> int:
-    return int(_lib.svd_greedy_select_and_verify(
-        _addr(p_logits), _addr(drafts), int(dtype), int(B), int(K), int(gamma), int(V),
-        float(temp_p), int(seed) & _M64, int(row_base) & _M64, _addr(selected),
-        _addr(accept_len), _addr(next_token), _addr(scores), _addr(alpha), _addr(workspace),
-        int(workspace_bytes), _addr(hip_stream)))
-
-
-def svd_rows_workspace_bytes(B: int, K: int, gamma: int, V: int, n_p_rows: int,
-                             n_q_rows: int) -> int:
-    return int(_lib.svd_rows_workspace_bytes(B, K, gamma, V, n_p_rows, n_q_rows))
-
-
-def svd_select_and_verify_rows(rule, p_rows, n_p_rows, p_index, q_rows, n_q_rows, q_index, drafts,
-                               dtype, B, K, gamma, V, temp_p, temp_q, seed, row_base, selected,
-                               accept_len, next_token, scores, alpha, workspace, workspace_bytes,
-                               hip_stream) -> int:
-    return int(_lib.svd_select_and_verify_rows(
-        int(rule), _addr(p_rows), int(n_p_rows), _addr(p_index), _addr(q_rows), int(n_q_rows),
-        _addr(q_index), _addr(drafts), int(dtype), int(B), int(K), int(gamma), int(V),
-        float(temp_p), float(temp_q), int(seed) & _M64, int(row_base) & _M64, _addr(selected),
-        _addr(accept_len), _addr(next_token), _addr(scores), _addr(alpha), _addr(workspace),
-        int(workspace_bytes), _addr(hip_stream)))
-
-
-def svd_verify_window(rule, p_logits, q_logits, drafts, gamma_b, eos, early_exit, dtype, B, K,
-                      gamma, V, temp_p, temp_q, seed, row_base, selected, accept_len, next_token,
-                      scores, alpha, workspace, workspace_bytes, hip_stream) -> int:
-    return int(_lib.svd_verify_window(
-        int(rule), _addr(p_logits), _addr(q_logits), _addr(drafts), _addr(gamma_b), int(eos),
-        int(early_exit), int(dtype), int(B), int(K), int(gamma), int(V), float(temp_p),
-        float(temp_q), int(seed) & _M64, int(row_base) & _M64, _addr(selected), _addr(accept_len),
-        _addr(next_token), _addr(scores), _addr(alpha), _addr(workspace), int(workspace_bytes),
-        _addr(hip_stream)))
-
-
-def svd_cps_workspace_bytes(B: int, G: int) -> int:
-    return int(_lib.svd_cps_workspace_bytes(B, G))
-
-
-def svd_cps_lattice(q_logits, dtype, B, G, V, temp_q, tau, m_max, eos, cand, cand_logp, n_cand,
-                    length, workspace, workspace_bytes, hip_stream) -> int:
-    return int(_lib.svd_cps_lattice(
-        _addr(q_logits), int(dtype), int(B), int(G), int(V), float(temp_q), float(tau),
-        int(m_max), int(eos), _addr(cand), _addr(cand_logp), _addr(n_cand), _addr(length),
-        _addr(workspace), int(workspace_bytes), _addr(hip_stream)))
-
-
-def svd_cps_beam(cand, cand_logp, n_cand, length, fluency, lam, B, G, m_max, beam, paths,
-                 path_score, path_len, hip_stream) -> int:
-    return int(_lib.svd_cps_beam(
-        _addr(cand), _addr(cand_logp), _addr(n_cand), _addr(length), _addr(fluency), float(lam),
-        int(B), int(G), int(m_max), int(beam), _addr(paths), _addr(path_score), _addr(path_len),
-        _addr(hip_stream)))
-
-
-def svd_strerror(status: int) -> str:
-    return _lib.svd_strerror(int(status)).decode()
-
-
-def svd_profile_enable(kernels=()) -> int:
-    """Time the named kernels (names from KERNELS; "all" for every one) in
-    later calls; an empty selection stops timing."""
-    if kernels == "all":
-        kernels = KERNELS
-    mask = 0
-    for k in kernels:
-        mask |= 1 << KERNELS.index(k)
-    return int(_lib.svd_profile_enable(mask))
-
-
-def svd_profile_read():
-    """(milliseconds per kernel, launches per kernel), indexed like KERNELS."""
-    n = len(KERNELS)
-    ms = (ctypes.c_double * n)()
-    cnt = (ctypes.c_int64 * n)()
-    st = _lib.svd_profile_read(ctypes.cast(ms, ctypes.c_void_p), ctypes.cast(cnt, ctypes.c_void_p), n)
-    if st != SVD_OK:
-        raise SvdError(st, "svd_profile_read")
-    return list(ms), list(cnt)
+svd_workspace_bytes = _default.svd_workspace_bytes
+svd_verify = _default.svd_verify
+svd_select_and_verify = _default.svd_select_and_verify
+svd_greedy_verify = _default.svd_greedy_verify
+svd_greedy_select_and_verify = _default.svd_greedy_select_and_verify
+svd_rows_workspace_bytes = _default.svd_rows_workspace_bytes
+svd_select_and_verify_rows = _default.svd_select_and_verify_rows
+svd_verify_window = _default.svd_verify_window
+svd_cps_workspace_bytes = _default.svd_cps_workspace_bytes
+svd_cps_lattice = _default.svd_cps_lattice
+svd_cps_beam = _default.svd_cps_beam
+svd_strerror = _default.svd_strerror
 
 
 # --------------------------------------------------------------------------
@@ -479,8 +508,9 @@ def verify_window(p, q, drafts, gamma_b=None, eos=-1, rule="standard", early_exi
     return out
 
 
-def cps_lattice(q, temp_q=1.0, tau=0.8, m_max=15, eos=-1, stream=None):
-    """Candidate lattice of drafter logits q [B, G, V] (bf16 or fp32)."""
+def cps_lattice(q, temp_q=1.0, tau=0.8, m_max=15, eos=-1, stream=None, lib=None):
+    """Candidate lattice of drafter logits q [B, G, V] (bf16 or fp32); lib: the
+    Library to call (default: the product library)."""
     import torch
     dev = q.device
     _check(q, "q", dev)
@@ -494,15 +524,17 @@ def cps_lattice(q, temp_q=1.0, tau=0.8, m_max=15, eos=-1, stream=None):
         raise ValueError("sizes out of range")
     ws = torch.empty(n, dtype=torch.uint8, device=dev)
     st = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    rc = svd_cps_lattice(q, _dtype_code(q), B, G, V, temp_q, tau, m_max, eos, out["cand"],
-                         out["cand_logp"], out["n_cand"], out["len"], ws, n, st)
+    lib = _default if lib is None else lib
+    rc = lib.svd_cps_lattice(q, _dtype_code(q), B, G, V, temp_q, tau, m_max, eos, out["cand"],
+                             out["cand_logp"], out["n_cand"], out["len"], ws, n, st)
     if rc != SVD_OK:
         raise SvdError(rc, "svd_cps_lattice")
     return out
 
 
-def cps_beam(lat, fluency=None, lam=1.0, beam=3, stream=None):
-    """Beam search over a lattice from cps_lattice; fluency [B, G, m_max, m_max] fp32 or None."""
+def cps_beam(lat, fluency=None, lam=1.0, beam=3, stream=None, lib=None):
+    """Beam search over a lattice from cps_lattice; fluency [B, G, m_max, m_max] fp32 or None;
+    lib: the Library to call (default: the product library)."""
     import torch
     cand = lat["cand"]
     dev = cand.device
@@ -515,8 +547,9 @@ def cps_beam(lat, fluency=None, lam=1.0, beam=3, stream=None):
            "score": torch.empty((B, beam), dtype=torch.float32, device=dev),
            "path_len": torch.empty((B, beam), dtype=torch.int32, device=dev)}
     st = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    rc = svd_cps_beam(cand, lat["cand_logp"], lat["n_cand"], lat["len"], fluency, lam, B, G, M,
-                      beam, out["paths"], out["score"], out["path_len"], st)
+    lib = _default if lib is None else lib
+    rc = lib.svd_cps_beam(cand, lat["cand_logp"], lat["n_cand"], lat["len"], fluency, lam, B, G,
+                          M, beam, out["paths"], out["score"], out["path_len"], st)
     if rc != SVD_OK:
         raise SvdError(rc, "svd_cps_beam")
     return out

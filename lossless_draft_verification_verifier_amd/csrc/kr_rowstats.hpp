@@ -19,26 +19,15 @@
 
 namespace svd {
 
-// Launch shape of the standalone streaming kernel: threads per workgroup,
-// 16-byte loads in flight per thread and row, and nontemporal loads.
-#ifndef SVD_ROW_BLOCK
-#define SVD_ROW_BLOCK 1024
-#endif
-#ifndef SVD_ROW_UNROLL
-#define SVD_ROW_UNROLL 2
-#endif
-#ifndef SVD_ROW_NT
-#define SVD_ROW_NT 1
-#endif
-constexpr int kRowBlock = SVD_ROW_BLOCK;
-constexpr int kRowUnroll = SVD_ROW_UNROLL;
+// Launch shape of the standalone streaming kernel (from a sweep of threads
+// per workgroup and loads in flight): 1024 threads, two 16-byte loads in
+// flight per thread and row.
+constexpr int kRowBlock = 1024;
+constexpr int kRowUnroll = 2;
 
+// Streaming loads are nontemporal: every logit byte is read once.
 __device__ __forceinline__ vec16 stream_load(const vec16 *p) {
-#if SVD_ROW_NT
   return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
 }
 
 // Fold one vector of n logits into a thread's (max, sum) state.
@@ -299,10 +288,7 @@ namespace svd {
 // its n * J rows into as many slices as fill that grid, so the later chunks,
 // with few prefixes left, still spread over every CU.  The slicing depends
 // only on n, so a row's statistics do not depend on which prefixes are live.
-#ifndef SVD_LIVE_GRID
-#define SVD_LIVE_GRID 1024
-#endif
-constexpr int kLiveGrid = SVD_LIVE_GRID;
+constexpr int kLiveGrid = 1024;
 
 struct LivePlan {
   int S;      // slices per row

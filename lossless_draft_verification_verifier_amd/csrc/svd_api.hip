@@ -9,6 +9,8 @@
 #include <utility>
 
 #include "svd.h"
+#include "svd_timing.h"
+#include "svd_timing.hpp"
 #include "kr_beta.hpp"
 #include "kr_cps.hpp"
 #include "kr_draw.hpp"
@@ -109,51 +111,6 @@ hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s
   return hipLaunchKernel((const void *)kernel, grid, block, ptrs, 0, stream);
 }
 
-// ---------------------------------------------------------------------------
-// Kernel timing (svd_profile_*): a start and an end event around every launch
-// of a call, recorded on the stream the kernel goes to.
-
-constexpr int kProfCalls = 4096;
-constexpr int kProfLaunches = 48;
-
-struct Profiler {
-  unsigned mask = 0;  // bit k: time kernel k
-  int ncalls = 0;
-  hipEvent_t ev[kProfCalls][kProfLaunches][2] = {};
-  int kid[kProfCalls][kProfLaunches];
-  int nl[kProfCalls] = {};
-};
-Profiler g_prof;
-
-struct CallTimer {
-  int slot = -1;
-  CallTimer() {
-    if (!g_prof.mask || g_prof.ncalls >= kProfCalls) return;
-    slot = g_prof.ncalls++;
-    g_prof.nl[slot] = 0;
-  }
-  // start of a launch of kernel `kernel_id` on `s`; returns its record or -1
-  int begin(int kernel_id, hipStream_t s) {
-    if (slot < 0 || !((g_prof.mask >> kernel_id) & 1u)) return -1;
-    const int i = g_prof.nl[slot];
-    if (i >= kProfLaunches) return -1;
-    hipEvent_t *e = g_prof.ev[slot][i];
-    for (int j = 0; j < 2; ++j)
-      if (!e[j] && hipEventCreate(&e[j]) != hipSuccess) {
-        e[j] = nullptr;
-        return -1;
-      }
-    if (hipEventRecord(e[0], s) != hipSuccess) return -1;
-    g_prof.kid[slot][i] = -1;  // until the end event is recorded
-    g_prof.nl[slot] = i + 1;
-    return i;
-  }
-  void end(int rec, int kernel_id, hipStream_t s) {
-    if (rec < 0) return;
-    if (hipEventRecord(g_prof.ev[slot][rec][1], s) == hipSuccess) g_prof.kid[slot][rec] = kernel_id;
-  }
-};
-
 // Index tables of the shared-row layout ([B][K][gamma+1] and [B][K][gamma]);
 // null tables mean the dense layout.
 struct RowIndex {
@@ -208,11 +165,7 @@ constexpr int64_t kLatticeSplitRows = 128;
 
 // Positions per chunk when one draft per prefix is streamed up to its first
 // rejection: enough workgroups per launch to fill the GPU about once.
-#ifndef SVD_EARLY_CHUNK
-#define SVD_EARLY_CHUNK 0
-#endif
 int early_chunk(int64_t B, int G) {
-  if (SVD_EARLY_CHUNK > 0) return std::min(SVD_EARLY_CHUNK, G);
   const int64_t want = (512 + B - 1) / B;
   return (int)std::max<int64_t>(1, std::min<int64_t>(want, G));
 }
@@ -541,7 +494,13 @@ int run(const Call &c) {
   return rc != SVD_OK ? rc : enqueue_draw<E, kVec>(a, stream, tm);
 }
 
-bool temp_ok(float t) { return std::isfinite(t) && t > 0.0f; }
+// A temperature must be finite and positive, and log2(e) / T (the fp32 factor
+// of every exp2 argument) finite: T below about 4.2e-39 is rejected.
+bool temp_ok(float t) {
+  if (!(std::isfinite(t) && t > 0.0f)) return false;
+  const float c = (float)(1.4426950408889634 / (double)t);
+  return std::isfinite(c);
+}
 
 bool pools_ok(int64_t np, int64_t nq, bool greedy) {
   const int64_t lim = (int64_t)1 << 30;
@@ -810,33 +769,6 @@ const char *svd_strerror(int status) {
     case SVD_EHIP: return "HIP kernel launch failed";
     default: return "unknown status";
   }
-}
-
-int svd_profile_enable(unsigned kernel_mask) {
-  g_prof.mask = kernel_mask & ((1u << SVD_KERNEL_COUNT) - 1u);
-  return SVD_OK;
-}
-
-int svd_profile_read(double *ms, int64_t *launches, int n) {
-  if (!ms || n < 0) return SVD_EINVAL;
-  for (int i = 0; i < n; ++i) {
-    ms[i] = 0.0;
-    if (launches) launches[i] = 0;
-  }
-  for (int c = 0; c < g_prof.ncalls; ++c) {
-    for (int i = 0; i < g_prof.nl[c]; ++i) {
-      const int k = g_prof.kid[c][i];
-      if (k < 0 || k >= n) continue;
-      if (hipEventSynchronize(g_prof.ev[c][i][1]) != hipSuccess) return SVD_EHIP;
-      float t = 0.0f;
-      if (hipEventElapsedTime(&t, g_prof.ev[c][i][0], g_prof.ev[c][i][1]) != hipSuccess)
-        return SVD_EHIP;
-      ms[k] += t;
-      if (launches) launches[k] += 1;
-    }
-  }
-  g_prof.ncalls = 0;
-  return SVD_OK;
 }
 
 }  // extern "C"

@@ -204,8 +204,8 @@ static int do_prefix(const job_t *J, int64_t b, double *P, double *Q, double *R,
 
   /* The window: draft k proposes positions j < n (n = gamma_b[b], or gamma);
    * with an end-of-sequence token, a draft's usable positions stop at its
-   * first EOS, included (DiffuSpec section 3, "Accepted prefix length":
-   * decoding ends early at an accepted EOS).  m_k = that length. */
+   * first EOS, included (DiffuSpec section 3, "Accepted prefix length": an
+   * accepted EOS finishes the sequence).  m_k = that length. */
   const int32_t n = J->gamma_b ? J->gamma_b[b] : G;
   if (n < 1 || n > G) {
     mark_invalid(J, b);

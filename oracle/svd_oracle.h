@@ -112,8 +112,8 @@ int svdo_greedy_select_and_verify(const void *p_logits, const int32_t *drafts, i
 
 /*
  * Ragged, EOS-aware windows (DiffuSpec section 3, "Accepted prefix length":
- * the committed tokens are the accepted prefix, and decoding ends early at an
- * accepted EOS; section 4.3: the draft length k_t changes from step to step).
+ * a step commits the kept draft's accepted tokens, and an accepted EOS ends
+ * the sequence with no draw; section 4.3: k_t is chosen anew every step).
  * Prefix b drafts n = gamma_b[b] positions (1 <= n <= gamma; NULL: gamma) in
  * arrays padded to gamma.  With eos >= 0, draft k's usable length m_k stops at
  * its first drafted EOS, included (else m_k = n).  Then

@@ -1,6 +1,7 @@
 """The C ABI without a GPU: the library loads, exports every function that
 include/svd.h declares, sizes its workspace, and rejects bad arguments on the
-host before any HIP call."""
+host before any HIP call.  The timing build exports svd.h and svd_timing.h;
+the product library exports no timing call."""
 import ctypes
 import os
 import re
@@ -10,20 +11,21 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "svd.h")
+TIMING_HEADER = os.path.join(ROOT, "include", "svd_timing.h")
 
 
 @pytest.fixture(scope="module")
 def svd():
-    lib = os.path.join(ROOT, "lossless_draft_verification_verifier_amd", "libsvd.so")
-    if not os.path.exists(lib):
+    pkg = os.path.join(ROOT, "lossless_draft_verification_verifier_amd")
+    if not all(os.path.exists(os.path.join(pkg, f)) for f in ("libsvd.so", "libsvd_timed.so")):
         from lossless_draft_verification_verifier_amd import _build
         _build.build()
     import lossless_draft_verification_verifier_amd as m
     return m
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(svd_\w+)\s*\(", text, flags=re.M)
     return sorted(set(names))
@@ -45,6 +47,34 @@ def test_every_declared_symbol_is_exported(svd):
     exported = set(re.findall(r"\bT (svd_\w+)", out))
     assert set(declared_functions()) <= exported
     assert set(svd.C_EXPORTS) == set(declared_functions())
+    # the product library keeps no timing state and exports no timing call
+    assert not exported & set(declared_functions(TIMING_HEADER))
+
+
+def test_timing_build_exports_both_headers(svd):
+    out = subprocess.run(["nm", "-D", "--defined-only", svd.TIMED_LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (svd_\w+)", out))
+    timing = set(declared_functions(TIMING_HEADER))
+    assert timing == set(svd.TIMING_EXPORTS)
+    assert set(declared_functions()) | timing <= exported
+    t = svd.timing_library()
+    assert t.svd_workspace_bytes(256, 1, 8, 152064) == svd.svd_workspace_bytes(256, 1, 8, 152064)
+    assert t.svd_profile_enable(()) == svd.SVD_OK
+    ms, n = t.svd_profile_read()
+    assert ms == [0.0] * len(svd.KERNELS) and n == [0] * len(svd.KERNELS)
+    with pytest.raises(RuntimeError):
+        svd._default.svd_profile_read()
+
+
+def test_product_library_has_no_mutable_namespace_scope_state():
+    # every object with static storage in the product library's source is
+    # const or constexpr (the timing state lives in svd_timing.hip only)
+    src = open(os.path.join(ROOT, "lossless_draft_verification_verifier_amd", "csrc",
+                            "svd_api.hip")).read()
+    src = re.sub(r"//[^\n]*", "", src)
+    assert "g_prof" not in src and "Profiler" not in src
+    assert not re.search(r"^static\s+(?!const|constexpr|inline)", src, flags=re.M)
 
 
 def test_workspace_bytes(svd):
@@ -83,6 +113,9 @@ def _call(svd, **kw):
     (dict(dtype=2), -2), (dict(B=0), -1), (dict(K=0), -1), (dict(K=65), -1), (dict(G=0), -1),
     (dict(G=4097), -1), (dict(V=0), -1), (dict(tp=0.0), -1), (dict(tq=-1.0), -1),
     (dict(tp=float("nan")), -1), (dict(tq=float("inf")), -1), (dict(ws=(1 << 20) + 64), -1),
+    # log2(e)/T overflows fp32 below T ~ 4.2e-39 (a subnormal temperature)
+    (dict(tp=1e-40), -1), (dict(tq=4.0e-39), -1), (dict(tp=1e-45), -1),
+    (dict(tp=4.5e-39), -3),  # still a valid temperature: only the workspace is missing
     (dict(), -3),  # workspace of 0 bytes
 ])
 def test_host_side_argument_errors(svd, kw, want):
@@ -112,7 +145,7 @@ def _greedy(svd, **kw):
     (dict(p=None), -1), (dict(d=None), -1), (dict(sel=None), -1), (dict(L=None), -1),
     (dict(tok=None), -1), (dict(ws=None), -1), (dict(dtype=7), -2), (dict(B=0), -1),
     (dict(K=65), -1), (dict(G=0), -1), (dict(V=0), -1), (dict(tp=0.0), -1),
-    (dict(tp=float("inf")), -1), (dict(ws=(1 << 20) + 32), -1),
+    (dict(tp=float("inf")), -1), (dict(ws=(1 << 20) + 32), -1), (dict(tp=2e-39), -1),
     (dict(), -3),  # workspace of 0 bytes
 ])
 def test_greedy_host_side_argument_errors(svd, kw, want):
@@ -142,8 +175,8 @@ def test_binding_fails_loudly_without_library(tmp_path):
 
 
 def test_profile_kernel_names_follow_the_header(svd):
-    # the binding's KERNELS tuple is indexed by the header's SVD_KERNEL_* ids
-    text = open(HEADER).read()
+    # the binding's KERNELS tuple is indexed by the timing header's SVD_KERNEL_* ids
+    text = open(TIMING_HEADER).read()
     ids = {m.group(1).lower(): int(m.group(2))
            for m in re.finditer(r"SVD_KERNEL_([A-Z_]+) = (\d+)", text)}
     count = ids.pop("count")

@@ -1,7 +1,8 @@
 """Losslessness of the oracle: committed tokens follow the verifier.
 
-SpecDiff-2 section 2 and DiffuSpec section 3 state that the acceptance and
-replacement rules preserve the verifier's output distribution.  Two pins:
+SpecDiff-2 section 2 and DiffuSpec section 3: accepting or resampling as the
+rule says leaves the committed tokens distributed exactly as the verifier's own
+samples would be.  Two pins:
 
 * brute force: for a tiny vocabulary and window, enumerate every draft and
   compute the exact law of the committed tokens from the oracle's alpha and

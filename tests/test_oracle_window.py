@@ -1,6 +1,6 @@
 """Pins of the oracle's ragged, EOS-aware windows (DiffuSpec section 3,
-"Accepted prefix length": the commit is the accepted prefix and decoding ends
-early at an accepted EOS; section 4.3: the draft length changes per step).
+"Accepted prefix length": a step commits the kept draft's accepted tokens and
+an accepted EOS finishes the sequence; section 4.3: k_t is chosen per step).
 
 * full windows without EOS reproduce the dense oracle bit for bit;
 * a window of n positions equals the dense oracle on the arrays cut to n
