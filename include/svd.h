@@ -81,7 +81,8 @@ enum {
   SVD_EINVAL = -1,
   SVD_EDTYPE = -2,
   SVD_EWORKSPACE = -3,
-  SVD_EHIP = -4
+  SVD_EHIP = -4,
+  SVD_ESCRATCH = -5  /* svd_select_and_verify_noalloc: sizes need more than its scratch */
 };
 
 /* Documented limits. */
@@ -283,6 +284,34 @@ int svd_cps_beam(const int32_t *cand, const float *cand_logp, const int32_t *n_c
                  const int32_t *len, const float *fluency, float lambda, int64_t B, int32_t G,
                  int32_t m_max, int32_t beam, int32_t *paths, float *path_score,
                  int32_t *path_len, void *hip_stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * operation, arguments and outputs as svd_select_and_verify (bit for bit), but
+ * no workspace argument: the workspace is a device array of
+ * SVD_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, allocated when
+ * the library's code is loaded on that GPU and held until the process ends.
+ * The call itself allocates and frees nothing; its first call on a device
+ * looks up the array's address there (hipGetSymbolAddress), with that device
+ * current, so hip_stream must belong to the current device.
+ *   - SVD_ESCRATCH when svd_workspace_bytes(B, K, gamma, V) exceeds
+ *     SVD_NOALLOC_SCRATCH_BYTES (16 MiB: at gamma = 8 and V = 152064, up to
+ *     about 1000 prefixes), SVD_EINVAL for sizes svd_workspace_bytes rejects;
+ *     both before any HIP call.  Other errors as for svd_select_and_verify,
+ *     and SVD_EHIP when the array's address cannot be found.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents; each call writes every part it reads before reading it.
+ *     Calls that overlap on one GPU (on different streams, or from different
+ *     threads without ordering) race on the array: order them.
+ */
+#define SVD_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int svd_select_and_verify_noalloc(const void *p_logits, const void *q_logits,
+                                  const int32_t *drafts, svd_dtype_t dtype, int64_t B, int32_t K,
+                                  int32_t gamma, int32_t V, float temp_p, float temp_q,
+                                  uint64_t seed, uint64_t row_base, int32_t *selected,
+                                  int32_t *accept_len, int32_t *next_token, float *scores,
+                                  float *alpha, float *beta, void *hip_stream);
 
 /* Static text for a status code. */
 const char *svd_strerror(int status);

@@ -8,7 +8,8 @@ Raw entry points (same names and argument order as the C ABI; pointer
 arguments take an int address or a tensor):
     svd_workspace_bytes, svd_verify, svd_select_and_verify, svd_greedy_verify,
     svd_greedy_select_and_verify, svd_rows_workspace_bytes, svd_select_and_verify_rows,
-    svd_verify_window, svd_cps_workspace_bytes, svd_cps_lattice, svd_cps_beam, svd_strerror
+    svd_verify_window, svd_cps_workspace_bytes, svd_cps_lattice, svd_cps_beam,
+    svd_select_and_verify_noalloc, svd_strerror
 Tensor conveniences that allocate the outputs and the workspace with torch:
     verify, select_and_verify, greedy_verify, greedy_select_and_verify,
     select_and_verify_rows, verify_window, cps_lattice, cps_beam, workspace_bytes
@@ -29,7 +30,8 @@ LIB_PATH = os.path.join(_PKG, "libsvd.so")
 TIMED_LIB_PATH = os.path.join(_PKG, "libsvd_timed.so")
 
 SVD_F32, SVD_BF16 = 0, 1
-SVD_OK, SVD_EINVAL, SVD_EDTYPE, SVD_EWORKSPACE, SVD_EHIP = 0, -1, -2, -3, -4
+SVD_OK, SVD_EINVAL, SVD_EDTYPE, SVD_EWORKSPACE, SVD_EHIP, SVD_ESCRATCH = 0, -1, -2, -3, -4, -5
+SVD_NOALLOC_SCRATCH_BYTES = 16 << 20
 SVD_MAX_K, SVD_MAX_GAMMA = 64, 4096
 # kernel ids of the timing build (SVD_KERNEL_* in include/svd_timing.h)
 KERNELS = ("rowstats", "select", "draw_pass", "draw_pick", "beta", "mark", "pool_stats",
@@ -40,7 +42,7 @@ SVD_RULE_STANDARD, SVD_RULE_GREEDY = 0, 1
 C_EXPORTS = ("svd_workspace_bytes", "svd_verify", "svd_select_and_verify", "svd_greedy_verify",
              "svd_greedy_select_and_verify", "svd_rows_workspace_bytes",
              "svd_select_and_verify_rows", "svd_verify_window", "svd_cps_workspace_bytes",
-             "svd_cps_lattice", "svd_cps_beam", "svd_strerror")
+             "svd_cps_lattice", "svd_cps_beam", "svd_select_and_verify_noalloc", "svd_strerror")
 TIMING_EXPORTS = ("svd_profile_enable", "svd_profile_read")
 
 _M64 = 0xFFFFFFFFFFFFFFFF
@@ -85,6 +87,9 @@ def _declare(L: ctypes.CDLL, timing: bool) -> ctypes.CDLL:
                                   vp, vp, sz, vp]
     L.svd_cps_beam.restype = ctypes.c_int
     L.svd_cps_beam.argtypes = [vp, vp, vp, vp, vp, f32, i64, i32, i32, i32, vp, vp, vp, vp]
+    L.svd_select_and_verify_noalloc.restype = ctypes.c_int
+    L.svd_select_and_verify_noalloc.argtypes = [vp, vp, vp, ctypes.c_int, i64, i32, i32, i32, f32,
+                                                f32, u64, u64, vp, vp, vp, vp, vp, vp, vp]
     L.svd_strerror.restype = ctypes.c_char_p
     L.svd_strerror.argtypes = [ctypes.c_int]
     if timing:
@@ -199,6 +204,15 @@ class Library:
             float(lam), int(B), int(G), int(m_max), int(beam), _addr(paths), _addr(path_score),
             _addr(path_len), _addr(hip_stream)))
 
+    def svd_select_and_verify_noalloc(self, p_logits, q_logits, drafts, dtype, B, K, gamma, V,
+                                      temp_p, temp_q, seed, row_base, selected, accept_len,
+                                      next_token, scores, alpha, beta, hip_stream) -> int:
+        return int(self._lib.svd_select_and_verify_noalloc(
+            _addr(p_logits), _addr(q_logits), _addr(drafts), int(dtype), int(B), int(K),
+            int(gamma), int(V), float(temp_p), float(temp_q), int(seed) & _M64,
+            int(row_base) & _M64, _addr(selected), _addr(accept_len), _addr(next_token),
+            _addr(scores), _addr(alpha), _addr(beta), _addr(hip_stream)))
+
     def svd_strerror(self, status: int) -> str:
         return self._lib.svd_strerror(int(status)).decode()
 
@@ -251,6 +265,7 @@ svd_verify_window = _default.svd_verify_window
 svd_cps_workspace_bytes = _default.svd_cps_workspace_bytes
 svd_cps_lattice = _default.svd_cps_lattice
 svd_cps_beam = _default.svd_cps_beam
+svd_select_and_verify_noalloc = _default.svd_select_and_verify_noalloc
 svd_strerror = _default.svd_strerror
 
 

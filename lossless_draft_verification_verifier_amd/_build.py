@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsvd.so")
 TIMED_LIB = os.path.join(PKG, "libsvd_timed.so")
-SOURCES = [os.path.join(CSRC, "svd_api.hip")]
+SOURCES = [os.path.join(CSRC, "svd_api.hip"), os.path.join(CSRC, "svd_noalloc.hip")]
 TIMED_SOURCES = SOURCES + [os.path.join(CSRC, "svd_timing.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".hpp")]
 

@@ -767,6 +767,7 @@ const char *svd_strerror(int status) {
     case SVD_EDTYPE: return "unsupported logit dtype";
     case SVD_EWORKSPACE: return "workspace smaller than svd_workspace_bytes()";
     case SVD_EHIP: return "HIP kernel launch failed";
+    case SVD_ESCRATCH: return "sizes need a workspace larger than the no-allocation scratch (SVD_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -92,7 +92,7 @@ def test_workspace_bytes(svd):
 
 
 def test_strerror(svd):
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert isinstance(svd.svd_strerror(st), str) and svd.svd_strerror(st)
     assert svd.svd_strerror(12345) == "unknown status"
 
@@ -182,3 +182,18 @@ def test_profile_kernel_names_follow_the_header(svd):
     count = ids.pop("count")
     assert len(svd.KERNELS) == count
     assert {name: i for i, name in enumerate(svd.KERNELS)} == ids
+
+
+def test_noalloc_host_side_errors(svd):
+    # sizes are checked on the host before any HIP call (fake addresses)
+    def call(B, K, G, V):
+        return svd.svd_select_and_verify_noalloc(4096, 8192, 12288, svd.SVD_BF16, B, K, G, V, 1.0,
+                                                 1.0, 0, 0, 16384, 20480, 24576, None, None,
+                                                 None, None)
+    assert svd.svd_workspace_bytes(2048, 1, 8, 152064) > svd.SVD_NOALLOC_SCRATCH_BYTES
+    assert call(2048, 1, 8, 152064) == svd.SVD_ESCRATCH
+    for bad in [(0, 1, 8, 100), (1, 65, 8, 100), (1, 1, 0, 100), (1, 1, 8, 0)]:
+        assert call(*bad) == svd.SVD_EINVAL, bad
+    text = open(HEADER).read()
+    assert "#define SVD_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
+    assert svd.SVD_NOALLOC_SCRATCH_BYTES == 16 << 20
