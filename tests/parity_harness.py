@@ -25,6 +25,7 @@ ALPHA_TOL = 1e-5
 ACCEPT_EPS = 1e-5
 EMIT_EPS = 1e-10
 LITERAL_CDF_WINDOW = 1e-6
+EXCUSED_RATE = 1e-4  # excused mismatches per decision kind: under 0.01 %
 
 
 @dataclass
@@ -46,6 +47,25 @@ class ParityReport:
     def flag_rate(self) -> float:
         n = sum(self.decisions.values())
         return sum(self.flagged.values()) / max(n, 1)
+
+    def excused_within(self, rate: float = EXCUSED_RATE) -> bool:
+        """Excused (near-tie) mismatches at most `rate` of the decisions
+        compared, per decision kind (with few decisions: none at all)."""
+        return all(self.flagged[k] <= rate * self.decisions[k] for k in self.flagged)
+
+    def merge(self, other: "ParityReport") -> "ParityReport":
+        self.prefixes += other.prefixes
+        self.invalid += other.invalid
+        for k in self.decisions:
+            self.decisions[k] += other.decisions[k]
+            self.flagged[k] += other.flagged[k]
+            self.near_ties[k] += other.near_ties[k]
+        self.literal_cdf_window += other.literal_cdf_window
+        self.max_alpha_err = max(self.max_alpha_err, other.max_alpha_err)
+        self.max_beta_err = max(self.max_beta_err, other.max_beta_err)
+        self.max_score_err = max(self.max_score_err, other.max_score_err)
+        self.failures += other.failures
+        return self
 
     def summary(self) -> str:
         return ("prefixes=%d invalid=%d decisions=%s mismatches_excused=%s near_ties=%s "

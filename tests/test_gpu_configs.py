@@ -1,21 +1,22 @@
 """GPU parity at the full workload sizes (V = 152064, bf16), in the launch
-configuration the benchmark times: the whole batch runs on the GPU; the oracle
-checks a sample of prefixes one by one; properties that hold at any size are
-checked on every prefix; two runs must agree bit for bit."""
+configuration the benchmark times: the whole batch runs on the GPU and the
+oracle recomputes every prefix (the long window's in two halves, to bound host
+memory); properties that hold at any size are checked on every prefix; a
+second run, which also asks for the overlap mass beta, must agree with the
+first bit for bit, and its beta is compared with the oracle's.  Mismatches
+excused as near-ties must stay under 0.01 % of each kind of decision."""
 import numpy as np
 import pytest
 import torch
 
 import workloads as W
 from gpu_util import check_ranges, gen, host_inputs, require_gpu, run_select, say
-from parity_harness import compare
+from parity_harness import ParityReport, compare
 
 pytestmark = pytest.mark.gpu
 
-# workload id -> prefixes the oracle recomputes: every prefix of the single
-# stream, self-selection and batched-serving batches (2048 positions or fewer),
-# the first half of the long window's (16384 of its 32768 positions)
-SAMPLES = {2: [0], 3: list(range(16)), 4: list(range(256)), 5: list(range(32))}
+# workload id -> the prefix ranges the oracle recomputes, one host copy each
+CHUNKS = {2: [range(1)], 3: [range(16)], 4: [range(256)], 5: [range(32), range(32, 64)]}
 
 
 @pytest.mark.parametrize("cid", [2, 3, 4, 5])
@@ -32,25 +33,31 @@ def test_full_size_workload(orc, cid):
     assert np.all(kept >= g["scores"].max(1))
     # alpha in [0, 1]
     assert np.all((g["alpha"] >= 0) & (g["alpha"] <= 1))
-    # run-to-run determinism
-    g2 = run_select(svd, d, cfg.temp, cfg.seed)
+    # run-to-run determinism; the second run also computes beta, which must
+    # leave every other output as it was
+    g2 = run_select(svd, d, cfg.temp, cfg.seed, want_beta=True)
     for k in ("selected", "accept_len", "next_token", "scores", "alpha"):
         assert np.array_equal(g[k], g2[k]), k
-    # oracle on sampled prefixes
-    idx = SAMPLES[cid]
-    hp, hq, hd = host_inputs(d, idx)
-    say("oracle on prefixes", idx)
-    rep = compare(orc, hp, hq, hd, g, cfg.temp, cfg.temp, cfg.seed, prefixes=idx)
+    assert np.all((g2["beta"] >= 0) & (g2["beta"] <= 1 + 1e-6))
+    # the oracle on every prefix, beta included
+    rep = ParityReport()
+    for chunk in CHUNKS[cid]:
+        idx = list(chunk)
+        hp, hq, hd = host_inputs(d, idx)
+        say("oracle on prefixes %d..%d" % (idx[0], idx[-1]))
+        compare(orc, hp, hq, hd, g2, cfg.temp, cfg.temp, cfg.seed, prefixes=idx, rep=rep)
+        del hp, hq, hd
     say(rep.summary())
+    assert rep.prefixes == cfg.B
     assert rep.ok(), rep.failures
-    del hp, hq, hd
+    assert rep.excused_within(), rep.summary()
     say("mean accepted length %.3f  MAT %.3f" % (g["accept_len"].mean(), g["accept_len"].mean() + 1))
     del d
     torch.cuda.empty_cache()
 
 
 def test_serving_workload_more_seeds(orc):
-    # batched serving: several uniform seeds over the same logits, 16 sampled prefixes each
+    # batched serving: more uniform seeds over the same logits, 16 sampled prefixes each
     svd = require_gpu()
     cfg = W.get_config(4)
     d = gen(cfg)
@@ -62,3 +69,31 @@ def test_serving_workload_more_seeds(orc):
         rep = compare(orc, hp, hq, hd, g, cfg.temp, cfg.temp, seed, row_base=1000, prefixes=idx)
         say(seed, rep.summary())
         assert rep.ok(), rep.failures
+        assert rep.excused_within(), rep.summary()
+
+
+@pytest.mark.parametrize("cid,data_seeds,seeds", [(4, 2, 8), (3, 2, 8)])
+def test_near_tie_rate_at_full_size(orc, cid, data_seeds, seeds):
+    # at V = 152064 the acceptance tests and draws of every prefix, over several
+    # logit draws and uniform seeds: batched serving gives over 10^4 acceptance
+    # decisions and 4096 draws, self-selection 256 selections; excused
+    # mismatches stay under 0.01 % of each kind
+    svd = require_gpu()
+    cfg = W.get_config(cid)
+    rep = ParityReport()
+    for ds in range(data_seeds):
+        d = gen(cfg, data_seed=cfg.data_seed + 100 + ds)
+        hp, hq, hd = host_inputs(d)
+        for s in range(seeds):
+            seed = 1000 + 37 * ds + s
+            g = run_select(svd, d, cfg.temp, seed, row_base=ds << 20)
+            compare(orc, hp, hq, hd, g, cfg.temp, cfg.temp, seed, row_base=ds << 20, rep=rep)
+            assert rep.ok(), rep.failures[:5]
+        say("data seed", ds, rep.summary())
+        del hp, hq, hd, d
+        torch.cuda.empty_cache()
+    if cid == 4:
+        assert rep.decisions["accept"] >= 10_000
+    else:
+        assert rep.decisions["select"] >= 256
+    assert rep.excused_within(), rep.summary()

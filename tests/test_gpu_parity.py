@@ -106,7 +106,7 @@ def test_many_prefixes_flag_rates(orc):
     rep = compare(orc, *host_inputs(d), g, 0.7, 0.7, 9)
     say(rep.summary())
     assert rep.ok(), rep.failures[:5]
-    assert rep.flag_rate() < 1e-3
+    assert rep.excused_within(), rep.summary()
 
 
 # 8 prefixes of 20000 tokens are drawn in segments of 1024 tokens, 400 in

@@ -65,6 +65,8 @@ def generate(cfg: Config, device="cpu", B: int | None = None, data_seed: int | N
     G = cfg.gamma if gamma is None else gamma
     dt = cfg.dtype if dtype is None else dtype
     ds = cfg.data_seed if data_seed is None else data_seed
+    if dt not in ("f32", "bf16"):
+        raise ValueError("dtype must be 'f32' or 'bf16', got %r" % (dt,))
     tdtype = torch.float32 if dt == "f32" else torch.bfloat16
     p = torch.empty((B, K, G + 1, V), dtype=tdtype, device=device)
     q = torch.empty((B, K, G, V), dtype=tdtype, device=device)
@@ -97,6 +99,8 @@ def generate_pooled(cfg: Config, device="cpu", B: int | None = None,
     dt = cfg.dtype if dtype is None else dtype
     ds = cfg.data_seed if data_seed is None else data_seed
     tau = cfg.tau if tau is None else tau
+    if dt not in ("f32", "bf16"):
+        raise ValueError("dtype must be 'f32' or 'bf16', got %r" % (dt,))
     tdtype = torch.float32 if dt == "f32" else torch.bfloat16
     p_rows, q_rows = [], []
     p_index = torch.empty((B, K, G + 1), dtype=torch.int32)
