@@ -355,3 +355,28 @@ def cps_beam(lat: dict, fluency=None, lam=1.0, beam=3) -> dict:
     if rc != 0:
         raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
     return {"paths": paths, "score": score, "path_len": plen, "rank_margin": rm}
+
+
+def adl_next(drafts, selected, accept_len, avg, gamma_b=None, eos=-1, k_min=1, k_max=64,
+             step=4, shift=2, slack=64):
+    """Adaptive draft length: the next window of every prefix and the updated
+    state.  drafts [B, K, gamma] int32; selected, accept_len, gamma_b [B]
+    int32; avg [B, 2] int32 (recent accepted and generated lengths in 1/256ths
+    of a token).  Returns (next [B] int32, avg' [B, 2] int32)."""
+    d = np.ascontiguousarray(drafts, dtype=np.int32)
+    B, K, G = d.shape
+    sel = np.ascontiguousarray(selected, dtype=np.int32)
+    L = np.ascontiguousarray(accept_len, dtype=np.int32)
+    gb = None if gamma_b is None else np.ascontiguousarray(gamma_b, dtype=np.int32)
+    st = np.array(avg, dtype=np.int32, copy=True).reshape(B, 2)
+    nxt = np.empty(B, np.int32)
+    lb = lib()
+    lb.svdo_adl_next.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    lb.svdo_adl_next.argtypes = [ctypes.c_void_p] * 4 + [i32, ctypes.c_int64, i32, i32, i32, i32,
+                                                         i32, i32, i32] + [ctypes.c_void_p] * 2
+    rc = lb.svdo_adl_next(_ptr(d), _ptr(sel), _ptr(L), _ptr(gb), int(eos), B, K, G, int(k_min),
+                          int(k_max), int(step), int(shift), int(slack), _ptr(st), _ptr(nxt))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+    return nxt, st

@@ -731,3 +731,71 @@ int svdo_cps_beam(const int32_t *cand, const double *cand_logp, const int32_t *n
   free(idx); free(nidx); free(sc); free(nsc); free(es); free(ep); free(ei); free(used);
   return status;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Adaptive draft length (DiffuSpec section 4.3): the controller uses the
+ * EOS-aware generated length and the accepted length; it grows the window
+ * while acceptance keeps up with generation on average and stops growing it
+ * once the generated length saturates at EOS.  Shrinking toward the recent
+ * accepted length when acceptance lags is this oracle's reading of "avoid
+ * over-drafting" (DiffuSpec section 6).  The averages are kept in 1/256ths of
+ * a token so every decision is an exact integer comparison. */
+
+/* x / 2^shift rounded toward minus infinity, for |x| < 2^31 */
+static int32_t adl_floor_div(int32_t x, int32_t shift) {
+  return (int32_t)floor((double)x / (double)((int64_t)1 << shift));
+}
+
+int svdo_adl_next(const int32_t *drafts, const int32_t *selected, const int32_t *accept_len,
+                  const int32_t *gamma_b, int32_t eos, int64_t B, int32_t K, int32_t gamma,
+                  int32_t k_min, int32_t k_max, int32_t step, int32_t shift, int32_t slack,
+                  int32_t *avg, int32_t *next) {
+  const int32_t lim = 1 << 20;
+  if (B < 0 || K < 1 || K > 64 || gamma < 1 || gamma > 4096 || k_min < 1 || k_max < k_min ||
+      k_max > 4096 || step < 0 || step > 4096 || shift < 0 || shift > 16 || slack < 0 ||
+      slack > lim)
+    return -1;
+  for (int64_t b = 0; b < B; ++b) {
+    const int32_t n = gamma_b ? gamma_b[b] : gamma;
+    if (n < 1 || n > gamma) {
+      next[b] = -1;
+      continue;
+    }
+    const int32_t k = selected[b], L = accept_len[b];
+    if (k < 0 || k >= K || L < 0 || L > n) {
+      next[b] = n;
+      continue;
+    }
+    int32_t A = avg[2 * b], G = avg[2 * b + 1];
+    if (A < 0 || A > lim || G < 0 || G > lim) {
+      next[b] = -1;
+      continue;
+    }
+    /* the kept draft's generated length: up to and including its first EOS */
+    int32_t g = n;
+    if (eos >= 0)
+      for (int32_t j = 0; j < n; ++j)
+        if (drafts[((size_t)b * K + k) * gamma + j] == eos) {
+          g = j + 1;
+          break;
+        }
+    /* recent lengths, 1/256ths of a token */
+    A = A + adl_floor_div(256 * L - A, shift);
+    G = G + adl_floor_div(256 * g - G, shift);
+    avg[2 * b] = A;
+    avg[2 * b + 1] = G;
+    int32_t w;
+    if (g < n) {
+      w = n;                                   /* generated length saturated: hold */
+    } else if (A + slack >= G) {
+      w = n + step;                            /* acceptance keeps pace: expand */
+    } else {
+      w = (int32_t)ceil((double)A / 256.0) + 1;  /* acceptance lags: shrink */
+      if (w > n) w = n;
+    }
+    if (w < k_min) w = k_min;
+    if (w > k_max) w = k_max;
+    next[b] = w;
+  }
+  return 0;
+}

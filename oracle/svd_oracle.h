@@ -163,6 +163,37 @@ int svdo_cps_beam(const int32_t *cand, const double *cand_logp, const int32_t *n
                   int32_t m_max, int32_t beam, int32_t *paths, double *path_score,
                   int32_t *path_len, double *rank_margin);
 
+/*
+ * Adaptive draft length (DiffuSpec section 4.3, "Adaptive Draft Length"): the
+ * next step's window of every sequence, from this step's accepted length and
+ * EOS-aware generated length, read as follows.  Per prefix b:
+ *   n  = gamma_b[b] (NULL: gamma), this step's window; outside [1, gamma]:
+ *        a data error (next[b] = -1, state unchanged);
+ *   k  = selected[b], L = accept_len[b]; either negative (a prefix whose
+ *        inputs were invalid): next[b] = n, state unchanged;
+ *   g  = the generated length of draft k: its first eos at j < n gives j + 1,
+ *        else n (eos < 0: n);
+ *   the state avg[b] = {A, G} holds the recent accepted and generated lengths
+ *   in 1/256ths of a token, each moved toward this step's value by 2^-shift
+ *   of the gap, rounded down:  A += floor((256 L - A) / 2^shift), the same
+ *   for G with g; a state outside [0, 2^20] is a data error (-1, unchanged);
+ *   then
+ *     g < n (the draft ended at EOS inside the window: the generated length
+ *            has saturated)                   next = n              (hold)
+ *     A + slack >= G (acceptance keeps pace with generation, on average)
+ *                                              next = n + step       (expand)
+ *     otherwise                                next = ceil(A / 256) + 1, at
+ *                                              most n                (shrink)
+ *   and next is clamped to [k_min, k_max].
+ * Returns 0, or -1 for parameters out of range (1 <= k_min <= k_max <= 4096,
+ * 0 <= step <= 4096, 0 <= shift <= 16, 0 <= slack <= 2^20, 1 <= gamma <= 4096,
+ * 1 <= K <= 64).
+ */
+int svdo_adl_next(const int32_t *drafts, const int32_t *selected, const int32_t *accept_len,
+                  const int32_t *gamma_b, int32_t eos, int64_t B, int32_t K, int32_t gamma,
+                  int32_t k_min, int32_t k_max, int32_t step, int32_t shift, int32_t slack,
+                  int32_t *avg, int32_t *next);
+
 #ifdef __cplusplus
 }
 #endif
