@@ -64,9 +64,13 @@ def kernel_samples(steps: int) -> int:
     return max(5, min(steps, 20))
 
 
-def time_kernels(torch, tl, fn, kernels, n):
+def time_kernels(torch, tl, fn, kernels, n, warm=3):
     """(ms per kernel, launches per kernel) over n calls of fn, with the timing
-    build recording HIP events around the launches of `kernels`."""
+    build recording HIP events around the launches of `kernels`.  The first
+    `warm` calls go untimed: a kernel's first launch from a library loads its
+    code object."""
+    for _ in range(warm):
+        fn()
     torch.cuda.synchronize()
     tl.svd_profile_read()  # clear
     tl.svd_profile_enable(kernels)

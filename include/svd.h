@@ -286,6 +286,41 @@ int svd_cps_beam(const int32_t *cand, const float *cand_logp, const int32_t *n_c
                  int32_t *path_len, void *hip_stream);
 
 /*
+ * Adaptive draft length (DiffuSpec section 4.3, "Adaptive Draft Length": the
+ * controller sets each sequence's next draft length k_t from the EOS-aware
+ * generated length and the accepted length; it expands the window while
+ * acceptance keeps pace with generation on average and stops expanding once
+ * the generated length saturates).  Run after svd_verify_window (or any
+ * select-and-verify call) on its inputs and outputs; `next` can be the next
+ * call's gamma_b directly, with no trip to the host.  Per prefix b:
+ *   n   = gamma_b[b] (gamma_b nullable: gamma) is this step's window, and
+ *   g   = the generated length of the kept draft k = selected[b]: through its
+ *         first drafted eos among positions < n (eos >= 0), else n;
+ *   avg [B][2] int32 in/out holds {A, G}, the recent accepted and generated
+ *         lengths in 1/256ths of a token (start them at 256 * the first window);
+ *         each moves toward this step's 256 * L (L = accept_len[b]) and 256 * g
+ *         by 2^-shift of the gap, rounded down;
+ *   next[b] = n              when g < n (the draft ended at EOS inside the
+ *                            window: the generated length has saturated),
+ *             n + step       else when A + slack >= G (acceptance keeps pace),
+ *             min(n, ceil(A / 256) + 1) otherwise (acceptance lags: the recent
+ *                            streak plus the position that is rejected),
+ *           clamped to [k_min, k_max].
+ *   A prefix whose selected or accept_len is -1 (or out of range) keeps its
+ *   window and state; a window outside [1, gamma] or a state outside
+ *   [0, 2^20] gives next[b] = -1 and leaves the state.
+ *   drafts [B][K][gamma] int32 as given to the verification call.
+ * Errors (SVD_EINVAL, nothing enqueued): a NULL pointer other than gamma_b;
+ * B, K or gamma out of the limits above; not 1 <= k_min <= k_max <= 4096;
+ * step outside [0, 4096]; shift outside [0, 16]; slack outside [0, 2^20].
+ * No workspace.
+ */
+int svd_adl_next(const int32_t *drafts, const int32_t *selected, const int32_t *accept_len,
+                 const int32_t *gamma_b, int32_t eos, int64_t B, int32_t K, int32_t gamma,
+                 int32_t k_min, int32_t k_max, int32_t step, int32_t shift, int32_t slack,
+                 int32_t *avg, int32_t *next, void *hip_stream);
+
+/*
  * For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
  * operation, arguments and outputs as svd_select_and_verify (bit for bit), but

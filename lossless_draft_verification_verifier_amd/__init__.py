@@ -9,10 +9,10 @@ arguments take an int address or a tensor):
     svd_workspace_bytes, svd_verify, svd_select_and_verify, svd_greedy_verify,
     svd_greedy_select_and_verify, svd_rows_workspace_bytes, svd_select_and_verify_rows,
     svd_verify_window, svd_cps_workspace_bytes, svd_cps_lattice, svd_cps_beam,
-    svd_select_and_verify_noalloc, svd_strerror
+    svd_adl_next, svd_select_and_verify_noalloc, svd_strerror
 Tensor conveniences that allocate the outputs and the workspace with torch:
     verify, select_and_verify, greedy_verify, greedy_select_and_verify,
-    select_and_verify_rows, verify_window, cps_lattice, cps_beam, workspace_bytes
+    select_and_verify_rows, verify_window, cps_lattice, cps_beam, adl_next, workspace_bytes
 Kernel timing: timing_library() loads ``libsvd_timed.so`` (the same kernels with
 HIP-event timing compiled in, ``include/svd_timing.h``) as a Library whose raw
 entry points are those above plus svd_profile_enable and svd_profile_read.
@@ -42,7 +42,8 @@ SVD_RULE_STANDARD, SVD_RULE_GREEDY = 0, 1
 C_EXPORTS = ("svd_workspace_bytes", "svd_verify", "svd_select_and_verify", "svd_greedy_verify",
              "svd_greedy_select_and_verify", "svd_rows_workspace_bytes",
              "svd_select_and_verify_rows", "svd_verify_window", "svd_cps_workspace_bytes",
-             "svd_cps_lattice", "svd_cps_beam", "svd_select_and_verify_noalloc", "svd_strerror")
+             "svd_cps_lattice", "svd_cps_beam", "svd_adl_next", "svd_select_and_verify_noalloc",
+             "svd_strerror")
 TIMING_EXPORTS = ("svd_profile_enable", "svd_profile_read")
 
 _M64 = 0xFFFFFFFFFFFFFFFF
@@ -87,6 +88,9 @@ def _declare(L: ctypes.CDLL, timing: bool) -> ctypes.CDLL:
                                   vp, vp, sz, vp]
     L.svd_cps_beam.restype = ctypes.c_int
     L.svd_cps_beam.argtypes = [vp, vp, vp, vp, vp, f32, i64, i32, i32, i32, vp, vp, vp, vp]
+    L.svd_adl_next.restype = ctypes.c_int
+    L.svd_adl_next.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32, i32, vp, vp,
+                               vp]
     L.svd_select_and_verify_noalloc.restype = ctypes.c_int
     L.svd_select_and_verify_noalloc.argtypes = [vp, vp, vp, ctypes.c_int, i64, i32, i32, i32, f32,
                                                 f32, u64, u64, vp, vp, vp, vp, vp, vp, vp]
@@ -204,6 +208,13 @@ class Library:
             float(lam), int(B), int(G), int(m_max), int(beam), _addr(paths), _addr(path_score),
             _addr(path_len), _addr(hip_stream)))
 
+    def svd_adl_next(self, drafts, selected, accept_len, gamma_b, eos, B, K, gamma, k_min, k_max,
+                     step, shift, slack, avg, next_gamma, hip_stream) -> int:
+        return int(self._lib.svd_adl_next(
+            _addr(drafts), _addr(selected), _addr(accept_len), _addr(gamma_b), int(eos), int(B),
+            int(K), int(gamma), int(k_min), int(k_max), int(step), int(shift), int(slack),
+            _addr(avg), _addr(next_gamma), _addr(hip_stream)))
+
     def svd_select_and_verify_noalloc(self, p_logits, q_logits, drafts, dtype, B, K, gamma, V,
                                       temp_p, temp_q, seed, row_base, selected, accept_len,
                                       next_token, scores, alpha, beta, hip_stream) -> int:
@@ -266,6 +277,7 @@ svd_cps_workspace_bytes = _default.svd_cps_workspace_bytes
 svd_cps_lattice = _default.svd_cps_lattice
 svd_cps_beam = _default.svd_cps_beam
 svd_select_and_verify_noalloc = _default.svd_select_and_verify_noalloc
+svd_adl_next = _default.svd_adl_next
 svd_strerror = _default.svd_strerror
 
 
@@ -568,3 +580,30 @@ def cps_beam(lat, fluency=None, lam=1.0, beam=3, stream=None, lib=None):
     if rc != SVD_OK:
         raise SvdError(rc, "svd_cps_beam")
     return out
+
+
+def adl_next(drafts, selected, accept_len, avg, gamma_b=None, eos=-1, k_min=1, k_max=64, step=4,
+             shift=2, slack=64, stream=None):
+    """Adaptive draft length: the next window of every prefix, on the device.
+    drafts [B,K,gamma] int32 and selected, accept_len [B] int32 (a verification
+    call's inputs and outputs), gamma_b [B] int32 or None, avg [B,2] int32
+    updated in place.  Returns next [B] int32."""
+    import torch
+    dev = drafts.device
+    tens = [(drafts, "drafts"), (selected, "selected"), (accept_len, "accept_len"),
+            (avg, "avg")] + ([] if gamma_b is None else [(gamma_b, "gamma_b")])
+    for t, n in tens:
+        _check(t, n, dev)
+        if t.dtype != torch.int32:
+            raise TypeError("%s must be int32" % n)
+    B, K, G = drafts.shape
+    if (tuple(selected.shape) != (B,) or tuple(accept_len.shape) != (B,) or
+            tuple(avg.shape) != (B, 2) or (gamma_b is not None and tuple(gamma_b.shape) != (B,))):
+        raise ValueError("selected, accept_len, gamma_b must be [B] and avg [B, 2]")
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    rc = svd_adl_next(drafts, selected, accept_len, gamma_b, eos, B, K, G, k_min, k_max, step,
+                      shift, slack, avg, nxt, st)
+    if rc != SVD_OK:
+        raise SvdError(rc, "svd_adl_next")
+    return nxt

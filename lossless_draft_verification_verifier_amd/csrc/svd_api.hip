@@ -11,6 +11,7 @@
 #include "svd.h"
 #include "svd_timing.h"
 #include "svd_timing.hpp"
+#include "kr_adl.hpp"
 #include "kr_beta.hpp"
 #include "kr_cps.hpp"
 #include "kr_draw.hpp"
@@ -757,6 +758,25 @@ int svd_cps_beam(const int32_t *cand, const float *cand_logp, const int32_t *n_c
   SVD_LAUNCH(tm, SVD_KERNEL_BEAM, s, kr_cps_beam, dim3((unsigned)B), dim3(64), s, cand, cand_logp,
              n_cand, len, fluency, lambda, (int)G, (int)m_max, (int)beam, paths, path_score,
              path_len);
+  return SVD_OK;
+}
+
+int svd_adl_next(const int32_t *drafts, const int32_t *selected, const int32_t *accept_len,
+                 const int32_t *gamma_b, int32_t eos, int64_t B, int32_t K, int32_t gamma,
+                 int32_t k_min, int32_t k_max, int32_t step, int32_t shift, int32_t slack,
+                 int32_t *avg, int32_t *next, void *hip_stream) {
+  if (!drafts || !selected || !accept_len || !avg || !next) return SVD_EINVAL;
+  if (B < 1 || B >= ((int64_t)1 << 31) || K < 1 || K > SVD_MAX_K || gamma < 1 ||
+      gamma > SVD_MAX_GAMMA || B >= ((int64_t)1 << 31) / ((int64_t)K * gamma))
+    return SVD_EINVAL;
+  if (k_min < 1 || k_max < k_min || k_max > SVD_MAX_GAMMA || step < 0 || step > SVD_MAX_GAMMA ||
+      shift < 0 || shift > 16 || slack < 0 || slack > kAdlStateMax)
+    return SVD_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  CallTimer tm;
+  SVD_LAUNCH(tm, SVD_KERNEL_ADL, s, kr_adl, dim3((unsigned)((B + kBlock - 1) / kBlock)),
+             dim3(kBlock), s, drafts, selected, accept_len, gamma_b, (int)eos, B, (int)K,
+             (int)gamma, (int)k_min, (int)k_max, (int)step, (int)shift, (int)slack, avg, next);
   return SVD_OK;
 }
 

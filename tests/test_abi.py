@@ -197,3 +197,19 @@ def test_noalloc_host_side_errors(svd):
     text = open(HEADER).read()
     assert "#define SVD_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
     assert svd.SVD_NOALLOC_SCRATCH_BYTES == 16 << 20
+
+
+def test_adl_host_side_errors(svd):
+    # fake addresses: every rejection happens before any HIP call
+    def call(**kw):
+        a = dict(d=4096, sel=8192, L=12288, gb=None, eos=-1, B=4, K=2, G=8, k_min=1, k_max=16,
+                 step=4, shift=2, slack=64, avg=16384, nxt=20480)
+        a.update(kw)
+        return svd.svd_adl_next(a["d"], a["sel"], a["L"], a["gb"], a["eos"], a["B"], a["K"],
+                                a["G"], a["k_min"], a["k_max"], a["step"], a["shift"], a["slack"],
+                                a["avg"], a["nxt"], None)
+    for kw in (dict(d=None), dict(sel=None), dict(L=None), dict(avg=None), dict(nxt=None),
+               dict(B=0), dict(K=0), dict(K=65), dict(G=0), dict(G=4097), dict(k_min=0),
+               dict(k_min=9, k_max=8), dict(k_max=4097), dict(step=-1), dict(step=4097),
+               dict(shift=-1), dict(shift=17), dict(slack=-1), dict(slack=(1 << 20) + 1)):
+        assert call(**kw) == svd.SVD_EINVAL, kw
