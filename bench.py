@@ -137,9 +137,11 @@ def record_traffic(kernel, workload, mode, fetch_dir, write_dir, copy_fetch_dir,
     fscale, wscale = cfetch / copy_kib, cwrite / copy_kib
     hbm = (fetch / fscale + write / wscale) * 1024.0
     import workloads as W
-    cfg = W.get_config(workload)
+    cfg = W.get_config(workload.replace("cps_", "", 1))
     es = 2 if cfg.dtype == "bf16" else 4
-    if cfg.layout == "pooled":
+    if kernel == "lattice":  # one drafter row per (prefix, position), read once
+        alg = cfg.B * cfg.gamma * (cfg.V * es + CPS_MMAX * 8 + 8)
+    elif cfg.layout == "pooled":
         rows = pool_rows_read(W.generate_pooled(cfg), mode)
         alg = rows * (cfg.V * es + POOL_STAT_BYTES)
     else:
@@ -347,7 +349,8 @@ def bench_cps(args, torch, svd, W):
                       if n_all[i]},
         "roofline": {"kernel": "kr_lattice", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "bytes_per_unit": unit, "units_per_launch": rows,
+                     "traffic": measured_traffic("lattice", "cps_" + cfg.name),
+                     "bytes_per_unit": unit, "units_per_launch": rows,
                      "ms_per_launch": ms_lat, "sampled_steps": nsamp},
         "mean_lattice_width": float(lat["n_cand"].float().mean().item()),
     }
@@ -403,6 +406,9 @@ def main():
     args = ap.parse_args()
     if args.record_traffic:
         import workloads as W
+        if args.cps:
+            record_traffic("lattice", "cps_shared_marginal", args.mode, *args.record_traffic)
+            return
         kern = "pool_stats" if W.get_config(args.workload).layout == "pooled" else "rowstats"
         record_traffic(kern, args.workload, args.mode, *args.record_traffic)
         return

@@ -145,9 +145,14 @@ __device__ __forceinline__ void visit_row(const typename E::elem *z, int n, F &&
 // The 16 best (logit, index) pairs of z[lo, hi) and the slice's (max, sum),
 // by NT threads.  Results: (m, s) and, in lanes 0..15 of wave 0, the r-th best
 // pair in (bv, bi); other threads return with undefined values.
-template <typename E, bool kVec, int NT>
+// R > 0 (16-byte rows whose slice has at most R vectors per thread): every
+// vector is loaded once, all in one round at the start, and kept in registers
+// for the later stages, so the slice is read from memory once; R = 0: the
+// stages stream the slice from memory.
+template <typename E, bool kVec, int NT, int R = 0>
 __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int lo, int hi, float c,
                                               float &m_out, float &s_out, float &bv, int &bi) {
+  static_assert(R == 0 || kVec, "registers hold whole 16-byte vectors");
   constexpr int NW = NT / 64;
   __shared__ float lds[2 * NW + 2];
   __shared__ float wv[NW * kCpsMax];
@@ -164,7 +169,37 @@ __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int l
   const int n = hi - lo;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
-  // 1. one streaming pass: (max, sum) and this thread's largest logit
+  // the slice's vectors held by this thread (R > 0): vector tid + r * NT in buf[r]
+  vec16 buf[R > 0 ? R : 1];
+  if constexpr (R > 0) {
+    const vec16 *vz = reinterpret_cast<const vec16 *>(z);
+    const int nv = n / E::kPerVec;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (tid + r * NT < nv) buf[r] = vz[tid + r * NT];
+  }
+  // every element of the slice, f(index in the slice, logit): from the
+  // registers, or streamed
+  auto visit = [&](auto &&f) {
+    if constexpr (R > 0) {
+      constexpr int P = E::kPerVec;
+      const int nv = n / P;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int i = tid + r * NT;
+        if (i < nv) {
+          float x[P];
+          E::unpack(buf[r], x);
+#pragma unroll
+          for (int e = 0; e < P; ++e) f(i * P + e, x[e]);
+        }
+      }
+    } else {
+      visit_row<E, kVec, NT>(z, n, f);
+    }
+  };
+
+  // 1. one pass: (max, sum) and this thread's largest logit
   float m = kNegInf, s = 0.0f, tmax = kNegInf;
   int tidx = kNoIndex;
   if constexpr (kVec) {
@@ -182,7 +217,12 @@ __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int l
           tidx = lo + i * P + e;
         }
     };
-    int i = tid;
+    if constexpr (R > 0) {  // the same order as the streaming loop below
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (tid + r * NT < nv) fold(buf[r], tid + r * NT);
+    }
+    int i = R > 0 ? nv : tid;
     for (; i + (U - 1) * NT < nv; i += U * NT) {
       vec16 w[U];
 #pragma unroll
@@ -250,7 +290,7 @@ __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int l
   __syncthreads();
   // 3. second pass: every token at or above the bound into an LDS list
   const float thr = thr_s;
-  visit_row<E, kVec, NT>(z, n, [&](int i, float x) {
+  visit([&](int i, float x) {
     if (x >= thr) {
       const int k = atomicAdd(&n_found, 1);
       if (k < kCandCap) {
@@ -270,6 +310,8 @@ __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int l
       tv[k] = kNegInf;
       ti[k] = kNoIndex;
     }
+    // (rare: streamed again even when the slice is in registers, which keeps
+    // every register access in a fully unrolled loop)
     visit_row<E, kVec, NT>(z, n, [&](int i, float x) { top_insert(tv, ti, x, lo + i); });
     float v16;
     int i16;
@@ -352,8 +394,19 @@ __device__ __forceinline__ void lattice_finish(int64_t row, float rm, float rs, 
   }
 }
 
-// one workgroup per drafter row
+// Vectors per thread a whole-row workgroup holds in registers: a bf16 row of
+// up to 19 * 1024 * 8 = 155648 tokens (a Qwen2.5-size vocabulary) is read
+// once; longer rows and fp32 rows stream twice.
+constexpr int kLatticeRegVecs = 19;
+
 template <typename E, bool kVec>
+constexpr int lattice_regs() {
+  return kVec && sizeof(typename E::elem) == 2 ? kLatticeRegVecs : 0;
+}
+
+// one workgroup per drafter row; R > 0: the row is held in registers (the
+// host launches this form only when it has at most R vectors per thread)
+template <typename E, bool kVec, int R>
 __global__ __launch_bounds__(kRowBlock) void kr_lattice(
     const typename E::elem *__restrict__ q, int V, float c, float tau, int m_max, int eos,
     int32_t *__restrict__ cand, float *__restrict__ cand_logp, int32_t *__restrict__ n_cand,
@@ -361,7 +414,7 @@ __global__ __launch_bounds__(kRowBlock) void kr_lattice(
   const int64_t row = blockIdx.x;  // b * G + j
   float m, s, bv;
   int bi;
-  lattice_slice<E, kVec, kRowBlock>(q + row * (int64_t)V, 0, V, c, m, s, bv, bi);
+  lattice_slice<E, kVec, kRowBlock, R>(q + row * (int64_t)V, 0, V, c, m, s, bv, bi);
   if (threadIdx.x >= 64) return;
   lattice_finish(row, m, s, bv, bi, c, tau, m_max, eos, cand, cand_logp, n_cand, flags);
 }

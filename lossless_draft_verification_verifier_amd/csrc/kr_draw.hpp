@@ -48,6 +48,8 @@
 // token order, so the result is deterministic.
 #pragma once
 
+#include <type_traits>
+
 #include "kr_select.hpp"
 
 namespace svd {
@@ -236,16 +238,70 @@ constexpr int pass_unit() {
   return kVec ? 4 : 1;
 }
 
+// The raw bits of one pass unit, so that the next unit's load can be in
+// flight while the current one is computed: 8 bytes of bf16, 16 of fp32, or
+// one element of a row without 16-byte alignment.
+template <typename E, bool kVec>
+struct PassRaw {
+  static_assert(!kVec, "element-wise rows");
+  using T = float;
+  __device__ static T load(const typename E::elem *row, int i) { return E::at(row, i); }
+  __device__ static void unpack(T t, float (&x)[1]) { x[0] = t; }
+};
+template <>
+struct PassRaw<BF16, true> {
+  using T = uint2;
+  __device__ static T load(const BF16::elem *row, int i) {
+    return reinterpret_cast<const uint2 *>(row)[i];
+  }
+  __device__ static void unpack(T a, float (&x)[4]) {
+    x[0] = __uint_as_float(a.x << 16); x[1] = __uint_as_float(a.x & 0xffff0000u);
+    x[2] = __uint_as_float(a.y << 16); x[3] = __uint_as_float(a.y & 0xffff0000u);
+  }
+};
+template <>
+struct PassRaw<F32, true> {
+  using T = vec16;
+  __device__ static T load(const F32::elem *row, int i) {
+    return reinterpret_cast<const vec16 *>(row)[i];
+  }
+  __device__ static void unpack(T a, float (&x)[4]) { F32::unpack(a, x); }
+};
+
 // Visit the logits of [lo, hi) of one or two rows with NT threads, P tokens
 // per unit: f(v, zp, zq).  kVec: rows start 16-byte aligned and hi - lo is a
 // multiple of a vector.
-template <typename E, bool kVec, bool kTwo, int NT, int P = (kVec ? E::kPerVec : 1), typename F>
+// The next unit's load is issued before the current unit is visited.
+template <typename E, bool kVec, bool kTwo, int NT, typename F>
 __device__ __forceinline__ void visit_segment(const typename E::elem *rp, const typename E::elem *rq,
                                      int lo, int hi, F &&f) {
-  for (int i = lo / P + (int)threadIdx.x; i < (hi + P - 1) / P; i += NT) {
+  constexpr int P = kVec ? E::kPerVec : 1;
+  // raw bits of one unit: a 16-byte vector, or one element
+  using T = typename std::conditional<kVec, vec16, float>::type;
+  auto load = [](const typename E::elem *row, int i) -> T {
+    if constexpr (kVec) return reinterpret_cast<const vec16 *>(row)[i];
+    else return E::at(row, i);
+  };
+  auto unpack = [](const T &t, float (&x)[P]) {
+    if constexpr (kVec) E::unpack(t, x);
+    else x[0] = t;
+  };
+  const int iend = (hi + P - 1) / P;
+  int i = lo / P + (int)threadIdx.x;
+  T np_{}, nq_{};
+  if (i < iend) {
+    np_ = load(rp, i);
+    if constexpr (kTwo) nq_ = load(rq, i);
+  }
+  for (; i < iend; i += NT) {
+    const T cp_ = np_, cq_ = nq_;
+    if (i + NT < iend) {
+      np_ = load(rp, i + NT);
+      if constexpr (kTwo) nq_ = load(rq, i + NT);
+    }
     float xp[P], xq[P];
-    load_unit<E, kVec, P>(rp, i, xp);
-    if constexpr (kTwo) load_unit<E, kVec, P>(rq, i, xq);
+    unpack(cp_, xp);
+    if constexpr (kTwo) unpack(cq_, xq);
 #pragma unroll
     for (int e = 0; e < P; ++e) f(i * P + e, xp[e], kTwo ? xq[e] : 0.0f);
   }
@@ -304,12 +360,26 @@ __device__ __forceinline__ void pass_residual(PassShared<NT> &S, const typename 
   dn = uniform_d(dn);
   double sp = 0.0, sq = 0.0, ap = 0.0, aq = 0.0, ep = 0.0, eq = 0.0;
   // one unit of tokens at a time; its margin tokens are settled after it,
-  // behind one branch
+  // behind one branch.  The next unit's logits are loaded before the current
+  // unit is computed, so a wave always has a load in flight.
   constexpr int P = pass_unit<E, kVec>();
-  for (int i = lo / P + (int)threadIdx.x; i < (hi + P - 1) / P; i += NT) {
+  using Raw = PassRaw<E, kVec>;
+  const int iend = (hi + P - 1) / P;
+  int i = lo / P + (int)threadIdx.x;
+  typename Raw::T np_ = {}, nq_ = {};
+  if (i < iend) {
+    np_ = Raw::load(rp, i);
+    nq_ = Raw::load(rq, i);
+  }
+  for (; i < iend; i += NT) {
+    const typename Raw::T cp_ = np_, cq_ = nq_;
+    if (i + NT < iend) {
+      np_ = Raw::load(rp, i + NT);
+      nq_ = Raw::load(rq, i + NT);
+    }
     float xp[P], xq[P];
-    load_unit<E, kVec, P>(rp, i, xp);
-    load_unit<E, kVec, P>(rq, i, xq);
+    Raw::unpack(cp_, xp);
+    Raw::unpack(cq_, xq);
     uint32_t margin = 0;
 #pragma unroll
     for (int e = 0; e < P; ++e) {

@@ -723,20 +723,26 @@ int svd_cps_lattice(const void *q_logits, svd_dtype_t dtype, int64_t B, int32_t 
                m_max, e, S, (const LatticePart *)part, cand, cand_logp, n_cand, flags);
   } else if (dtype == SVD_BF16) {
     const auto *q = static_cast<const BF16::elem *>(q_logits);
-    if (vec)
-      SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<BF16, true>, grid, dim3(kRowBlock), s, q, V,
-                 c, tau, m_max, e, cand, cand_logp, n_cand, flags);
-    else
-      SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<BF16, false>, grid, dim3(kRowBlock), s, q,
+    // a row of at most kLatticeRegVecs vectors per thread is held in registers
+    constexpr int RB = lattice_regs<BF16, true>();
+    const bool in_regs = ((int64_t)V / BF16::kPerVec + kRowBlock - 1) / kRowBlock <= RB;
+    if (vec && in_regs)
+      SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<BF16, true, RB>, grid, dim3(kRowBlock), s,
+                 q, V, c, tau, m_max, e, cand, cand_logp, n_cand, flags);
+    else if (vec)
+      SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<BF16, true, 0>, grid, dim3(kRowBlock), s, q,
                  V, c, tau, m_max, e, cand, cand_logp, n_cand, flags);
+    else
+      SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<BF16, false, 0>, grid, dim3(kRowBlock), s,
+                 q, V, c, tau, m_max, e, cand, cand_logp, n_cand, flags);
   } else {
     const auto *q = static_cast<const F32::elem *>(q_logits);
     if (vec)
-      SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<F32, true>, grid, dim3(kRowBlock), s, q, V,
-                 c, tau, m_max, e, cand, cand_logp, n_cand, flags);
+      SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<F32, true, 0>, grid, dim3(kRowBlock), s, q,
+                 V, c, tau, m_max, e, cand, cand_logp, n_cand, flags);
     else
-      SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<F32, false>, grid, dim3(kRowBlock), s, q, V,
-                 c, tau, m_max, e, cand, cand_logp, n_cand, flags);
+      SVD_LAUNCH(tm, SVD_KERNEL_LATTICE, s, kr_lattice<F32, false, 0>, grid, dim3(kRowBlock), s, q,
+                 V, c, tau, m_max, e, cand, cand_logp, n_cand, flags);
   }
   SVD_LAUNCH(tm, SVD_KERNEL_LATTICE_LEN, s, kr_lattice_len,
              dim3((unsigned)((B * 64 + kBlock - 1) / kBlock)),
