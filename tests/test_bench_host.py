@@ -49,8 +49,17 @@ def test_counter_record_needs_matching_sources(tmp_path, monkeypatch):
 def test_committed_records_match_their_kernels():
     # the committed counter records were taken on the committed kernel sources
     for kern, mode in (("rowstats", "standard"), ("rowstats", "greedy"),
-                       ("pool_stats", "standard"), ("pool_stats", "greedy")):
+                       ("pool_stats", "standard"), ("pool_stats", "greedy"),
+                       ("lattice", "standard")):
         with open(bench.traffic_file(kern, mode)) as f:
             rec = json.load(f)
         assert rec["kernel_hash"] == bench.kernel_hash(kern), (kern, mode)
         assert 1.0 <= rec["traffic_over_algorithmic"] < 1.01, (kern, mode)
+
+
+def test_lattice_algorithmic_bytes():
+    # one read of each of the 256 drafter rows, plus the 15 candidates (token and
+    # log-probability) and the count written per row
+    rec = json.load(open(bench.traffic_file("lattice")))
+    assert rec["algorithmic_bytes_per_launch"] == 256 * (152064 * 2 + 15 * 8 + 8)
+    assert rec["workload"] == "cps_shared_marginal"

@@ -158,3 +158,43 @@ def test_committed_tokens_follow_the_verifier_at_four_drafts():
         pv.append(_chisq_p(np.bincount(y, minlength=V), softmax(zp[j].astype(np.float64))))
     say("p-values", pv)
     assert min(pv) > 1e-3 / (G + 1), pv
+
+
+@pytest.mark.parametrize("cid", [4, 3])
+def test_full_size_greedy_with_accepted_runs(orc, cid):
+    # V = 152064 with confident verifier rows: accepted runs, residual draws past
+    # position 0 and bonus draws, on every prefix of the batch
+    svd = require_gpu()
+    cfg = W.get_config(cid)
+    d = _confident(cfg, 77 + cid, mode_frac=0.85 if cfg.K == 1 else 0.95)
+    g = run_greedy(svd, d, cfg.temp, cfg.seed)
+    check_ranges(g, cfg.K, cfg.gamma, cfg.V)
+    L = g["accept_len"]
+    say("greedy confident", cfg.name, "mean L %.2f" % L.mean(), "bonus", int((L == cfg.gamma).sum()),
+        "L histogram", np.bincount(L, minlength=cfg.gamma + 1).tolist())
+    assert L.mean() > 1.0 and ((L > 0) & (L < cfg.gamma)).sum() > 0
+    if cfg.K == 1:
+        assert (L == cfg.gamma).sum() > 0  # bonus draws
+    else:
+        assert L.max() >= 5  # long accepted runs of the kept draft
+    hp, hd = host_pd(d)
+    rep = compare(orc, hp, None, hd, g, cfg.temp, cfg.temp, cfg.seed, greedy=True)
+    say(rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    assert rep.excused_within(), rep.summary()
+
+
+def _confident(cfg, seed, mode_frac):
+    # the workload's rows with each verifier row's mode logit raised by a
+    # further 2, 3, 4, 5 or 6 (so p(mode) spans about 0.2 to 0.99997 at T = 0.7),
+    # and a fraction mode_frac of drafted tokens set to their row's mode
+    d = gen(cfg)
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    p = d["p"]
+    mode = p.argmax(-1, keepdim=True)
+    extra = torch.randint(2, 7, mode.shape, generator=g, device="cuda").float()
+    p.scatter_(-1, mode, (p.gather(-1, mode).float() + extra).to(p.dtype))
+    G = cfg.gamma
+    take = torch.rand(d["drafts"].shape, generator=g, device="cuda") < mode_frac
+    d["drafts"] = torch.where(take, mode[:, :, :G, 0].to(torch.int32), d["drafts"]).contiguous()
+    return d
