@@ -366,7 +366,10 @@ def bench_cps(args, torch, svd, W):
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": rows * reps / dt, "unit": "rows/s", "cores": 1,
                                   "kind": "oracle",
-                                  "sample": "the %d drafter rows %d times, %.1f s" % (rows, reps, dt)}
+                                  "sample": "the %d drafter rows %d times, %.1f s on one thread "
+                                            "(the lattice and beam oracles are single-threaded)"
+                                            % (rows, reps, dt),
+                                  "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
     print(json.dumps(result), flush=True)
 
 

@@ -217,10 +217,39 @@ __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int l
           tidx = lo + i * P + e;
         }
     };
-    if constexpr (R > 0) {  // the same order as the streaming loop below
+    if constexpr (R > 0) {
+      // the same folds in the same order as the streaming loop below; the
+      // thread's best is tracked per vector (its first vector holding the
+      // largest logit; NaN never wins) and located inside that vector after
+      // the loop, which keeps the (logit descending, index ascending) order
+      int tvec = -1;
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (tid + r * NT < nv) fold(buf[r], tid + r * NT);
+      for (int r = 0; r < R; ++r) {
+        if (tid + r * NT < nv) {
+          float x[P];
+          E::unpack(buf[r], x);
+          ms_fold<P>(m, s, x, c);
+          float vm = x[0];
+#pragma unroll
+          for (int e = 1; e < P; ++e) vm = fmaxf(vm, x[e]);
+          if (vm == vm && (tvec < 0 || vm > tmax)) {
+            tmax = vm;
+            tvec = r;
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (r == tvec) {
+          float x[P];
+          E::unpack(buf[r], x);
+          int e0 = P - 1;
+#pragma unroll
+          for (int e = P - 1; e >= 0; --e)
+            if (x[e] == tmax) e0 = e;
+          tidx = lo + (tid + r * NT) * P + e0;
+        }
+      }
     }
     int i = R > 0 ? nv : tid;
     for (; i + (U - 1) * NT < nv; i += U * NT) {

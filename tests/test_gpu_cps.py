@@ -170,3 +170,46 @@ def test_split_rows_with_ties_inside_one_slice():
     o = oracle.cps_lattice(hz, tau=0.99, m_max=16)
     _check_lattice(g, o, 16)
     assert list(g["cand"][0, 0, :2]) == [5000, 5001]
+
+
+# Whole rows held in registers: launches of at least 128 rows of bf16 with at
+# most 19 16-byte vectors per thread of a 1024-thread workgroup (V <= 155648);
+# V = 155656 is the first size that streams instead.
+@pytest.mark.parametrize("V", [152064, 155648, 155656, 8192, 1000])
+def test_register_rows_match_oracle(V):
+    svd = require_gpu()
+    B, G = 16, 8  # 128 rows: whole-row workgroups
+    say("register rows", V)
+    q, hz = _rows(17 + V % 97, B, G, V, "bf16", scale=2.0)
+    g = host(svd.cps_lattice(q, temp_q=0.7, tau=0.8, m_max=15))
+    o = oracle.cps_lattice(hz, temp_q=0.7, tau=0.8, m_max=15)
+    assert _check_lattice(g, o, 15) <= 2
+
+
+def test_register_rows_with_ties_infinities_and_nan():
+    # in whole-row workgroups held in registers: equal top logits across
+    # threads and inside one vector, more ties at the bound than the candidate
+    # list holds, rows whose first threads see only -inf, a row of -inf but
+    # for a few tokens, and NaN rows (invalid), against the oracle
+    svd = require_gpu()
+    B, G, V = 16, 8, 152064
+    q, hz = _rows(29, B, G, V, "bf16", scale=2.0)
+    hz = hz.copy()
+    ninf, nan = np.uint16(0xFF80), np.uint16(0x7FC0)
+    top = np.uint16(0x4180)  # 16.0
+    hz[0, 0, [5, 6, 7, 8000, 151000]] = top              # ties inside one vector and across threads
+    hz[0, 1, 1000:1700] = np.uint16(0x4140)              # 700 tokens at 12.0: the list overflows
+    hz[1, 0, : V // 2] = ninf                            # the first half of the row is -inf
+    # threads 0..511 of the workgroup hold vectors t + 1024 r: all -inf here
+    hz[1, 2, ((np.arange(V) // 8) % 1024) < 512] = ninf
+    hz[1, 1, :] = ninf                                   # all -inf but four tokens
+    hz[1, 1, [3, 70000, 150000, 152063]] = np.uint16(0x3F80)
+    hz[2, 3, 123456] = nan                               # NaN: the row is invalid
+    hz[3, :, 0:8] = top                                  # a whole vector tied at the top
+    q = torch.from_numpy(hz.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    g = host(svd.cps_lattice(q, temp_q=1.0, tau=0.9, m_max=16))
+    o = oracle.cps_lattice(hz, temp_q=1.0, tau=0.9, m_max=16)
+    assert g["len"][2] == o["len"][2] == -1
+    _check_lattice(g, o, 16)
+    assert list(g["cand"][0, 0, :5]) == [5, 6, 7, 8000, 151000]
+    assert list(g["cand"][1, 1, :4]) == [3, 70000, 150000, 152063]
