@@ -90,3 +90,40 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
                                            1.0, 1.0, 0, 0, 16384, 20480, 24576, None, None, None,
                                            None)
     assert rc == svd.SVD_ESCRATCH
+
+
+def test_noalloc_graph_replays():
+    # a call captured in a HIP graph (through torch's graph API) after an eager
+    # call on the device, replayed three times with eager calls of other sizes
+    # and seeds in between (they leave their own contents in the shared
+    # scratch): every replay gives the eager call's outputs bit for bit
+    svd = require_gpu()
+    cfg = W.Config(99, "custom", B=64, K=2, gamma=6, V=30000, dtype="bf16", sigma0=1.0,
+                   sigma_step=0.0, temp=0.8, boost=8.0, boost_prob=1.0)
+    d, other = gen(cfg, data_seed=31), gen(SMALL, data_seed=32)
+    dev = d["p"].device
+    o = _outputs(cfg, dev)
+    code = svd.SVD_BF16
+
+    def call():
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = svd.svd_select_and_verify_noalloc(
+            d["p"], d["q"], d["drafts"], code, cfg.B, cfg.K, cfg.gamma, cfg.V, cfg.temp,
+            cfg.temp, 41, 0, o["selected"], o["accept_len"], o["next_token"], o["scores"],
+            o["alpha"], None, stream)
+        assert rc == svd.SVD_OK
+        return o
+
+    torch.cuda.synchronize()
+    ref = host(call())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for r in range(3):
+        _call(svd, SMALL, other, 50 + r, True)  # eager, different sizes, same scratch
+        g.replay()
+        torch.cuda.synchronize()
+        got = host(o)
+        for k in ("selected", "accept_len", "next_token", "scores", "alpha"):
+            assert np.array_equal(got[k], ref[k], equal_nan=True), (r, k)
+        say("noalloc replay", r, "matches the eager call")
