@@ -9,14 +9,17 @@
 // scores between consecutive candidates.
 //
 // kr_lattice (one workgroup per drafter row): candidates are ordered by
-//   (logit descending, index ascending), the order of decreasing probability.
-//   One streaming pass keeps the online (max, sum) and each thread's largest
-//   logit; the 16th largest of those maxima bounds the row's 16th largest from
-//   below; a second pass puts every token at or above the bound (a few dozen)
-//   into an LDS list, which wave 0 sorts and pops.  If more than kCandCap
-//   tokens tie at the bound, per-thread sorted lists over the whole row are
-//   merged instead.  The first lanes then turn the 16 best into probabilities
-//   and cut at tau.
+//   (logit descending, index ascending), the order of decreasing probability,
+//   compared as one unsigned 64-bit key.  One pass keeps the online
+//   (max, sum) and each thread's largest logit; the 16th largest of those
+//   maxima bounds the row's 16th largest from below; every token at or above
+//   the bound (a few dozen) goes into an LDS list, and each listed token's
+//   rank is the count of listed keys above its own.  A bf16 row of at most
+//   kLatticeRegVecs vectors per thread is held in registers and read once,
+//   its bound taken from the first vectors while the rest arrive; other rows
+//   are streamed twice.  If more than kCandCap tokens tie at the bound,
+//   per-thread sorted lists over the whole row are merged instead.  The first
+//   lanes then turn the 16 best into probabilities and cut at tau.
 // kr_lattice_len (one thread per prefix): the lattice length (first position
 //   whose best token is EOS, included) and the cleared tail.
 // kr_cps_beam (one wave per prefix): expansions (path rank, candidate rank) in
@@ -38,6 +41,24 @@ constexpr int kBeamChunk = 16;   // positions of lattice data a beam loads at on
 // (va, ia) comes before (vb, ib)
 __device__ __forceinline__ bool ahead(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
+}
+
+// The same order as one unsigned 64-bit key: a larger key is ahead.  The high
+// word maps the logit's bits to an order-preserving unsigned value (-0 counts
+// as +0, as the float comparison has it), the low word is the inverted index.
+// Key 0 stands for "no token": every real key is larger (the high word of -inf
+// is 0x007fffff).  NaN is never keyed.
+__device__ __forceinline__ uint64_t rank_key(float v, int i) {
+  uint32_t b = __float_as_uint(v + 0.0f);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)~(uint32_t)i;
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t b = (uint32_t)(k >> 32);
+  return k ? __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b) : kNegInf;
+}
+__device__ __forceinline__ int key_index(uint64_t k) {
+  return k ? (int)~(uint32_t)k : kNoIndex;
 }
 
 // insert into a sorted list of kCpsMax entries (the last one drops out)
@@ -104,6 +125,8 @@ __device__ __forceinline__ void wave_pop16(float (&lv)[N], int (&li)[N], float &
 enum : uint32_t { kRowInvalid = 1u, kRowEosTop = 2u };
 
 constexpr int kCandCap = 512;  // LDS list of tokens at or above the threshold
+// vectors per thread of a row held in registers from which its bound is taken
+constexpr int kLatticeBoundVecs = 10;
 constexpr int kLatticeMaxSlices = 64;  // slices of one row (one per lane of the merge)
 
 // visit the logits of a row with kRowBlock threads: f(index, value)
@@ -142,67 +165,157 @@ __device__ __forceinline__ void visit_row(const typename E::elem *z, int n, F &&
   }
 }
 
+// LDS of one workgroup finding a row's (or slice's) 16 best tokens; H > 0:
+// the largest logit of each of the first H vectors that every thread holds.
+template <int NT, int H>
+struct LatticeLds {
+  static constexpr int NW = NT / 64;
+  static constexpr int NE = NW * kCpsMax;  // the waves' 16 best keys
+  static constexpr int Q = NE / 4;         // one quarter of them
+  float ms[2 * NW + 2];                    // block_ms partials, then the (max, sum)
+  uint64_t ak[NT];                         // every thread's best key
+  // wave w's 16 best keys by rank at entry w * 16 + rank, quarter q of the
+  // entries padded by two keys, so that the four readers of one rank step
+  // (one per quarter) use different LDS banks
+  uint64_t wk[NE + 8];
+  uint64_t ck[kCandCap];  // the keys of the tokens at or above the bound
+  uint64_t sk[kCpsMax];   // the 16 best of those, by rank
+  float vmx[H > 0 ? H * NT : 1];
+  int n_found;
+  float thr;
+  __device__ static int slot(int e) { return e + 2 * (e / Q); }
+};
+
+// Clears the rank slots and the candidate count; the first barrier of
+// lattice_bound orders this before any use.
+template <class L>
+__device__ __forceinline__ void lattice_lds_init(L &sh) {
+  const int tid = threadIdx.x;
+  for (int k = tid; k < L::NE + 8; k += L::NW * 64) sh.wk[k] = 0;
+  if (tid < kCpsMax) sh.sk[tid] = 0;
+  if (tid == 0) {
+    sh.thr = kNegInf;  // fewer than 16 keyed tokens: all of them
+    sh.n_found = 0;
+  }
+}
+
+// The 16th largest of the threads' keys (key 0: no token) bounds the 16th
+// largest logit of the tokens they were taken from, and so of any set holding
+// those tokens, from below: 16 distinct tokens reach it.  Each wave ranks its
+// 64 keys against each other and keeps its 16 best in rank slots; then four
+// threads rank each of those NE against a quarter of them each.  Keys are
+// unique (they hold the token index).  Returns the bound's logit in every
+// thread (-inf with fewer than 16 keyed tokens).
+template <class L>
+__device__ __forceinline__ float lattice_bound(L &sh, uint64_t key) {
+  const int tid = threadIdx.x, w = tid >> 6;
+  sh.ak[tid] = key;
+  __syncthreads();
+  if (key) {
+    int r = 0;
+#pragma unroll 16
+    for (int k = w * 64; k < w * 64 + 64; ++k) r += sh.ak[k] > key;
+    if (r < kCpsMax) sh.wk[L::slot(w * kCpsMax + r)] = key;
+  }
+  __syncthreads();
+  {
+    const int e = tid >> 2, q = tid & 3;  // NE == NT / 4 entries, four threads each
+    const uint64_t ke = sh.wk[L::slot(e)];
+    const uint64_t *qk = sh.wk + q * (L::Q + 2);
+    int r = 0;
+#pragma unroll 16
+    for (int k = 0; k < L::Q; ++k) r += qk[k] > ke;
+    r += __shfl_xor(r, 1, 64);
+    r += __shfl_xor(r, 2, 64);
+    if (q == 0 && ke && r == kCpsMax - 1) sh.thr = key_value(ke);
+  }
+  __syncthreads();
+  return sh.thr;
+}
+
+// Appends the token (index i, logit x) to the candidate list when it reaches
+// the bound (past kCandCap only counted).
+template <class L>
+__device__ __forceinline__ void lattice_take(L &sh, float thr, int i, float x) {
+  if (x >= thr) {
+    const int k = atomicAdd(&sh.n_found, 1);
+    if (k < kCandCap) sh.ck[k] = rank_key(x, i);
+  }
+}
+
+// The 16 best of the nf listed candidates, in lanes 0..15 of wave 0 (bv, bi);
+// other waves return with undefined values.  When more than kCandCap tokens
+// reached the bound (many ties at it), per-thread sorted lists over the
+// whole set are merged instead: restream(f) calls f(index, logit) on every
+// token of this thread's share.
+template <class L, class Restream>
+__device__ __forceinline__ void lattice_top16(L &sh, int nf, Restream &&restream, float &bv,
+                                              int &bi) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (nf > kCandCap) {
+    float tv[kCpsMax];
+    int ti[kCpsMax];
+#pragma unroll
+    for (int k = 0; k < kCpsMax; ++k) {
+      tv[k] = kNegInf;
+      ti[k] = kNoIndex;
+    }
+    restream([&](int i, float x) { top_insert(tv, ti, x, i); });
+    float v16;
+    int i16;
+    wave_pop16<kCpsMax>(tv, ti, v16, i16);
+    if (lane < kCpsMax)
+      sh.wk[L::slot(w * kCpsMax + lane)] = i16 != kNoIndex ? rank_key(v16, i16) : 0;
+  } else {
+    // every listed token counts the ones ahead of it; the 16 best take their
+    // rank slots
+    for (int t = tid; t < nf; t += L::NW * 64) {
+      const uint64_t kt = sh.ck[t];
+      int r = 0;
+#pragma unroll 8
+      for (int k = 0; k < nf; ++k) r += sh.ck[k] > kt;
+      if (r < kCpsMax) sh.sk[r] = kt;
+    }
+  }
+  __syncthreads();
+  if (w != 0) return;
+  if (nf > kCandCap) {
+    constexpr int PER = (L::NE + 63) / 64;
+    float lv[PER];
+    int li[PER];
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      const int k = PER * lane + t;
+      const uint64_t kk = k < L::NE ? sh.wk[L::slot(k)] : 0;
+      lv[t] = key_value(kk);
+      li[t] = key_index(kk);
+    }
+    wave_pop16<PER>(lv, li, bv, bi);
+  } else {
+    const uint64_t kk = lane < kCpsMax ? sh.sk[lane] : 0;
+    bv = key_value(kk);
+    bi = key_index(kk);
+  }
+}
+
 // The 16 best (logit, index) pairs of z[lo, hi) and the slice's (max, sum),
-// by NT threads.  Results: (m, s) and, in lanes 0..15 of wave 0, the r-th best
-// pair in (bv, bi); other threads return with undefined values.
-// R > 0 (16-byte rows whose slice has at most R vectors per thread): every
-// vector is loaded once, all in one round at the start, and kept in registers
-// for the later stages, so the slice is read from memory once; R = 0: the
-// stages stream the slice from memory.
-template <typename E, bool kVec, int NT, int R = 0>
+// by NT threads streaming the slice from memory: one pass for the (max, sum)
+// and each thread's largest logit, the bound from those, a second pass that
+// lists the tokens at or above it.  Results: (m, s) and, in lanes 0..15 of
+// wave 0, the r-th best pair in (bv, bi); other threads return with
+// undefined values.
+template <typename E, bool kVec, int NT>
 __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int lo, int hi, float c,
                                               float &m_out, float &s_out, float &bv, int &bi) {
-  static_assert(R == 0 || kVec, "registers hold whole 16-byte vectors");
-  constexpr int NW = NT / 64;
-  __shared__ float lds[2 * NW + 2];
-  __shared__ float wv[NW * kCpsMax];
-  __shared__ int wi[NW * kCpsMax];
-  __shared__ float cv[kCandCap];
-  __shared__ int cix[kCandCap];
-  __shared__ float av[NT];  // every thread's largest logit
-  __shared__ int ai[NT];
-  __shared__ float sv[kCpsMax];  // the 16 best of the candidate list, by rank
-  __shared__ int si[kCpsMax];
-  __shared__ int n_found;
-  __shared__ float thr_s;
+  using L = LatticeLds<NT, 0>;
+  __shared__ L sh;
   const typename E::elem *z = row + lo;  // 16-byte aligned when kVec
   const int n = hi - lo;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-
-  // the slice's vectors held by this thread (R > 0): vector tid + r * NT in buf[r]
-  vec16 buf[R > 0 ? R : 1];
-  if constexpr (R > 0) {
-    const vec16 *vz = reinterpret_cast<const vec16 *>(z);
-    const int nv = n / E::kPerVec;
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (tid + r * NT < nv) buf[r] = vz[tid + r * NT];
-  }
-  // every element of the slice, f(index in the slice, logit): from the
-  // registers, or streamed
-  auto visit = [&](auto &&f) {
-    if constexpr (R > 0) {
-      constexpr int P = E::kPerVec;
-      const int nv = n / P;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int i = tid + r * NT;
-        if (i < nv) {
-          float x[P];
-          E::unpack(buf[r], x);
-#pragma unroll
-          for (int e = 0; e < P; ++e) f(i * P + e, x[e]);
-        }
-      }
-    } else {
-      visit_row<E, kVec, NT>(z, n, f);
-    }
-  };
-
-  // 1. one pass: (max, sum) and this thread's largest logit
+  const int tid = threadIdx.x;
+  lattice_lds_init(sh);
   float m = kNegInf, s = 0.0f, tmax = kNegInf;
   int tidx = kNoIndex;
-  if constexpr (kVec) {
+  if constexpr (kVec) {  // whole vectors (the slice is one), kLatticeUnroll loads in flight
     constexpr int P = E::kPerVec, U = kLatticeUnroll;
     const vec16 *vz = reinterpret_cast<const vec16 *>(z);
     const int nv = n / P;
@@ -217,41 +330,7 @@ __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int l
           tidx = lo + i * P + e;
         }
     };
-    if constexpr (R > 0) {
-      // the same folds in the same order as the streaming loop below; the
-      // thread's best is tracked per vector (its first vector holding the
-      // largest logit; NaN never wins) and located inside that vector after
-      // the loop, which keeps the (logit descending, index ascending) order
-      int tvec = -1;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (tid + r * NT < nv) {
-          float x[P];
-          E::unpack(buf[r], x);
-          ms_fold<P>(m, s, x, c);
-          float vm = x[0];
-#pragma unroll
-          for (int e = 1; e < P; ++e) vm = fmaxf(vm, x[e]);
-          if (vm == vm && (tvec < 0 || vm > tmax)) {
-            tmax = vm;
-            tvec = r;
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (r == tvec) {
-          float x[P];
-          E::unpack(buf[r], x);
-          int e0 = P - 1;
-#pragma unroll
-          for (int e = P - 1; e >= 0; --e)
-            if (x[e] == tmax) e0 = e;
-          tidx = lo + (tid + r * NT) * P + e0;
-        }
-      }
-    }
-    int i = R > 0 ? nv : tid;
+    int i = tid;
     for (; i + (U - 1) * NT < nv; i += U * NT) {
       vec16 w[U];
 #pragma unroll
@@ -270,119 +349,125 @@ __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int l
       }
     }
   }
-  block_ms<NW>(m, s, c, lds);  // valid in thread 0
+  block_ms<L::NW>(m, s, c, sh.ms);  // valid in thread 0
   if (tid == 0) {
-    lds[2 * NW] = m;
-    lds[2 * NW + 1] = s;
-    n_found = 0;
+    sh.ms[2 * L::NW] = m;
+    sh.ms[2 * L::NW + 1] = s;
   }
-  // 2. the 16th largest of the threads' maxima (in (logit, index) order)
-  //    bounds the slice's 16th largest logit from below: every one of its 16
-  //    best is at least that.  Each wave ranks its 64 maxima against each
-  //    other and keeps its 16 best in rank slots; then four threads rank each
-  //    of those NW * 16 against a quarter of them each.  Every key is unique
-  //    (a token index), and threads without a token take no slot.
-  av[tid] = tmax;
-  ai[tid] = tidx;
-  for (int k = tid; k < NW * kCpsMax; k += NT) {
-    wv[k] = kNegInf;
-    wi[k] = kNoIndex;
-  }
-  if (tid < kCpsMax) {
-    sv[tid] = kNegInf;
-    si[tid] = kNoIndex;
-  }
-  if (tid == 0) thr_s = kNegInf;  // fewer than 16 tokens: all of them
+  const float thr = lattice_bound(sh, tidx != kNoIndex ? rank_key(tmax, tidx) : 0);
+  visit_row<E, kVec, NT>(z, n, [&](int i, float x) { lattice_take(sh, thr, lo + i, x); });
   __syncthreads();
-  if (tidx != kNoIndex) {
-    int r = 0;
-#pragma unroll 8
-    for (int k = w * 64; k < w * 64 + 64; ++k) r += ahead(av[k], ai[k], tmax, tidx);
-    if (r < kCpsMax) {
-      wv[w * kCpsMax + r] = tmax;
-      wi[w * kCpsMax + r] = tidx;
-    }
-  }
-  __syncthreads();
-  {
-    constexpr int NE = NW * kCpsMax;  // NT / 4: four threads per entry
-    const int e = tid >> 2, k0 = (tid & 3) * (NE / 4);
-    const float ve = wv[e];
-    const int ie = wi[e];
-    int r = 0;
-#pragma unroll 8
-    for (int k = k0; k < k0 + NE / 4; ++k) r += ahead(wv[k], wi[k], ve, ie);
-    r += __shfl_xor(r, 1, 64);
-    r += __shfl_xor(r, 2, 64);
-    if ((tid & 3) == 0 && ie != kNoIndex && r == kCpsMax - 1) thr_s = ve;
-  }
-  __syncthreads();
-  // 3. second pass: every token at or above the bound into an LDS list
-  const float thr = thr_s;
-  visit([&](int i, float x) {
-    if (x >= thr) {
-      const int k = atomicAdd(&n_found, 1);
-      if (k < kCandCap) {
-        cv[k] = x;
-        cix[k] = lo + i;
-      }
-    }
-  });
-  __syncthreads();
-  const int nf = n_found;
-  if (nf > kCandCap) {
-    // many tokens tie at the bound: sorted per-thread lists over the whole slice
-    float tv[kCpsMax];
-    int ti[kCpsMax];
+  const int nf = sh.n_found;
+  lattice_top16(sh, nf, [&](auto &&f) {
+    visit_row<E, kVec, NT>(z, n, [&](int i, float x) { f(lo + i, x); });
+  }, bv, bi);
+  m_out = sh.ms[2 * L::NW];
+  s_out = sh.ms[2 * L::NW + 1];
+}
+
+// A whole 16-byte row of at most R vectors per thread, held in registers and
+// read from memory once, with nontemporal loads.  Every load is issued at the
+// start, a thread past the row's end re-reading its last vector (the folds
+// skip it; the row holds at least one vector): loads under a condition would
+// make the first fold wait for all of them instead of for each vector as it
+// arrives.  The bound comes from the first H vectors of every thread while
+// the later ones are still arriving (a bound from part of the row holds for
+// all of it); those H are then listed against it, and each later vector is
+// folded into the (max, sum) and listed as it arrives.  The (max, sum) folds
+// every vector in the same order as the streaming form.  Results as
+// lattice_slice's.
+template <typename E, int NT, int R>
+__device__ __forceinline__ void lattice_row_regs(const typename E::elem *z, int n, float c,
+                                                 float &m_out, float &s_out, float &bv, int &bi) {
+  constexpr int P = E::kPerVec;
+  constexpr int H = kLatticeBoundVecs < R ? kLatticeBoundVecs : R;
+  using L = LatticeLds<NT, H>;
+  __shared__ L sh;
+  const int tid = threadIdx.x;
+  const vec16 *vz = reinterpret_cast<const vec16 *>(z);
+  const int nv = n / P;
+  vec16 buf[R];
 #pragma unroll
-    for (int k = 0; k < kCpsMax; ++k) {
-      tv[k] = kNegInf;
-      ti[k] = kNoIndex;
-    }
-    // (rare: streamed again even when the slice is in registers, which keeps
-    // every register access in a fully unrolled loop)
-    visit_row<E, kVec, NT>(z, n, [&](int i, float x) { top_insert(tv, ti, x, lo + i); });
-    float v16;
-    int i16;
-    wave_pop16<kCpsMax>(tv, ti, v16, i16);
-    if (lane < kCpsMax) {
-      wv[w * kCpsMax + lane] = v16;
-      wi[w * kCpsMax + lane] = i16;
-    }
-  } else {
-    // every listed token counts the ones ahead of it; the 16 best take their
-    // rank slots (token indices are unique)
-    for (int t = tid; t < nf; t += NT) {
-      const float v = cv[t];
-      const int i = cix[t];
-      int r = 0;
-#pragma unroll 4
-      for (int k = 0; k < nf; ++k) r += ahead(cv[k], cix[k], v, i);
-      if (r < kCpsMax) {
-        sv[r] = v;
-        si[r] = i;
+  for (int r = 0; r < R; ++r) buf[r] = __builtin_nontemporal_load(vz + min(tid + r * NT, nv - 1));
+  lattice_lds_init(sh);
+
+  // the first H vectors: (max, sum), each vector's largest logit, and the
+  // thread's best, tracked per vector (its first vector holding the largest
+  // logit; NaN never wins) and located inside that vector afterwards, which
+  // keeps the (logit descending, index ascending) order
+  float m = kNegInf, s = 0.0f, tmax = kNegInf;
+  int tvec = -1;
+#pragma unroll
+  for (int r = 0; r < H; ++r) {
+    if (tid + r * NT < nv) {
+      float x[P];
+      E::unpack(buf[r], x);
+      ms_fold<P>(m, s, x, c);
+      float vm = x[0];
+#pragma unroll
+      for (int e = 1; e < P; ++e) vm = fmaxf(vm, x[e]);
+      sh.vmx[r * NT + tid] = vm;  // NaN only for a vector of NaN
+      if (vm == vm && (tvec < 0 || vm > tmax)) {
+        tmax = vm;
+        tvec = r;
       }
     }
   }
-  __syncthreads();
-  m_out = lds[2 * NW];
-  s_out = lds[2 * NW + 1];
-  if (w != 0) return;
-  if (nf > kCandCap) {
-    constexpr int PER = (NW * kCpsMax + 63) / 64;
-    float lv[PER];
-    int li[PER];
+  int tidx = kNoIndex;
 #pragma unroll
-    for (int t = 0; t < PER; ++t) {
-      const int k = PER * lane + t;
-      lv[t] = k < NW * kCpsMax ? wv[k] : kNegInf;
-      li[t] = k < NW * kCpsMax ? wi[k] : kNoIndex;
+  for (int r = 0; r < H; ++r) {
+    if (r == tvec) {
+      float x[P];
+      E::unpack(buf[r], x);
+      int e0 = P - 1;
+#pragma unroll
+      for (int e = P - 1; e >= 0; --e)
+        if (x[e] == tmax) e0 = e;
+      tidx = (tid + r * NT) * P + e0;
     }
-    wave_pop16<PER>(lv, li, bv, bi);
-  } else {
-    bv = lane < kCpsMax ? sv[lane] : kNegInf;
-    bi = lane < kCpsMax ? si[lane] : kNoIndex;
   }
+  const float thr = lattice_bound(sh, tidx != kNoIndex ? rank_key(tmax, tidx) : 0);
+
+  // the first H vectors against the bound: only those whose largest logit
+  // reaches it
+#pragma unroll
+  for (int r = 0; r < H; ++r) {
+    const int i = tid + r * NT;
+    if (i < nv && sh.vmx[r * NT + tid] >= thr) {
+      float x[P];
+      E::unpack(buf[r], x);
+#pragma unroll
+      for (int e = 0; e < P; ++e) lattice_take(sh, thr, i * P + e, x[e]);
+    }
+  }
+  // the later vectors: (max, sum) and the list together
+#pragma unroll
+  for (int r = H; r < R; ++r) {
+    const int i = tid + r * NT;
+    if (i < nv) {
+      float x[P];
+      E::unpack(buf[r], x);
+      ms_fold<P>(m, s, x, c);
+      float vm = x[0];
+#pragma unroll
+      for (int e = 1; e < P; ++e) vm = fmaxf(vm, x[e]);
+      if (vm >= thr) {
+#pragma unroll
+        for (int e = 0; e < P; ++e) lattice_take(sh, thr, i * P + e, x[e]);
+      }
+    }
+  }
+  block_ms<L::NW>(m, s, c, sh.ms);  // valid in thread 0; its barriers end the listing
+  if (tid == 0) {
+    sh.ms[2 * L::NW] = m;
+    sh.ms[2 * L::NW + 1] = s;
+  }
+  const int nf = sh.n_found;
+  // (the rare many-ties merge streams the row again, which keeps every
+  // register access in a fully unrolled loop)
+  lattice_top16(sh, nf, [&](auto &&f) { visit_row<E, true, NT>(z, n, f); }, bv, bi);
+  m_out = sh.ms[2 * L::NW];
+  s_out = sh.ms[2 * L::NW + 1];
 }
 
 // Wave 0 with the row's 16 best pairs (lane r holds the r-th in bv, bi) and its
@@ -443,7 +528,10 @@ __global__ __launch_bounds__(kRowBlock) void kr_lattice(
   const int64_t row = blockIdx.x;  // b * G + j
   float m, s, bv;
   int bi;
-  lattice_slice<E, kVec, kRowBlock, R>(q + row * (int64_t)V, 0, V, c, m, s, bv, bi);
+  if constexpr (R > 0)
+    lattice_row_regs<E, kRowBlock, R>(q + row * (int64_t)V, V, c, m, s, bv, bi);
+  else
+    lattice_slice<E, kVec, kRowBlock>(q + row * (int64_t)V, 0, V, c, m, s, bv, bi);
   if (threadIdx.x >= 64) return;
   lattice_finish(row, m, s, bv, bi, c, tau, m_max, eos, cand, cand_logp, n_cand, flags);
 }
