@@ -761,7 +761,7 @@ int svd_cps_beam(const int32_t *cand, const float *cand_logp, const int32_t *n_c
     return SVD_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   CallTimer tm;
-  SVD_LAUNCH(tm, SVD_KERNEL_BEAM, s, kr_cps_beam, dim3((unsigned)B), dim3(64), s, cand, cand_logp,
+  SVD_LAUNCH(tm, SVD_KERNEL_BEAM, s, kr_cps_beam, dim3((unsigned)B), dim3(kBeamBlock), s, cand, cand_logp,
              n_cand, len, fluency, lambda, (int)G, (int)m_max, (int)beam, paths, path_score,
              path_len);
   return SVD_OK;

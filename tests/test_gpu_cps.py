@@ -213,3 +213,36 @@ def test_register_rows_with_ties_infinities_and_nan():
     _check_lattice(g, o, 16)
     assert list(g["cand"][0, 0, :5]) == [5, 6, 7, 8000, 151000]
     assert list(g["cand"][1, 1, :4]) == [3, 70000, 150000, 152063]
+
+
+def test_register_rows_bound_from_the_first_vectors():
+    # the register form takes its bound from each thread's first vectors
+    # (tokens [0, 81920) at V = 152064 with 1024 threads): rows whose best
+    # tokens all lie beyond that part, so the bound is loose, with a few
+    # hundred tokens at or above it, or so many that the list overflows into
+    # the streamed merge; and +0 tied with -0 at the top (equal probabilities:
+    # the lower index first), against the oracle
+    svd = require_gpu()
+    B, G, V = 16, 8, 152064
+    first = 10 * 1024 * 8
+    rng = np.random.default_rng(41)
+    z = (rng.standard_normal((B, G, V)) * 2.0).astype(np.float32)
+    z[0, 0, :first] = -8.0                   # every first-part maximum ties at -8: overflow
+    z[0, 1, :first] -= 1.5                   # a loose bound: some hundreds listed
+    z[0, 2, :first] -= 40.0                  # the first part far below the rest
+    z[1, 0, :] = -np.inf                     # +0 and -0 at the top, then -1
+    z[1, 0, [3, 50]] = 0.0
+    z[1, 0, [100, 90000]] = -0.0
+    z[1, 0, [7, 120000, 151999]] = -1.0
+    t = torch.from_numpy(z).to(torch.bfloat16)
+    hz = t.view(torch.int16).numpy().view(np.uint16).copy()
+    assert hz[1, 0, 100] == 0x8000 and hz[1, 0, 50] == 0x0000
+    q = t.cuda()
+    g = host(svd.cps_lattice(q, temp_q=1.0, tau=0.99, m_max=16))
+    o = oracle.cps_lattice(hz, temp_q=1.0, tau=0.99, m_max=16)
+    _check_lattice(g, o, 16)
+    assert list(g["cand"][1, 0, :7]) == [3, 50, 100, 90000, 7, 120000, 151999]
+    # the best tokens of the rows with a low first part lie beyond it
+    for j in (0, 1, 2):
+        n = int(g["n_cand"][0, j])
+        assert n >= 1 and np.all(g["cand"][0, j, :n] >= first), (j, g["cand"][0, j, :n])
