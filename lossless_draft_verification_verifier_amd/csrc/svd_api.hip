@@ -12,6 +12,7 @@
 #include "svd_timing.h"
 #include "svd_timing.hpp"
 #include "kr_adl.hpp"
+#include "kr_beam.hpp"
 #include "kr_beta.hpp"
 #include "kr_cps.hpp"
 #include "kr_draw.hpp"
