@@ -172,6 +172,21 @@ int early_chunk(int64_t B, int G) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(want, G));
 }
 
+// Length of chunk c: J positions for the first two chunks, then twice the
+// chunk before, at most cap.  Fewer prefixes reach each later chunk, so
+// reading a few positions past a rejection there costs less than another
+// round of launches.
+int early_chunk_len(int c, int J, int cap) {
+  return c < 2 ? J : std::max(J, std::min(J << std::min(c - 1, 20), cap));
+}
+
+// chunks of a window of G positions
+int early_chunks(int G, int J, int cap) {
+  int n = 0;
+  for (int j0 = 0; j0 < G; j0 += early_chunk_len(n, J, cap)) ++n;
+  return n;
+}
+
 // Split rows: slices per row pair (1: not split) and the slice length for a
 // launch of `rows` row pairs.
 template <typename E>
@@ -261,7 +276,10 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   const int units = a.V / unit;
   const int smax = (int)std::max<int64_t>(1, units / (2 * kSplitBlock));
   const bool live = a.early && a.B * J < kSplitRows && smax > 1;
-  const int nchunks = (a.G + J - 1) / J;
+  // a live-list chunk of the whole batch must fit the fixed grid (one slice
+  // per row at most)
+  const int cap = live ? (int)std::max<int64_t>(J, kLiveGrid / a.B) : a.G;
+  const int nchunks = a.early ? early_chunks(a.G, J, cap) : 1;
   const int32_t *mlen = nullptr;
   if (a.windowed) {
     const int64_t bk = a.B * a.K;
@@ -274,49 +292,49 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
   if (live) {
     // chunk c reads list c % 2 and its counter c, and writes the next ones
     const unsigned gw = (unsigned)((a.B * 64 + kBlock - 1) / kBlock);  // a wave per prefix
-    for (int c = 0; c < nchunks; ++c) {
-      const int j0 = c * J;
+    for (int c = 0, j0 = 0; c < nchunks; j0 += early_chunk_len(c, J, cap), ++c) {
+      const int Jc = std::min(early_chunk_len(c, J, cap), a.G - j0);
       const int32_t *cur = a.live + (c % 2) * a.B;
       int32_t *next = a.live + ((c + 1) % 2) * a.B;
       const uint32_t *cnt = a.counts + c;
       uint32_t *cnt_next = c + 1 < nchunks ? a.counts + c + 1 : nullptr;
       // the first chunk holds every prefix: with enough row pairs to give each
       // CU two, it streams whole rows (kr_rowstats), and the merge only tests
-      const bool whole = c == 0 && a.B * J >= kLiveWholeRows;
+      const bool whole = c == 0 && a.B * Jc >= kLiveWholeRows;
       const PartStats *part = whole ? nullptr : a.part;
       if (whole) {
         {
-          const int rc = launch_rowstats<E, kVec>(a, s, tm, (unsigned)(a.B * J), mlen, nullptr, 0,
-                                                  J);
+          const int rc = launch_rowstats<E, kVec>(a, s, tm, (unsigned)(a.B * Jc), mlen, nullptr, 0,
+                                                  Jc);
           if (rc != SVD_OK) return rc;
         }
         if (a.greedy)
           SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_combine_advance<E, true>, dim3(gw),
                      dim3(kBlock), s, a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, units, unit, smax,
-                     mlen, cur, cnt, j0, J, part, a.stats, a.alpha_ws, a.alpha, a.seed,
+                     mlen, cur, cnt, j0, Jc, part, a.stats, a.alpha_ws, a.alpha, a.seed,
                      a.row_base, next, cnt_next);
         else
           SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_combine_advance<E, false>, dim3(gw),
                      dim3(kBlock), s, a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, units, unit, smax,
-                     mlen, cur, cnt, j0, J, part, a.stats, a.alpha_ws, a.alpha, a.seed,
+                     mlen, cur, cnt, j0, Jc, part, a.stats, a.alpha_ws, a.alpha, a.seed,
                      a.row_base, next, cnt_next);
         continue;
       }
       if (a.greedy) {
         SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS_LIVE, s, kr_rowstats_live<E, kVec, true>,
                    dim3(kLiveGrid), dim3(kSplitBlock), s, a.p, a.q, a.G, a.V, a.cp, a.cq, units,
-                   unit, smax, mlen, cur, cnt, j0, J, a.part);
+                   unit, smax, mlen, cur, cnt, j0, Jc, a.part);
         SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_combine_advance<E, true>, dim3(gw),
                    dim3(kBlock), s, a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, units, unit, smax,
-                   mlen, cur, cnt, j0, J, (const PartStats *)a.part, a.stats, a.alpha_ws,
+                   mlen, cur, cnt, j0, Jc, (const PartStats *)a.part, a.stats, a.alpha_ws,
                    a.alpha, a.seed, a.row_base, next, cnt_next);
       } else {
         SVD_LAUNCH(tm, SVD_KERNEL_ROWSTATS_LIVE, s, kr_rowstats_live<E, kVec, false>,
                    dim3(kLiveGrid), dim3(kSplitBlock), s, a.p, a.q, a.G, a.V, a.cp, a.cq, units,
-                   unit, smax, mlen, cur, cnt, j0, J, a.part);
+                   unit, smax, mlen, cur, cnt, j0, Jc, a.part);
         SVD_LAUNCH(tm, SVD_KERNEL_COMBINE, s, kr_combine_advance<E, false>, dim3(gw),
                    dim3(kBlock), s, a.p, a.q, a.drafts, a.G, a.V, a.cp, a.cq, units, unit, smax,
-                   mlen, cur, cnt, j0, J, (const PartStats *)a.part, a.stats, a.alpha_ws,
+                   mlen, cur, cnt, j0, Jc, (const PartStats *)a.part, a.stats, a.alpha_ws,
                    a.alpha, a.seed, a.row_base, next, cnt_next);
       }
     }
@@ -371,12 +389,13 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
     // stream after the chunk holding its first rejection
     const unsigned gb = (unsigned)((a.B + kBlock - 1) / kBlock);
     SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_fill_u32, dim3(gb), dim3(kBlock), s, a.alive, a.B, 1u);
-    for (int j0 = 0; j0 < a.G; j0 += J) {
-      const int rc = stream_rows(j0, std::min(J, a.G - j0), a.alive);
+    for (int c = 0, j0 = 0; j0 < a.G; j0 += early_chunk_len(c, J, cap), ++c) {
+      const int Jc = std::min(early_chunk_len(c, J, cap), a.G - j0);
+      const int rc = stream_rows(j0, Jc, a.alive);
       if (rc != SVD_OK) return rc;
-      if (j0 + J < a.G)
+      if (j0 + Jc < a.G)
         SVD_LAUNCH(tm, SVD_KERNEL_SELECT, s, kr_advance, dim3(gb), dim3(kBlock), s,
-                   (const float *)a.alpha_ws, (const int32_t *)a.mlen, a.B, a.G, j0, J, a.seed,
+                   (const float *)a.alpha_ws, (const int32_t *)a.mlen, a.B, a.G, j0, Jc, a.seed,
                    a.row_base, a.alive);
     }
   }

@@ -246,3 +246,34 @@ def test_register_rows_bound_from_the_first_vectors():
     for j in (0, 1, 2):
         n = int(g["n_cand"][0, j])
         assert n >= 1 and np.all(g["cand"][0, j, :n] >= first), (j, g["cand"][0, j, :n])
+
+
+def test_cps_on_the_shared_marginal_workload():
+    # the benchmark's search at full size: the 256 shared drafter rows of the
+    # shared-marginal workload (B = 16, gamma = 16, V = 152064, bf16), held in
+    # registers by the lattice; tau 0.8, M_max 15, beam 3 over random
+    # transition scores; every row and every prefix against the oracle
+    import workloads as W
+    svd = require_gpu()
+    cfg = W.get_config("shared_marginal")
+    B, G, V, M = cfg.B, cfg.gamma, cfg.V, 15
+    d = W.generate_pooled(cfg, device=torch.device("cuda:0"))
+    q = d["q_pool"].view(B, G, V)
+    assert q.dtype == torch.bfloat16 and q.is_contiguous()
+    hz = q.cpu().view(torch.int16).numpy().view(np.uint16)
+    f = (np.random.default_rng(cfg.data_seed + 5).standard_normal((B, G, M, M)) * 0.3).astype(
+        np.float32)
+    gl = svd.cps_lattice(q, temp_q=cfg.temp, tau=0.8, m_max=M)
+    g = host(svd.cps_beam(gl, torch.from_numpy(f).cuda(), lam=0.5, beam=3))
+    ol = oracle.cps_lattice(hz, temp_q=cfg.temp, tau=0.8, m_max=M)
+    flagged = _check_lattice(host(gl), ol, M)
+    ob = oracle.cps_beam(ol, f, lam=0.5, beam=3)
+    compared = 0
+    for b in range(B):
+        if np.min(ol["cum_margin"][b]) < CUM_EPS or ob["rank_margin"][b] < RANK_EPS:
+            continue
+        compared += 1
+        assert np.array_equal(g["paths"][b], ob["paths"][b]), b
+        assert np.allclose(g["score"][b], ob["score"][b], atol=1e-3)
+    say("rows with a cut near tau", flagged, "prefixes compared", compared, "of", B)
+    assert compared >= B - 2

@@ -79,6 +79,25 @@ def test_ragged_eos_windows_match_oracle(orc, rule, case):
             assert np.all(np.isnan(g["alpha"][b, k, m:])) and not np.any(np.isnan(g["alpha"][b, k, :m]))
 
 
+def _chunk_ends(B, G, V, dt):
+    """The early exit's chunks: J = ceil(512 / B) positions (at most G) for the
+    first two, then twice the chunk before; when the chunks follow a live list
+    (rows cut into at least two slices, fewer than 1024 row pairs per chunk of
+    J), at most max(J, 1024 // B), so that a chunk of the whole batch fits the
+    list's grid.  Returns J and the end of every chunk."""
+    J = min(G, -(-512 // B))
+    es = 2 if dt == "bf16" else 4
+    unit = 16 // es if (V * es) % 16 == 0 else 1
+    smax = max(1, (V // unit) // 512)
+    cap = max(J, 1024 // B) if (B * J < 1024 and smax > 1) else G
+    ends, j0, c = [], 0, 0
+    while j0 < G:
+        j0 += J if c < 2 else max(J, min(J << (c - 1), cap))
+        ends.append(min(j0, G))
+        c += 1
+    return J, ends
+
+
 @pytest.mark.parametrize("rule", ["standard", "greedy"])
 @pytest.mark.parametrize("B,V,dt", [(300, 4096, "bf16"), (300, 20000, "bf16"), (300, 20000, "f32"),
                                     (300, 20001, "bf16"), (20, 20000, "bf16")])
@@ -98,9 +117,10 @@ def test_early_exit_equals_full_streaming(orc, rule, B, V, dt):
     for k in ("selected", "accept_len", "next_token"):
         assert np.array_equal(a[k], b[k]), k
     # every position up to the first rejection was streamed, with the same alpha,
-    # and nothing past the chunk of J = ceil(512 / B) positions that holds it
+    # and nothing past the chunk that holds it
     L = a["accept_len"]
-    J = min(G, -(-512 // B))
+    J, ends = _chunk_ends(B, G, V, dt)
+    say("chunk ends", ends)
     hd = W.to_host(d["drafts"])
     for i in range(B):
         hits = np.nonzero(hd[i, 0, :int(gb[i])] == 17)[0]
@@ -110,7 +130,8 @@ def test_early_exit_equals_full_streaming(orc, rule, B, V, dt):
             assert np.array_equal(a["alpha"][i, 0, :n], b["alpha"][i, 0, :n], equal_nan=True)
         else:
             assert np.all(np.abs(a["alpha"][i, 0, :n] - b["alpha"][i, 0, :n]) <= 1e-5)
-        end = min(m, (min(int(L[i]), m - 1) // J + 1) * J)
+        t = min(int(L[i]), m - 1)  # the position that ends the prefix's stream
+        end = min(m, next(e for e in ends if e > t))
         assert not np.any(np.isnan(a["alpha"][i, 0, :end])), i
         assert np.all(np.isnan(a["alpha"][i, 0, end:])), i
     streamed = np.sum(~np.isnan(a["alpha"]))
