@@ -30,6 +30,34 @@ __global__ __launch_bounds__(kBlock) void kr_fill_u32(uint32_t *__restrict__ dst
   for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) dst[i] = value;
 }
 
+// Pools of at most this many rows are flagged by one workgroup in LDS.
+constexpr int kMarkLdsRows = 32768;
+
+// flags[0, nrows) in one launch: one workgroup clears a byte per row in LDS,
+// flags the rows read (as kr_mark_rows), then writes every flag out, each
+// thread its own rows
+__global__ __launch_bounds__(1024) void kr_mark_rows_one(const int32_t *__restrict__ p_index,
+                                                         const int32_t *__restrict__ q_index,
+                                                         int64_t n, int gamma, int64_t np,
+                                                         int64_t nq, int64_t nrows,
+                                                         uint32_t *__restrict__ flags) {
+  __shared__ uint8_t f[kMarkLdsRows];
+  const int tid = threadIdx.x;
+  for (int64_t r = tid; r < nrows; r += 1024) f[r] = 0;
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += 1024) {  // (b, k, j < gamma)
+    const int64_t bk = i / gamma, j = i - bk * gamma;
+    const int32_t pi = p_index[bk * (gamma + 1) + j];
+    if (pi >= 0 && pi < np) f[pi] = 1;
+    if (q_index) {
+      const int32_t qi = q_index[i];
+      if (qi >= 0 && qi < nq) f[np + qi] = 1;
+    }
+  }
+  __syncthreads();
+  for (int64_t r = tid; r < nrows; r += 1024) flags[r] = f[r];
+}
+
 // flags[0, np) for p rows, flags[np, np + nq) for q rows
 __global__ __launch_bounds__(kBlock) void kr_mark_rows(const int32_t *__restrict__ p_index,
                                                        const int32_t *__restrict__ q_index,
@@ -64,15 +92,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void kr
   if (threadIdx.x == 0) pstat[r] = PoolStat{m, s};
 }
 
+// alpha and the statistics record of scored position i = (b, k, j < gamma)
 template <typename E, bool kGreedy>
-__global__ __launch_bounds__(kBlock) void kr_alpha_rows(
+__device__ __forceinline__ void alpha_row(
     const typename E::elem *__restrict__ p_pool, const typename E::elem *__restrict__ q_pool,
     const int32_t *__restrict__ p_index, const int32_t *__restrict__ q_index,
-    const int32_t *__restrict__ drafts, int64_t n, int gamma, int V, int64_t np, int64_t nq,
-    float cp, float cq, const PoolStat *__restrict__ pstat, RowStats *__restrict__ stats,
-    float *__restrict__ alpha_ws, float *__restrict__ alpha_out) {
-  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;  // (b, k, j < gamma)
-  if (i >= n) return;
+    const int32_t *__restrict__ drafts, int gamma, int V, int64_t np, int64_t nq, float cp,
+    float cq, const PoolStat *__restrict__ pstat, RowStats *stats, float *alpha_ws,
+    float *__restrict__ alpha_out, int64_t i) {
   const int64_t bk = i / gamma, j = i - bk * gamma;
   const int32_t pi = p_index[bk * (gamma + 1) + j];
   const int32_t qi = kGreedy ? 0 : q_index[i];
@@ -91,6 +118,19 @@ __global__ __launch_bounds__(kBlock) void kr_alpha_rows(
   stats[i] = st;
   alpha_ws[i] = a;
   if (alpha_out) alpha_out[i] = a;
+}
+
+template <typename E, bool kGreedy>
+__global__ __launch_bounds__(kBlock) void kr_alpha_rows(
+    const typename E::elem *__restrict__ p_pool, const typename E::elem *__restrict__ q_pool,
+    const int32_t *__restrict__ p_index, const int32_t *__restrict__ q_index,
+    const int32_t *__restrict__ drafts, int64_t n, int gamma, int V, int64_t np, int64_t nq,
+    float cp, float cq, const PoolStat *__restrict__ pstat, RowStats *__restrict__ stats,
+    float *__restrict__ alpha_ws, float *__restrict__ alpha_out) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;  // (b, k, j < gamma)
+  if (i >= n) return;
+  alpha_row<E, kGreedy>(p_pool, q_pool, p_index, q_index, drafts, gamma, V, np, nq, cp, cq, pstat,
+                        stats, alpha_ws, alpha_out, i);
 }
 
 }  // namespace svd

@@ -14,7 +14,7 @@
 // appendix B.4).
 #pragma once
 
-#include "kr_rowstats.hpp"
+#include "kr_rows.hpp"  // PoolStat, alpha_row; kr_rowstats.hpp
 
 namespace svd {
 
@@ -244,6 +244,31 @@ __global__ __launch_bounds__(64 * kFuseRows) void kr_combine_select(
                           0, sel.gamma, part, stats, alpha_ws, alpha_out,
                           b * kg + (threadIdx.x >> 6), threadIdx.x & 63);
   __syncthreads();  // the rows' alpha and statistics, visible to wave 0
+  if (threadIdx.x < 64) {
+    const DrawDesc d = select_prefix(sel, b);
+    if (threadIdx.x == 0) desc[b] = d;
+  }
+}
+
+// Shared rows with at most kAlphaSelectMax scored positions per prefix: one
+// workgroup per prefix forms the alpha of its positions (a thread each, as
+// kr_alpha_rows), and after the barrier wave 0 selects, so the selection
+// needs no launch of its own.
+constexpr int kAlphaSelectMax = 1024;
+
+template <typename E, bool kGreedy>
+__global__ __launch_bounds__(kAlphaSelectMax) void kr_alpha_select(
+    const typename E::elem *__restrict__ p_pool, const typename E::elem *__restrict__ q_pool,
+    int V, int64_t nq, float cp, float cq, const PoolStat *__restrict__ pstat, RowStats *stats,
+    float *alpha_ws, float *__restrict__ alpha_out, const SelectArgs sel,
+    DrawDesc *__restrict__ desc) {
+  // sel.stats and sel.alpha_ws are stats and alpha_ws, read back after the barrier
+  const int64_t b = blockIdx.x;
+  const int kg = sel.K * sel.gamma;
+  for (int t = threadIdx.x; t < kg; t += blockDim.x)
+    alpha_row<E, kGreedy>(p_pool, q_pool, sel.p_index, sel.q_index, sel.drafts, sel.gamma, V,
+                          sel.np, nq, cp, cq, pstat, stats, alpha_ws, alpha_out, b * kg + t);
+  __syncthreads();  // the positions' alpha and statistics, visible to wave 0
   if (threadIdx.x < 64) {
     const DrawDesc d = select_prefix(sel, b);
     if (threadIdx.x == 0) desc[b] = d;

@@ -143,7 +143,7 @@ struct Batch {
   uint32_t *counts;  // early exit: live prefixes per chunk
   PartStats *part;
   bool vec;  // 16-byte loads
-  bool fuse_select;  // the selection runs in the split rows' merge (kr_combine_select)
+  bool fuse_select;  // the selection runs in the launch that forms alpha (kr_combine_select, kr_alpha_select)
   int32_t *selected, *accept_len, *next_token;
   float *scores, *alpha, *beta;
   RowStats *stats;
@@ -247,10 +247,15 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
     const int64_t nrows = a.np + (a.greedy ? 0 : a.nq);
     const unsigned gp = (unsigned)((rp + kBlock - 1) / kBlock);
     const unsigned gf = (unsigned)std::min<int64_t>((nrows + kBlock - 1) / kBlock, 4096);
-    SVD_LAUNCH(tm, SVD_KERNEL_MARK, s, kr_fill_u32, dim3(gf), dim3(kBlock), s, a.flags, nrows,
-               0u);
-    SVD_LAUNCH(tm, SVD_KERNEL_MARK, s, kr_mark_rows, dim3(gp), dim3(kBlock), s, a.ix.p,
-               a.greedy ? nullptr : a.ix.q, (int64_t)rp, a.G, a.np, a.nq, a.flags);
+    if (nrows <= kMarkLdsRows) {
+      SVD_LAUNCH(tm, SVD_KERNEL_MARK, s, kr_mark_rows_one, dim3(1), dim3(1024), s, a.ix.p,
+                 a.greedy ? nullptr : a.ix.q, (int64_t)rp, a.G, a.np, a.nq, nrows, a.flags);
+    } else {
+      SVD_LAUNCH(tm, SVD_KERNEL_MARK, s, kr_fill_u32, dim3(gf), dim3(kBlock), s, a.flags, nrows,
+                 0u);
+      SVD_LAUNCH(tm, SVD_KERNEL_MARK, s, kr_mark_rows, dim3(gp), dim3(kBlock), s, a.ix.p,
+                 a.greedy ? nullptr : a.ix.q, (int64_t)rp, a.G, a.np, a.nq, a.flags);
+    }
     if ((int64_t)a.V * (int64_t)sizeof(typename E::elem) < kShortRowBytes)
       SVD_LAUNCH(tm, SVD_KERNEL_POOL_STATS, s, kr_pool_stats<E, kVec, kShortRowBlock>,
                  dim3((unsigned)nrows), dim3(kShortRowBlock), s, a.p, a.q, a.np, a.V, a.cp, a.cq,
@@ -259,6 +264,20 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
       SVD_LAUNCH(tm, SVD_KERNEL_POOL_STATS, s, kr_pool_stats<E, kVec>, dim3((unsigned)nrows),
                  dim3(kRowBlock), s, a.p, a.q, a.np, a.V, a.cp, a.cq, (const uint32_t *)a.flags,
                  a.pstat);
+    if (a.fuse_select) {  // alpha and the selection, a workgroup per prefix
+      const SelectArgs sel = make_select(a);
+      const int kg = a.K * a.G;
+      const dim3 tb((unsigned)std::min(kAlphaSelectMax, std::max(64, (kg + 63) / 64 * 64)));
+      if (a.greedy)
+        SVD_LAUNCH(tm, SVD_KERNEL_ALPHA_ROWS, s, kr_alpha_select<E, true>, dim3((unsigned)a.B),
+                   tb, s, a.p, a.q, a.V, a.nq, a.cp, a.cq, (const PoolStat *)a.pstat, a.stats,
+                   a.alpha_ws, a.alpha, sel, a.desc);
+      else
+        SVD_LAUNCH(tm, SVD_KERNEL_ALPHA_ROWS, s, kr_alpha_select<E, false>, dim3((unsigned)a.B),
+                   tb, s, a.p, a.q, a.V, a.nq, a.cp, a.cq, (const PoolStat *)a.pstat, a.stats,
+                   a.alpha_ws, a.alpha, sel, a.desc);
+      return SVD_OK;
+    }
     if (a.greedy)
       SVD_LAUNCH(tm, SVD_KERNEL_ALPHA_ROWS, s, kr_alpha_rows<E, true>, dim3(gp), dim3(kBlock), s,
                  a.p, a.q, a.ix.p, a.ix.q, a.drafts, (int64_t)rp, a.G, a.V, a.np, a.nq, a.cp,
@@ -507,7 +526,10 @@ int run(const Call &c) {
   // selection joins the merge of the split rows
   int S_all, slice_all;
   split_plan<E>(a, a.B * a.K * a.G, S_all, slice_all);
-  a.fuse_select = !a.ix.p && !a.early && S_all > 1 && a.K * a.G <= kFuseRows;
+  // the selection runs in the launch that forms alpha: split rows merged a
+  // prefix per workgroup, or shared rows with few positions per prefix
+  a.fuse_select = (!a.ix.p && !a.early && S_all > 1 && a.K * a.G <= kFuseRows) ||
+                  (a.ix.p && a.K * a.G <= kAlphaSelectMax);
 
   hipStream_t stream = static_cast<hipStream_t>(c.stream);
   CallTimer tm;
