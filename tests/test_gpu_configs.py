@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import check_ranges, gen, host_inputs, require_gpu, run_select, say
+from gpu_util import check_ranges, gen, host, host_inputs, require_gpu, run_select, say
 from parity_harness import ParityReport, compare
 
 pytestmark = pytest.mark.gpu
@@ -96,4 +96,28 @@ def test_near_tie_rate_at_full_size(orc, cid, data_seeds, seeds):
         assert rep.decisions["accept"] >= 10_000
     else:
         assert rep.decisions["select"] >= 256
+    assert rep.excused_within(), rep.summary()
+
+
+@pytest.mark.parametrize("rule", ["standard", "greedy"])
+def test_vocabulary_shard_at_full_size(orc, rule):
+    # one GPU's share of an 8-way vocabulary-sharded verifier, in the
+    # configuration the benchmark times: batched serving (B = 256, K = 1,
+    # gamma = 8) at V = 152064 / 8 = 19008, every prefix against the oracle
+    import dataclasses
+    svd = require_gpu()
+    cfg = dataclasses.replace(W.get_config(4), V=152064 // 8, name="batched_serving_vshard8")
+    d = gen(cfg)
+    if rule == "greedy":
+        g = host(svd.greedy_select_and_verify(d["p"], d["drafts"], temp_p=cfg.temp, seed=cfg.seed,
+                                              want_alpha=True, want_scores=True))
+        hp, hd, hq = W.to_host(d["p"]), W.to_host(d["drafts"]), None
+    else:
+        g = run_select(svd, d, cfg.temp, cfg.seed)
+        hp, hq, hd = host_inputs(d)
+    check_ranges(g, cfg.K, cfg.gamma, cfg.V)
+    rep = compare(orc, hp, hq, hd, g, cfg.temp, cfg.temp, cfg.seed, greedy=rule == "greedy")
+    say(rule, rep.summary())
+    assert rep.prefixes == cfg.B
+    assert rep.ok(), rep.failures[:5]
     assert rep.excused_within(), rep.summary()
