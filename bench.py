@@ -294,6 +294,32 @@ def calibrate_copy(torch, steps):
 CPS_TAU, CPS_MMAX, CPS_BEAM, CPS_LAMBDA = 0.8, 15, 3, 0.5
 
 
+def cps_cpu_baseline(hq, flu, cfg, seconds=10.0):
+    """The lattice and beam oracles, untuned: the prefixes split over the host's
+    thread share (each thread runs both oracles on its slice; the oracle's C
+    calls release the interpreter lock), and on one thread, each repeated
+    until about `seconds` of wall time have passed."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    B, G = hq.shape[0], hq.shape[1]
+
+    def one(sl):
+        ol = oracle.cps_lattice(hq[sl], temp_q=cfg.temp, tau=CPS_TAU, m_max=CPS_MMAX)
+        oracle.cps_beam(ol, flu[sl], lam=CPS_LAMBDA, beam=CPS_BEAM)
+
+    threads = min(host_threads(), B)
+    parts = [slice(i * B // threads, (i + 1) * B // threads) for i in range(threads)]
+    with ThreadPoolExecutor(threads) as ex:
+        reps, dt = _time_oracle(lambda: list(ex.map(one, parts)), seconds)
+    reps1, dt1 = _time_oracle(lambda: one(slice(0, B)), seconds)
+    rows = B * G
+    return {"value": rows * reps / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": "the %d drafter rows %d times on %d threads (%.1f s), %d times on one "
+                      "(%.1f s)" % (rows, reps, threads, dt, reps1, dt1),
+            "single_thread": {"value": rows * reps1 / dt1, "seconds": dt1, "reps": reps1},
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+
+
 def bench_cps(args, torch, svd, W):
     """Causal-consistency path search over one drafter row per (prefix, position): the
     shared drafter rows of the shared_marginal workload (B = 16, gamma = 16)."""
@@ -355,21 +381,7 @@ def bench_cps(args, torch, svd, W):
         "mean_lattice_width": float(lat["n_cand"].float().mean().item()),
     }
     if not args.no_cpu_baseline:
-        import oracle
-        hq = W.to_host(q)
-        t0 = time.perf_counter()
-        reps = 0
-        while reps == 0 or time.perf_counter() - t0 < 10.0:
-            ol = oracle.cps_lattice(hq, temp_q=cfg.temp, tau=CPS_TAU, m_max=CPS_MMAX)
-            oracle.cps_beam(ol, flu.cpu().numpy(), lam=CPS_LAMBDA, beam=CPS_BEAM)
-            reps += 1
-        dt = time.perf_counter() - t0
-        result["cpu_baseline"] = {"value": rows * reps / dt, "unit": "rows/s", "cores": 1,
-                                  "kind": "oracle",
-                                  "sample": "the %d drafter rows %d times, %.1f s on one thread "
-                                            "(the lattice and beam oracles are single-threaded)"
-                                            % (rows, reps, dt),
-                                  "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+        result["cpu_baseline"] = cps_cpu_baseline(W.to_host(q), flu.cpu().numpy(), cfg)
     print(json.dumps(result), flush=True)
 
 
