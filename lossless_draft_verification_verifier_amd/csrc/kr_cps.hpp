@@ -121,6 +121,8 @@ enum : uint32_t { kRowInvalid = 1u, kRowEosTop = 2u };
 constexpr int kCandCap = 512;  // LDS list of tokens at or above the threshold
 // vectors per thread of a row held in registers from which its bound is taken
 constexpr int kLatticeBoundVecs = 10;
+// keys each wave keeps for the bound of a row held in registers
+constexpr int kLatticeWaveKeep = 4;
 constexpr int kLatticeMaxSlices = 64;  // slices of one row (one per lane of the merge)
 
 // visit the logits of a row with kRowBlock threads: f(index, value)
@@ -159,33 +161,38 @@ __device__ __forceinline__ void visit_row(const typename E::elem *z, int n, F &&
   }
 }
 
-// LDS of one workgroup finding a row's (or slice's) 16 best tokens; H > 0:
-// the largest logit of each of the first H vectors that every thread holds.
-template <int NT, int H>
+// LDS of one workgroup finding a row's (or slice's) 16 best tokens.  Each
+// wave keeps its KEEP best thread keys (16: the 16th largest of what the waves
+// keep is the 16th largest of all threads' keys; fewer: still a lower bound,
+// as any subset's 16th largest is); H > 0: the largest logit of each of the
+// first H vectors that every thread holds.
+template <int NT, int H, int KEEP = kCpsMax>
 struct LatticeLds {
   static constexpr int NW = NT / 64;
-  static constexpr int NE = NW * kCpsMax;  // the waves' 16 best keys
-  static constexpr int Q = NE / 4;         // one quarter of them
-  float ms[2 * NW + 2];                    // block_ms partials, then the (max, sum)
-  uint64_t ak[NT];                         // every thread's best key
-  // wave w's 16 best keys by rank at entry w * 16 + rank, quarter q of the
-  // entries padded by two keys, so that the four readers of one rank step
-  // (one per quarter) use different LDS banks
-  uint64_t wk[NE + 8];
+  static constexpr int NE = NW * KEEP;  // the keys the waves keep
+  static constexpr int T = NT / NE;     // threads ranking one of them
+  static constexpr int PER = NE / T;    // keys each of those threads compares
+  static_assert(NE >= kCpsMax && T * NE == NT && T <= 64, "a bound needs 16 kept keys");
+  float ms[2 * NW + 2];                 // block_ms partials, then the (max, sum)
+  uint64_t ak[NT];                      // every thread's best key; later the merge's lists
+  // wave w's kept keys by rank at entry w * KEEP + rank, each group of PER
+  // entries padded by two keys, so that the T readers of one rank step use
+  // different LDS banks
+  uint64_t wk[NE + 2 * T];
   uint64_t ck[kCandCap];  // the keys of the tokens at or above the bound
   uint64_t sk[kCpsMax];   // the 16 best of those, by rank
   float vmx[H > 0 ? H * NT : 1];
   int n_found;
   float thr;
-  __device__ static int slot(int e) { return e + 2 * (e / Q); }
+  __device__ static int slot(int e) { return e + 2 * (e / PER); }
 };
 
-// Clears the rank slots and the candidate count; the first barrier of
-// lattice_bound orders this before any use.
+// Clears the candidate ranks and count and sets the bound to -inf; a barrier
+// before their first use orders this.  (Each wave clears its own rank slots
+// in wave_rank16.)
 template <class L>
 __device__ __forceinline__ void lattice_lds_init(L &sh) {
   const int tid = threadIdx.x;
-  for (int k = tid; k < L::NE + 8; k += L::NW * 64) sh.wk[k] = 0;
   if (tid < kCpsMax) sh.sk[tid] = 0;
   if (tid == 0) {
     sh.thr = kNegInf;  // fewer than 16 keyed tokens: all of them
@@ -200,31 +207,48 @@ __device__ __forceinline__ void lattice_lds_init(L &sh) {
 // threads rank each of those NE against a quarter of them each.  Keys are
 // unique (they hold the token index).  Returns the bound's logit in every
 // thread (-inf with fewer than 16 keyed tokens).
+// The first step, within each wave (no workgroup barrier: a wave reads only
+// the keys its own lanes wrote, and its LDS accesses run in program order).
 template <class L>
-__device__ __forceinline__ float lattice_bound(L &sh, uint64_t key) {
-  const int tid = threadIdx.x, w = tid >> 6;
+__device__ __forceinline__ void wave_rank16(L &sh, uint64_t key) {
+  constexpr int KEEP = L::NE / L::NW;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (lane < KEEP) sh.wk[L::slot(w * KEEP + lane)] = 0;
   sh.ak[tid] = key;
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();
   if (key) {
     int r = 0;
 #pragma unroll 16
     for (int k = w * 64; k < w * 64 + 64; ++k) r += sh.ak[k] > key;
-    if (r < kCpsMax) sh.wk[L::slot(w * kCpsMax + r)] = key;
+    if (r < KEEP) sh.wk[L::slot(w * KEEP + r)] = key;
   }
-  __syncthreads();
+}
+
+// The second step, after a workgroup barrier that follows every wave's first
+// step; returns the bound with a barrier after it.
+template <class L>
+__device__ __forceinline__ float merge_rank16(L &sh) {
+  const int tid = threadIdx.x;
   {
-    const int e = tid >> 2, q = tid & 3;  // NE == NT / 4 entries, four threads each
+    const int e = tid / L::T, part = tid % L::T;  // NE entries, T threads each
     const uint64_t ke = sh.wk[L::slot(e)];
-    const uint64_t *qk = sh.wk + q * (L::Q + 2);
+    const uint64_t *qk = sh.wk + L::slot(part * L::PER);
     int r = 0;
 #pragma unroll 16
-    for (int k = 0; k < L::Q; ++k) r += qk[k] > ke;
-    r += __shfl_xor(r, 1, 64);
-    r += __shfl_xor(r, 2, 64);
-    if (q == 0 && ke && r == kCpsMax - 1) sh.thr = key_value(ke);
+    for (int k = 0; k < L::PER; ++k) r += qk[k] > ke;
+#pragma unroll
+    for (int off = 1; off < L::T; off <<= 1) r += __shfl_xor(r, off, 64);
+    if (part == 0 && ke && r == kCpsMax - 1) sh.thr = key_value(ke);
   }
   __syncthreads();
   return sh.thr;
+}
+
+template <class L>
+__device__ __forceinline__ float lattice_bound(L &sh, uint64_t key) {
+  wave_rank16(sh, key);
+  __syncthreads();
+  return merge_rank16(sh);
 }
 
 // Appends the token (index i, logit x) to the candidate list when it reaches
@@ -258,8 +282,7 @@ __device__ __forceinline__ void lattice_top16(L &sh, int nf, Restream &&restream
     float v16;
     int i16;
     wave_pop16<kCpsMax>(tv, ti, v16, i16);
-    if (lane < kCpsMax)
-      sh.wk[L::slot(w * kCpsMax + lane)] = i16 != kNoIndex ? rank_key(v16, i16) : 0;
+    if (lane < kCpsMax) sh.ak[w * kCpsMax + lane] = i16 != kNoIndex ? rank_key(v16, i16) : 0;
   } else {
     // every listed token counts the ones ahead of it; the 16 best take their
     // rank slots
@@ -274,13 +297,14 @@ __device__ __forceinline__ void lattice_top16(L &sh, int nf, Restream &&restream
   __syncthreads();
   if (w != 0) return;
   if (nf > kCandCap) {
-    constexpr int PER = (L::NE + 63) / 64;
+    constexpr int NL = L::NW * kCpsMax;  // the waves' lists
+    constexpr int PER = (NL + 63) / 64;
     float lv[PER];
     int li[PER];
 #pragma unroll
     for (int t = 0; t < PER; ++t) {
       const int k = PER * lane + t;
-      const uint64_t kk = k < L::NE ? sh.wk[L::slot(k)] : 0;
+      const uint64_t kk = k < NL ? sh.ak[k] : 0;
       lv[t] = key_value(kk);
       li[t] = key_index(kk);
     }
@@ -364,20 +388,22 @@ __device__ __forceinline__ void lattice_slice(const typename E::elem *row, int l
 // start, a thread past the row's end re-reading its last vector (the folds
 // skip it; the row holds at least one vector): loads under a condition would
 // make the first fold wait for all of them instead of for each vector as it
-// arrives.  The bound comes from the first H vectors of every thread while
-// the later ones are still arriving (a bound from part of the row holds for
-// all of it); those H are then listed against it, and each later vector is
-// folded into the (max, sum) and listed as it arrives.  The (max, sum) folds
-// every vector in the same order as the streaming form.  Results as
-// lattice_slice's.
+// arrives.  Each wave works on until a single workgroup barrier: it folds
+// every vector into its (max, sum) as it arrives and keeps each vector's
+// largest logit in LDS, ranks the best keys of its threads' first H vectors
+// among themselves (a bound from part of the row holds for all of it), and
+// leaves its (max, sum).  After the barrier the waves' 16 best give the bound,
+// the held vectors whose largest logit reaches it are listed, and wave 0
+// merges the waves' (max, sum) in wave order, the order of the streaming
+// form's reduction.  Results as lattice_slice's.
 template <typename E, int NT, int R>
 __device__ __forceinline__ void lattice_row_regs(const typename E::elem *z, int n, float c,
                                                  float &m_out, float &s_out, float &bv, int &bi) {
   constexpr int P = E::kPerVec;
   constexpr int H = kLatticeBoundVecs < R ? kLatticeBoundVecs : R;
-  using L = LatticeLds<NT, H>;
+  using L = LatticeLds<NT, R, kLatticeWaveKeep>;
   __shared__ L sh;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const vec16 *vz = reinterpret_cast<const vec16 *>(z);
   const int nv = n / P;
   vec16 buf[R];
@@ -385,14 +411,14 @@ __device__ __forceinline__ void lattice_row_regs(const typename E::elem *z, int 
   for (int r = 0; r < R; ++r) buf[r] = __builtin_nontemporal_load(vz + min(tid + r * NT, nv - 1));
   lattice_lds_init(sh);
 
-  // the first H vectors: (max, sum), each vector's largest logit, and the
-  // thread's best, tracked per vector (its first vector holding the largest
-  // logit; NaN never wins) and located inside that vector afterwards, which
+  // every vector as it arrives: (max, sum) and its largest logit; over the
+  // first H, the thread's best, tracked per vector (its first vector holding
+  // the largest logit; NaN never wins) and located inside it afterwards, which
   // keeps the (logit descending, index ascending) order
   float m = kNegInf, s = 0.0f, tmax = kNegInf;
   int tvec = -1;
 #pragma unroll
-  for (int r = 0; r < H; ++r) {
+  for (int r = 0; r < R; ++r) {
     if (tid + r * NT < nv) {
       float x[P];
       E::unpack(buf[r], x);
@@ -401,31 +427,45 @@ __device__ __forceinline__ void lattice_row_regs(const typename E::elem *z, int 
 #pragma unroll
       for (int e = 1; e < P; ++e) vm = fmaxf(vm, x[e]);
       sh.vmx[r * NT + tid] = vm;  // NaN only for a vector of NaN
-      if (vm == vm && (tvec < 0 || vm > tmax)) {
+      if (r < H && vm == vm && (tvec < 0 || vm > tmax)) {
         tmax = vm;
         tvec = r;
       }
     }
-  }
-  int tidx = kNoIndex;
+    if (r == H - 1) {  // the thread's best of the first H vectors, ranked in the wave
+      int tidx = kNoIndex;
 #pragma unroll
-  for (int r = 0; r < H; ++r) {
-    if (r == tvec) {
-      float x[P];
-      E::unpack(buf[r], x);
-      int e0 = P - 1;
+      for (int q = 0; q < H; ++q) {
+        if (q == tvec) {
+          float y[P];
+          E::unpack(buf[q], y);
+          int e0 = P - 1;
 #pragma unroll
-      for (int e = P - 1; e >= 0; --e)
-        if (x[e] == tmax) e0 = e;
-      tidx = (tid + r * NT) * P + e0;
+          for (int e = P - 1; e >= 0; --e)
+            if (y[e] == tmax) e0 = e;
+          tidx = (tid + q * NT) * P + e0;
+        }
+      }
+      wave_rank16(sh, tidx != kNoIndex ? rank_key(tmax, tidx) : 0);
     }
   }
-  const float thr = lattice_bound(sh, tidx != kNoIndex ? rank_key(tmax, tidx) : 0);
-
-  // the first H vectors against the bound: only those whose largest logit
-  // reaches it
+  // this wave's (max, sum), by the butterfly of block_ms
 #pragma unroll
-  for (int r = 0; r < H; ++r) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const float mo = __shfl_xor(m, off, 64);
+    const float so = __shfl_xor(s, off, 64);
+    ms_merge(m, s, mo, so, c);
+  }
+  if (lane == 0) {
+    sh.ms[2 * w] = m;
+    sh.ms[2 * w + 1] = s;
+  }
+  __syncthreads();
+  const float thr = merge_rank16(sh);
+
+  // the held vectors whose largest logit reaches the bound
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
     const int i = tid + r * NT;
     if (i < nv && sh.vmx[r * NT + tid] >= thr) {
       float x[P];
@@ -434,34 +474,18 @@ __device__ __forceinline__ void lattice_row_regs(const typename E::elem *z, int 
       for (int e = 0; e < P; ++e) lattice_take(sh, thr, i * P + e, x[e]);
     }
   }
-  // the later vectors: (max, sum) and the list together
-#pragma unroll
-  for (int r = H; r < R; ++r) {
-    const int i = tid + r * NT;
-    if (i < nv) {
-      float x[P];
-      E::unpack(buf[r], x);
-      ms_fold<P>(m, s, x, c);
-      float vm = x[0];
-#pragma unroll
-      for (int e = 1; e < P; ++e) vm = fmaxf(vm, x[e]);
-      if (vm >= thr) {
-#pragma unroll
-        for (int e = 0; e < P; ++e) lattice_take(sh, thr, i * P + e, x[e]);
-      }
-    }
-  }
-  block_ms<L::NW>(m, s, c, sh.ms);  // valid in thread 0; its barriers end the listing
-  if (tid == 0) {
-    sh.ms[2 * L::NW] = m;
-    sh.ms[2 * L::NW + 1] = s;
-  }
+  __syncthreads();
   const int nf = sh.n_found;
   // (the rare many-ties merge streams the row again, which keeps every
   // register access in a fully unrolled loop)
   lattice_top16(sh, nf, [&](auto &&f) { visit_row<E, true, NT>(z, n, f); }, bv, bi);
-  m_out = sh.ms[2 * L::NW];
-  s_out = sh.ms[2 * L::NW + 1];
+  if (w != 0) return;
+  m = sh.ms[0];
+  s = sh.ms[1];
+#pragma unroll 1
+  for (int k = 1; k < L::NW; ++k) ms_merge(m, s, sh.ms[2 * k], sh.ms[2 * k + 1], c);
+  m_out = m;
+  s_out = s;
 }
 
 // Wave 0 with the row's 16 best pairs (lane r holds the r-th in bv, bi) and its
