@@ -411,6 +411,9 @@ def main():
                     help="one GPU's share of a vocabulary-sharded verifier: the workload with "
                          "V / N columns per row (the statistics exchange between shards is not "
                          "part of the step)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="the workload with this many prefixes instead of its own B (a sweep of "
+                         "batch sizes over one row shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (for counter calibration)")
@@ -451,6 +454,9 @@ def main():
         import dataclasses
         cfg = dataclasses.replace(cfg, V=cfg.V // args.vocab_shards,
                                   name="%s_vshard%d" % (cfg.name, args.vocab_shards))
+    if args.batch > 0:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, B=args.batch, name="%s_B%d" % (cfg.name, args.batch))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pooled = cfg.layout == "pooled"
