@@ -3,7 +3,7 @@
 * The SplitMix64 output function against the published outputs of the
   generator started from state 0 (tests/golden/splitmix64_seed0.txt).
 * The four-fold key composition and the 53-bit uniform against a third,
-  independent big-integer implementation written here.
+  independent big-integer implementation (tests/hash_ref.py).
 """
 import os
 import random
@@ -11,9 +11,9 @@ import random
 import numpy as np
 import pytest
 
+from hash_ref import GOLDEN, M64, key as _py_key
+
 HERE = os.path.dirname(os.path.abspath(__file__))
-M64 = (1 << 64) - 1
-GOLDEN = 0x9E3779B97F4A7C15
 
 
 def _load_golden():
@@ -26,19 +26,6 @@ def _load_golden():
             n, h = line.split()
             rows.append((int(n), int(h, 16)))
     return rows
-
-
-def _py_mix(x):
-    # SplitMix64 output function with Python integers (arbitrary precision,
-    # reduced mod 2^64 after every step)
-    z = (x + GOLDEN) & M64
-    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & M64
-    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M64
-    return z ^ (z >> 31)
-
-
-def _py_key(seed, row, pos, purpose):
-    return _py_mix(_py_mix(_py_mix(_py_mix(seed) ^ row) ^ pos) ^ purpose)
 
 
 def test_published_splitmix64_sequence(orc):
