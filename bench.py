@@ -625,8 +625,10 @@ def main():
         bi = svd.KERNELS.index("beta")
         ms_beta = ms_all[bi] / max(launches_all[bi], 1)
         gbps = positions * 2 * V * es / (ms_beta * 1e-3) / 1e9
+        ci = svd.KERNELS.index("beta_combine")  # few row pairs: the slices' sums added
+        ms_comb = ms_all[ci] / launches_all[ci] if launches_all[ci] else 0.0
         result["beta"] = {"kernel": "kr_beta", "ms": ms_beta, "achieved": gbps, "unit": "GB/s",
-                          "frac": gbps / HBM_PEAK_GBPS}
+                          "frac": gbps / HBM_PEAK_GBPS, "combine_ms": ms_comb}
         result["config"]["beta"] = True
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, cfg, cfg.seed, args.mode, pooled, want_beta=args.beta)

@@ -45,7 +45,8 @@ enum {
   SVD_KERNEL_ROWSTATS_SPLIT = 12, /* split rows: statistics of each slice of a row pair  */
   SVD_KERNEL_ROWSTATS_LIVE = 13,  /* early exit: slices of the live prefixes' row pairs   */
   SVD_KERNEL_ADL = 14,       /* adaptive draft length: next window per prefix            */
-  SVD_KERNEL_COUNT = 15
+  SVD_KERNEL_BETA_COMBINE = 15, /* split rows: beta from its slices' sums               */
+  SVD_KERNEL_COUNT = 16
 };
 
 int svd_profile_enable(unsigned kernel_mask);

@@ -36,7 +36,7 @@ SVD_MAX_K, SVD_MAX_GAMMA = 64, 4096
 # kernel ids of the timing build (SVD_KERNEL_* in include/svd_timing.h)
 KERNELS = ("rowstats", "select", "draw_pass", "draw_pick", "beta", "mark", "pool_stats",
            "alpha_rows", "lattice", "beam", "lattice_len", "combine", "rowstats_split",
-           "rowstats_live", "adl")
+           "rowstats_live", "adl", "beta_combine")
 SVD_RULE_STANDARD, SVD_RULE_GREEDY = 0, 1
 
 C_EXPORTS = ("svd_workspace_bytes", "svd_verify", "svd_select_and_verify", "svd_greedy_verify",

@@ -418,9 +418,19 @@ int enqueue_rows(const Batch<E> &a, hipStream_t s, CallTimer &tm) {
                    a.row_base, a.alive);
     }
   }
-  if (a.beta)
-    SVD_LAUNCH(tm, SVD_KERNEL_BETA, s, kr_beta<E, kVec>, dim3(rp), dim3(kBlock), s, a.p, a.q, a.G,
-               a.V, a.cp, a.cq, (const RowStats *)a.stats, a.beta);
+  if (a.beta) {
+    // few row pairs: slices, as for the statistics, then their sums added
+    int S, slice;
+    split_plan<E>(a, rp, S, slice);
+    float *part = reinterpret_cast<float *>(a.part);  // free again once the stream is merged
+    SVD_LAUNCH(tm, SVD_KERNEL_BETA, s, kr_beta<E, kVec>, dim3((unsigned)(rp * S)), dim3(kBlock),
+               s, a.p, a.q, a.G, a.V, a.cp, a.cq, (const RowStats *)a.stats, S, slice, a.beta,
+               part);
+    if (S > 1)
+      SVD_LAUNCH(tm, SVD_KERNEL_BETA_COMBINE, s, kr_beta_combine,
+                 dim3((unsigned)((rp + kBlock - 1) / kBlock)), dim3(kBlock), s, (int64_t)rp, S,
+                 (const float *)part, a.beta);
+  }
   return SVD_OK;
 }
 
