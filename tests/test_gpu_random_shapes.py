@@ -1,0 +1,147 @@
+"""GPU parity over seeded random shapes: 48 configurations drawn once from a
+fixed generator, each run through the library and compared with the oracle on
+every prefix (parity_harness rules: decisions exact unless flagged as a
+near-tie, alpha, scores and beta within their tolerances).
+
+The draws mix what the fixed cases take one at a time: prefix counts on both
+sides of the split-row threshold (1024 scored positions) and of the small
+draw segments (fewer than 768 pass workgroups of 8192 tokens), vocabularies
+with and without 16-byte rows, fp32 and bf16 logits, distinct verifier and
+drafter temperatures, both acceptance rules, and beta on some standard cases.
+A second set takes the windowed entry point the same way: ragged windows, an
+EOS token planted in the drafts, and early exit on one-draft cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import check_ranges, gen, host, host_inputs, require_gpu, say
+from parity_harness import compare
+
+pytestmark = pytest.mark.gpu
+
+MAX_ELEMS = 3_000_000  # logits per case, so the oracle stays quick
+
+
+def _cases(n=48, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        V = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 5000)),
+                            int(rng.integers(5000, 70000))]))
+        if rng.random() < 0.4:
+            V = max(8, V - V % 8)  # whole 16-byte rows (bf16)
+        K = int(rng.choice([1, 1, 2, 3, 8]))
+        G = int(rng.choice([1, 2, 4, 8, 16, 33]))
+        B = int(rng.choice([1, 2, 5, 16, 48, 130]))
+        while B > 1 and B * K * (G + 1) * V > MAX_ELEMS:
+            B //= 2
+        if B * K * (G + 1) * V > MAX_ELEMS:
+            continue
+        dt = "f32" if rng.random() < 0.3 else "bf16"
+        tp = float(np.float32(rng.choice([0.4, 0.7, 1.0, 1.6])))
+        tq = tp if rng.random() < 0.5 else float(np.float32(rng.choice([0.5, 0.9, 1.3])))
+        rule = "greedy" if rng.random() < 0.3 else "standard"
+        beta = rule == "standard" and tq == tp and rng.random() < 0.3
+        out.append((len(out), B, K, G, V, dt, tp, tq, rule, beta))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "c%d_B%d_K%d_G%d_V%d_%s_%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], c[8]))
+def test_random_shapes_match_oracle(orc, case):
+    svd = require_gpu()
+    i, B, K, G, V, dt, tp, tq, rule, beta = case
+    say("case", case)
+    cfg = W.Config(120 + i, "custom", B=B, K=K, gamma=G, V=V, dtype=dt, sigma0=1.0,
+                   sigma_step=0.03, temp=tp, boost=5.0, boost_prob=0.7)
+    d = gen(cfg, data_seed=1000 + i)
+    seed, row_base = 77 + i, 5 * i
+    if rule == "greedy":
+        out = svd.greedy_select_and_verify(d["p"], d["drafts"], temp_p=tp, seed=seed,
+                                           row_base=row_base, want_alpha=True, want_scores=True)
+    else:
+        out = svd.select_and_verify(d["p"], d["q"], d["drafts"], temp_p=tp, temp_q=tq, seed=seed,
+                                    row_base=row_base, want_alpha=True, want_beta=beta,
+                                    want_scores=True)
+    torch.cuda.synchronize()
+    g = host(out)
+    check_ranges(g, K, G, V)
+    hp, hq, hd = host_inputs(d)
+    rep = compare(orc, hp, hq, hd, g, tp, tq, seed, row_base=row_base, greedy=rule == "greedy")
+    say(rep.summary())
+    assert rep.prefixes == B
+    assert rep.ok(), rep.failures[:5]
+    assert rep.excused_within(), rep.summary()
+
+
+def _window_cases(n=32, seed=4711):
+    # the windowed entry point: ragged windows, an EOS token planted in the
+    # drafts, early exit (one draft per prefix) on half of the one-draft cases
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        V = int(rng.choice([int(rng.integers(2, 3000)), int(rng.integers(3000, 40000))]))
+        if rng.random() < 0.5:
+            V = max(8, V - V % 8)
+        K = int(rng.choice([1, 1, 2, 4]))
+        G = int(rng.choice([2, 5, 8, 12, 20]))
+        B = int(rng.choice([1, 3, 20, 70, 300]))
+        while B > 1 and B * K * (G + 1) * V > MAX_ELEMS:
+            B //= 2
+        if B * K * (G + 1) * V > MAX_ELEMS:
+            continue
+        dt = "f32" if rng.random() < 0.3 else "bf16"
+        rule = "greedy" if rng.random() < 0.4 else "standard"
+        ragged = rng.random() < 0.7
+        use_eos = rng.random() < 0.6
+        early = K == 1 and rng.random() < 0.5
+        tq = 0.9 if rng.random() < 0.5 else 1.2
+        out.append((len(out), B, K, G, V, dt, rule, ragged, use_eos, early, tq))
+    return out
+
+
+WINDOW_CASES = _window_cases()
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "w%d_B%d_K%d_G%d_V%d_%s_%s%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], "_early" if c[9] else ""))
+def test_random_windows_match_oracle(orc, case):
+    svd = require_gpu()
+    i, B, K, G, V, dt, rule, ragged, use_eos, early, tq = case
+    say("window case", case)
+    tp = 0.9
+    cfg = W.Config(200 + i, "custom", B=B, K=K, gamma=G, V=V, dtype=dt, sigma0=0.8,
+                   sigma_step=0.02, temp=tp, boost=5.0, boost_prob=0.8)
+    d = gen(cfg, data_seed=3000 + i)
+    rng = np.random.default_rng(i)
+    gb = rng.integers(1, G + 1, B).astype(np.int32) if ragged else None
+    hd = W.to_host(d["drafts"]).copy()
+    eos = -1
+    if use_eos:
+        eos = int(np.bincount(hd.ravel(), minlength=V).argmax())
+        hd[rng.random(hd.shape) < 0.1] = eos
+        d["drafts"] = torch.from_numpy(hd).cuda()
+    seed, row_base = 500 + i, 3 * i
+    out = svd.verify_window(d["p"], d["q"], d["drafts"],
+                            gamma_b=None if gb is None else torch.from_numpy(gb).cuda(), eos=eos,
+                            rule=rule, early_exit=early, temp_p=tp, temp_q=tq, seed=seed,
+                            row_base=row_base, want_alpha=True, want_scores=not early)
+    torch.cuda.synchronize()
+    g = host(out)
+    ok = g["selected"] >= 0
+    assert np.all((g["accept_len"][ok] >= 0) & (g["accept_len"][ok] <= G))
+    assert np.all((g["next_token"][ok] >= -2) & (g["next_token"][ok] < V))
+    if early:  # alpha is streamed only up to each prefix's first rejection: decisions only
+        g = dict(g, alpha=None)
+    win = dict(gamma_b=np.full(B, G, np.int32) if gb is None else gb, eos=eos)
+    rep = compare(orc, W.to_host(d["p"]), W.to_host(d["q"]), hd, g, tp, tq, seed,
+                  row_base=row_base, greedy=rule == "greedy", window=win)
+    say(rep.summary())
+    assert rep.prefixes == B
+    assert rep.ok(), rep.failures[:5]
+    assert rep.excused_within(), rep.summary()
