@@ -9,7 +9,9 @@ draw segments (fewer than 768 pass workgroups of 8192 tokens), vocabularies
 with and without 16-byte rows, fp32 and bf16 logits, distinct verifier and
 drafter temperatures, both acceptance rules, and beta on some standard cases.
 A second set takes the windowed entry point the same way: ragged windows, an
-EOS token planted in the drafts, and early exit on one-draft cases.
+EOS token planted in the drafts, and early exit on one-draft cases.  A third
+takes the shared-row entry point with random index tables into pools drawn
+from the generated rows: shared rows, repeated rows and rows nobody reads.
 """
 import numpy as np
 import pytest
@@ -144,4 +146,68 @@ def test_random_windows_match_oracle(orc, case):
     say(rep.summary())
     assert rep.prefixes == B
     assert rep.ok(), rep.failures[:5]
+    assert rep.excused_within(), rep.summary()
+
+
+def _pool_cases(n=24, seed=9090):
+    # the shared-row entry point: pools smaller or larger than the rows the
+    # index tables read (shared rows, and rows nobody reads)
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        V = int(rng.choice([int(rng.integers(2, 3000)), int(rng.integers(3000, 60000))]))
+        if rng.random() < 0.5:
+            V = max(8, V - V % 8)
+        K = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 3, 8, 16]))
+        B = int(rng.choice([1, 4, 16, 60]))
+        while B > 1 and B * K * (G + 1) * V > MAX_ELEMS:
+            B //= 2
+        if B * K * (G + 1) * V > MAX_ELEMS:
+            continue
+        share = float(rng.choice([0.3, 1.0, 1.5]))  # pool rows per indexed row
+        dt = "f32" if rng.random() < 0.3 else "bf16"
+        rule = "greedy" if rng.random() < 0.4 else "standard"
+        tq = 0.8 if rng.random() < 0.5 else 1.1
+        out.append((len(out), B, K, G, V, dt, rule, share, tq))
+    return out
+
+
+POOL_CASES = _pool_cases()
+
+
+@pytest.mark.parametrize("case", POOL_CASES, ids=lambda c: "p%d_B%d_K%d_G%d_V%d_%s_%s" % c[:7])
+def test_random_pools_match_oracle(orc, case):
+    svd = require_gpu()
+    i, B, K, G, V, dt, rule, share, tq = case
+    say("pool case", case)
+    tp = 0.8
+    cfg = W.Config(300 + i, "custom", B=B, K=K, gamma=G, V=V, dtype=dt, sigma0=0.7,
+                   sigma_step=0.0, temp=tp, boost=5.0, boost_prob=0.8)
+    d = gen(cfg, data_seed=5000 + i)
+    rng = np.random.default_rng(100 + i)
+    prow, qrow = d["p"].reshape(-1, V), d["q"].reshape(-1, V)
+    NP = max(1, int(prow.shape[0] * share))
+    NQ = max(1, int(qrow.shape[0] * share))
+    # pools drawn from the generated rows (repeats allowed), indices into them
+    p_pool = prow[torch.from_numpy(rng.integers(0, prow.shape[0], NP)).cuda()].contiguous()
+    q_pool = qrow[torch.from_numpy(rng.integers(0, qrow.shape[0], NQ)).cuda()].contiguous()
+    pi = rng.integers(0, NP, (B, K, G + 1)).astype(np.int32)
+    qi = rng.integers(0, NQ, (B, K, G)).astype(np.int32)
+    seed, row_base = 900 + i, 11 * i
+    out = svd.select_and_verify_rows(p_pool, torch.from_numpy(pi).cuda(), q_pool,
+                                     torch.from_numpy(qi).cuda(), d["drafts"], rule=rule,
+                                     temp_p=tp, temp_q=tq, seed=seed, row_base=row_base,
+                                     want_alpha=True, want_scores=True)
+    torch.cuda.synchronize()
+    g = host(out)
+    check_ranges(g, K, G, V)
+    hpp, hqp = W.to_host(p_pool), W.to_host(q_pool)
+    hp, hq = np.ascontiguousarray(hpp[pi]), np.ascontiguousarray(hqp[qi])
+    rep = compare(orc, hp, hq, W.to_host(d["drafts"]), g, tp, tq, seed, row_base=row_base,
+                  greedy=rule == "greedy")
+    say(rep.summary())
+    assert rep.prefixes == B
+    assert rep.ok(), rep.failures[:5]
+    assert rep.invalid == 0
     assert rep.excused_within(), rep.summary()
