@@ -11,7 +11,8 @@ drafter temperatures, both acceptance rules, and beta on some standard cases.
 A second set takes the windowed entry point the same way: ragged windows, an
 EOS token planted in the drafts, and early exit on one-draft cases.  A third
 takes the shared-row entry point with random index tables into pools drawn
-from the generated rows: shared rows, repeated rows and rows nobody reads.
+from the generated rows: shared rows, repeated rows and rows nobody reads.  The
+last runs the causal-consistency path search (lattice, then a beam over it).
 """
 import numpy as np
 import pytest
@@ -211,3 +212,86 @@ def test_random_pools_match_oracle(orc, case):
     assert rep.ok(), rep.failures[:5]
     assert rep.invalid == 0
     assert rep.excused_within(), rep.summary()
+
+
+CUM_EPS = 1e-5   # a running sum this close to tau may cut either way
+RANK_EPS = 1e-4  # expansions this close in score may rank either way
+
+
+def _cps_cases(n=24, seed=31337):
+    # causal-consistency path search: the lattice (tau cut, M_max, EOS) and a
+    # beam over it, on rows of the register, streamed and split forms
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        V = int(rng.choice([int(rng.integers(2, 2000)), int(rng.integers(2000, 160000))]))
+        if rng.random() < 0.6:
+            V = max(8, V - V % 8)
+        G = int(rng.choice([1, 3, 8, 16, 20]))
+        B = int(rng.choice([1, 2, 6, 16, 40]))
+        while B > 1 and B * G * V > MAX_ELEMS:
+            B //= 2
+        if B * G * V > MAX_ELEMS:
+            continue
+        dt = "f32" if rng.random() < 0.3 else "bf16"
+        tau = float(rng.choice([0.3, 0.6, 0.8, 0.95]))
+        m_max = int(rng.choice([1, 3, 8, 15, 16]))
+        beam = int(rng.choice([1, 2, 3, 8]))
+        eos = int(rng.integers(0, V)) if rng.random() < 0.4 else -1
+        tq = float(rng.choice([0.7, 1.0, 1.4]))
+        out.append((len(out), B, G, V, dt, tau, m_max, beam, eos, tq))
+    return out
+
+
+CPS_CASES = _cps_cases()
+
+
+@pytest.mark.parametrize("case", CPS_CASES, ids=lambda c: "s%d_B%d_G%d_V%d_%s_m%d_b%d" % (
+    c[0], c[1], c[2], c[3], c[4], c[6], c[7]))
+def test_random_path_searches_match_oracle(case):
+    import oracle
+    svd = require_gpu()
+    i, B, G, V, dt, tau, m_max, beam, eos, tq = case
+    say("cps case", case)
+    rng = np.random.default_rng(7000 + i)
+    z = (rng.standard_normal((B, G, V)) * 2.0).astype(np.float32)
+    z[:, :, rng.integers(0, V, 3)] += 3.0
+    if eos >= 0:  # EOS on top of a few rows
+        for _ in range(max(1, B // 2)):
+            b, j = int(rng.integers(0, B)), int(rng.integers(0, G))
+            z[b, j, eos] = z[b, j].max() + 2.0
+    t = torch.from_numpy(z)
+    if dt == "bf16":
+        t = t.to(torch.bfloat16)
+        hz = t.view(torch.int16).numpy().view(np.uint16)
+    else:
+        hz = z
+    gl = svd.cps_lattice(t.cuda(), temp_q=tq, tau=tau, m_max=m_max, eos=eos)
+    g = host(gl)
+    o = oracle.cps_lattice(hz, temp_q=tq, tau=tau, m_max=m_max, eos=eos)
+    assert np.array_equal(g["len"], o["len"])
+    for b in range(B):
+        for j in range(G):
+            n_g, n_o = int(g["n_cand"][b, j]), int(o["n_cand"][b, j])
+            if n_g != n_o:
+                assert o["cum_margin"][b, j] < CUM_EPS, (b, j, n_g, n_o)
+            n = min(n_g, n_o)
+            assert np.array_equal(g["cand"][b, j, :n], o["cand"][b, j, :n]), (b, j)
+            lo = o["cand_logp"][b, j, :n]
+            assert np.all(np.abs(g["cand_logp"][b, j, :n] - lo) <= 2e-6 * np.maximum(1, np.abs(lo)))
+            assert np.all(g["cand"][b, j, n_g:] == -1)
+    # the beam over each side's own lattice, compared where neither lattice nor
+    # ranking sits within its tolerance of a tie
+    f = (rng.standard_normal((B, G, m_max, m_max)) * 0.4).astype(np.float32)
+    gb = host(svd.cps_beam(gl, torch.from_numpy(f).cuda(), lam=0.6, beam=beam))
+    ob = oracle.cps_beam(o, f, lam=0.6, beam=beam)
+    compared = 0
+    for b in range(B):
+        if np.min(o["cum_margin"][b]) < CUM_EPS or ob["rank_margin"][b] < RANK_EPS:
+            continue
+        compared += 1
+        assert np.array_equal(gb["path_len"][b], ob["path_len"][b]), b
+        assert np.array_equal(gb["paths"][b], ob["paths"][b]), b
+        live = ob["path_len"][b] > 0
+        assert np.allclose(gb["score"][b][live], ob["score"][b][live], atol=1e-3)
+    assert compared >= B // 2
