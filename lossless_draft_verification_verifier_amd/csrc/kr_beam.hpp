@@ -6,7 +6,7 @@
 // scores come in as a tensor of transition scores between consecutive
 // candidates (lambda weighs them).
 //
-// kr_cps_beam (one 256-thread workgroup per prefix): expansions (path rank,
+// kr_cps_beam (one 1024-thread workgroup per prefix): expansions (path rank,
 //   candidate rank) in fp64, each ranked against all the step's expansions in
 //   LDS by a few threads together (the earlier expansion on an exact tie, a NaN
 //   score as -inf), the best `beam` kept by rank, backpointers in LDS, paths
@@ -20,7 +20,7 @@ namespace svd {
 constexpr int kCpsBeam = 8;      // beam width, at most
 constexpr int kCpsMaxG = 1024;   // positions of a beam search, at most
 constexpr int kBeamChunk = 16;   // positions of lattice data a beam loads at once
-constexpr int kBeamBlock = 256;  // threads of a beam workgroup (one per prefix)
+constexpr int kBeamBlock = 1024;  // threads of a beam workgroup (one per prefix)
 
 // n floats from global memory into LDS by the NT threads of the workgroup,
 // 16 loads in flight per thread
@@ -55,11 +55,17 @@ __device__ __forceinline__ int expansion_rank(const double *es, int k0, int n, d
   return r;
 }
 
-// the sum of x over lanes 4q..4q+3 (T = 4) or 2q..2q+1 (T = 2), by quad
-// permutes (every lane active)
+// the sum of x over lanes Tq..Tq+T-1 (T = 16, 8 or 4), by quad permutes and,
+// past 4, rotations inside the row of 16 lanes (every lane active)
 __device__ __forceinline__ int group_sum(int x, int T) {
   x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);  // lane ^ 1
-  if (T == 4) x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+  if (T >= 8) {  // row_ror:n hands lane l the value of lane l - n (mod 16)
+    const int lo = __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false);  // lane - 4
+    const int hi = __builtin_amdgcn_update_dpp(0, x, 0x12C, 0xF, 0xF, false);  // lane + 4
+    x += (threadIdx.x & 4) ? lo : hi;
+  }
+  if (T == 16) x += __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);  // lane +- 8
   return x;
 }
 
@@ -67,7 +73,7 @@ __device__ __forceinline__ int group_sum(int x, int T) {
 // step has slot p * kCpsMax + i; slots with i past the position's candidates
 // hold NaN, which comes before nothing and is never kept, so slot order is the
 // (p, i) order the ranks use.  Every step scores its slots (one thread each),
-// then ranks each against all of them with 4 threads per slot (2 past 64
+// then ranks each against all of them with 16 threads per slot (8 past 64
 // slots), each counting over its share.
 __global__ __launch_bounds__(kBeamBlock) void kr_cps_beam(
     const int32_t *__restrict__ cand, const float *__restrict__ cand_logp,
@@ -133,9 +139,9 @@ __global__ __launch_bounds__(kBeamBlock) void kr_cps_beam(
     __syncthreads();
     const int ne = nb * nc, keep = ne < beam ? ne : beam;
     // slot e's T threads are adjacent lanes of one wave
-    const int sh = ns <= 64 ? 2 : 1, T = 1 << sh;
+    const int sh = ns <= 64 ? 4 : 3, T = 1 << sh;
     const int e = tid >> sh, part = tid & (T - 1);
-    const int per = ns >> sh;  // a multiple of 4
+    const int per = ns >> sh;  // a multiple of 2
     double v = 0.0;
     int r = 0;
     if (e < ns) {
