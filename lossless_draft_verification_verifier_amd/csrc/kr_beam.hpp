@@ -55,20 +55,6 @@ __device__ __forceinline__ int expansion_rank(const double *es, int k0, int n, d
   return r;
 }
 
-// the sum of x over lanes Tq..Tq+T-1 (T = 16, 8 or 4), by quad permutes and,
-// past 4, rotations inside the row of 16 lanes (every lane active)
-__device__ __forceinline__ int group_sum(int x, int T) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);  // lane ^ 1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);  // lane ^ 2
-  if (T >= 8) {  // row_ror:n hands lane l the value of lane l - n (mod 16)
-    const int lo = __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false);  // lane - 4
-    const int hi = __builtin_amdgcn_update_dpp(0, x, 0x12C, 0xF, 0xF, false);  // lane + 4
-    x += (threadIdx.x & 4) ? lo : hi;
-  }
-  if (T == 16) x += __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);  // lane +- 8
-  return x;
-}
-
 // One workgroup per prefix.  Expansion (parent rank p, candidate rank i) of a
 // step has slot p * kCpsMax + i; slots with i past the position's candidates
 // hold NaN, which comes before nothing and is never kept, so slot order is the

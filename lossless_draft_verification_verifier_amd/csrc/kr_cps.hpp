@@ -115,6 +115,20 @@ __device__ __forceinline__ void wave_pop16(float (&lv)[N], int (&li)[N], float &
   }
 }
 
+// the sum of x over lanes Tq..Tq+T-1 (T = 16, 8 or 4), by quad permutes and,
+// past 4, rotations inside the row of 16 lanes (every lane active)
+__device__ __forceinline__ int group_sum(int x, int T) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+  if (T >= 8) {  // row_ror:n hands lane l the value of lane l - n (mod 16)
+    const int lo = __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false);  // lane - 4
+    const int hi = __builtin_amdgcn_update_dpp(0, x, 0x12C, 0xF, 0xF, false);  // lane + 4
+    x += (threadIdx.x & 4) ? lo : hi;
+  }
+  if (T == 16) x += __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);  // lane +- 8
+  return x;
+}
+
 // row flags written by kr_lattice for kr_lattice_len
 enum : uint32_t { kRowInvalid = 1u, kRowEosTop = 2u };
 
@@ -284,14 +298,17 @@ __device__ __forceinline__ void lattice_top16(L &sh, int nf, Restream &&restream
     wave_pop16<kCpsMax>(tv, ti, v16, i16);
     if (lane < kCpsMax) sh.ak[w * kCpsMax + lane] = i16 != kNoIndex ? rank_key(v16, i16) : 0;
   } else {
-    // every listed token counts the ones ahead of it; the 16 best take their
-    // rank slots
-    for (int t = tid; t < nf; t += L::NW * 64) {
-      const uint64_t kt = sh.ck[t];
+    // every listed token counts the ones ahead of it, 16 adjacent threads per
+    // token over every 16th key, summed by DPP; the 16 best take their rank
+    // slots (the trip counts are the same in every lane: the sums need them all)
+    constexpr int kPer = L::NW * 4;  // tokens per round
+    for (int t0 = 0; t0 < nf; t0 += kPer) {
+      const int t = t0 + (tid >> 4), part = tid & 15;
+      const uint64_t kt = t < nf ? sh.ck[t] : 0;
       int r = 0;
-#pragma unroll 8
-      for (int k = 0; k < nf; ++k) r += sh.ck[k] > kt;
-      if (r < kCpsMax) sh.sk[r] = kt;
+      for (int k = part; k < nf; k += 16) r += sh.ck[k] > kt;
+      r = group_sum(r, 16);
+      if (part == 0 && t < nf && r < kCpsMax) sh.sk[r] = kt;
     }
   }
   __syncthreads();
@@ -480,10 +497,13 @@ __device__ __forceinline__ void lattice_row_regs(const typename E::elem *z, int 
   // register access in a fully unrolled loop)
   lattice_top16(sh, nf, [&](auto &&f) { visit_row<E, true, NT>(z, n, f); }, bv, bi);
   if (w != 0) return;
-  m = sh.ms[0];
-  s = sh.ms[1];
-#pragma unroll 1
-  for (int k = 1; k < L::NW; ++k) ms_merge(m, s, sh.ms[2 * k], sh.ms[2 * k + 1], c);
+  float v[2 * L::NW];  // (all read at once; the merge keeps the wave order)
+#pragma unroll
+  for (int k = 0; k < 2 * L::NW; ++k) v[k] = sh.ms[k];
+  m = v[0];
+  s = v[1];
+#pragma unroll
+  for (int k = 1; k < L::NW; ++k) ms_merge(m, s, v[2 * k], v[2 * k + 1], c);
   m_out = m;
   s_out = s;
 }

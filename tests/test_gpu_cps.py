@@ -248,6 +248,55 @@ def test_register_rows_bound_from_the_first_vectors():
         assert n >= 1 and np.all(g["cand"][0, j, :n] >= first), (j, g["cand"][0, j, :n])
 
 
+def _bf16_rows(z):
+    t = torch.from_numpy(np.ascontiguousarray(z, dtype=np.float32)).to(torch.bfloat16)
+    return t.cuda(), t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def test_register_rows_rising_maxima_and_large_logits():
+    # whole rows held in registers whose running maxima rise at every vector
+    # (each sum rescaled every time), fall from the first vector on, or tie by
+    # the hundred in bf16; and logits near 5000 at temperature 20 (32 apart in
+    # bf16, 2.3 octaves), a spread distribution far from zero
+    svd = require_gpu()
+    B, G, V = 16, 8, 152064
+    rng = np.random.default_rng(43)
+    ramp = np.arange(V, dtype=np.float32) * 1e-3
+    z = (rng.standard_normal((B, G, V)) * 2.0).astype(np.float32)
+    z[0, 0] = ramp + rng.standard_normal(V).astype(np.float32)
+    z[0, 1] = ramp[::-1] + rng.standard_normal(V).astype(np.float32)
+    z[0, 2] = ramp * 5.0  # ties in bf16: hundreds of tokens share each top value
+    q, hz = _bf16_rows(z)
+    g = host(svd.cps_lattice(q, temp_q=1.0, tau=0.9, m_max=16))
+    o = oracle.cps_lattice(hz, temp_q=1.0, tau=0.9, m_max=16)
+    assert _check_lattice(g, o, 16) <= 2
+    assert g["cand"][0, 0, 0] > V - 8192 and g["cand"][0, 1, 0] < 8192
+    z = 5000.0 + rng.standard_normal((B, G, V)).astype(np.float32) * 200.0
+    q, hz = _bf16_rows(z)
+    g = host(svd.cps_lattice(q, temp_q=20.0, tau=0.8, m_max=15))
+    o = oracle.cps_lattice(hz, temp_q=20.0, tau=0.8, m_max=15)
+    assert _check_lattice(g, o, 15) <= 2
+    assert np.mean(g["n_cand"]) > 2  # a spread distribution, not one token
+
+
+@pytest.mark.parametrize("temp", [1e-6, 1e-9])
+def test_register_rows_at_extreme_temperatures(temp):
+    # temperatures of 1e-6 and 1e-9: scaled logits z / temp * log2(e) near
+    # 1e7 and past 1e9, so each row's distribution sits on its top token (or
+    # its ties), with a row of logits below 0.009 and one with a lone 13.0
+    svd = require_gpu()
+    B, G, V = 16, 8, 152064
+    rng = np.random.default_rng(47)
+    z = (rng.standard_normal((B, G, V)) * 2.0).astype(np.float32)
+    z[0, 0] = rng.standard_normal(V).astype(np.float32) * 0.002
+    z[1, 1, 77] = 13.0  # a row past 11.6
+    q, hz = _bf16_rows(z)
+    g = host(svd.cps_lattice(q, temp_q=temp, tau=0.8, m_max=15))
+    o = oracle.cps_lattice(hz, temp_q=temp, tau=0.8, m_max=15)
+    assert _check_lattice(g, o, 15) <= 2
+    assert g["cand"][1, 1, 0] == 77
+
+
 def test_cps_on_the_shared_marginal_workload():
     # the benchmark's search at full size: the 256 shared drafter rows of the
     # shared-marginal workload (B = 16, gamma = 16, V = 152064, bf16), held in
