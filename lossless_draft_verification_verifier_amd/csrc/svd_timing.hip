@@ -48,8 +48,10 @@ int timing_launch_begin(int slot, int kernel_id, hipStream_t s) {
   const int i = P.nl[slot];
   if (i >= kProfLaunches) return -1;
   hipEvent_t *e = P.ev[slot][i];
+  // timing-only events: no system-scope fence (cache writeback and invalidate)
+  // when recorded, which would otherwise be charged to the timed launch
   for (int j = 0; j < 2; ++j)
-    if (!e[j] && hipEventCreate(&e[j]) != hipSuccess) {
+    if (!e[j] && hipEventCreateWithFlags(&e[j], hipEventDisableSystemFence) != hipSuccess) {
       e[j] = nullptr;
       return -1;
     }
