@@ -59,6 +59,14 @@ def settle(torch, stream, step, warmup, settle_ms):
             n += 1
 
 
+def run_env(torch, **seeds) -> dict:
+    """What reproduces a line: the device, the software and the seeds."""
+    prop = torch.cuda.get_device_properties(0)
+    return dict({"gpu": torch.cuda.get_device_name(0), "arch": getattr(prop, "gcnArchName", None),
+                 "compute_units": prop.multi_processor_count, "torch": torch.__version__,
+                 "hip": getattr(torch.version, "hip", None)}, **seeds)
+
+
 def kernel_samples(steps: int) -> int:
     """Steps whose dominant-kernel launches are timed: at least 5, whatever --steps is."""
     return max(5, min(steps, 20))
@@ -379,6 +387,7 @@ def bench_cps(args, torch, svd, W):
                      "bytes_per_unit": unit, "units_per_launch": rows,
                      "ms_per_launch": ms_lat, "sampled_steps": nsamp},
         "mean_lattice_width": float(lat["n_cand"].float().mean().item()),
+        "env": run_env(torch, data_seed=cfg.data_seed, fluency_seed=cfg.data_seed + 5),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cps_cpu_baseline(W.to_host(q), flu.cpu().numpy(), cfg)
@@ -620,6 +629,7 @@ def main():
         "mean_accept_len": float(L_host.mean()),
         "mat": float(L_host.mean() + 1.0),
         "wall_s": wall,
+        "env": run_env(torch, data_seed=cfg.data_seed, seed=cfg.seed, row_base=0),
     }
     if args.beta:  # the second pass over every scored row pair (logit bytes of both rows)
         bi = svd.KERNELS.index("beta")
