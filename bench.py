@@ -67,6 +67,31 @@ def run_env(torch, **seeds) -> dict:
                  "hip": getattr(torch.version, "hip", None)}, **seeds)
 
 
+def time_adl(torch, svd, stream, drafts, sel, L, B, K, G, calls=200):
+    """svd_adl_next on a windowed call's inputs and outputs: microseconds per
+    call over `calls` calls back to back on the call's stream (after 20 untimed)."""
+    dev = drafts.device
+    avg = torch.full((B, 2), 256 * G, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def call():
+        rc = svd.svd_adl_next(drafts, sel, L, None, -1, B, K, G, 1, G, 4, 2, 64, avg, nxt,
+                              stream.cuda_stream)
+        if rc != svd.SVD_OK:
+            raise svd.SvdError(rc, "svd_adl_next")
+
+    for _ in range(20):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"kernel": "kr_adl", "us_per_call": e0.elapsed_time(e1) * 1e3 / calls,
+            "calls": calls, "prefixes": B}
+
+
 def kernel_samples(steps: int) -> int:
     """Steps whose dominant-kernel launches are timed: at least 5, whatever --steps is."""
     return max(5, min(steps, 20))
@@ -631,6 +656,8 @@ def main():
         "wall_s": wall,
         "env": run_env(torch, data_seed=cfg.data_seed, seed=cfg.seed, row_base=0),
     }
+    if early:  # the window controller that follows a windowed call (one thread per prefix)
+        result["adl"] = time_adl(torch, svd, stream, d["drafts"], sel, L, B, K, G)
     if args.beta:  # the second pass over every scored row pair (logit bytes of both rows)
         bi = svd.KERNELS.index("beta")
         ms_beta = ms_all[bi] / max(launches_all[bi], 1)
