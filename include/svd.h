@@ -73,8 +73,16 @@
 extern "C" {
 #endif
 
-/* element type of both logit arrays (p and q share one) */
-typedef enum { SVD_F32 = 0, SVD_BF16 = 1 } svd_dtype_t;
+/* element type of both logit arrays (p and q share one).  The two range
+ * markers give the type every int32 value, so that any value a caller passes
+ * is a valid argument, rejected by the checks (SVD_EDTYPE) when it names no
+ * type. */
+typedef enum {
+  SVD_F32 = 0,
+  SVD_BF16 = 1,
+  SVD_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  SVD_DTYPE_RANGE_MAX_ = 2147483647
+} svd_dtype_t;
 
 enum {
   SVD_OK = 0,
@@ -192,7 +200,12 @@ int svd_greedy_select_and_verify(const void *p_logits, const int32_t *drafts, sv
  * standard rule); the workspace is svd_rows_workspace_bytes(B, K, gamma, V,
  * n_p_rows, n_q_rows) bytes (0 for sizes out of range).  No beta output.
  */
-typedef enum { SVD_RULE_STANDARD = 0, SVD_RULE_GREEDY = 1 } svd_rule_t;
+typedef enum {
+  SVD_RULE_STANDARD = 0,
+  SVD_RULE_GREEDY = 1,
+  SVD_RULE_RANGE_MIN_ = -2147483647 - 1, /* any int32 is a valid argument, rejected */
+  SVD_RULE_RANGE_MAX_ = 2147483647       /* (SVD_EINVAL) unless it names a rule */
+} svd_rule_t;
 size_t svd_rows_workspace_bytes(int64_t B, int32_t K, int32_t gamma, int32_t V,
                                 int64_t n_p_rows, int64_t n_q_rows);
 int svd_select_and_verify_rows(svd_rule_t rule, const void *p_rows, int64_t n_p_rows,
@@ -332,9 +345,9 @@ int svd_adl_next(const int32_t *drafts, const int32_t *selected, const int32_t *
  * current, so hip_stream must belong to the current device.
  *   - SVD_ESCRATCH when svd_workspace_bytes(B, K, gamma, V) exceeds
  *     SVD_NOALLOC_SCRATCH_BYTES (16 MiB: at gamma = 8 and V = 152064, up to
- *     about 1000 prefixes), SVD_EINVAL for sizes svd_workspace_bytes rejects;
- *     both before any HIP call.  Other errors as for svd_select_and_verify,
- *     and SVD_EHIP when the array's address cannot be found.
+ *     about 1000 prefixes); every argument error as for svd_select_and_verify;
+ *     all of them before any HIP call.  SVD_EHIP when the array's address
+ *     cannot be found.
  *   - Every call on one GPU shares that GPU's array, which keeps the last
  *     call's contents; each call writes every part it reads before reading it.
  *     Calls that overlap on one GPU (on different streams, or from different

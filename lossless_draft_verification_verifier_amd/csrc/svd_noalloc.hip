@@ -50,6 +50,14 @@ extern "C" int svd_select_and_verify_noalloc(
   const size_t need = svd_workspace_bytes(B, K, gamma, V);
   if (need == 0) return SVD_EINVAL;
   if (need > kScratchBytes) return SVD_ESCRATCH;
+  // every other check too: with a zero-byte workspace (at a fake, never used,
+  // aligned address) the checked entry point stops at the workspace's size
+  // once the arguments pass, before any HIP call
+  const int pre = svd_select_and_verify(p_logits, q_logits, drafts, dtype, B, K, gamma, V, temp_p,
+                                        temp_q, seed, row_base, selected, accept_len, next_token,
+                                        scores, alpha, beta, reinterpret_cast<void *>(uintptr_t{256}),
+                                        0, hip_stream);
+  if (pre != SVD_EWORKSPACE) return pre;
   void *ws = nullptr;
   const int rc = scratch_on_current_device(&ws);
   if (rc != SVD_OK) return rc;

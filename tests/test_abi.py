@@ -194,6 +194,13 @@ def test_noalloc_host_side_errors(svd):
     assert call(2048, 1, 8, 152064) == svd.SVD_ESCRATCH
     for bad in [(0, 1, 8, 100), (1, 65, 8, 100), (1, 1, 0, 100), (1, 1, 8, 0)]:
         assert call(*bad) == svd.SVD_EINVAL, bad
+    # every other argument error too, before the scratch array's lookup (a HIP call)
+    def call2(dtype=svd.SVD_BF16, tp=1.0, sel=16384):
+        return svd.svd_select_and_verify_noalloc(4096, 8192, 12288, dtype, 2, 1, 8, 100, tp, 1.0,
+                                                 0, 0, sel, 20480, 24576, None, None, None, None)
+    assert call2(dtype=5) == svd.SVD_EDTYPE
+    assert call2(tp=0.0) == svd.SVD_EINVAL
+    assert call2(sel=None) == svd.SVD_EINVAL
     text = open(HEADER).read()
     assert "#define SVD_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
     assert svd.SVD_NOALLOC_SCRATCH_BYTES == 16 << 20
