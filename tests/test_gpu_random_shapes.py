@@ -1,5 +1,5 @@
-"""GPU parity over seeded random shapes: 48 configurations drawn once from a
-fixed generator, each run through the library and compared with the oracle on
+"""GPU parity over seeded random shapes: 96 configurations drawn once from two
+fixed generators, each run through the library and compared with the oracle on
 every prefix (parity_harness rules: decisions exact unless flagged as a
 near-tie, alpha, scores and beta within their tolerances).
 
@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 MAX_ELEMS = 3_000_000  # logits per case, so the oracle stays quick
 
 
-def _cases(n=48, seed=2026):
+def _cases(n=48, seed=2026, first=0):
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
@@ -47,11 +47,11 @@ def _cases(n=48, seed=2026):
         tq = tp if rng.random() < 0.5 else float(np.float32(rng.choice([0.5, 0.9, 1.3])))
         rule = "greedy" if rng.random() < 0.3 else "standard"
         beta = rule == "standard" and tq == tp and rng.random() < 0.3
-        out.append((len(out), B, K, G, V, dt, tp, tq, rule, beta))
+        out.append((first + len(out), B, K, G, V, dt, tp, tq, rule, beta))
     return out
 
 
-CASES = _cases()
+CASES = _cases() + _cases(48, seed=3037, first=48)
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "c%d_B%d_K%d_G%d_V%d_%s_%s" % (
@@ -82,7 +82,7 @@ def test_random_shapes_match_oracle(orc, case):
     assert rep.excused_within(), rep.summary()
 
 
-def _window_cases(n=32, seed=4711):
+def _window_cases(n=32, seed=4711, first=0):
     # the windowed entry point: ragged windows, an EOS token planted in the
     # drafts, early exit (one draft per prefix) on half of the one-draft cases
     rng = np.random.default_rng(seed)
@@ -104,11 +104,11 @@ def _window_cases(n=32, seed=4711):
         use_eos = rng.random() < 0.6
         early = K == 1 and rng.random() < 0.5
         tq = 0.9 if rng.random() < 0.5 else 1.2
-        out.append((len(out), B, K, G, V, dt, rule, ragged, use_eos, early, tq))
+        out.append((first + len(out), B, K, G, V, dt, rule, ragged, use_eos, early, tq))
     return out
 
 
-WINDOW_CASES = _window_cases()
+WINDOW_CASES = _window_cases() + _window_cases(32, seed=5821, first=32)
 
 
 @pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "w%d_B%d_K%d_G%d_V%d_%s_%s%s" % (
@@ -150,7 +150,7 @@ def test_random_windows_match_oracle(orc, case):
     assert rep.excused_within(), rep.summary()
 
 
-def _pool_cases(n=24, seed=9090):
+def _pool_cases(n=24, seed=9090, first=0):
     # the shared-row entry point: pools smaller or larger than the rows the
     # index tables read (shared rows, and rows nobody reads)
     rng = np.random.default_rng(seed)
@@ -170,11 +170,11 @@ def _pool_cases(n=24, seed=9090):
         dt = "f32" if rng.random() < 0.3 else "bf16"
         rule = "greedy" if rng.random() < 0.4 else "standard"
         tq = 0.8 if rng.random() < 0.5 else 1.1
-        out.append((len(out), B, K, G, V, dt, rule, share, tq))
+        out.append((first + len(out), B, K, G, V, dt, rule, share, tq))
     return out
 
 
-POOL_CASES = _pool_cases()
+POOL_CASES = _pool_cases() + _pool_cases(24, seed=9191, first=24)
 
 
 @pytest.mark.parametrize("case", POOL_CASES, ids=lambda c: "p%d_B%d_K%d_G%d_V%d_%s_%s" % c[:7])
@@ -218,7 +218,7 @@ CUM_EPS = 1e-5   # a running sum this close to tau may cut either way
 RANK_EPS = 1e-4  # expansions this close in score may rank either way
 
 
-def _cps_cases(n=24, seed=31337):
+def _cps_cases(n=24, seed=31337, first=0):
     # causal-consistency path search: the lattice (tau cut, M_max, EOS) and a
     # beam over it, on rows of the register, streamed and split forms
     rng = np.random.default_rng(seed)
@@ -239,11 +239,11 @@ def _cps_cases(n=24, seed=31337):
         beam = int(rng.choice([1, 2, 3, 8]))
         eos = int(rng.integers(0, V)) if rng.random() < 0.4 else -1
         tq = float(rng.choice([0.7, 1.0, 1.4]))
-        out.append((len(out), B, G, V, dt, tau, m_max, beam, eos, tq))
+        out.append((first + len(out), B, G, V, dt, tau, m_max, beam, eos, tq))
     return out
 
 
-CPS_CASES = _cps_cases()
+CPS_CASES = _cps_cases() + _cps_cases(24, seed=27182, first=24)
 
 
 @pytest.mark.parametrize("case", CPS_CASES, ids=lambda c: "s%d_B%d_G%d_V%d_%s_m%d_b%d" % (
