@@ -1,5 +1,5 @@
-"""GPU parity over seeded random shapes: 96 configurations drawn once from two
-fixed generators, each run through the library and compared with the oracle on
+"""GPU parity over seeded random shapes: 112 configurations drawn once from
+three fixed generators (the third at full-size vocabularies), each run through the library and compared with the oracle on
 every prefix (parity_harness rules: decisions exact unless flagged as a
 near-tie, alpha, scores and beta within their tolerances).
 
@@ -27,20 +27,22 @@ pytestmark = pytest.mark.gpu
 MAX_ELEMS = 3_000_000  # logits per case, so the oracle stays quick
 
 
-def _cases(n=48, seed=2026, first=0):
+def _cases(n=48, seed=2026, first=0, max_elems=MAX_ELEMS, large=False):
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
         V = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 5000)),
                             int(rng.integers(5000, 70000))]))
+        if large:  # vocabularies at full size
+            V = int(rng.integers(100000, 160001))
         if rng.random() < 0.4:
             V = max(8, V - V % 8)  # whole 16-byte rows (bf16)
         K = int(rng.choice([1, 1, 2, 3, 8]))
         G = int(rng.choice([1, 2, 4, 8, 16, 33]))
         B = int(rng.choice([1, 2, 5, 16, 48, 130]))
-        while B > 1 and B * K * (G + 1) * V > MAX_ELEMS:
+        while B > 1 and B * K * (G + 1) * V > max_elems:
             B //= 2
-        if B * K * (G + 1) * V > MAX_ELEMS:
+        if B * K * (G + 1) * V > max_elems:
             continue
         dt = "f32" if rng.random() < 0.3 else "bf16"
         tp = float(np.float32(rng.choice([0.4, 0.7, 1.0, 1.6])))
@@ -51,7 +53,8 @@ def _cases(n=48, seed=2026, first=0):
     return out
 
 
-CASES = _cases() + _cases(48, seed=3037, first=48)
+CASES = (_cases() + _cases(48, seed=3037, first=48) +
+         _cases(16, seed=6151, first=96, max_elems=30_000_000, large=True))
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "c%d_B%d_K%d_G%d_V%d_%s_%s" % (
@@ -82,7 +85,7 @@ def test_random_shapes_match_oracle(orc, case):
     assert rep.excused_within(), rep.summary()
 
 
-def _window_cases(n=32, seed=4711, first=0):
+def _window_cases(n=32, seed=4711, first=0, max_elems=MAX_ELEMS):
     # the windowed entry point: ragged windows, an EOS token planted in the
     # drafts, early exit (one draft per prefix) on half of the one-draft cases
     rng = np.random.default_rng(seed)
@@ -94,9 +97,9 @@ def _window_cases(n=32, seed=4711, first=0):
         K = int(rng.choice([1, 1, 2, 4]))
         G = int(rng.choice([2, 5, 8, 12, 20]))
         B = int(rng.choice([1, 3, 20, 70, 300]))
-        while B > 1 and B * K * (G + 1) * V > MAX_ELEMS:
+        while B > 1 and B * K * (G + 1) * V > max_elems:
             B //= 2
-        if B * K * (G + 1) * V > MAX_ELEMS:
+        if B * K * (G + 1) * V > max_elems:
             continue
         dt = "f32" if rng.random() < 0.3 else "bf16"
         rule = "greedy" if rng.random() < 0.4 else "standard"
@@ -150,7 +153,7 @@ def test_random_windows_match_oracle(orc, case):
     assert rep.excused_within(), rep.summary()
 
 
-def _pool_cases(n=24, seed=9090, first=0):
+def _pool_cases(n=24, seed=9090, first=0, max_elems=MAX_ELEMS):
     # the shared-row entry point: pools smaller or larger than the rows the
     # index tables read (shared rows, and rows nobody reads)
     rng = np.random.default_rng(seed)
@@ -162,9 +165,9 @@ def _pool_cases(n=24, seed=9090, first=0):
         K = int(rng.choice([1, 2, 4, 8]))
         G = int(rng.choice([1, 3, 8, 16]))
         B = int(rng.choice([1, 4, 16, 60]))
-        while B > 1 and B * K * (G + 1) * V > MAX_ELEMS:
+        while B > 1 and B * K * (G + 1) * V > max_elems:
             B //= 2
-        if B * K * (G + 1) * V > MAX_ELEMS:
+        if B * K * (G + 1) * V > max_elems:
             continue
         share = float(rng.choice([0.3, 1.0, 1.5]))  # pool rows per indexed row
         dt = "f32" if rng.random() < 0.3 else "bf16"
@@ -218,7 +221,7 @@ CUM_EPS = 1e-5   # a running sum this close to tau may cut either way
 RANK_EPS = 1e-4  # expansions this close in score may rank either way
 
 
-def _cps_cases(n=24, seed=31337, first=0):
+def _cps_cases(n=24, seed=31337, first=0, max_elems=MAX_ELEMS):
     # causal-consistency path search: the lattice (tau cut, M_max, EOS) and a
     # beam over it, on rows of the register, streamed and split forms
     rng = np.random.default_rng(seed)
