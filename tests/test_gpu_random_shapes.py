@@ -1,5 +1,6 @@
 """GPU parity over seeded random shapes: 112 configurations drawn once from
-three fixed generators (the third at full-size vocabularies), each run through the library and compared with the oracle on
+three fixed generators (the third at full-size vocabularies, as are the last
+sets of the windowed and shared-row cases), each run through the library and compared with the oracle on
 every prefix (parity_harness rules: decisions exact unless flagged as a
 near-tie, alpha, scores and beta within their tolerances).
 
@@ -85,13 +86,15 @@ def test_random_shapes_match_oracle(orc, case):
     assert rep.excused_within(), rep.summary()
 
 
-def _window_cases(n=32, seed=4711, first=0, max_elems=MAX_ELEMS):
+def _window_cases(n=32, seed=4711, first=0, max_elems=MAX_ELEMS, large=False):
     # the windowed entry point: ragged windows, an EOS token planted in the
     # drafts, early exit (one draft per prefix) on half of the one-draft cases
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
         V = int(rng.choice([int(rng.integers(2, 3000)), int(rng.integers(3000, 40000))]))
+        if large:  # vocabularies at full size
+            V = int(rng.integers(100000, 160001))
         if rng.random() < 0.5:
             V = max(8, V - V % 8)
         K = int(rng.choice([1, 1, 2, 4]))
@@ -111,7 +114,8 @@ def _window_cases(n=32, seed=4711, first=0, max_elems=MAX_ELEMS):
     return out
 
 
-WINDOW_CASES = _window_cases() + _window_cases(32, seed=5821, first=32)
+WINDOW_CASES = (_window_cases() + _window_cases(32, seed=5821, first=32) +
+                _window_cases(12, seed=7607, first=64, max_elems=30_000_000, large=True))
 
 
 @pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "w%d_B%d_K%d_G%d_V%d_%s_%s%s" % (
@@ -153,13 +157,15 @@ def test_random_windows_match_oracle(orc, case):
     assert rep.excused_within(), rep.summary()
 
 
-def _pool_cases(n=24, seed=9090, first=0, max_elems=MAX_ELEMS):
+def _pool_cases(n=24, seed=9090, first=0, max_elems=MAX_ELEMS, large=False):
     # the shared-row entry point: pools smaller or larger than the rows the
     # index tables read (shared rows, and rows nobody reads)
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
         V = int(rng.choice([int(rng.integers(2, 3000)), int(rng.integers(3000, 60000))]))
+        if large:  # vocabularies at full size
+            V = int(rng.integers(100000, 160001))
         if rng.random() < 0.5:
             V = max(8, V - V % 8)
         K = int(rng.choice([1, 2, 4, 8]))
@@ -177,7 +183,8 @@ def _pool_cases(n=24, seed=9090, first=0, max_elems=MAX_ELEMS):
     return out
 
 
-POOL_CASES = _pool_cases() + _pool_cases(24, seed=9191, first=24)
+POOL_CASES = (_pool_cases() + _pool_cases(24, seed=9191, first=24) +
+              _pool_cases(8, seed=9337, first=48, max_elems=30_000_000, large=True))
 
 
 @pytest.mark.parametrize("case", POOL_CASES, ids=lambda c: "p%d_B%d_K%d_G%d_V%d_%s_%s" % c[:7])
